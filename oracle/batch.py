@@ -1,0 +1,80 @@
+"""Batched drivers of the oracle over a whole workload (CPU, float64).
+
+TEST INFRASTRUCTURE (see ``oracle/fourier_attention.py``).  These loops only
+walk the (sequence, KV head) blocks of a workload and call the per-head oracle;
+they add no arithmetic.  The workload object is duck-typed (``cfg``, ``lens``,
+``natural_kv``, ``comp_dims``, ``q``, ``f64``); nothing from the GPU library is
+imported.
+
+Query head i of a sequence reads KV head ``i // (Hq / Hkv)`` (a reading: the
+pages do not discuss grouped heads).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import fourier_attention as fa
+
+
+def project_block(w, b: int, h: int):
+    """(C_K, C_V) [k, Dc] of sequence b, KV head h; zeros when M = 0."""
+    c = w.cfg
+    K, V = w.natural_kv(b, h)
+    start, M = fa.segment(K.shape[0], c.sink, c.recent)
+    cd = w.comp_dims(h)
+    if M == 0:
+        z = np.zeros((c.n_coef, c.n_comp))
+        return z, z.copy()
+    return (fa.project(K[start:start + M][:, cd], c.n_coef),
+            fa.project(V[start:start + M][:, cd], c.n_coef))
+
+
+def project_all(w):
+    """Coefficients for every block, in the library's [B*Hkv, k, Dc] layout."""
+    c = w.cfg
+    ck = np.zeros((c.batch * c.n_kv_heads, c.n_coef, c.n_comp))
+    cv = np.zeros_like(ck)
+    for b in range(c.batch):
+        for h in range(c.n_kv_heads):
+            ck[b * c.n_kv_heads + h], cv[b * c.n_kv_heads + h] = project_block(w, b, h)
+    return ck, cv
+
+
+def decode_block(w, ck_blk, cv_blk, scale: float, b: int, h: int, heads=None):
+    """Outputs [len(heads), D] for the query heads of KV head h in sequence b.
+
+    ``heads`` defaults to all G query heads that read KV head h.
+    """
+    c = w.cfg
+    G = c.n_q_heads // c.n_kv_heads
+    if heads is None:
+        heads = list(range(h * G, (h + 1) * G))
+    K, V = w.natural_kv(b, h)
+    q = w.f64(w.q[b, heads])
+    return fa.decode(q, K, V, w.comp_dims(h), ck_blk, cv_blk,
+                     c.sink, c.recent, scale)
+
+
+def decode_all(w, ck, cv, scale: float):
+    """out [B, Hq, D] for every query row, given coefficients [B*Hkv, k, Dc]."""
+    c = w.cfg
+    G = c.n_q_heads // c.n_kv_heads
+    out = np.zeros((c.batch, c.n_q_heads, c.head_dim))
+    for b in range(c.batch):
+        for h in range(c.n_kv_heads):
+            i = b * c.n_kv_heads + h
+            out[b, h * G:(h + 1) * G] = decode_block(w, ck[i], cv[i], scale, b, h)
+    return out
+
+
+def exact_all(w, scale: float):
+    """Uncompressed attention for every query row (context only)."""
+    c = w.cfg
+    G = c.n_q_heads // c.n_kv_heads
+    out = np.zeros((c.batch, c.n_q_heads, c.head_dim))
+    for b in range(c.batch):
+        for h in range(c.n_kv_heads):
+            K, V = w.natural_kv(b, h)
+            q = w.f64(w.q[b, h * G:(h + 1) * G])
+            out[b, h * G:(h + 1) * G] = fa.exact_attention(q, K, V, scale)
+    return out

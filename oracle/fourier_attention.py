@@ -1,0 +1,148 @@
+"""CPU oracle for Fourier-approximated KV-cache decode (float64, numpy).
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The GPU library never calls it, and it
+shares no code with the GPU library: it is a plain, slow restatement of what the
+method computes, written so that each step can be checked by eye against the
+pages that describe the method.
+
+Sources (cited by title and section; no text is quoted):
+
+* [SKILL] the skill page "fourier-approximated-kv-cache" (agent-skills.jp,
+  "Beyond homogeneous attention: memory-efficient LLMs via a Fourier-approximated
+  KV cache"), sections Core concept, Architecture overview, Step 2 (Fourier-basis
+  compression), Step 3 (selective token retention), Step 4 (reconstruction during
+  decoding).
+* [ABSTRACT] "Beyond Homogeneous Attention: Memory-Efficient LLMs via
+  Fourier-Approximated KV Cache", arXiv 2506.11886, English abstract (as printed
+  on the shd-paper.top and fugumt.com pages).
+
+What the method computes, restated:
+
+1. Segmentation [SKILL Step 3]: the first ``sink`` tokens and the last
+   ``recent`` tokens stay exact; the ``M = L - sink - recent`` tokens between
+   them are the "middle".  With ``L <= sink + recent`` there is no middle and
+   every token stays exact (each token once).
+2. Dim split [SKILL Core concept, Step 3; ABSTRACT]: a per-head set of
+   compressible dims; the other dims stay exact for every token.
+3. Projection [SKILL Step 2; ABSTRACT]: each compressible dim's time series over
+   the middle tokens is projected onto ``k`` orthonormal Fourier basis functions
+   (``fourier_basis``).  The pages show a complex ``rfft`` truncated to its first
+   bins; the real orthonormal basis below spans the same space as the first
+   ``(k+1)/2`` rfft bins for odd ``k`` (pinned in the tests through numpy's
+   rfft/irfft).
+4. Reconstruction [SKILL Step 4]: the middle compressible entries are replaced by
+   ``Phi @ C`` (the real-basis form of zero-padding the kept bins and inverting).
+5. Decode: standard softmax attention of the query over the cache in which the
+   middle compressible entries are the reconstruction.
+
+Readings where the pages are silent (each is listed in the design notes too):
+basis order is the constant term, then (cos, sin) pairs of ascending frequency;
+orthonormal scaling ``sqrt(2/M)``, with ``1/sqrt(M)`` for the constant and the
+Nyquist cosine; tau = 0 is the first middle token; query head i reads KV head
+``i // (Hq/Hkv)``.
+
+Parity pins for every function here live in ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# --------------------------------------------------------------- step 1 -----
+
+def segment(L: int, sink: int, recent: int):
+    """Return (first middle token, M) for a sequence of length L [SKILL Step 3].
+
+    The middle is tokens [sink, L - recent).  When L <= sink + recent the
+    sequence has no middle (M = 0) and all L tokens are kept exactly.
+    """
+    M = max(0, L - sink - recent)
+    return sink, M
+
+
+# --------------------------------------------------------------- step 3 -----
+
+def fourier_basis(M: int, k: int) -> np.ndarray:
+    """Orthonormal real Fourier basis Phi [M, k]: Phi[tau, n] = phi_n(tau).
+
+    phi_0 is the constant; basis index n >= 1 has frequency f = ceil(n/2); odd n
+    is the cosine and even n the sine of 2 pi f tau / M.  Scale sqrt(2/M), or
+    1/sqrt(M) for the constant and for the Nyquist cosine (2f = M).  The phase
+    f*tau is reduced mod M in integer arithmetic before the trig call.
+    [ABSTRACT: orthogonal Fourier bases; SKILL Step 2.]
+    """
+    if not (1 <= k <= M):
+        raise ValueError("need 1 <= k <= M (k=%d, M=%d)" % (k, M))
+    tau = np.arange(M, dtype=np.int64)
+    n = np.arange(k, dtype=np.int64)
+    f = (n + 1) // 2
+    r = np.outer(tau, f) % M
+    angle = 2.0 * np.pi * r / M
+    use_cos = (n == 0) | (n % 2 == 1)
+    phi = np.where(use_cos[None, :], np.cos(angle), np.sin(angle))
+    scale = np.where((f == 0) | (2 * f == M), 1.0 / np.sqrt(M), np.sqrt(2.0 / M))
+    return phi * scale[None, :]
+
+
+def project(x_mid: np.ndarray, k: int) -> np.ndarray:
+    """Fourier coefficients C [k, c] = Phi^T x_mid of middle rows x_mid [M, c].
+
+    [SKILL Step 2: project the middle tokens onto k << M basis functions.]
+    """
+    x_mid = np.asarray(x_mid, dtype=np.float64)
+    Phi = fourier_basis(x_mid.shape[0], k)
+    return Phi.T @ x_mid
+
+
+# --------------------------------------------------------------- step 4 -----
+
+def reconstruct(coef: np.ndarray, M: int) -> np.ndarray:
+    """Approximate middle rows [M, c] = Phi @ coef  [SKILL Step 4]."""
+    coef = np.asarray(coef, dtype=np.float64)
+    return fourier_basis(M, coef.shape[0]) @ coef
+
+
+def approximate_cache(X: np.ndarray, comp_dims, coef, sink: int, recent: int):
+    """The cache as decode sees it: X [L, D] with the middle rows' compressible
+    dims replaced by their reconstruction from ``coef`` [k, len(comp_dims)].
+
+    Sink rows, recent rows and the exact dims are untouched [SKILL Step 3].
+    """
+    X = np.array(X, dtype=np.float64, copy=True)
+    start, M = segment(X.shape[0], sink, recent)
+    comp_dims = np.asarray(comp_dims, dtype=np.int64)
+    if M > 0 and comp_dims.size > 0:
+        X[start:start + M][:, comp_dims] = reconstruct(coef, M)
+    return X
+
+
+# --------------------------------------------------------------- step 5 -----
+
+def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                      return_probs: bool = False):
+    """out[i] = sum_t p_it V[t], p_i = softmax_t(scale * q[i] . K[t])."""
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    s = scale * (q @ np.asarray(K, dtype=np.float64).T)
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    p = e / e.sum(axis=1, keepdims=True)
+    out = p @ np.asarray(V, dtype=np.float64)
+    return (out, p) if return_probs else out
+
+
+def decode(q_rows, K, V, comp_dims, ck, cv, sink: int, recent: int, scale: float):
+    """One decode step of the query rows q_rows [G, D] that share one KV head.
+
+    K, V: [L, D] in natural dim order (their middle compressible entries are not
+    used: those come from the coefficients ck, cv [k, Dc]).  Reconstruct, then
+    attend [SKILL Step 4, then standard attention].
+    """
+    Kt = approximate_cache(K, comp_dims, ck, sink, recent)
+    Vt = approximate_cache(V, comp_dims, cv, sink, recent)
+    return softmax_attention(q_rows, Kt, Vt, scale)
+
+
+def exact_attention(q_rows, K, V, scale: float):
+    """Uncompressed attention (context only: the approximation error)."""
+    return softmax_attention(q_rows, K, V, scale)

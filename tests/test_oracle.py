@@ -1,0 +1,389 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin checks the oracle against one of: numpy's FFT (a library routine the
+pages' own code uses), closed forms, invariants of orthonormal projections and
+of softmax attention, PyTorch's CPU attention (a library routine), the pages'
+printed defaults (tests/golden/pages_facts.json) and brute force with
+pure-Python loops on tiny inputs.  ``test_mutants_are_caught`` plants plausible
+mistakes in the oracle (on the CPU) and checks that some pin fails for each.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import fourier_attention as fa
+from oracle import batch as ob
+from long_context_decode_fourier_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ------------------------------------------------------------------ pins ----
+# Each pin takes the oracle module (possibly mutated) and raises on failure.
+
+def pin_orthonormal(o):
+    """P-1: Phi^T Phi = I_k (the pages call the bases orthogonal; the abstract)."""
+    for M, k in [(1, 1), (2, 2), (3, 3), (7, 7), (8, 8), (8, 5), (416, 33),
+                 (416, 416), (1000, 201)]:
+        P = o.fourier_basis(M, k)
+        assert P.shape == (M, k)
+        err = np.abs(P.T @ P - np.eye(k)).max()
+        assert err < 1e-12, (M, k, err)
+
+
+def pin_rfft(o):
+    """P-2: coefficients equal scaled real/imag parts of numpy.fft.rfft."""
+    rng = _rng(1)
+    for M in (5, 8, 13, 416):
+        x = rng.standard_normal(M)
+        X = np.fft.rfft(x)
+        c = o.project(x[:, None], M)[:, 0]
+        assert abs(c[0] - X[0].real / math.sqrt(M)) < 1e-12
+        for j in range(1, (M + 1) // 2):
+            assert abs(c[2 * j - 1] - math.sqrt(2.0 / M) * X[j].real) < 1e-12
+            assert abs(c[2 * j] + math.sqrt(2.0 / M) * X[j].imag) < 1e-12
+        if M % 2 == 0:
+            assert abs(c[M - 1] - X[M // 2].real / math.sqrt(M)) < 1e-12
+
+
+def pin_irfft_lowpass(o):
+    """P-3: the pages' reconstruction (keep the first bins of rfft, zero-pad,
+    irfft with n = M; skill page Steps 2 and 4) equals reconstruct(project(x))
+    for k = 2P + 1 real coefficients <-> P + 1 kept bins."""
+    rng = _rng(2)
+    for M, P in [(9, 2), (16, 3), (416, 16), (4000, 200), (7, 3)]:
+        k = 2 * P + 1
+        x = rng.standard_normal((M, 3))
+        X = np.fft.rfft(x, axis=0)
+        kept = np.zeros_like(X)
+        kept[:P + 1] = X[:P + 1]
+        ref = np.fft.irfft(kept, n=M, axis=0)
+        got = o.reconstruct(o.project(x, k), M)
+        assert np.abs(got - ref).max() < 1e-12, (M, P)
+
+
+def pin_parseval_bessel(o):
+    """P-4: k = M reconstructs exactly and keeps the energy (Parseval); k < M
+    loses energy (Bessel) and leaves a residual orthogonal to every basis fn."""
+    rng = _rng(3)
+    for M in (6, 7, 64, 415):
+        x = rng.standard_normal((M, 2))
+        c = o.project(x, M)
+        assert np.abs(o.reconstruct(c, M) - x).max() < 1e-11
+        assert abs((c ** 2).sum() - (x ** 2).sum()) < 1e-9 * (x ** 2).sum()
+        k = max(1, M // 3)
+        ck = o.project(x, k)
+        assert (ck ** 2).sum() <= (x ** 2).sum() + 1e-12
+        resid = x - o.reconstruct(ck, M)
+        assert np.abs(o.fourier_basis(M, k).T @ resid).max() < 1e-10
+
+
+def pin_closed_form(o):
+    """P-5: A sin(2 pi j tau / M + ph) has exactly two non-zero coefficients,
+    A sqrt(M/2) sin(ph) on the cosine and A sqrt(M/2) cos(ph) on the sine of
+    frequency j; a constant c has only c sqrt(M) on the constant term."""
+    M, k = 48, 21
+    tau = np.arange(M)
+    for j, A, ph in [(1, 1.0, 0.3), (4, -2.5, 2.0), (10, 0.7, -1.1)]:
+        x = A * np.sin(2 * np.pi * j * tau / M + ph)
+        c = o.project(x[:, None], k)[:, 0]
+        want = np.zeros(k)
+        want[2 * j - 1] = A * math.sqrt(M / 2) * math.sin(ph)
+        want[2 * j] = A * math.sqrt(M / 2) * math.cos(ph)
+        assert np.abs(c - want).max() < 1e-12, j
+    c = o.project(np.full((M, 1), 3.0), k)[:, 0]
+    want = np.zeros(k)
+    want[0] = 3.0 * math.sqrt(M)
+    assert np.abs(c - want).max() < 1e-12
+
+
+def pin_golden_basis(o):
+    """Hand-derived basis values for M = 4 (tests/golden/basis_m4.json)."""
+    with open(os.path.join(GOLDEN, "basis_m4.json")) as f:
+        g = json.load(f)
+    P = o.fourier_basis(g["M"], g["k"])
+    assert np.abs(P - np.array(g["phi"])).max() < 1e-15
+
+
+def pin_segment(o):
+    """Segmentation follows the pages' Step 3 slicing: initial = the first 32
+    tokens, recent = the last 64, middle in between; no middle when the
+    sequence is not longer than both (tests/golden/pages_facts.json)."""
+    with open(os.path.join(GOLDEN, "pages_facts.json")) as f:
+        facts = json.load(f)
+    S, R = facts["preserve_initial"], facts["preserve_recent"]
+    for L in (512, 4096, 97, 96, 50, 1):
+        toks = list(range(L))
+        start, M = o.segment(L, S, R)
+        if L > S + R:
+            middle = toks[S:L - R]
+            assert (start, M) == (middle[0], len(middle)), L
+        else:
+            assert M == 0, L
+
+
+def _tiny_case(seed, L=8, D=4, Dc=2, S=1, R=1, k=3, G=2):
+    rng = _rng(seed)
+    K = rng.standard_normal((L, D))
+    V = rng.standard_normal((L, D))
+    q = rng.standard_normal((G, D))
+    comp = np.array(sorted(rng.permutation(D)[:Dc]), dtype=np.int64)
+    return K, V, q, comp, S, R, k
+
+
+def _brute_force(K, V, q, comp, S, R, k, scale):
+    """Pure-Python loops: basis, projection, reconstruction, attention."""
+    L, D = len(K), len(K[0])
+    M = max(0, L - S - R)
+    Kt = [list(map(float, row)) for row in K]
+    Vt = [list(map(float, row)) for row in V]
+    if M > 0:
+        def phi(n, t):
+            f = (n + 1) // 2
+            r = (f * t) % M
+            a = 1.0 / math.sqrt(M) if (f == 0 or 2 * f == M) else math.sqrt(2.0 / M)
+            trig = math.cos if (n == 0 or n % 2 == 1) else math.sin
+            return a * trig(2.0 * math.pi * r / M)
+        for X, Xt in ((K, Kt), (V, Vt)):
+            for d in comp:
+                coef = [sum(phi(n, t) * float(X[S + t][d]) for t in range(M))
+                        for n in range(k)]
+                for t in range(M):
+                    Xt[S + t][d] = sum(phi(n, t) * coef[n] for n in range(k))
+    outs = []
+    for qi in q:
+        s = [scale * sum(float(qi[d]) * Kt[t][d] for d in range(D)) for t in range(L)]
+        m = max(s)
+        e = [math.exp(v - m) for v in s]
+        z = sum(e)
+        outs.append([sum(e[t] * Vt[t][d] for t in range(L)) / z for d in range(D)])
+    return np.array(outs)
+
+
+def _oracle_decode(o, K, V, q, comp, S, R, k, scale):
+    start, M = o.segment(len(K), S, R)
+    if M > 0:
+        ck = o.project(K[start:start + M][:, comp], k)
+        cv = o.project(V[start:start + M][:, comp], k)
+    else:
+        ck = cv = np.zeros((k, len(comp)))
+    return o.decode(q, K, V, comp, ck, cv, S, R, scale)
+
+
+def pin_brute_force(o):
+    """P-8: the whole pipeline against pure-Python loops on tiny inputs."""
+    cases = [dict(), dict(L=7, k=5), dict(L=6, D=3, Dc=3, k=4), dict(L=2),
+             dict(L=8, S=2, R=2, k=4, G=3), dict(L=5, Dc=0, k=1)]
+    for i, kw in enumerate(cases):
+        K, V, q, comp, S, R, k = _tiny_case(10 + i, **kw)
+        scale = 0.7
+        want = _brute_force(K, V, q, comp, S, R, k, scale)
+        got = _oracle_decode(o, K, V, q, comp, S, R, k, scale)
+        assert np.abs(got - want).max() < 1e-12, (i, kw)
+
+
+def _sdpa(q, K, V, scale):
+    import torch
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        t(q)[None, None], t(K)[None, None], t(V)[None, None], scale=scale)
+    return out[0, 0].numpy()
+
+
+def pin_reduces_to_attention(o):
+    """P-6: k = M, no compressible dims, or L <= S + R leave the cache exact,
+    so decode equals PyTorch's CPU scaled-dot-product attention."""
+    rng = _rng(5)
+    for L, D, Dc, S, R, kfull in [(40, 8, 4, 3, 5, True), (40, 8, 0, 3, 5, False),
+                                  (8, 8, 4, 3, 5, False), (200, 16, 7, 32, 64, True)]:
+        K = rng.standard_normal((L, D))
+        V = rng.standard_normal((L, D))
+        q = rng.standard_normal((3, D))
+        comp = np.sort(rng.permutation(D)[:Dc]).astype(np.int64)
+        start, M = o.segment(L, S, R)
+        k = M if (kfull and M > 0) else 1
+        got = _oracle_decode(o, K, V, q, comp, S, R, k, 0.3)
+        assert np.abs(got - _sdpa(q, K, V, 0.3)).max() < 1e-12, (L, Dc)
+
+
+def pin_factored(o):
+    """P-7: scores scale*(q_U.k_U + a.phi(tau)) with a = q_C C_K^T, and values
+    o_U + W C_V with W = sum_tau p phi(tau): the factored form the GPU computes
+    equals reconstruct-then-attend."""
+    rng = _rng(6)
+    L, D, Dc, S, R, k, G = 300, 16, 10, 32, 64, 37, 3
+    K = rng.standard_normal((L, D))
+    V = rng.standard_normal((L, D))
+    q = rng.standard_normal((G, D))
+    comp = np.sort(rng.permutation(D)[:Dc])
+    exact = np.setdiff1d(np.arange(D), comp)
+    start, M = o.segment(L, S, R)
+    ck = o.project(K[start:start + M][:, comp], k)
+    cv = o.project(V[start:start + M][:, comp], k)
+    got = o.decode(q, K, V, comp, ck, cv, S, R, 0.25)
+    # factored form, written independently here
+    P = o.fourier_basis(M, k)
+    mid = np.zeros(L, bool)
+    mid[start:start + M] = True
+    s = 0.25 * (q @ K.T)
+    s[:, mid] = 0.25 * (q[:, exact] @ K[mid][:, exact].T) + (0.25 * q[:, comp] @ ck.T) @ P.T
+    p = np.exp(s - s.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    out = np.zeros((G, D))
+    out[:, exact] = p @ V[:, exact]
+    W = p[:, mid] @ P
+    out[:, comp] = p[:, ~mid] @ V[~mid][:, comp] + W @ cv
+    assert np.abs(got - out).max() < 1e-12
+
+
+def pin_softmax_invariants(o):
+    """P-9: probabilities sum to 1, outputs lie in the convex hull of V's rows,
+    equal scores average V, and one dominant score selects its row."""
+    rng = _rng(7)
+    K = rng.standard_normal((50, 6))
+    V = rng.standard_normal((50, 6))
+    q = rng.standard_normal((4, 6))
+    out, p = o.softmax_attention(q, K, V, 0.5, return_probs=True)
+    assert np.abs(p.sum(1) - 1).max() < 1e-14
+    assert (out <= V.max(0) + 1e-12).all() and (out >= V.min(0) - 1e-12).all()
+    flat = o.softmax_attention(np.zeros((1, 6)), K, V, 0.5)
+    assert np.abs(flat[0] - V.mean(0)).max() < 1e-13
+    Kd = K.copy()
+    Kd[17] = 1e3 * q[0]
+    dom = o.softmax_attention(q[:1], Kd, V, 1.0)
+    assert np.abs(dom[0] - V[17]).max() < 1e-12
+
+
+def pin_gqa_stacking(o):
+    """P-10: a GQA workload's batched oracle equals separate single-head calls
+    with query head i reading KV head i // G, and decode of stacked query rows
+    equals one call per row."""
+    cfg = wl.custom(dtype="f32", batch=2, n_q_heads=6, n_kv_heads=2, head_dim=8,
+                    n_comp=3, n_coef=5, sink=2, recent=3, mask="seeded", seed=9)
+    w = wl.make(cfg, lens=[20, 13])
+    ck, cv = ob.project_all(w)
+    out = ob.decode_all(w, ck, cv, 0.4)
+    for b in range(2):
+        for i in range(6):
+            h = i // 3
+            K, V = w.natural_kv(b, h)
+            q = w.f64(w.q[b, i])[None]
+            single = o.decode(q, K, V, w.comp_dims(h), ck[b * 2 + h], cv[b * 2 + h],
+                              2, 3, 0.4)
+            assert np.abs(out[b, i] - single[0]).max() < 1e-13
+
+
+PINS = [pin_orthonormal, pin_rfft, pin_irfft_lowpass, pin_parseval_bessel,
+        pin_closed_form, pin_golden_basis, pin_segment, pin_brute_force,
+        pin_reduces_to_attention, pin_factored, pin_softmax_invariants,
+        pin_gqa_stacking]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin(fa)
+
+
+# --------------------------------------------------------------- mutants ----
+# Plausible mistakes planted in the oracle (CPU only).  Each must fail a pin.
+
+def _basis_variant(**mut):
+    def basis(M, k):
+        if not (1 <= k <= M):
+            raise ValueError
+        tau = np.arange(M, dtype=np.int64) + mut.get("tau_shift", 0)
+        n = np.arange(k)
+        f = n // 2 if mut.get("freq_off") else (n + 1) // 2
+        ang = 2 * np.pi * (np.outer(tau, f) % M) / M
+        use_cos = (n == 0) | (n % 2 == 1)
+        if mut.get("swap"):
+            use_cos = (n == 0) | ((n % 2 == 0) & (n > 0))
+        sin = -np.sin(ang) if mut.get("neg_sin") else np.sin(ang)
+        phi = np.where(use_cos[None], np.cos(ang), sin)
+        a = np.where((f == 0) | (2 * f == M), 1 / np.sqrt(M), np.sqrt(2 / M))
+        if mut.get("nyquist"):
+            a = np.where(f == 0, 1 / np.sqrt(M), np.sqrt(2 / M))
+        if mut.get("no_scale"):
+            a = np.ones_like(a)
+        return phi * a[None]
+    return basis
+
+
+def _decode_no_scale(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale):
+    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent)
+    Vt = fa.approximate_cache(V, comp_dims, cv, sink, recent)
+    return fa.softmax_attention(q_rows, Kt, Vt, 1.0)
+
+
+def _decode_values_exact(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale):
+    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent)
+    return fa.softmax_attention(q_rows, Kt, V, scale)
+
+
+def _segment_off_by_one(L, sink, recent):
+    return sink + 1, max(0, L - sink - recent)
+
+
+def _segment_keeps_recent_short(L, sink, recent):
+    return sink, max(0, L - sink)
+
+
+def _approx_wrong_dims(X, comp_dims, coef, sink, recent):
+    X = np.array(X, dtype=np.float64, copy=True)
+    start, M = fa.segment(X.shape[0], sink, recent)
+    cd = np.sort(np.asarray(comp_dims))[::-1]  # dims permuted vs the coefficients
+    if M > 0 and cd.size > 0:
+        X[start:start + M][:, cd] = fa.reconstruct(coef, M)
+    return X
+
+
+def _softmax_transposed_v(q, K, V, scale, return_probs=False):
+    q = np.atleast_2d(q)
+    s = scale * (q @ K.T)
+    p = np.exp(s - s.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    out = p @ V[::-1]
+    return (out, p) if return_probs else out
+
+
+MUTANTS = {
+    "sin_cos_swapped": ("fourier_basis", _basis_variant(swap=True)),
+    "sin_sign": ("fourier_basis", _basis_variant(neg_sin=True)),
+    "freq_off_by_one": ("fourier_basis", _basis_variant(freq_off=True)),
+    "nyquist_scale": ("fourier_basis", _basis_variant(nyquist=True)),
+    "no_normalisation": ("fourier_basis", _basis_variant(no_scale=True)),
+    "phase_origin": ("fourier_basis", _basis_variant(tau_shift=1)),
+    "decode_no_scale": ("decode", _decode_no_scale),
+    "values_not_reconstructed": ("decode", _decode_values_exact),
+    "segment_off_by_one": ("segment", _segment_off_by_one),
+    "segment_drops_recent": ("segment", _segment_keeps_recent_short),
+    "comp_dims_permuted": ("approximate_cache", _approx_wrong_dims),
+    "value_rows_reversed": ("softmax_attention", _softmax_transposed_v),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutants_are_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(fa, attr, fn)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(fa)
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(pin.__name__)
+    assert failed, "mutant %s passed every pin" % name
+
+
+def test_k_greater_than_m_rejected():
+    with pytest.raises(ValueError):
+        fa.fourier_basis(4, 5)
+    with pytest.raises(ValueError):
+        fa.fourier_basis(4, 0)
