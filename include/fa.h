@@ -1,0 +1,145 @@
+/*
+ * fa.h - C ABI of libfa: Fourier-approximated KV-cache attention on MI355X.
+ *
+ * The method (arXiv 2506.11886, "Beyond Homogeneous Attention: Memory-Efficient
+ * LLMs via Fourier-Approximated KV Cache", abstract; skill page
+ * "fourier-approximated-kv-cache", Core concept and Steps 2-4): for each KV head
+ * a set of "compressible" head dims is chosen; along the sequence, the first
+ * `sink` tokens and the last `recent` tokens are kept exactly; the
+ * M = L - sink - recent tokens between them (the middle) keep only k << M
+ * coefficients per compressible dim, their projection onto an orthonormal real
+ * Fourier basis over the M middle positions.  The other dims are kept exactly
+ * for every token.
+ *
+ * Basis (tau = 0 .. M-1 counts middle tokens, n = 0 .. k-1):
+ *   phi_0(tau)      = 1/sqrt(M)
+ *   phi_{2j-1}(tau) = a_j cos(2 pi j tau / M)
+ *   phi_{2j}(tau)   = a_j sin(2 pi j tau / M)
+ *   a_j = sqrt(2/M), or 1/sqrt(M) for the Nyquist cosine (2j = M).
+ *
+ * ----------------------------------------------------------------------------
+ * Cache layout ("dim-split" cache).  For KV head h, dims[h] (int32, D entries)
+ * lists the exact dims ascending, then the compressible dims ascending; Du =
+ * D - Dc.  Tensors are row-major, dtype = desc.dtype unless noted:
+ *
+ *   kx, vx  [rows, Du]   exact dims of every token;
+ *   kc, vc  [rows, Dc]   compressible dims of every token (input of fa_project);
+ *       row of (sequence b, KV head h, token t) = Hkv*off_b + h*L_b + t,
+ *       off_b = L_0 + ... + L_{b-1}.  Column j of kx is dim dims[h][j],
+ *       column c of kc is dim dims[h][Du + c].
+ *   ke, ve  [B*Hkv, sink+recent, Dc]  compressible dims of the retained rows of
+ *       block b*Hkv+h: the sink tokens, then the recent tokens.  When
+ *       L_b <= sink+recent the block holds all L_b tokens in order and the rest
+ *       of its rows are ignored.
+ *   ck, cv  [B*Hkv, k, Dc]  float32 Fourier coefficients of the middle rows.
+ *   q       [B, Hq, D]   queries, natural dim order.
+ *   out     [B, Hq, D]   float32 attention outputs, natural dim order.
+ *
+ * Query head i reads KV head i / (Hq/Hkv).
+ *
+ * ----------------------------------------------------------------------------
+ * Ownership and streams.  The caller owns every buffer, including the
+ * workspace (size from the *_workspace_size queries, alignment 256 bytes).
+ * The library allocates no memory, copies nothing between host and device and
+ * never synchronises: calls enqueue kernels on `stream` (a hipStream_t; NULL is
+ * the default stream) and return.  Outputs must not overlap inputs.  Calls that
+ * share a workspace must be ordered on one stream.
+ *
+ * Errors.  Arguments are validated on the host before any HIP call; a failed
+ * check returns its code and enqueues nothing.  A failing kernel launch returns
+ * FA_ERR_HIP.  fa_last_error() gives a text for the last failure on the calling
+ * thread.  Device arrays are not read by the host: entries of `dims` outside
+ * [0, D) are skipped by the kernels (no fault) and give unspecified results.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  FA_ERR_SHAPE = 2,     /* sizes out of range or inconsistent                */
+  FA_ERR_DTYPE = 3,     /* unknown dtype                                     */
+  FA_ERR_WORKSPACE = 4, /* workspace missing, too small or misaligned        */
+  FA_ERR_HIP = 5,       /* the HIP runtime reported an error                 */
+  FA_ERR_ALIAS = 6      /* an output overlaps an input or another output     */
+} fa_status_t;
+
+typedef enum {
+  FA_F32 = 0, /* float32 q, K, V                                             */
+  FA_BF16 = 1 /* bfloat16 q, K, V (coefficients and outputs stay float32)    */
+} fa_dtype_t;
+
+#define FA_MAX_BATCH 64
+
+typedef struct {
+  int32_t dtype;       /* fa_dtype_t                                          */
+  int32_t batch;       /* B, 1 .. FA_MAX_BATCH                                */
+  int32_t n_q_heads;   /* Hq, a positive multiple of n_kv_heads               */
+  int32_t n_kv_heads;  /* Hkv >= 1                                            */
+  int32_t head_dim;    /* D, 1 .. 256                                         */
+  int32_t n_comp_dims; /* Dc, 0 .. D                                          */
+  int32_t sink;        /* tokens kept exactly at the start, >= 0              */
+  int32_t recent;      /* tokens kept exactly at the end, >= 0                */
+  int32_t n_coef;      /* k >= 1; k <= M_b for every b with M_b > 0           */
+  int32_t reserved;    /* must be 0                                           */
+  const int32_t *seq_len; /* HOST array [B], L_b >= 1                         */
+  const int32_t *dims;    /* DEVICE array [Hkv][D] (fa_decode only)           */
+} fa_desc_t;
+
+/* Workspace bytes fa_project needs for `desc` (0 is possible). */
+fa_status_t fa_project_workspace_size(const fa_desc_t *desc, size_t *bytes);
+
+/*
+ * fa_project: prefill compression.  For every sequence b with M_b > 0 and
+ * KV head h:  ck[b*Hkv+h][n][c] = sum_tau phi_n(tau) * kc[row(b,h,sink+tau)][c]
+ * (and cv from vc), the projection of the middle rows onto the first k basis
+ * functions (skill page, Step 2; arXiv 2506.11886 abstract).  Blocks of
+ * sequences with M_b = 0 are set to zero.  When ke (ve) is not NULL the
+ * retained sink/recent rows of kc (vc) are also gathered into it (skill page,
+ * Step 3).  Either matrix may be skipped: pass kc = ck = ke = NULL (or the V
+ * trio).  With n_comp_dims = 0 the call does nothing and every pointer may be
+ * NULL.  The 16-bit path needs n_comp_dims % 8 == 0 and 16-byte aligned kc/vc;
+ * it computes in fp16 operands, so |kc|, |vc| must stay below 65504.
+ * desc.dims is not used.
+ */
+fa_status_t fa_project(const fa_desc_t *desc, const void *kc, const void *vc,
+                       float *ck, float *cv, void *ke, void *ve,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_decode needs for `desc`. */
+fa_status_t fa_decode_workspace_size(const fa_desc_t *desc, size_t *bytes);
+
+/*
+ * fa_decode: one decode step.  For sequence b and query head i (KV head
+ * g = i / (Hq/Hkv)) over the cache in which the middle rows' compressible dims
+ * are the Fourier reconstruction sum_n phi_n(tau) ck[n][c] (skill page, Step 4):
+ *   s_t = scale * q[b][i] . K~[t],   p = softmax_t(s),
+ *   out[b][i] = sum_t p_t V~[t]      for t = 0 .. L_b-1.
+ * The reconstruction is never formed: compressed scores are
+ * (scale q_C ck^T) . phi(tau) and compressed values are (sum_tau p phi(tau)) cv.
+ */
+fa_status_t fa_decode(const fa_desc_t *desc, const void *q, const void *kx,
+                      const void *vx, const void *ke, const void *ve,
+                      const float *ck, const float *cv, float scale, float *out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *fa_status_string(fa_status_t status);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char *fa_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_H */

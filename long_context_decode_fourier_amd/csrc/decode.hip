@@ -1,0 +1,542 @@
+// decode.hip - one decode step over the Fourier-approximated KV cache.
+//
+// The pages reconstruct the middle tokens (zero-padded inverse transform) and
+// then attend (skill page "fourier-approximated-kv-cache", Step 4).  Here the
+// reconstruction is never formed.  For a query row q and its KV head:
+//
+//   middle token tau:  s = scale q_U . kx[tau] + sum_n a_n b_n(tau),
+//                      a_n = scale alpha_n (q_C . ck[n])     (decode_prep)
+//   edge token t:      s = scale q . [kx[t], ke[t]]
+//   out_U = sum_t p_t vx[t]
+//   out_C = sum_{edge t} p_t ve[t] + sum_n W_n alpha_n cv[n],
+//           W_n = sum_tau p_tau b_n(tau)
+//
+// with b_n the unscaled cos/sin of the basis (alpha_n its scale) and p the
+// softmax of s over all L tokens.  The sequence is split into token ranges
+// (split-L); each split keeps a running max m, sum l, o_U, the edge part of
+// o_C and W (online softmax), and decode_merge combines the splits with the
+// usual log-sum-exp weights in a fixed order, applies C_V and scatters dims.
+//
+// decode_split is a VALU kernel: for each token the basis along n is produced
+// by complex rotation (e^{i theta_j tau} times e^{i 2 pi tau / M}), for each
+// coefficient the basis along tau by rotation with e^{i 2 pi j / M}; both are
+// re-anchored from exact integer phases.
+#include "kernels.hpp"
+
+namespace fa {
+namespace {
+
+template <typename T> __device__ inline float ld(const void* p, int64_t i) {
+  return load_f32<T>(static_cast<const T*>(p), i);
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ inline float basis_alpha(int n, int M) {
+  const int f = basis_freq(n);
+  return (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
+                                 : sqrtf(2.0f / static_cast<float>(M));
+}
+
+// e^{i 2 pi (j * tau mod M) / M} for any integer tau (negative allowed).
+__device__ inline float2 unit_phase(int j, int tau, int M) {
+  int64_t r = (static_cast<int64_t>(j) * tau) % M;
+  if (r < 0) r += M;
+  float s, c;
+  sincos_phase(static_cast<int>(r), M, &s, &c);
+  return make_float2(c, s);
+}
+
+__device__ inline float2 cmul(float2 a, float2 b) {
+  return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+
+// Query rows of row group rg: query head and KV head of row r.
+__device__ inline void row_heads(const DecodeArgs& a, int rg, int r, int* i, int* h) {
+  if (a.G <= kDecRows) {
+    const int hpg = a.rows / a.G;
+    *h = rg * hpg + r / a.G;
+    *i = *h * a.G + r % a.G;
+  } else {
+    const int gph = a.G / kDecRows;
+    *h = rg / gph;
+    *i = *h * a.G + (rg % gph) * kDecRows + r;
+  }
+}
+
+// --------------------------------------------------------------- prep ----
+// A[b][i][n] = scale * alpha_n * sum_c q[b][i][comp_c] ck[b,h][n][c].
+template <typename T>
+__global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  constexpr int kRowChunk = 8;
+  const int bh = blockIdx.x;
+  const int b = bh / a.hkv, h = bh % a.hkv;
+  const int M = a.seq.mid[b];
+  const int n = blockIdx.y * 64 + (threadIdx.x & 63);
+  const int part = threadIdx.x >> 6;
+  float* qc = smem;                            // [kRowChunk][dc]
+  float* red = smem + kRowChunk * a.dc;        // [4][kRowChunk][64]
+  const int cper = (a.dc + 3) / 4;
+  const int c0 = part * cper, c1 = min(a.dc, c0 + cper);
+  for (int g0 = 0; g0 < a.G; g0 += kRowChunk) {
+    const int ng = min(kRowChunk, a.G - g0);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ng * a.dc; idx += blockDim.x) {
+      const int g = idx / a.dc, c = idx % a.dc;
+      const int d = a.dims[h * a.D + a.du + c];
+      const int i = h * a.G + g0 + g;
+      qc[g * a.dc + c] = (d >= 0 && d < a.D)
+                             ? a.scale * ld<T>(a.q, (static_cast<int64_t>(b) * a.hq + i) * a.D + d)
+                             : 0.0f;
+    }
+    __syncthreads();
+    float acc[kRowChunk];
+#pragma unroll
+    for (int g = 0; g < kRowChunk; ++g) acc[g] = 0.0f;
+    if (n < a.k && M > 0) {
+      const float* ckrow = a.ck + ((static_cast<int64_t>(b) * a.hkv + h) * a.k + n) * a.dc;
+      for (int c = c0; c < c1; ++c) {
+        const float v = ckrow[c];
+#pragma unroll
+        for (int g = 0; g < kRowChunk; ++g)
+          if (g < ng) acc[g] = fmaf(qc[g * a.dc + c], v, acc[g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kRowChunk; ++g) red[(part * kRowChunk + g) * 64 + (threadIdx.x & 63)] = acc[g];
+    __syncthreads();
+    if (part == 0 && n < a.k) {
+      const float alpha = (M > 0) ? basis_alpha(n, M) : 0.0f;
+      for (int g = 0; g < ng; ++g) {
+        const int t = threadIdx.x & 63;
+        const float s = (red[(0 * kRowChunk + g) * 64 + t] + red[(1 * kRowChunk + g) * 64 + t]) +
+                        (red[(2 * kRowChunk + g) * 64 + t] + red[(3 * kRowChunk + g) * 64 + t]);
+        const int i = h * a.G + g0 + g;
+        a.A[(static_cast<int64_t>(b) * a.hq + i) * a.kpad + n] = alpha * s;
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------- split ----
+constexpr int kMaxSlots = 9;  // ceil((4097/2 + 1) / 256)
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  constexpr int R = kDecRows;
+  constexpr int TT = kDecTile;
+  extern __shared__ float smem[];
+  float* qs = smem;                      // [R][D]
+  float* As = qs + R * a.D;              // [R][kpad]
+  float* sc = As + R * a.kpad;           // [4][R][TT]
+  float* ps = sc + 4 * R * TT;           // [TT][R]
+  float* corr = ps + TT * R;             // [R]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int item = blockIdx.x;
+  const int b = seq_of_item(a.seq, a.nseq, item);
+  const int local = item - a.seq.item0[b];
+  const int ns = a.seq.nsplit[b];
+  const int rg = local / ns, sp = local % ns;
+  const int L = a.seq.len[b], M = a.seq.mid[b];
+  const int S = a.sink, E = a.sink + a.recent;
+  const int t_begin = sp * a.seq.chunk[b];
+  const int t_end = min(L, t_begin + a.seq.chunk[b]);
+  const int64_t row0 = a.seq.row0[b];
+  const bool comp = a.dc > 0;
+  const bool has_mid = comp && M > 0;
+
+  int qi[R], kh[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int i = 0, h = 0;
+    if (r < a.rows) row_heads(a, rg, r, &i, &h);
+    qi[r] = i;
+    kh[r] = h;
+  }
+
+  // q rows in dim-split order, scaled; A rows.
+  for (int idx = tid; idx < R * a.D; idx += blockDim.x) {
+    const int r = idx / a.D, j = idx % a.D;
+    float v = 0.0f;
+    if (r < a.rows) {
+      const int d = a.dims[kh[r] * a.D + j];
+      if (d >= 0 && d < a.D)
+        v = a.scale * ld<T>(a.q, (static_cast<int64_t>(b) * a.hq + qi[r]) * a.D + d);
+    }
+    qs[idx] = v;
+  }
+  if (has_mid)
+    for (int idx = tid; idx < R * a.kpad; idx += blockDim.x) {
+      const int r = idx / a.kpad, n = idx % a.kpad;
+      As[idx] = (r < a.rows && n < a.k)
+                    ? a.A[(static_cast<int64_t>(b) * a.hq + qi[r]) * a.kpad + n]
+                    : 0.0f;
+    }
+
+  const int nslots = a.k / 2 + 1;  // slot 0: n = 0; slot j: n = 2j-1, 2j
+  const int du4 = (a.du + 3) / 4, dc4 = (a.dc + 3) / 4, sl4 = (nslots + 3) / 4;
+  const int part = wave;  // phase A: thread (token lane, part)
+
+  // running softmax state (wave r owns row r)
+  float m_run = -INFINITY, l_run = 0.0f;
+  float oacc[4], eacc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) oacc[j] = eacc[j] = 0.0f;
+  float2 wstep[kMaxSlots];
+  float wacc[kMaxSlots][2][R];
+#pragma unroll
+  for (int i = 0; i < kMaxSlots; ++i) {
+    const int j = tid + 256 * i;
+    wstep[i] = (has_mid && j < nslots) ? unit_phase(j, 1, M) : make_float2(1.0f, 0.0f);
+#pragma unroll
+    for (int r = 0; r < R; ++r) wacc[i][0][r] = wacc[i][1][r] = 0.0f;
+  }
+  __syncthreads();
+
+  for (int tile0 = t_begin; tile0 < t_end; tile0 += TT) {
+    // ---------------- phase A: partial scores
+    {
+      const int t = tile0 + lane;
+      float acc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+      if (t < t_end) {
+        const int d0 = part * du4, d1 = min(a.du, d0 + du4);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r >= a.rows) break;
+          const int64_t base = (row0 + static_cast<int64_t>(kh[r]) * L + t) * a.du;
+          for (int d = d0; d < d1; ++d) acc[r] = fmaf(qs[r * a.D + d], ld<T>(a.kx, base + d), acc[r]);
+        }
+        if (comp) {
+          const bool edge = (M == 0) || t < S || t >= S + M;
+          if (edge) {
+            const int e = (M == 0 || t < S) ? t : t - M;
+            const int c0 = part * dc4, c1 = min(a.dc, c0 + dc4);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              if (r >= a.rows) break;
+              const int64_t base = ((static_cast<int64_t>(b) * a.hkv + kh[r]) * E + e) * a.dc;
+              for (int c = c0; c < c1; ++c)
+                acc[r] = fmaf(qs[r * a.D + a.du + c], ld<T>(a.ke, base + c), acc[r]);
+            }
+          } else {
+            const int tau = t - S;
+            const int j0 = part * sl4, j1 = min(nslots, j0 + sl4);
+            const float2 w = unit_phase(1, tau, M);
+            float2 z = make_float2(1.0f, 0.0f);
+            for (int j = j0; j < j1; ++j) {
+              if (((j - j0) & 31) == 0) z = unit_phase(j, tau, M);
+              if (j == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fmaf(As[r * a.kpad], z.x, acc[r]);
+              } else {
+                const int n = 2 * j - 1;
+                const bool has_sin = n + 1 < a.k;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                  acc[r] = fmaf(As[r * a.kpad + n], z.x, acc[r]);
+                  if (has_sin) acc[r] = fmaf(As[r * a.kpad + n + 1], z.y, acc[r]);
+                }
+              }
+              z = cmul(z, w);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) sc[(part * R + r) * TT + lane] = acc[r];
+    }
+    __syncthreads();
+
+    // ---------------- phase B: online softmax, wave r owns row r
+    if (wave < a.rows) {
+      const int r = wave;
+      const int t = tile0 + lane;
+      const bool valid = t < t_end;
+      float s = (sc[(0 * R + r) * TT + lane] + sc[(1 * R + r) * TT + lane]) +
+                (sc[(2 * R + r) * TT + lane] + sc[(3 * R + r) * TT + lane]);
+      s = valid ? s : -INFINITY;
+      const float m_new = fmaxf(m_run, wave_max(s));
+      const float c = (m_run == -INFINITY) ? 0.0f : __expf(m_run - m_new);
+      const float p = valid ? __expf(s - m_new) : 0.0f;
+      l_run = l_run * c + wave_sum(p);
+      m_run = m_new;
+      ps[lane * R + r] = p;
+      if (lane == 0) corr[r] = c;
+    } else if (wave < R) {
+      ps[lane * R + wave] = 0.0f;
+      if (lane == 0) corr[wave] = 1.0f;
+    }
+    __syncthreads();
+
+    // ---------------- phase C: values
+    const int nt = min(TT, t_end - tile0);
+    // exact dims
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + 256 * j;
+      if (idx >= a.rows * a.du) break;
+      const int r = idx / a.du, d = idx % a.du;
+      float o = oacc[j] * corr[r];
+      const int64_t base = (row0 + static_cast<int64_t>(kh[r]) * L + tile0) * a.du + d;
+      for (int tl = 0; tl < nt; ++tl) o = fmaf(ps[tl * R + r], ld<T>(a.vx, base + static_cast<int64_t>(tl) * a.du), o);
+      oacc[j] = o;
+    }
+    if (comp) {
+      // compressible dims of edge tokens
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + 256 * j;
+        if (idx >= a.rows * a.dc) break;
+        const int r = idx / a.dc, c = idx % a.dc;
+        float o = eacc[j] * corr[r];
+        const int64_t base = (static_cast<int64_t>(b) * a.hkv + kh[r]) * E * a.dc + c;
+        for (int tl = 0; tl < nt; ++tl) {
+          const int t = tile0 + tl;
+          if (M == 0 || t < S || t >= S + M) {
+            const int e = (M == 0 || t < S) ? t : t - M;
+            o = fmaf(ps[tl * R + r], ld<T>(a.ve, base + static_cast<int64_t>(e) * a.dc), o);
+          }
+        }
+        eacc[j] = o;
+      }
+    }
+    if (has_mid) {
+      // W_n = sum_tau p b_n(tau) over the middle tokens of this tile
+      const int mid_lo = max(0, S - tile0), mid_hi = min(nt, S + M - tile0);
+      float2 z[kMaxSlots];
+#pragma unroll
+      for (int i = 0; i < kMaxSlots; ++i) {
+        const int j = tid + 256 * i;
+        // anchor at the tile's first middle token (tau >= 0)
+        z[i] = (j < nslots && mid_lo < mid_hi) ? unit_phase(j, tile0 + mid_lo - S, M)
+                                              : make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          wacc[i][0][r] *= corr[r];
+          wacc[i][1][r] *= corr[r];
+        }
+      }
+      for (int tl = mid_lo; tl < mid_hi; ++tl) {
+        const float4 p = *reinterpret_cast<const float4*>(&ps[tl * R]);
+#pragma unroll
+        for (int i = 0; i < kMaxSlots; ++i) {
+          wacc[i][0][0] = fmaf(p.x, z[i].x, wacc[i][0][0]);
+          wacc[i][1][0] = fmaf(p.x, z[i].y, wacc[i][1][0]);
+          wacc[i][0][1] = fmaf(p.y, z[i].x, wacc[i][0][1]);
+          wacc[i][1][1] = fmaf(p.y, z[i].y, wacc[i][1][1]);
+          wacc[i][0][2] = fmaf(p.z, z[i].x, wacc[i][0][2]);
+          wacc[i][1][2] = fmaf(p.z, z[i].y, wacc[i][1][2]);
+          wacc[i][0][3] = fmaf(p.w, z[i].x, wacc[i][0][3]);
+          wacc[i][1][3] = fmaf(p.w, z[i].y, wacc[i][1][3]);
+          z[i] = cmul(z[i], wstep[i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---------------- write partials
+  if (wave < a.rows) {
+    const int r = wave;
+    float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(qi[r]) * ns + sp) * a.RS;
+    if (lane == 0) {
+      P[0] = m_run;
+      P[1] = l_run;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = tid + 256 * j;
+    if (idx < a.rows * a.du) {
+      const int r = idx / a.du, d = idx % a.du;
+      a.part[(static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(qi[r]) * ns + sp) * a.RS + 2 + d] = oacc[j];
+    }
+    if (idx < a.rows * a.dc) {
+      const int r = idx / a.dc, c = idx % a.dc;
+      a.part[(static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(qi[r]) * ns + sp) * a.RS + 2 + a.du + c] = eacc[j];
+    }
+  }
+  if (has_mid) {
+#pragma unroll
+    for (int i = 0; i < kMaxSlots; ++i) {
+      const int j = tid + 256 * i;
+      if (j >= nslots) continue;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r >= a.rows) break;
+        float* Wp = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(qi[r]) * ns + sp) * a.RS + 2 + a.du + a.dc;
+        if (j == 0) {
+          Wp[0] = wacc[i][0][r];
+        } else {
+          Wp[2 * j - 1] = wacc[i][0][r];
+          if (2 * j < a.k) Wp[2 * j] = wacc[i][1][r];
+        }
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------- merge ----
+// One block per (sequence, KV head): combine the splits of its G query rows.
+constexpr int kMergeRows = 4;
+
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int b = blockIdx.x / a.hkv, h = blockIdx.x % a.hkv;
+  const int ns = a.seq.nsplit[b];
+  const int M = a.seq.mid[b];
+  const bool has_mid = a.dc > 0 && M > 0;
+  float* wsp = smem;                           // [kMergeRows][ns]
+  float* Wm = wsp + kMergeRows * ns;           // [kMergeRows][kpad]
+  float* red = Wm + kMergeRows * a.kpad;       // [256][kMergeRows]
+  __shared__ float Lsum[kMergeRows];
+  const int tid = threadIdx.x;
+
+  for (int g0 = 0; g0 < a.G; g0 += kMergeRows) {
+    const int ng = min(kMergeRows, a.G - g0);
+    __syncthreads();
+    // softmax weights of the splits
+    for (int g = tid >> 6; g < ng; g += 4) {
+      const int lane = tid & 63;
+      const int i = h * a.G + g0 + g;
+      const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS;
+      float mx = -INFINITY;
+      for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, P[static_cast<int64_t>(s) * a.RS]);
+      mx = wave_max(mx);
+      float lsum = 0.0f;
+      for (int s = lane; s < ns; s += 64) {
+        const float m = P[static_cast<int64_t>(s) * a.RS];
+        const float w = (m == -INFINITY) ? 0.0f : __expf(m - mx);
+        wsp[g * ns + s] = w;
+        lsum += w * P[static_cast<int64_t>(s) * a.RS + 1];
+      }
+      lsum = wave_sum(lsum);
+      if (lane == 0) Lsum[g] = lsum;
+    }
+    __syncthreads();
+    // exact dims and merged W
+    for (int idx = tid; idx < ng * a.du; idx += blockDim.x) {
+      const int g = idx / a.du, d = idx % a.du;
+      const int i = h * a.G + g0 + g;
+      const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS + 2 + d;
+      float o = 0.0f;
+      for (int s = 0; s < ns; ++s) o = fmaf(wsp[g * ns + s], P[static_cast<int64_t>(s) * a.RS], o);
+      const int dd = a.dims[h * a.D + d];
+      if (dd >= 0 && dd < a.D) a.out[(static_cast<int64_t>(b) * a.hq + i) * a.D + dd] = o / Lsum[g];
+    }
+    if (has_mid)
+      for (int idx = tid; idx < ng * a.k; idx += blockDim.x) {
+        const int g = idx / a.k, n = idx % a.k;
+        const int i = h * a.G + g0 + g;
+        const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS + 2 + a.du + a.dc + n;
+        float w = 0.0f;
+        for (int s = 0; s < ns; ++s) w = fmaf(wsp[g * ns + s], P[static_cast<int64_t>(s) * a.RS], w);
+        Wm[g * a.kpad + n] = w * basis_alpha(n, M);
+      }
+    __syncthreads();
+    // compressible dims: edge part + W . C_V; threads (c, n-group)
+    if (a.dc > 0) {
+      const int dcp = (a.dc + 63) / 64 * 64;
+      const int ngrp = max(1, 256 / dcp);
+      for (int c0 = 0; c0 < dcp; c0 += 256) {
+        const int c = c0 + tid % dcp, grp = tid / dcp;
+        float acc[kMergeRows];
+#pragma unroll
+        for (int g = 0; g < kMergeRows; ++g) acc[g] = 0.0f;
+        if (c < a.dc && grp < ngrp && has_mid) {
+          const float* cvb = a.cv + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc + c;
+          for (int n = grp; n < a.k; n += ngrp) {
+            const float v = cvb[static_cast<int64_t>(n) * a.dc];
+#pragma unroll
+            for (int g = 0; g < kMergeRows; ++g)
+              if (g < ng) acc[g] = fmaf(Wm[g * a.kpad + n], v, acc[g]);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < kMergeRows; ++g) red[tid * kMergeRows + g] = acc[g];
+        __syncthreads();
+        if (grp == 0 && c < a.dc) {
+          for (int g = 0; g < ng; ++g) {
+            float s = 0.0f;
+            for (int q = 0; q < ngrp; ++q) s += red[(q * dcp + (tid % dcp)) * kMergeRows + g];
+            const int i = h * a.G + g0 + g;
+            const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS + 2 + a.du + c;
+            float e = 0.0f;
+            for (int sp = 0; sp < ns; ++sp) e = fmaf(wsp[g * ns + sp], P[static_cast<int64_t>(sp) * a.RS], e);
+            const int dd = a.dims[h * a.D + a.du + c];
+            if (dd >= 0 && dd < a.D) a.out[(static_cast<int64_t>(b) * a.hq + i) * a.D + dd] = (s + e) / Lsum[g];
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t decode_prep_smem(const DecodeArgs& a) { return sizeof(float) * (8 * a.dc + 4 * 8 * 64); }
+size_t decode_split_smem(const DecodeArgs& a) {
+  return sizeof(float) * (kDecRows * a.D + kDecRows * a.kpad + 4 * kDecRows * kDecTile +
+                          kDecTile * kDecRows + kDecRows);
+}
+size_t decode_merge_smem(const DecodeArgs& a, int max_splits) {
+  return sizeof(float) * (kMergeRows * max_splits + kMergeRows * a.kpad + 256 * kMergeRows);
+}
+
+hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
+  if (a.dc == 0) return hipSuccess;
+  dim3 grid(a.nseq * a.hkv, (a.k + 63) / 64);
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(decode_prep_kernel<uint16_t>, grid, dim3(256), decode_prep_smem(a), s, a);
+  else
+    hipLaunchKernelGGL(decode_prep_kernel<float>, grid, dim3(256), decode_prep_smem(a), s, a);
+  return hipGetLastError();
+}
+
+// Kernels whose dynamic LDS may pass 64 KB declare their need first.
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s) {
+  if (nitems == 0) return hipSuccess;
+  const size_t sm = decode_split_smem(a);
+  hipError_t e;
+  if (a.dtype == 1) {
+    if ((e = allow_lds(decode_split_kernel<uint16_t>, sm)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_split_kernel<uint16_t>, dim3(nitems), dim3(256), sm, s, a);
+  } else {
+    if ((e = allow_lds(decode_split_kernel<float>, sm)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_split_kernel<float>, dim3(nitems), dim3(256), sm, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
+  int max_splits = 1;
+  for (int b = 0; b < a.nseq; ++b) max_splits = max(max_splits, a.seq.nsplit[b]);
+  const size_t sm = decode_merge_smem(a, max_splits);
+  const hipError_t e = allow_lds(decode_merge_kernel, sm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.nseq * a.hkv), dim3(256), sm, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa

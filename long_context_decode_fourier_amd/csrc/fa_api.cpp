@@ -1,0 +1,444 @@
+// fa_api.cpp - the C ABI of libfa (declared in include/fa.h).
+//
+// Every entry point validates its arguments on the host first (no HIP call on
+// failure), plans the work split from the host-side sequence lengths, and
+// enqueues kernels on the caller's stream.  Nothing is allocated here and
+// nothing is synchronised.
+#include "fa.h"
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kNumCU = 256;         // MI355X compute units
+constexpr int kMaxCoef = 4097;      // decode keeps per-thread coefficient slots
+constexpr int kMaxHeadDim = 256;
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_err;
+
+fa_status_t fail(fa_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+fa_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Shape {
+  int dtype, B, Hq, Hkv, G, D, Dc, Du, S, R, k;
+  int L[fa::kMaxBatch], M[fa::kMaxBatch];
+  int64_t row0[fa::kMaxBatch];
+  int64_t total_len;
+  bool any_mid;
+};
+
+fa_status_t validate(const fa_desc_t* d, Shape* sh) {
+  if (!d) return fail(FA_ERR_NULL, "desc is NULL");
+  if (d->dtype != FA_F32 && d->dtype != FA_BF16) return fail(FA_ERR_DTYPE, "unknown dtype %d", d->dtype);
+  if (d->reserved != 0) return fail(FA_ERR_SHAPE, "desc.reserved must be 0");
+  if (d->batch < 1 || d->batch > FA_MAX_BATCH)
+    return fail(FA_ERR_SHAPE, "batch %d outside [1, %d]", d->batch, FA_MAX_BATCH);
+  if (!d->seq_len) return fail(FA_ERR_NULL, "desc.seq_len is NULL");
+  if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads)
+    return fail(FA_ERR_SHAPE, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                d->n_q_heads, d->n_kv_heads);
+  if (d->head_dim < 1 || d->head_dim > kMaxHeadDim)
+    return fail(FA_ERR_SHAPE, "head_dim %d outside [1, %d]", d->head_dim, kMaxHeadDim);
+  if (d->n_comp_dims < 0 || d->n_comp_dims > d->head_dim)
+    return fail(FA_ERR_SHAPE, "n_comp_dims %d outside [0, head_dim]", d->n_comp_dims);
+  if (d->sink < 0 || d->recent < 0) return fail(FA_ERR_SHAPE, "sink and recent must be >= 0");
+  if (d->n_coef < 1 || d->n_coef > kMaxCoef)
+    return fail(FA_ERR_SHAPE, "n_coef %d outside [1, %d]", d->n_coef, kMaxCoef);
+  sh->dtype = d->dtype;
+  sh->B = d->batch;
+  sh->Hq = d->n_q_heads;
+  sh->Hkv = d->n_kv_heads;
+  sh->G = d->n_q_heads / d->n_kv_heads;
+  sh->D = d->head_dim;
+  sh->Dc = d->n_comp_dims;
+  sh->Du = d->head_dim - d->n_comp_dims;
+  sh->S = d->sink;
+  sh->R = d->recent;
+  sh->k = d->n_coef;
+  sh->total_len = 0;
+  sh->any_mid = false;
+  for (int b = 0; b < sh->B; ++b) {
+    const int L = d->seq_len[b];
+    if (L < 1 || L > (1 << 30)) return fail(FA_ERR_SHAPE, "seq_len[%d] = %d outside [1, 2^30]", b, L);
+    const int64_t M = std::max<int64_t>(0, static_cast<int64_t>(L) - sh->S - sh->R);
+    if (M > 0 && sh->Dc > 0 && sh->k > M)
+      return fail(FA_ERR_SHAPE, "n_coef %d exceeds the %lld middle tokens of sequence %d", sh->k,
+                  static_cast<long long>(M), b);
+    sh->L[b] = L;
+    sh->M[b] = static_cast<int>(M);
+    sh->row0[b] = static_cast<int64_t>(sh->Hkv) * sh->total_len;
+    sh->total_len += L;
+    sh->any_mid = sh->any_mid || M > 0;
+  }
+  return FA_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// ---------------------------------------------------------------- project --
+
+struct ProjPlan {
+  fa::ProjArgs args;
+  int nitems;
+  bool f16;
+  size_t ws_bytes;
+};
+
+// Split count of one sequence so that items fill the CUs in whole rounds.
+int choose_splits(int tiles, int steps, int slots) {
+  int best = 1;
+  double best_cost = 1e300;
+  for (int s = 1; s <= std::min(64, std::max(1, steps)); ++s) {
+    const int items = tiles * s;
+    const int rounds = (items + slots - 1) / slots;
+    const double per_item = static_cast<double>((steps + s - 1) / s);
+    const double cost = rounds * per_item + (s > 1 ? 0.02 * steps : 0.0);  // partial traffic
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
+fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
+  fa::ProjArgs& a = p->args;
+  std::memset(&a, 0, sizeof a);
+  a.nmat = nmat;
+  a.hkv = sh.Hkv;
+  a.dc = sh.Dc;
+  a.k = sh.k;
+  a.sink = sh.S;
+  a.ncols = nmat * sh.Hkv * sh.Dc;
+  a.nseq = sh.B;
+  p->f16 = sh.dtype == FA_BF16;
+  p->nitems = 0;
+  p->ws_bytes = 0;
+  for (int b = 0; b < sh.B; ++b) {
+    a.seq.len[b] = sh.L[b];
+    a.seq.mid[b] = sh.M[b];
+    a.seq.row0[b] = sh.row0[b];
+  }
+  if (!p->f16 || a.ncols == 0) return FA_OK;
+  if (sh.Dc % 8) return fail(FA_ERR_SHAPE, "bf16 projection needs n_comp_dims %% 8 == 0 (got %d)", sh.Dc);
+
+  // Large tiles (256 x 256, one 8-wave block per CU) when they still give at
+  // least one tile per CU's worth of work; else 64 x 128 tiles (4 waves).
+  double flops = 0.0;
+  for (int b = 0; b < sh.B; ++b) flops += 2.0 * sh.M[b] * sh.k * a.ncols;
+  const bool big = flops > 1.0e11;
+  a.tk = big ? 256 : 64;
+  a.tn = big ? 256 : 128;
+  a.nktiles = (sh.k + a.tk - 1) / a.tk;
+  a.nctiles = (a.ncols + a.tn - 1) / a.tn;
+  const int tiles = a.nktiles * a.nctiles;
+  const int slots = big ? kNumCU : 2 * kNumCU;
+  int64_t total_steps = 0;
+  for (int b = 0; b < sh.B; ++b) total_steps += (sh.M[b] + fa::kProjTT - 1) / fa::kProjTT;
+  bool any_split = false;
+  int item = 0;
+  for (int b = 0; b < sh.B; ++b) {
+    a.seq.item0[b] = item;
+    const int steps = (sh.M[b] + fa::kProjTT - 1) / fa::kProjTT;
+    if (steps == 0) {
+      a.seq.nsplit[b] = 0;
+      a.seq.chunk[b] = 0;
+      continue;
+    }
+    // slots shared among sequences in proportion to their length
+    const int my_slots = std::max(1, static_cast<int>(static_cast<double>(slots) * steps /
+                                                      static_cast<double>(total_steps)));
+    int s = choose_splits(tiles, steps, my_slots);
+    const int chunk_steps = (steps + s - 1) / s;
+    s = (steps + chunk_steps - 1) / chunk_steps;
+    a.seq.nsplit[b] = s;
+    a.seq.chunk[b] = chunk_steps * fa::kProjTT;
+    any_split = any_split || s > 1;
+    item += tiles * s;
+  }
+  p->nitems = item;
+  (void)any_split;
+  p->ws_bytes = align_up(static_cast<size_t>(item) * a.tk * a.tn * sizeof(float));
+  return FA_OK;
+}
+
+// ----------------------------------------------------------------- decode --
+
+struct DecPlan {
+  fa::DecodeArgs args;
+  int nitems;
+  size_t off_A, off_part, ws_bytes;
+};
+
+fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
+  fa::DecodeArgs& a = p->args;
+  std::memset(&a, 0, sizeof a);
+  a.dtype = sh.dtype;
+  a.nseq = sh.B;
+  a.hq = sh.Hq;
+  a.hkv = sh.Hkv;
+  a.G = sh.G;
+  a.D = sh.D;
+  a.du = sh.Du;
+  a.dc = sh.Dc;
+  a.k = sh.k;
+  a.kpad = (sh.k + 3) / 4 * 4;
+  a.sink = sh.S;
+  a.recent = sh.R;
+  if (sh.G <= fa::kDecRows) {
+    int hg = 1;
+    for (int c = 1; c <= sh.Hkv; ++c)
+      if (sh.Hkv % c == 0 && c * sh.G <= fa::kDecRows) hg = c;
+    a.rows = hg * sh.G;
+    a.ngroups = sh.Hkv / hg;
+  } else {
+    if (sh.G % fa::kDecRows)
+      return fail(FA_ERR_SHAPE, "query heads per KV head (%d) must be <= %d or a multiple of it",
+                  sh.G, fa::kDecRows);
+    a.rows = fa::kDecRows;
+    a.ngroups = sh.Hkv * (sh.G / fa::kDecRows);
+  }
+  a.RS = 2 + a.du + a.dc + a.kpad;
+  const int64_t work = sh.total_len * a.ngroups;
+  const int64_t target = 2 * kNumCU;
+  int chunk = static_cast<int>(std::max<int64_t>(
+      fa::kDecTile, (work + target - 1) / target / fa::kDecTile * fa::kDecTile));
+  int item = 0, prow = 0;
+  for (int b = 0; b < sh.B; ++b) {
+    const int ns = (sh.L[b] + chunk - 1) / chunk;
+    a.seq.len[b] = sh.L[b];
+    a.seq.mid[b] = sh.M[b];
+    a.seq.row0[b] = sh.row0[b];
+    a.seq.item0[b] = item;
+    a.seq.nsplit[b] = ns;
+    a.seq.chunk[b] = chunk;
+    a.prow0[b] = prow;
+    item += ns * a.ngroups;
+    prow += ns * sh.Hq;
+  }
+  p->nitems = item;
+  p->off_A = 0;
+  p->off_part = align_up(static_cast<size_t>(sh.B) * sh.Hq * a.kpad * sizeof(float));
+  p->ws_bytes = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
+  return FA_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == FA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_project_workspace_size(const fa_desc_t* desc, size_t* bytes) {
+  Shape sh;
+  if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
+  fa_status_t st = validate(desc, &sh);
+  if (st != FA_OK) return st;
+  // enough for either matrix count (the plan depends on the column count)
+  size_t need = 0;
+  for (int nmat = 1; nmat <= 2; ++nmat) {
+    ProjPlan p;
+    st = plan_project(sh, nmat, &p);
+    if (st != FA_OK) return st;
+    need = std::max(need, p.ws_bytes);
+  }
+  *bytes = need;
+  return FA_OK;
+}
+
+fa_status_t fa_project(const fa_desc_t* desc, const void* kc, const void* vc, float* ck, float* cv,
+                       void* ke, void* ve, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape sh;
+  fa_status_t st = validate(desc, &sh);
+  if (st != FA_OK) return st;
+  if (sh.Dc == 0) return FA_OK;  // no compressible dims: nothing to project or gather
+  if (!kc && !vc) return fail(FA_ERR_NULL, "kc and vc are both NULL");
+  if ((kc && !ck) || (vc && !cv)) return fail(FA_ERR_NULL, "coefficient output missing");
+  if ((!kc && (ck || ke)) || (!vc && (cv || ve)))
+    return fail(FA_ERR_NULL, "outputs given for a matrix without input");
+  const size_t esz = elem_bytes(sh.dtype);
+  const size_t in_bytes = static_cast<size_t>(sh.Hkv) * sh.total_len * sh.Dc * esz;
+  const size_t coef_bytes = static_cast<size_t>(sh.B) * sh.Hkv * sh.k * sh.Dc * sizeof(float);
+  const size_t edge_bytes = static_cast<size_t>(sh.B) * sh.Hkv * (sh.S + sh.R) * sh.Dc * esz;
+  const void* ins[2] = {kc, vc};
+  const void* outs[4] = {ck, cv, ke, ve};
+  const size_t osz[4] = {coef_bytes, coef_bytes, edge_bytes, edge_bytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 2; ++j)
+      if (overlap(outs[i], osz[i], ins[j], in_bytes)) return fail(FA_ERR_ALIAS, "an output overlaps an input");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return fail(FA_ERR_ALIAS, "two outputs overlap");
+  }
+  const int nmat = (kc ? 1 : 0) + (vc ? 1 : 0);
+  ProjPlan p;
+  st = plan_project(sh, nmat, &p);
+  if (st != FA_OK) return st;
+  fa::ProjArgs& a = p.args;
+  int m = 0;
+  if (kc) { a.x[m] = kc; a.out[m] = ck; ++m; }
+  if (vc) { a.x[m] = vc; a.out[m] = cv; ++m; }
+  if (p.f16 && a.ncols > 0) {
+    for (int i = 0; i < nmat; ++i)
+      if (reinterpret_cast<uintptr_t>(a.x[i]) & 15) return fail(FA_ERR_SHAPE, "kc/vc must be 16-byte aligned");
+    if (p.ws_bytes && (!workspace || workspace_bytes < p.ws_bytes))
+      return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                  workspace ? workspace_bytes : 0);
+    if (workspace && (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+      return fail(FA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    a.partial = static_cast<float*>(workspace);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (sh.Dc > 0) {
+    if (p.f16) {
+      e = fa::launch_project_f16(a, p.nitems, s);
+      if (e != hipSuccess) return hip_fail(e, "project kernel");
+      e = fa::launch_project_reduce(a, s);
+      if (e != hipSuccess) return hip_fail(e, "project reduce kernel");
+    } else {
+      e = fa::launch_project_f32(a, s);
+      if (e != hipSuccess) return hip_fail(e, "project f32 kernel");
+    }
+  }
+  if ((ke || ve) && sh.Dc > 0) {
+    fa::EdgeArgs ea;
+    std::memset(&ea, 0, sizeof ea);
+    int n = 0;
+    if (ke) { ea.x[n] = kc; ea.e[n] = ke; ++n; }
+    if (ve) { ea.x[n] = vc; ea.e[n] = ve; ++n; }
+    ea.nmat = n;
+    ea.hkv = sh.Hkv;
+    ea.dc = sh.Dc;
+    ea.sink = sh.S;
+    ea.recent = sh.R;
+    ea.nseq = sh.B;
+    ea.elem_bytes = static_cast<int>(esz);
+    for (int b = 0; b < sh.B; ++b) {
+      ea.seq.len[b] = sh.L[b];
+      ea.seq.row0[b] = sh.row0[b];
+    }
+    e = fa::launch_edge_gather(ea, s);
+    if (e != hipSuccess) return hip_fail(e, "edge gather kernel");
+  }
+  return FA_OK;
+}
+
+fa_status_t fa_decode_workspace_size(const fa_desc_t* desc, size_t* bytes) {
+  Shape sh;
+  if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
+  fa_status_t st = validate(desc, &sh);
+  if (st != FA_OK) return st;
+  DecPlan p;
+  st = plan_decode(sh, &p);
+  if (st != FA_OK) return st;
+  *bytes = p.ws_bytes;
+  return FA_OK;
+}
+
+fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, const void* vx,
+                      const void* ke, const void* ve, const float* ck, const float* cv, float scale,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape sh;
+  fa_status_t st = validate(desc, &sh);
+  if (st != FA_OK) return st;
+  if (!q || !out) return fail(FA_ERR_NULL, "q and out are required");
+  if (!desc->dims) return fail(FA_ERR_NULL, "desc.dims is NULL");
+  if (sh.Du > 0 && (!kx || !vx)) return fail(FA_ERR_NULL, "kx and vx are required when Du > 0");
+  if (sh.Dc > 0 && (!ke || !ve)) return fail(FA_ERR_NULL, "ke and ve are required when Dc > 0");
+  if (sh.Dc > 0 && sh.any_mid && (!ck || !cv))
+    return fail(FA_ERR_NULL, "ck and cv are required when a sequence has middle tokens");
+  if (!(scale == scale)) return fail(FA_ERR_SHAPE, "scale is NaN");
+  DecPlan p;
+  st = plan_decode(sh, &p);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < p.ws_bytes)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                workspace ? workspace_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(FA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  const size_t esz = elem_bytes(sh.dtype);
+  const size_t out_bytes = static_cast<size_t>(sh.B) * sh.Hq * sh.D * sizeof(float);
+  const void* ins[8] = {q, kx, vx, ke, ve, ck, cv, desc->dims};
+  const size_t isz[8] = {static_cast<size_t>(sh.B) * sh.Hq * sh.D * esz,
+                         static_cast<size_t>(sh.Hkv) * sh.total_len * sh.Du * esz,
+                         static_cast<size_t>(sh.Hkv) * sh.total_len * sh.Du * esz,
+                         static_cast<size_t>(sh.B) * sh.Hkv * (sh.S + sh.R) * sh.Dc * esz,
+                         static_cast<size_t>(sh.B) * sh.Hkv * (sh.S + sh.R) * sh.Dc * esz,
+                         static_cast<size_t>(sh.B) * sh.Hkv * sh.k * sh.Dc * sizeof(float),
+                         static_cast<size_t>(sh.B) * sh.Hkv * sh.k * sh.Dc * sizeof(float),
+                         static_cast<size_t>(sh.Hkv) * sh.D * sizeof(int32_t)};
+  for (int i = 0; i < 8; ++i) {
+    if (overlap(out, out_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "out overlaps an input");
+    if (overlap(workspace, p.ws_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "workspace overlaps an input");
+  }
+  if (overlap(out, out_bytes, workspace, p.ws_bytes)) return fail(FA_ERR_ALIAS, "out overlaps the workspace");
+
+  fa::DecodeArgs& a = p.args;
+  a.q = q;
+  a.kx = kx;
+  a.vx = vx;
+  a.ke = ke;
+  a.ve = ve;
+  a.ck = ck;
+  a.cv = cv;
+  a.dims = desc->dims;
+  a.out = out;
+  a.scale = scale;
+  a.A = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_A);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_part);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (sh.Dc > 0 && sh.any_mid) {
+    e = fa::launch_decode_prep(a, s);
+    if (e != hipSuccess) return hip_fail(e, "decode prep kernel");
+  }
+  e = fa::launch_decode_split(a, p.nitems, s);
+  if (e != hipSuccess) return hip_fail(e, "decode split kernel");
+  e = fa::launch_decode_merge(a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode merge kernel");
+  return FA_OK;
+}
+
+const char* fa_status_string(fa_status_t s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "required pointer is NULL";
+    case FA_ERR_SHAPE: return "sizes out of range or inconsistent";
+    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_ALIAS: return "output overlaps another buffer";
+  }
+  return "unknown status";
+}
+
+const char* fa_last_error(void) { return g_err.c_str(); }
+
+int32_t fa_version(void) { return 100; }
+
+}  // extern "C"

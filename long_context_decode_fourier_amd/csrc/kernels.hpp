@@ -1,0 +1,74 @@
+// kernels.hpp - argument blocks and launchers of libfa's HIP kernels.
+//
+// The host API (fa_api.cpp) validates, plans the work split and fills these
+// blocks; the launchers enqueue kernels on the caller's stream.
+#pragma once
+
+#include "common.hpp"
+
+namespace fa {
+
+// ------------------------------------------------------------ projection --
+// Projection of the middle rows of kc / vc onto the first k basis functions.
+// Columns are numbered mat-major: col = (mat * Hkv + h) * Dc + c.
+constexpr int kProjTT = 64;   // middle positions per pipeline step (16-bit path)
+
+struct ProjArgs {
+  const void* x[2];  // kc / vc (element type from dtype); x[m] for mat index m
+  float* out[2];     // ck / cv
+  int nmat;          // matrices present (1 or 2)
+  int hkv, dc, k, sink;
+  int ncols;         // nmat * hkv * dc
+  int tk, tn;        // tile: coefficient rows x columns (16-bit path)
+  int nktiles, nctiles;
+  int nseq;
+  float* partial;    // [items][tk][tn] (16-bit path)
+  SeqTable seq;      // item0/nsplit: items = tiles * nsplit; chunk = positions per split
+};
+
+// Supported tiles (tk x tn): 256 x 256 and 64 x 128.
+bool project_tile_supported(int tk, int tn);
+hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s);
+hipError_t launch_project_reduce(const ProjArgs& a, hipStream_t s);
+hipError_t launch_project_f32(const ProjArgs& a, hipStream_t s);
+
+// Gather of the sink/recent rows of kc (vc) into ke (ve).
+struct EdgeArgs {
+  const void* x[2];
+  void* e[2];
+  int nmat, hkv, dc, sink, recent, nseq, elem_bytes;
+  SeqTable seq;
+};
+hipError_t launch_edge_gather(const EdgeArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- decode --
+constexpr int kDecRows = 4;    // query rows per work item (VALU path)
+constexpr int kDecTile = 64;   // tokens per tile
+
+struct DecodeArgs {
+  int dtype;                   // 0 f32, 1 bf16
+  const void* q;
+  const void* kx;
+  const void* vx;
+  const void* ke;
+  const void* ve;
+  const float* ck;
+  const float* cv;
+  const int32_t* dims;
+  float* out;
+  float* A;      // workspace [B][Hq][kpad]: scale * alpha_n * q_C . ck[n]
+  float* part;   // workspace partials [prow][RS]
+  int nseq, hq, hkv, G, D, du, dc, k, kpad, sink, recent;
+  int rows;      // query rows per work item
+  int ngroups;   // row groups per sequence
+  int RS;        // floats per partial row: 2 + du + dc + kpad
+  float scale;
+  SeqTable seq;  // item0/nsplit/chunk over (row group, split); prow0 below
+  int32_t prow0[kMaxBatch];  // first partial row of sequence b: sum Hq * nsplit
+};
+
+hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace fa

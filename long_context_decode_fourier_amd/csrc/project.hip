@@ -1,0 +1,360 @@
+// project.hip - prefill projection of the compressible dims of the middle
+// tokens onto the real Fourier basis (skill page "fourier-approximated-kv-cache",
+// Step 2; arXiv 2506.11886 abstract: projection onto orthogonal Fourier bases).
+//
+//   C[n][col] = sum_{tau < M} phi_n(tau) X[sink + tau][col]
+//
+// is a dense contraction over tau: per sequence, [k x M] basis times [M x cols]
+// cache rows.  16-bit inputs run it on MFMA (v_mfma_f32_32x32x16_f16): the
+// basis operand is generated in registers (never read from memory), the cache
+// tile is staged through LDS, transposed so that each lane reads its 8
+// consecutive positions with one 16-byte load.  Operands are fp16: bf16 inputs
+// convert to fp16 exactly for |x| in [2^-14, 65504], and the unscaled cos/sin
+// values in [-1, 1] keep 11 significant bits (bf16 would keep 8, which costs
+// an order of magnitude in coefficient accuracy).  Accumulation is fp32.
+//
+// Basis values along a lane's run of 16 consecutive positions come from the
+// three-term recurrence y(t+1) = 2 cos(theta) y(t) - y(t-1), seeded with two
+// exact values from the integer phase (f*tau mod M) and the hardware sin unit;
+// the run length bounds the recurrence's error growth (about 1e-5).
+//
+// fp32 inputs take a VALU kernel with correctly rounded phases (sincospi per
+// value) and compensated summation, which keeps coefficients within 1e-5.
+#include "kernels.hpp"
+
+namespace fa {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kLdsStride = kProjTT + 8;  // halves per LDS column (padding spreads banks)
+
+struct ProjItem {
+  int b, ktile, ctile, t_begin, t_end, M;
+};
+
+__device__ inline ProjItem proj_item(const ProjArgs& a, int item) {
+  ProjItem it;
+  it.b = seq_of_item(a.seq, a.nseq, item);
+  const int local = item - a.seq.item0[it.b];
+  const int ns = a.seq.nsplit[it.b];
+  const int tile = local / ns, sp = local % ns;
+  it.ktile = tile / a.nctiles;
+  it.ctile = tile % a.nctiles;
+  it.M = a.seq.mid[it.b];
+  it.t_begin = sp * a.seq.chunk[it.b];
+  it.t_end = min(it.M, it.t_begin + a.seq.chunk[it.b]);
+  return it;
+}
+
+// Wave grid WR x WC; each wave owns RB x CB blocks of 32 x 32 outputs.
+template <int WR, int WC, int RB, int CB>
+__global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
+  constexpr int kThreads = 64 * WR * WC;
+  constexpr int TK = WR * RB * 32;
+  constexpr int TN = WC * CB * 32;
+  constexpr int kColGroups = TN / 8;
+  constexpr int kPosGroups = kThreads / kColGroups;
+  constexpr int kPosPerThread = kProjTT / kPosGroups;
+  static_assert(kPosPerThread * kPosGroups == kProjTT, "tile/thread mismatch");
+  static_assert(kPosPerThread == 4, "loader packs 4 positions per column");
+
+  __shared__ __attribute__((aligned(16))) _Float16 xt[TN * kLdsStride];
+
+  const ProjItem it = proj_item(a, blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / WC, wc = wave % WC;
+  const int M = it.M;
+  const int L = a.seq.len[it.b];
+  const int64_t row0 = a.seq.row0[it.b];
+
+  // ---- loader: 8 consecutive columns x 4 positions per thread
+  const int cg = tid % kColGroups, pg = tid / kColGroups;
+  const int col0 = it.ctile * TN + cg * 8;
+  const bool col_ok = col0 < a.ncols;  // Dc % 8 == 0: the 8 columns share (mat, h)
+  const uint16_t* xbase = nullptr;
+  if (col_ok) {
+    const int blk = col0 / a.dc, c0 = col0 % a.dc;
+    const int mat = blk / a.hkv, h = blk % a.hkv;
+    xbase = static_cast<const uint16_t*>(a.x[mat]) +
+            (row0 + static_cast<int64_t>(h) * L + a.sink) * a.dc + c0;
+  }
+
+  // ---- basis generator state, one coefficient row per lane and row block
+  const float invM = 1.0f / static_cast<float>(M);
+  float c2[RB], off[RB];
+  int fr[RB], ph[RB], d16[RB], d64[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int n = it.ktile * TK + wr * (RB * 32) + rb * 32 + (lane & 31);
+    const int ne = min(n, a.k - 1);
+    const int f = basis_freq(ne) % M;
+    float s, c;
+    sincos_phase(f, M, &s, &c);
+    c2[rb] = 2.0f * c;
+    off[rb] = basis_is_cos(ne) ? 0.25f : 0.0f;  // cos(2 pi x) = sin(2 pi (x + 1/4))
+    fr[rb] = f;
+    ph[rb] = phase_mod(f, it.t_begin + 32 * (lane >> 5), M);
+    d16[rb] = phase_mod(f, 16, M);
+    d64[rb] = phase_mod(f, kProjTT, M);
+  }
+
+  floatx16 acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
+
+  for (int step = it.t_begin; step < it.t_end; step += kProjTT) {
+    uint4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tau = step + pg * 4 + i;
+      if (col_ok && tau < it.t_end)
+        raw[i] = *reinterpret_cast<const uint4*>(xbase + static_cast<int64_t>(tau) * a.dc);
+      else
+        raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();  // the previous step's MFMA reads of xt are done
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      half4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = (j < 2) ? raw[i].x : (j < 4) ? raw[i].y : (j < 6) ? raw[i].z : raw[i].w;
+        const uint32_t bits = (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
+        v[i] = static_cast<_Float16>(__uint_as_float(bits));
+      }
+      *reinterpret_cast<half4*>(&xt[(cg * 8 + j) * kLdsStride + pg * 4]) = v;
+    }
+    __syncthreads();
+
+    float yp[RB], yc[RB];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8 av[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float v[8];
+        if ((s & 1) == 0) {
+          int r0 = ph[rb];
+          if (s == 2) { r0 += d16[rb]; if (r0 >= M) r0 -= M; }
+          int r1 = r0 + fr[rb];
+          if (r1 >= M) r1 -= M;
+          v[0] = sin_rev(fmaf(static_cast<float>(r0), invM, off[rb]));
+          v[1] = sin_rev(fmaf(static_cast<float>(r1), invM, off[rb]));
+#pragma unroll
+          for (int e = 2; e < 8; ++e) v[e] = fmaf(c2[rb], v[e - 1], -v[e - 2]);
+        } else {
+          v[0] = fmaf(c2[rb], yc[rb], -yp[rb]);
+          v[1] = fmaf(c2[rb], v[0], -yc[rb]);
+#pragma unroll
+          for (int e = 2; e < 8; ++e) v[e] = fmaf(c2[rb], v[e - 1], -v[e - 2]);
+        }
+        yp[rb] = v[6];
+        yc[rb] = v[7];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[rb][e] = static_cast<_Float16>(v[e]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const half8 bv = *reinterpret_cast<const half8*>(
+            &xt[(wc * (CB * 32) + cb * 32 + (lane & 31)) * kLdsStride + 32 * (lane >> 5) + 8 * s]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rb], bv, acc[rb][cb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ph[rb] += d64[rb];
+      if (ph[rb] >= M) ph[rb] -= M;
+    }
+  }
+
+  float* P = a.partial + static_cast<int64_t>(blockIdx.x) * TK * TN;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int nl = wr * (RB * 32) + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int cl = wc * (CB * 32) + cb * 32 + (lane & 31);
+        P[nl * TN + cl] = acc[rb][cb][r];
+      }
+}
+
+// Fixed-order sum of the split partials of one tile row, scaled by the basis
+// normalisation, scattered to ck / cv.  Sequences without middle get zeros.
+__global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a) {
+  const int tk = a.tk, tn = a.tn;
+  const int tiles = a.nktiles * a.nctiles;
+  int g = blockIdx.x;
+  const int nl = g % tk;
+  g /= tk;
+  const int tile = g % tiles, b = g / tiles;
+  const int kt = tile / a.nctiles, ct = tile % a.nctiles;
+  const int n = kt * tk + nl;
+  for (int cl = threadIdx.x; cl < tn; cl += blockDim.x) {
+    const int col = ct * tn + cl;
+    if (n >= a.k || col >= a.ncols) continue;
+    const int ns = a.seq.nsplit[b];
+    const float* P = a.partial +
+                     (static_cast<int64_t>(a.seq.item0[b] + tile * ns) * tk + nl) * tn + cl;
+    float sum = 0.0f;
+    for (int sp = 0; sp < ns; ++sp) sum += P[static_cast<int64_t>(sp) * tk * tn];
+    const int M = a.seq.mid[b];
+    float alpha = 0.0f;
+    if (M > 0) {
+      const int f = basis_freq(n);
+      alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
+                                     : sqrtf(2.0f / static_cast<float>(M));
+    }
+    const int blk = col / a.dc, c = col % a.dc, mat = blk / a.hkv, h = blk % a.hkv;
+    a.out[mat][((static_cast<int64_t>(b) * a.hkv + h) * a.k + n) * a.dc + c] = alpha * sum;
+  }
+}
+
+// fp32 inputs: one block per (sequence, matrix, KV head, 8 coefficients).
+// Thread (c, lane-of-8 positions) sums phi_n(tau) x[tau][c] over its residue
+// class of tau with Kahan compensation; the 8 partial sums are added in a
+// fixed tree.  The basis value is computed from the exact integer phase.
+constexpr int kF32Coefs = 8;
+
+__global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
+  __shared__ float red[8][kF32Coefs][32];
+  const int ntile = (a.k + kF32Coefs - 1) / kF32Coefs;
+  int g = blockIdx.x;
+  const int nt = g % ntile;
+  g /= ntile;
+  const int h = g % a.hkv;
+  g /= a.hkv;
+  const int mat = g % a.nmat, b = g / a.nmat;
+  const int M = a.seq.mid[b], L = a.seq.len[b];
+  const int cl = threadIdx.x & 31, tl = threadIdx.x >> 5;
+  const float* X = static_cast<const float*>(a.x[mat]) +
+                   (a.seq.row0[b] + static_cast<int64_t>(h) * L + a.sink) * a.dc;
+  float* out = a.out[mat] + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc;
+  for (int c0 = 0; c0 < a.dc; c0 += 32) {
+    const int c = c0 + cl;
+    float sum[kF32Coefs], comp[kF32Coefs];
+#pragma unroll
+    for (int i = 0; i < kF32Coefs; ++i) sum[i] = comp[i] = 0.0f;
+    if (c < a.dc) {
+      for (int tau = tl; tau < M; tau += 8) {
+        const float x = X[static_cast<int64_t>(tau) * a.dc + c];
+#pragma unroll
+        for (int i = 0; i < kF32Coefs; ++i) {
+          const int n = min(nt * kF32Coefs + i, a.k - 1);
+          float s, co;
+          sincos_phase(phase_mod(basis_freq(n), tau, M), M, &s, &co);
+          const float term = x * (basis_is_cos(n) ? co : s) - comp[i];
+          const float t = sum[i] + term;
+          comp[i] = (t - sum[i]) - term;
+          sum[i] = t;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kF32Coefs; ++i) red[tl][i][cl] = sum[i];
+    __syncthreads();
+    if (tl == 0 && c < a.dc) {
+#pragma unroll
+      for (int i = 0; i < kF32Coefs; ++i) {
+        const int n = nt * kF32Coefs + i;
+        const float s01 = red[0][i][cl] + red[1][i][cl], s23 = red[2][i][cl] + red[3][i][cl];
+        const float s45 = red[4][i][cl] + red[5][i][cl], s67 = red[6][i][cl] + red[7][i][cl];
+        const float total = (s01 + s23) + (s45 + s67);
+        if (n < a.k) {
+          float alpha = 0.0f;
+          if (M > 0) {
+            const int f = basis_freq(n);
+            alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
+                                           : sqrtf(2.0f / static_cast<float>(M));
+          }
+          out[static_cast<int64_t>(n) * a.dc + c] = alpha * total;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Retained rows (sink, then recent; all rows when L <= sink + recent).
+__global__ __launch_bounds__(256) void edge_gather_kernel(EdgeArgs a) {
+  const int E = a.sink + a.recent;
+  int g = blockIdx.x;  // (b, mat, h, edge row)
+  const int e = g % E;
+  g /= E;
+  const int h = g % a.hkv;
+  g /= a.hkv;
+  const int mat = g % a.nmat, b = g / a.nmat;
+  const int L = a.seq.len[b];
+  int t;
+  if (L <= E) {
+    if (e >= L) return;
+    t = e;
+  } else {
+    t = (e < a.sink) ? e : L - E + e;
+  }
+  const int64_t src_row = a.seq.row0[b] + static_cast<int64_t>(h) * L + t;
+  const int64_t dst_row = (static_cast<int64_t>(b) * a.hkv + h) * E + e;
+  const int nbytes = a.dc * a.elem_bytes;
+  const char* src = static_cast<const char*>(a.x[mat]) + src_row * nbytes;
+  char* dst = static_cast<char*>(a.e[mat]) + dst_row * nbytes;
+  if ((nbytes & 3) == 0) {
+    for (int i = threadIdx.x; i < nbytes / 4; i += blockDim.x)
+      reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
+  } else {
+    for (int i = threadIdx.x; i < nbytes / 2; i += blockDim.x)
+      reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(src)[i];
+  }
+}
+
+}  // namespace
+
+// Tile configurations of the 16-bit kernel: 256 x 256 (8 waves) for large
+// problems, 64 x 128 (4 waves) when large tiles would leave CUs idle.
+bool project_tile_supported(int tk, int tn) {
+  return (tk == 256 && tn == 256) || (tk == 64 && tn == 128);
+}
+
+hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
+  if (nitems == 0) return hipSuccess;
+  if (a.tk == 256 && a.tn == 256)
+    hipLaunchKernelGGL((project_f16_kernel<4, 2, 2, 4>), dim3(nitems), dim3(512), 0, s, a);
+  else if (a.tk == 64 && a.tn == 128)
+    hipLaunchKernelGGL((project_f16_kernel<2, 2, 1, 2>), dim3(nitems), dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_project_reduce(const ProjArgs& a, hipStream_t s) {
+  const int blocks = a.nseq * a.nktiles * a.nctiles * a.tk;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(project_reduce_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_f32(const ProjArgs& a, hipStream_t s) {
+  const int ntile = (a.k + kF32Coefs - 1) / kF32Coefs;
+  const int blocks = a.nseq * a.nmat * a.hkv * ntile;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(project_f32_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_edge_gather(const EdgeArgs& a, hipStream_t s) {
+  const int blocks = a.nseq * a.nmat * a.hkv * (a.sink + a.recent);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(edge_gather_kernel, dim3(blocks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fa.h declares, and host validation returns its status codes before any
+HIP call (so these run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_decode_fourier_amd import binding as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fb.LIB_PATH),
+                                reason="libfa.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"fa_project", "fa_decode", "fa_project_workspace_size",
+            "fa_decode_workspace_size", "fa_status_string", "fa_last_error",
+            "fa_version"} <= set(names)
+    L = ctypes.CDLL(fb.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert fb.lib().fa_version() >= 100
+
+
+def test_status_strings():
+    for code in range(7):
+        assert fb.lib().fa_status_string(code)
+
+
+def _desc(**kw):
+    base = dict(dtype=fb.BF16, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                n_comp_dims=64, n_coef=33, seq_len=[4096, 1000])
+    base.update(kw)
+    return fb.Desc(**base)
+
+
+def _size(fn, d):
+    n = ctypes.c_size_t(0)
+    st = fn(ctypes.byref(d.c), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 3),
+    (dict(batch=0, seq_len=[]), 2),
+    (dict(batch=65, seq_len=[100] * 65), 2),
+    (dict(n_q_heads=7), 2),
+    (dict(n_kv_heads=0), 2),
+    (dict(head_dim=0), 2),
+    (dict(head_dim=512), 2),
+    (dict(n_comp_dims=129), 2),
+    (dict(n_comp_dims=-1), 2),
+    (dict(n_coef=0), 2),
+    (dict(n_coef=4098), 2),
+    (dict(seq_len=[4096, 0]), 2),
+    (dict(seq_len=[4096, 120]), 2),   # 24 middle tokens < 33 coefficients
+    (dict(sink=-1), 2),
+])
+def test_invalid_desc(kw, code):
+    d = _desc(**kw)
+    for fn in (fb.lib().fa_project_workspace_size, fb.lib().fa_decode_workspace_size):
+        st, _ = _size(fn, d)
+        assert st == code, (kw, st, fb.lib().fa_last_error())
+        assert fb.lib().fa_last_error()
+
+
+def test_workspace_sizes_and_short_sequences():
+    d = _desc()
+    st, n = _size(fb.lib().fa_decode_workspace_size, d)
+    assert st == 0 and n > 0 and n % 256 == 0
+    st, n = _size(fb.lib().fa_project_workspace_size, d)
+    assert st == 0 and n % 256 == 0
+    # sequences not longer than sink + recent have no middle: any k is accepted
+    st, _ = _size(fb.lib().fa_decode_workspace_size, _desc(seq_len=[96, 50], n_coef=4000))
+    assert st == 0
+    # no compressible dims: k is not checked against the middle length
+    st, _ = _size(fb.lib().fa_decode_workspace_size, _desc(n_comp_dims=0, seq_len=[100, 100]))
+    assert st == 0
+
+
+GB = 1 << 30  # fake device addresses, 1 GiB apart; every call below fails validation
+
+
+def _call_decode(d, q=1, kx=2, vx=3, ke=4, ve=5, ck=6, cv=7, out=8, ws=9 * GB, nws=1 << 30):
+    P = lambda v: ctypes.c_void_p(v * GB if 0 < v < 64 else v)
+    return fb.lib().fa_decode(ctypes.byref(d.c), P(q), P(kx), P(vx), P(ke), P(ve), P(ck), P(cv),
+                              ctypes.c_float(0.1), P(out), P(ws), nws, None)
+
+
+def test_decode_host_errors_without_gpu():
+    dims_holder = type("T", (), {"data_ptr": lambda self: 10 * GB})()
+    d = _desc(dims=dims_holder)
+    assert _call_decode(d, q=0) == 1
+    assert _call_decode(d, out=0) == 1
+    assert _call_decode(d, kx=0) == 1
+    assert _call_decode(d, ke=0) == 1
+    assert _call_decode(d, ck=0) == 1
+    assert _call_decode(d, ws=0) == 4
+    assert _call_decode(d, nws=16) == 4
+    assert _call_decode(d, ws=9 * GB + 8) == 4          # misaligned workspace
+    assert _call_decode(d, out=1 * GB + 64) == 6         # out inside q
+    assert _call_decode(d, ws=3 * GB + 256) == 6         # workspace inside vx
+    assert _call_decode(_desc()) == 1                    # desc.dims missing
+
+
+def test_project_host_errors_without_gpu():
+    d = _desc()
+    P = lambda v: ctypes.c_void_p(v)
+    f = fb.lib().fa_project
+    base = 1 << 40
+    # nothing to project
+    assert f(ctypes.byref(d.c), P(0), P(0), P(0), P(0), P(0), P(0), P(0), 0, None) == 1
+    # kc without ck
+    assert f(ctypes.byref(d.c), P(base), P(0), P(0), P(0), P(0), P(0), P(0), 0, None) == 1
+    # ck overlapping kc
+    assert f(ctypes.byref(d.c), P(base), P(0), P(base + 64), P(0), P(0), P(0), P(0), 0, None) == 6
+    # misaligned kc (bf16 path needs 16-byte rows)
+    assert f(ctypes.byref(d.c), P(base + 2), P(0), P(base * 2), P(0), P(0), P(0),
+             P(base * 3), 1 << 30, None) == 2
+    # workspace too small
+    assert f(ctypes.byref(d.c), P(base), P(0), P(base * 2), P(0), P(0), P(0), P(base * 3),
+             16, None) == 4
+    # bf16 projection needs Dc % 8 == 0
+    d12 = _desc(n_comp_dims=12)
+    assert f(ctypes.byref(d12.c), P(base), P(0), P(base * 2), P(0), P(0), P(0), P(base * 3),
+             1 << 30, None) == 2

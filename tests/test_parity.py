@@ -1,0 +1,271 @@
+"""GPU parity: libfa (through the C ABI) against the CPU oracle.
+
+Bars (per dtype of the inputs):
+* fp32 inputs: max-abs error <= 1e-5 for coefficients and outputs;
+* bf16 inputs: output max-abs error <= 3e-3; coefficient relative L2 error
+  <= 1e-3 in every (sequence, KV head, K/V) block.
+Decode is checked end to end (GPU coefficients on the GPU side, oracle
+coefficients on the oracle side) and in isolation (both sides fed the oracle's
+coefficients, rounded to fp32).  Full-size workloads are checked on sampled
+(sequence, KV head) blocks; small shapes span several tiles, ragged tails and
+the degenerate cases (no middle, k = M, k = 1, no compressible dims, all dims
+compressible).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from long_context_decode_fourier_amd import workloads as wl  # noqa: E402
+from oracle import batch as ob  # noqa: E402
+from oracle import fourier_attention as fa  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL_BF16 = 3e-3
+COEF_REL_BF16 = 1e-3
+TOL_F32 = 1e-5
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_decode_fourier_amd import binding
+    binding.lib()  # raises if libfa.so is missing: no fallback
+    return binding
+
+
+class Run:
+    """Uploads a workload and runs fa_project / fa_decode on it."""
+
+    def __init__(self, fb, w):
+        self.fb, self.w, c = fb, w, w.cfg
+        self.c = c
+        dev = "cuda"
+        self.dims = torch.from_numpy(w.dims).to(dev)
+        self.desc = fb.Desc.from_workload(w, self.dims)
+        self.kc = fb.to_device(w.kc)
+        self.vc = fb.to_device(w.vc)
+        self.q = fb.to_device(w.q) if w.q is not None else None
+        self.kx = fb.to_device(w.kx) if w.kx is not None else None
+        self.vx = fb.to_device(w.vx) if w.vx is not None else None
+        nblk = c.batch * c.n_kv_heads
+        self.ck = torch.full((nblk, c.n_coef, c.n_comp), float("nan"), device=dev)
+        self.cv = torch.full_like(self.ck, float("nan"))
+        E = c.sink + c.recent
+        self.ke = torch.zeros((nblk, E, c.n_comp), dtype=self.kc.dtype, device=dev)
+        self.ve = torch.zeros_like(self.ke)
+        self.scale = 1.0 / np.sqrt(c.head_dim)
+
+    def project(self):
+        self.fb.project(self.desc, self.kc, self.vc, self.ck, self.cv, self.ke, self.ve)
+        torch.cuda.synchronize()
+        return self.ck.cpu().numpy().astype(np.float64), self.cv.cpu().numpy().astype(np.float64)
+
+    def decode(self, ck=None, cv=None):
+        c = self.c
+        ck = self.ck if ck is None else torch.from_numpy(np.asarray(ck, np.float32)).cuda()
+        cv = self.cv if cv is None else torch.from_numpy(np.asarray(cv, np.float32)).cuda()
+        out = torch.full((c.batch, c.n_q_heads, c.head_dim), float("nan"), device="cuda")
+        self.fb.decode(self.desc, self.q, self.kx, self.vx, self.ke, self.ve, ck, cv,
+                       self.scale, out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+
+def _coef_errors(got, want):
+    """(worst per-block relative L2, max-abs) over blocks with a middle."""
+    rel, mab = 0.0, 0.0
+    if got.size == 0:
+        return rel, mab
+    for g, t in zip(got, want):
+        nt = np.linalg.norm(t)
+        if nt == 0:
+            assert np.abs(g).max() == 0
+            continue
+        rel = max(rel, np.linalg.norm(g - t) / nt)
+        mab = max(mab, np.abs(g - t).max())
+    return rel, mab
+
+
+def _check_coefs(w, got_k, got_v, want_k, want_v, blocks=None):
+    if blocks is not None:
+        got_k, got_v = got_k[blocks], got_v[blocks]
+    rel_k, mab_k = _coef_errors(got_k, want_k)
+    rel_v, mab_v = _coef_errors(got_v, want_v)
+    _say("  coef rel-L2 K %.2e V %.2e  max-abs K %.2e V %.2e" % (rel_k, rel_v, mab_k, mab_v))
+    if w.cfg.dtype == "f32":
+        assert max(mab_k, mab_v) <= TOL_F32
+    else:
+        assert max(rel_k, rel_v) <= COEF_REL_BF16
+
+
+def _check_out(w, got, want, what):
+    err = np.abs(got - want).max()
+    _say("  %s out max-abs %.2e" % (what, err))
+    assert np.isfinite(got).all()
+    assert err <= (TOL_F32 if w.cfg.dtype == "f32" else OUT_TOL_BF16)
+
+
+def _edges_ok(run):
+    w = run.w
+    for X, E in ((w.kc, run.ke), (w.vc, run.ve)):
+        want = w.edges(X)
+        got = E.cpu()
+        got = got.view(torch.int16).numpy().view(np.uint16) if w.cfg.dtype == "bf16" else got.numpy()
+        for b in range(w.cfg.batch):
+            n = min(int(w.lens[b]), w.cfg.sink + w.cfg.recent)
+            for h in range(w.cfg.n_kv_heads):
+                i = b * w.cfg.n_kv_heads + h
+                assert np.array_equal(got[i, :n], want[i, :n])
+
+
+def _full_check(fb, w):
+    run = Run(fb, w)
+    ck_g, cv_g = run.project()
+    _edges_ok(run)
+    ck_o, cv_o = ob.project_all(w)
+    _check_coefs(w, ck_g, cv_g, ck_o, cv_o)
+    want = ob.decode_all(w, ck_o, cv_o, run.scale)
+    _check_out(w, run.decode(), want, "end-to-end")
+    ck32, cv32 = ck_o.astype(np.float32), cv_o.astype(np.float32)
+    want32 = ob.decode_all(w, ck32.astype(np.float64), cv32.astype(np.float64), run.scale)
+    _check_out(w, run.decode(ck32, cv32), want32, "isolated")
+    return run
+
+
+SMALL = {
+    "f32_tiny": (dict(dtype="f32", batch=1, n_q_heads=1, n_kv_heads=1, head_dim=8, n_comp=4,
+                      n_coef=5, seq_len=120, mask="low"), None),
+    "f32_gqa_ragged": (dict(dtype="f32", batch=3, n_q_heads=4, n_kv_heads=2, head_dim=16,
+                            n_comp=8, n_coef=9), [200, 106, 333]),
+    "bf16_mha_ragged": (dict(dtype="bf16", batch=2, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                             n_comp=32, n_coef=33), [300, 517]),
+    "bf16_gqa4_tiles": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                             n_comp=64, n_coef=301), [1000, 777]),
+    "bf16_gqa8": (dict(dtype="bf16", batch=1, n_q_heads=16, n_kv_heads=2, head_dim=64,
+                       n_comp=16, n_coef=101), [400]),
+    "bf16_even_k": (dict(dtype="bf16", batch=1, n_q_heads=2, n_kv_heads=2, head_dim=32,
+                         n_comp=8, n_coef=64), [300]),
+    "bf16_k_equals_m": (dict(dtype="bf16", batch=2, n_q_heads=2, n_kv_heads=1, head_dim=32,
+                             n_comp=16, n_coef=50), [146, 146]),
+    "bf16_short_and_k1": (dict(dtype="bf16", batch=4, n_q_heads=4, n_kv_heads=2, head_dim=32,
+                               n_comp=8, n_coef=1), [50, 96, 97, 1]),
+    "bf16_no_comp_dims": (dict(dtype="bf16", batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                               n_comp=0, n_coef=3), [500, 130]),
+    "bf16_all_comp_dims": (dict(dtype="bf16", batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                                n_comp=64, n_coef=41), [700]),
+    "bf16_many_tiles": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=8, head_dim=128,
+                             n_comp=96, n_coef=513), [5000, 2345]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_shapes(fb, name):
+    kw, lens = SMALL[name]
+    cfg = wl.custom(name=name, seed=100 + sorted(SMALL).index(name), **kw)
+    _say("case %s lens=%s" % (name, lens))
+    w = wl.make(cfg, lens=lens)
+    _full_check(fb, w)
+
+
+def test_fp32_head(fb):
+    _say("case fp32_head")
+    _full_check(fb, wl.make(wl.CONFIGS["fp32_head"]))
+
+
+def test_llama2_7b_layer(fb):
+    _say("case llama2_7b_layer")
+    _full_check(fb, wl.make(wl.CONFIGS["llama2_7b_layer"]))
+
+
+def _sampled_decode_check(fb, w, blocks):
+    """GPU project + decode of the whole workload; oracle on sampled blocks."""
+    run = Run(fb, w)
+    ck_g, cv_g = run.project()
+    _edges_ok(run)
+    got = run.decode()
+    c = w.cfg
+    G = c.group
+    ck_i, cv_i = run.ck.clone(), run.cv.clone()
+    wants = []
+    for b, h in blocks:
+        i = b * c.n_kv_heads + h
+        ck_o, cv_o = ob.project_block(w, b, h)
+        _check_coefs(w, ck_g[[i]], cv_g[[i]], ck_o[None], cv_o[None])
+        want = ob.decode_block(w, ck_o, cv_o, run.scale, b, h)
+        _check_out(w, got[b, h * G:(h + 1) * G], want, "end-to-end b=%d h=%d" % (b, h))
+        ck_i[i] = torch.from_numpy(ck_o.astype(np.float32)).cuda()
+        cv_i[i] = torch.from_numpy(cv_o.astype(np.float32)).cuda()
+        wants.append((b, h, ob.decode_block(w, ck_o.astype(np.float32).astype(np.float64),
+                                            cv_o.astype(np.float32).astype(np.float64),
+                                            run.scale, b, h)))
+    iso = run.decode(ck_i.cpu().numpy(), cv_i.cpu().numpy())
+    for b, h, want in wants:
+        _check_out(w, iso[b, h * G:(h + 1) * G], want, "isolated b=%d h=%d" % (b, h))
+
+
+def test_llama3_8b_gqa(fb):
+    _say("case llama3_8b_gqa (sampled blocks)")
+    w = wl.make(wl.CONFIGS["llama3_8b_gqa"])
+    _sampled_decode_check(fb, w, [(0, 0), (3, 7)])
+
+
+def test_ragged_batch(fb):
+    _say("case ragged_batch (sampled blocks)")
+    w = wl.make(wl.CONFIGS["ragged_batch"])
+    longest = int(np.argmax(w.lens))
+    _sampled_decode_check(fb, w, [(longest, 5), (int(np.argmin(w.lens)), 0)])
+
+
+def test_prefill_projection(fb):
+    """Full-size projection; oracle on sampled column blocks (all k rows)."""
+    _say("case prefill_projection (sampled column blocks)")
+    w = wl.make(wl.CONFIGS["prefill_projection"])
+    c = w.cfg
+    dims = torch.from_numpy(w.dims).cuda()
+    desc = fb.Desc.from_workload(w, dims)
+    kc, vc = fb.to_device(w.kc), fb.to_device(w.vc)
+    ck = torch.full((c.n_kv_heads, c.n_coef, c.n_comp), float("nan"), device="cuda")
+    cv = torch.full_like(ck, float("nan"))
+    fb.project(desc, kc, vc, ck, cv)
+    torch.cuda.synchronize()
+    ck_g, cv_g = ck.cpu().numpy().astype(np.float64), cv.cpu().numpy().astype(np.float64)
+    assert np.isfinite(ck_g).all() and np.isfinite(cv_g).all()
+    M = int(w.lens[0]) - c.sink - c.recent
+    for h, which, cols in [(0, "k", [0, 1, 63]), (7, "v", [5, 40])]:
+        X = w.f64(w.block(w.kc if which == "k" else w.vc, 0, h))[c.sink:c.sink + M][:, cols]
+        want = fa.project(X, c.n_coef)
+        got = (ck_g if which == "k" else cv_g)[h][:, cols]
+        rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+        _say("  h=%d %s cols=%s rel-L2 %.2e" % (h, which, cols, rel))
+        assert rel <= COEF_REL_BF16
+
+
+def test_determinism(fb):
+    _say("case determinism")
+    cfg = wl.custom(name="det", dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                    n_comp=64, n_coef=257, seed=7)
+    w = wl.make(cfg, lens=[3000, 2100])
+    run = Run(fb, w)
+    a1 = run.project()
+    o1 = run.decode()
+    a2 = run.project()
+    o2 = run.decode()
+    assert np.array_equal(a1[0], a2[0]) and np.array_equal(a1[1], a2[1])
+    assert np.array_equal(o1, o2)
+
+
+def test_one_hip_runtime(fb):
+    with open("/proc/self/maps") as f:
+        libs = {l.split()[-1] for l in f if "libamdhip64" in l}
+    assert len(libs) == 1, libs
