@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the Fourier-approximated KV-cache hot path on one MI355X.
+
+One step = the whole path on one batch of synthetic input:
+``fa_project`` (coefficients of K and V plus the retained edge rows) followed by
+``fa_decode`` (one decode step for every query head).  The default workload is
+the LLaMA-2-7B-shaped layer (32/32 heads, head_dim 128, L = 4096, 64 of 128 dims
+compressible, k = 401).  Inputs are resident in HBM before timing starts and
+are rotated over enough copies that one step's inputs are not in the 256 MB
+last-level cache.
+
+Prints ONE JSON line: metric/value (KV-positions per second of the whole
+step), per-call figures (decode HBM GB/s, projection TFLOP/s), the roofline of
+the dominant kernel (algorithmic bytes or flops over its event-timed duration)
+and the CPU oracle's rate on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic(w):
+    """(decode must-read+write bytes, projection flops, KV positions) per step."""
+    c = w.cfg
+    esz = 2 if c.dtype == "bf16" else 4
+    E = c.sink + c.recent
+    dec = 0
+    flops = 0.0
+    for b in range(c.batch):
+        L, M = int(w.lens[b]), w.mid_len(b)
+        dec += c.n_kv_heads * L * c.n_exact * 2 * esz                 # kx, vx
+        dec += c.n_kv_heads * min(L, E) * c.n_comp * 2 * esz          # ke, ve
+        if M > 0:
+            dec += c.n_kv_heads * c.n_coef * c.n_comp * 2 * 4          # ck, cv
+            flops += 2.0 * M * c.n_coef * c.n_kv_heads * c.n_comp * 2  # K and V
+    dec += c.batch * c.n_q_heads * c.head_dim * (esz + 4)              # q in, out
+    pos = int(w.lens.sum()) * c.n_kv_heads
+    return dec, flops, pos
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_decode_fourier_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counters, if still valid."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("sources") != kernel_sources_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, scale, seconds):
+    """The oracle (fp64 numpy) on the same workload, repeated ~`seconds`."""
+    from oracle import batch as ob
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    steps = w.cfg.steps
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        ck, cv = ob.project_all(w)
+        if "decode" in steps:
+            ob.decode_all(w, ck, cv, scale)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return dt, threads, n
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama2_7b_layer")
+    ap.add_argument("--copies", type=int, default=0, help="input copies (0: enough to beat the LLC)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_decode_fourier_amd import binding as fb
+    from long_context_decode_fourier_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fb.lib()
+    cfg = wl.CONFIGS[args.workload]
+    w = wl.make(cfg)
+    c = cfg
+    steps = c.steps
+    dec_bytes, proj_flops, positions = algorithmic(w)
+    scale = 1.0 / np.sqrt(c.head_dim)
+
+    dev = "cuda"
+    dims = torch.from_numpy(w.dims).to(dev)
+    desc = fb.Desc.from_workload(w, dims)
+    nblk = c.batch * c.n_kv_heads
+    E = c.sink + c.recent
+    base = dict(kc=fb.to_device(w.kc), vc=fb.to_device(w.vc))
+    if "decode" in steps:
+        base.update(q=fb.to_device(w.q), kx=fb.to_device(w.kx), vx=fb.to_device(w.vx))
+    per_copy = sum(t.numel() * t.element_size() for t in base.values())
+    copies = args.copies or max(2, int(np.ceil(2 * LLC_BYTES / per_copy)) + 1)
+    sets = []
+    for i in range(copies):
+        s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
+        s["ck"] = torch.empty((nblk, c.n_coef, c.n_comp), device=dev)
+        s["cv"] = torch.empty_like(s["ck"])
+        s["ke"] = torch.empty((nblk, E, c.n_comp), dtype=base["kc"].dtype, device=dev)
+        s["ve"] = torch.empty_like(s["ke"])
+        if "decode" in steps:
+            s["out"] = torch.empty((c.batch, c.n_q_heads, c.head_dim), device=dev)
+        sets.append(s)
+    ws_p = fb.workspace(fb.project_workspace_size(desc))
+    ws_d = fb.workspace(fb.decode_workspace_size(desc)) if "decode" in steps else None
+    if "decode" in steps and "project" not in steps:
+        for s in sets:  # decode-only workloads: coefficients and edges made once
+            fb.project(desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], ws_p)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = sets[i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        if "project" in steps:
+            fb.project(desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], ws_p, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if "decode" in steps:
+            fb.decode(desc, s["q"], s.get("kx"), s.get("vx"), s["ke"], s["ve"], s["ck"], s["cv"],
+                      scale, s["out"], ws_d, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: whole-step throughput
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    # per-call durations with events on the launch stream (same calls again)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t_proj = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+
+    extra = {}
+    if "decode" in steps:
+        extra["decode_us"] = t_dec * 1e6
+        extra["decode_kv_positions_per_s"] = positions / t_dec
+        extra["decode_hbm_GBps"] = dec_bytes / t_dec / 1e9
+        extra["decode_algorithmic_bytes"] = dec_bytes
+    if "project" in steps:
+        extra["project_us"] = t_proj * 1e6
+        extra["project_tflops"] = proj_flops / t_proj / 1e12
+        extra["project_algorithmic_flops"] = proj_flops
+    # dominant call: the larger share of the step
+    if "decode" in steps and (t_dec >= t_proj or "project" not in steps):
+        ach = dec_bytes / t_dec / 1e9
+        roof = {"kernel": "fa_decode", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": measured_traffic(args.workload, "fa_decode")}
+    else:
+        ach = proj_flops / t_proj / 1e12
+        roof = {"kernel": "fa_project", "bound": "mfma", "achieved": ach,
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_F16_PEAK_TFLOPS,
+                "traffic": measured_traffic(args.workload, "fa_project")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        dt, threads, n = cpu_baseline(w, scale, args.cpu_seconds)
+        cpu = {"value": positions / dt, "unit": "KV-positions/s", "cores": threads, "kind": "oracle",
+               "sample": "%d full step(s) of %s (oracle project of K and V%s), %.2f s each"
+                         % (n, args.workload, " + decode" if "decode" in steps else "", dt)}
+
+    line = {
+        "metric": "KV-positions/s (fa_project K,V + fa_decode per step)" if len(steps) == 2
+                  else "KV-positions/s (%s)" % "+".join(steps),
+        "value": positions / (ms_step * 1e-3),
+        "unit": "KV-positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, fp16 MFMA operands, fp32 accumulate" if c.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded generator; no dataset or weights)",
+        "config": {"workload": args.workload, "note": c.note, "batch": c.batch,
+                   "seq_len": [int(x) for x in w.lens] if c.len_range else int(w.lens[0]),
+                   "n_q_heads": c.n_q_heads, "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
+                   "n_comp_dims": c.n_comp, "n_coef": c.n_coef, "sink": c.sink,
+                   "recent": c.recent, "input_copies": copies},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "calls": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

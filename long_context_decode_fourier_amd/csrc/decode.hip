@@ -1,4 +1,7 @@
-// decode.hip - one decode step over the Fourier-approximated KV cache.
+// decode.hip - one decode step over the Fourier-approximated KV cache:
+// query-side contraction (decode_prep), the VALU split kernel used for fp32
+// caches (decode_split) and the split merge (decode_merge).  The MFMA split
+// kernel for 16-bit caches is in decode_mfma.hip.
 //
 // The pages reconstruct the middle tokens (zero-padded inverse transform) and
 // then attend (skill page "fourier-approximated-kv-cache", Step 4).  Here the
@@ -15,12 +18,12 @@
 // softmax of s over all L tokens.  The sequence is split into token ranges
 // (split-L); each split keeps a running max m, sum l, o_U, the edge part of
 // o_C and W (online softmax), and decode_merge combines the splits with the
-// usual log-sum-exp weights in a fixed order, applies C_V and scatters dims.
+// log-sum-exp weights in a fixed order, applies C_V and scatters the dims.
 //
-// decode_split is a VALU kernel: for each token the basis along n is produced
-// by complex rotation (e^{i theta_j tau} times e^{i 2 pi tau / M}), for each
-// coefficient the basis along tau by rotation with e^{i 2 pi j / M}; both are
-// re-anchored from exact integer phases.
+// decode_split (fp32) produces the basis along n by complex rotation
+// (e^{i theta_j tau} times e^{i 2 pi tau / M}) and along tau by rotation with
+// e^{i 2 pi j / M}; both are re-anchored from exact integer phases through
+// sincospi, which keeps fp32 results within 1e-5 of the exact value.
 #include "kernels.hpp"
 
 namespace fa {
@@ -60,36 +63,42 @@ __device__ inline float2 cmul(float2 a, float2 b) {
   return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
 }
 
-// Query rows of row group rg: query head and KV head of row r.
-__device__ inline void row_heads(const DecodeArgs& a, int rg, int r, int* i, int* h) {
-  if (a.G <= kDecRows) {
-    const int hpg = a.rows / a.G;
-    *h = rg * hpg + r / a.G;
-    *i = *h * a.G + r % a.G;
-  } else {
-    const int gph = a.G / kDecRows;
-    *h = rg / gph;
-    *i = *h * a.G + (rg % gph) * kDecRows + r;
-  }
+// Pair-order position -> basis index (-1 for the unused slot and padding).
+__device__ inline int pair_pos_to_n(int pos, int k) {
+  const int j = pos >> 1;
+  const int n = (pos & 1) ? (j == 0 ? -1 : 2 * j) : (j == 0 ? 0 : 2 * j - 1);
+  return n < k ? n : -1;
 }
 
 // --------------------------------------------------------------- prep ----
-// A[b][i][n] = scale * alpha_n * sum_c q[b][i][comp_c] ck[b,h][n][c].
+// A[b][i][n] = scale * alpha_n * sum_c q[b][i][comp_c] ck[b,h][n][c], one
+// block per (sequence, KV head, 32 outputs); 8 threads split the c sum.
+constexpr int kPrepOut = 32;
+constexpr int kPrepParts = 8;
+constexpr int kPrepRows = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
-  constexpr int kRowChunk = 8;
+  float* qc = smem;                               // [kPrepRows][dc]
+  float* red = smem + kPrepRows * a.dc;           // [kPrepParts][kPrepRows][kPrepOut]
   const int bh = blockIdx.x;
   const int b = bh / a.hkv, h = bh % a.hkv;
   const int M = a.seq.mid[b];
-  const int n = blockIdx.y * 64 + (threadIdx.x & 63);
-  const int part = threadIdx.x >> 6;
-  float* qc = smem;                            // [kRowChunk][dc]
-  float* red = smem + kRowChunk * a.dc;        // [4][kRowChunk][64]
-  const int cper = (a.dc + 3) / 4;
+  const int o = threadIdx.x % kPrepOut, part = threadIdx.x / kPrepOut;
+  const int pos = blockIdx.y * kPrepOut + o;
+  const int len = a.mfma ? a.kpp : a.k;
+  const int n = (pos >= len) ? -1 : (a.mfma ? pair_pos_to_n(pos, a.k) : pos);
+  const int cper = (a.dc + kPrepParts - 1) / kPrepParts;
   const int c0 = part * cper, c1 = min(a.dc, c0 + cper);
-  for (int g0 = 0; g0 < a.G; g0 += kRowChunk) {
-    const int ng = min(kRowChunk, a.G - g0);
+  // coefficient loads first: they do not depend on q
+  float ckr[32];
+  const float* ckrow = a.ck + ((static_cast<int64_t>(b) * a.hkv + h) * a.k + max(n, 0)) * a.dc;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) ckr[c] = (n >= 0 && M > 0 && c0 + c < c1) ? ckrow[c0 + c] : 0.0f;
+  const float alpha = (n >= 0 && M > 0) ? basis_alpha(n, M) : 0.0f;
+  for (int g0 = 0; g0 < a.G; g0 += kPrepRows) {
+    const int ng = min(kPrepRows, a.G - g0);
     __syncthreads();
     for (int idx = threadIdx.x; idx < ng * a.dc; idx += blockDim.x) {
       const int g = idx / a.dc, c = idx % a.dc;
@@ -100,35 +109,36 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
                              : 0.0f;
     }
     __syncthreads();
-    float acc[kRowChunk];
+    float acc[kPrepRows];
 #pragma unroll
-    for (int g = 0; g < kRowChunk; ++g) acc[g] = 0.0f;
-    if (n < a.k && M > 0) {
-      const float* ckrow = a.ck + ((static_cast<int64_t>(b) * a.hkv + h) * a.k + n) * a.dc;
-      for (int c = c0; c < c1; ++c) {
-        const float v = ckrow[c];
+    for (int g = 0; g < kPrepRows; ++g) acc[g] = 0.0f;
 #pragma unroll
-        for (int g = 0; g < kRowChunk; ++g)
-          if (g < ng) acc[g] = fmaf(qc[g * a.dc + c], v, acc[g]);
-      }
-    }
+    for (int c = 0; c < 32; ++c)
+      if (c0 + c < c1)
 #pragma unroll
-    for (int g = 0; g < kRowChunk; ++g) red[(part * kRowChunk + g) * 64 + (threadIdx.x & 63)] = acc[g];
+        for (int g = 0; g < kPrepRows; ++g)
+          if (g < ng) acc[g] = fmaf(qc[g * a.dc + c0 + c], ckr[c], acc[g]);
+#pragma unroll
+    for (int g = 0; g < kPrepRows; ++g) red[(part * kPrepRows + g) * kPrepOut + o] = acc[g];
     __syncthreads();
-    if (part == 0 && n < a.k) {
-      const float alpha = (M > 0) ? basis_alpha(n, M) : 0.0f;
+    if (part == 0 && pos < len) {
       for (int g = 0; g < ng; ++g) {
-        const int t = threadIdx.x & 63;
-        const float s = (red[(0 * kRowChunk + g) * 64 + t] + red[(1 * kRowChunk + g) * 64 + t]) +
-                        (red[(2 * kRowChunk + g) * 64 + t] + red[(3 * kRowChunk + g) * 64 + t]);
-        const int i = h * a.G + g0 + g;
-        a.A[(static_cast<int64_t>(b) * a.hq + i) * a.kpad + n] = alpha * s;
+        float s = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kPrepParts; ++p) s += red[(p * kPrepRows + g) * kPrepOut + o];
+        const int64_t i = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
+        if (a.mfma)
+          static_cast<_Float16*>(a.A16)[i * a.kpp + pos] = static_cast<_Float16>(alpha * s);
+        else
+          a.A[i * a.kpad + pos] = alpha * s;
       }
     }
   }
 }
 
 // -------------------------------------------------------------- split ----
+// VALU kernel: rows <= kDecRows consecutive query heads, tiles of kDecTile
+// tokens.  Thread slots own basis pairs j = tid + 256 i (slot 0 = constant).
 constexpr int kMaxSlots = 9;  // ceil((4097/2 + 1) / 256)
 
 template <typename T>
@@ -159,10 +169,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   int qi[R], kh[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    int i = 0, h = 0;
-    if (r < a.rows) row_heads(a, rg, r, &i, &h);
-    qi[r] = i;
-    kh[r] = h;
+    qi[r] = rg * a.rows + min(r, a.rows - 1);
+    kh[r] = qi[r] / a.G;
   }
 
   // q rows in dim-split order, scaled; A rows.
@@ -185,6 +193,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
 
   const int nslots = a.k / 2 + 1;  // slot 0: n = 0; slot j: n = 2j-1, 2j
+  const int nown = (nslots > tid) ? (nslots - tid + 255) / 256 : 0;
   const int du4 = (a.du + 3) / 4, dc4 = (a.dc + 3) / 4, sl4 = (nslots + 3) / 4;
   const int part = wave;  // phase A: thread (token lane, part)
 
@@ -197,8 +206,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   float wacc[kMaxSlots][2][R];
 #pragma unroll
   for (int i = 0; i < kMaxSlots; ++i) {
-    const int j = tid + 256 * i;
-    wstep[i] = (has_mid && j < nslots) ? unit_phase(j, 1, M) : make_float2(1.0f, 0.0f);
+    wstep[i] = (has_mid && i < nown) ? unit_phase(tid + 256 * i, 1, M) : make_float2(1.0f, 0.0f);
 #pragma unroll
     for (int r = 0; r < R; ++r) wacc[i][0][r] = wacc[i][1][r] = 0.0f;
   }
@@ -283,7 +291,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
     // ---------------- phase C: values
     const int nt = min(TT, t_end - tile0);
-    // exact dims
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = tid + 256 * j;
@@ -295,7 +302,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       oacc[j] = o;
     }
     if (comp) {
-      // compressible dims of edge tokens
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int idx = tid + 256 * j;
@@ -313,16 +319,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         eacc[j] = o;
       }
     }
-    if (has_mid) {
-      // W_n = sum_tau p b_n(tau) over the middle tokens of this tile
+    if (has_mid && nown > 0) {
       const int mid_lo = max(0, S - tile0), mid_hi = min(nt, S + M - tile0);
       float2 z[kMaxSlots];
 #pragma unroll
       for (int i = 0; i < kMaxSlots; ++i) {
-        const int j = tid + 256 * i;
         // anchor at the tile's first middle token (tau >= 0)
-        z[i] = (j < nslots && mid_lo < mid_hi) ? unit_phase(j, tile0 + mid_lo - S, M)
-                                              : make_float2(0.0f, 0.0f);
+        z[i] = (i < nown && mid_lo < mid_hi) ? unit_phase(tid + 256 * i, tile0 + mid_lo - S, M)
+                                             : make_float2(0.0f, 0.0f);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           wacc[i][0][r] *= corr[r];
@@ -333,15 +337,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const float4 p = *reinterpret_cast<const float4*>(&ps[tl * R]);
 #pragma unroll
         for (int i = 0; i < kMaxSlots; ++i) {
-          wacc[i][0][0] = fmaf(p.x, z[i].x, wacc[i][0][0]);
-          wacc[i][1][0] = fmaf(p.x, z[i].y, wacc[i][1][0]);
-          wacc[i][0][1] = fmaf(p.y, z[i].x, wacc[i][0][1]);
-          wacc[i][1][1] = fmaf(p.y, z[i].y, wacc[i][1][1]);
-          wacc[i][0][2] = fmaf(p.z, z[i].x, wacc[i][0][2]);
-          wacc[i][1][2] = fmaf(p.z, z[i].y, wacc[i][1][2]);
-          wacc[i][0][3] = fmaf(p.w, z[i].x, wacc[i][0][3]);
-          wacc[i][1][3] = fmaf(p.w, z[i].y, wacc[i][1][3]);
-          z[i] = cmul(z[i], wstep[i]);
+          if (i < nown) {
+            wacc[i][0][0] = fmaf(p.x, z[i].x, wacc[i][0][0]);
+            wacc[i][1][0] = fmaf(p.x, z[i].y, wacc[i][1][0]);
+            wacc[i][0][1] = fmaf(p.y, z[i].x, wacc[i][0][1]);
+            wacc[i][1][1] = fmaf(p.y, z[i].y, wacc[i][1][1]);
+            wacc[i][0][2] = fmaf(p.z, z[i].x, wacc[i][0][2]);
+            wacc[i][1][2] = fmaf(p.z, z[i].y, wacc[i][1][2]);
+            wacc[i][0][3] = fmaf(p.w, z[i].x, wacc[i][0][3]);
+            wacc[i][1][3] = fmaf(p.w, z[i].y, wacc[i][1][3]);
+            z[i] = cmul(z[i], wstep[i]);
+          }
         }
       }
     }
@@ -372,8 +378,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   if (has_mid) {
 #pragma unroll
     for (int i = 0; i < kMaxSlots; ++i) {
+      if (i >= nown) continue;
       const int j = tid + 256 * i;
-      if (j >= nslots) continue;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (r >= a.rows) break;
@@ -390,7 +396,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 }
 
 // -------------------------------------------------------------- merge ----
-// One block per (sequence, KV head): combine the splits of its G query rows.
+// One block per (sequence, KV head): combine the splits of its G query rows
+// (in chunks of kMergeRows), apply the basis scale and C_V, scatter dims.
 constexpr int kMergeRows = 4;
 
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
@@ -399,16 +406,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int ns = a.seq.nsplit[b];
   const int M = a.seq.mid[b];
   const bool has_mid = a.dc > 0 && M > 0;
+  const int K = has_mid ? a.k : 0;
   float* wsp = smem;                           // [kMergeRows][ns]
   float* Wm = wsp + kMergeRows * ns;           // [kMergeRows][kpad]
-  float* red = Wm + kMergeRows * a.kpad;       // [256][kMergeRows]
-  __shared__ float Lsum[kMergeRows];
+  float* oe = Wm + kMergeRows * a.kpad;        // [kMergeRows][dc]
+  float* red = oe + kMergeRows * a.dc;         // [256][kMergeRows]
+  __shared__ float Linv[kMergeRows];
   const int tid = threadIdx.x;
 
   for (int g0 = 0; g0 < a.G; g0 += kMergeRows) {
     const int ng = min(kMergeRows, a.G - g0);
     __syncthreads();
-    // softmax weights of the splits
     for (int g = tid >> 6; g < ng; g += 4) {
       const int lane = tid & 63;
       const int i = h * a.G + g0 + g;
@@ -424,28 +432,37 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         lsum += w * P[static_cast<int64_t>(s) * a.RS + 1];
       }
       lsum = wave_sum(lsum);
-      if (lane == 0) Lsum[g] = lsum;
+      if (lane == 0) Linv[g] = 1.0f / lsum;
     }
     __syncthreads();
-    // exact dims and merged W
-    for (int idx = tid; idx < ng * a.du; idx += blockDim.x) {
-      const int g = idx / a.du, d = idx % a.du;
-      const int i = h * a.G + g0 + g;
-      const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS + 2 + d;
-      float o = 0.0f;
-      for (int s = 0; s < ns; ++s) o = fmaf(wsp[g * ns + s], P[static_cast<int64_t>(s) * a.RS], o);
-      const int dd = a.dims[h * a.D + d];
-      if (dd >= 0 && dd < a.D) a.out[(static_cast<int64_t>(b) * a.hq + i) * a.D + dd] = o / Lsum[g];
-    }
-    if (has_mid)
-      for (int idx = tid; idx < ng * a.k; idx += blockDim.x) {
-        const int g = idx / a.k, n = idx % a.k;
+    // weighted sums of o_U, o_E and W over the splits
+    const int nvec = a.du + a.dc + K;
+    for (int idx = tid; idx < nvec; idx += blockDim.x) {
+      for (int g = 0; g < ng; ++g) {
         const int i = h * a.G + g0 + g;
-        const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS + 2 + a.du + a.dc + n;
-        float w = 0.0f;
-        for (int s = 0; s < ns; ++s) w = fmaf(wsp[g * ns + s], P[static_cast<int64_t>(s) * a.RS], w);
-        Wm[g * a.kpad + n] = w * basis_alpha(n, M);
+        const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS + 2 + idx;
+        const float* w = wsp + g * ns;
+        float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
+        int s = 0;
+        for (; s + 4 <= ns; s += 4) {
+          v0 = fmaf(w[s], P[static_cast<int64_t>(s) * a.RS], v0);
+          v1 = fmaf(w[s + 1], P[static_cast<int64_t>(s + 1) * a.RS], v1);
+          v2 = fmaf(w[s + 2], P[static_cast<int64_t>(s + 2) * a.RS], v2);
+          v3 = fmaf(w[s + 3], P[static_cast<int64_t>(s + 3) * a.RS], v3);
+        }
+        for (; s < ns; ++s) v0 = fmaf(w[s], P[static_cast<int64_t>(s) * a.RS], v0);
+        const float v = (v0 + v1) + (v2 + v3);
+        if (idx < a.du) {
+          const int dd = a.dims[h * a.D + idx];
+          if (dd >= 0 && dd < a.D) a.out[(static_cast<int64_t>(b) * a.hq + i) * a.D + dd] = v * Linv[g];
+        } else if (idx < a.du + a.dc) {
+          oe[g * a.dc + idx - a.du] = v;
+        } else {
+          const int n = idx - a.du - a.dc;
+          Wm[g * a.kpad + n] = v * basis_alpha(n, M);
+        }
       }
+    }
     __syncthreads();
     // compressible dims: edge part + W . C_V; threads (c, n-group)
     if (a.dc > 0) {
@@ -473,11 +490,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
             float s = 0.0f;
             for (int q = 0; q < ngrp; ++q) s += red[(q * dcp + (tid % dcp)) * kMergeRows + g];
             const int i = h * a.G + g0 + g;
-            const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS + 2 + a.du + c;
-            float e = 0.0f;
-            for (int sp = 0; sp < ns; ++sp) e = fmaf(wsp[g * ns + sp], P[static_cast<int64_t>(sp) * a.RS], e);
             const int dd = a.dims[h * a.D + a.du + c];
-            if (dd >= 0 && dd < a.D) a.out[(static_cast<int64_t>(b) * a.hq + i) * a.D + dd] = (s + e) / Lsum[g];
+            if (dd >= 0 && dd < a.D)
+              a.out[(static_cast<int64_t>(b) * a.hq + i) * a.D + dd] = (s + oe[g * a.dc + c]) * Linv[g];
           }
         }
         __syncthreads();
@@ -486,33 +501,37 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-}  // namespace
-
-size_t decode_prep_smem(const DecodeArgs& a) { return sizeof(float) * (8 * a.dc + 4 * 8 * 64); }
-size_t decode_split_smem(const DecodeArgs& a) {
-  return sizeof(float) * (kDecRows * a.D + kDecRows * a.kpad + 4 * kDecRows * kDecTile +
-                          kDecTile * kDecRows + kDecRows);
-}
-size_t decode_merge_smem(const DecodeArgs& a, int max_splits) {
-  return sizeof(float) * (kMergeRows * max_splits + kMergeRows * a.kpad + 256 * kMergeRows);
-}
-
-hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
-  if (a.dc == 0) return hipSuccess;
-  dim3 grid(a.nseq * a.hkv, (a.k + 63) / 64);
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(decode_prep_kernel<uint16_t>, grid, dim3(256), decode_prep_smem(a), s, a);
-  else
-    hipLaunchKernelGGL(decode_prep_kernel<float>, grid, dim3(256), decode_prep_smem(a), s, a);
-  return hipGetLastError();
-}
-
 // Kernels whose dynamic LDS may pass 64 KB declare their need first.
 template <typename K>
 hipError_t allow_lds(K kernel, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+}  // namespace
+
+size_t decode_prep_smem(const DecodeArgs& a) {
+  return sizeof(float) * (kPrepRows * a.dc + kPrepParts * kPrepRows * kPrepOut);
+}
+size_t decode_split_smem(const DecodeArgs& a) {
+  return sizeof(float) * (kDecRows * a.D + kDecRows * a.kpad + 4 * kDecRows * kDecTile +
+                          kDecTile * kDecRows + kDecRows);
+}
+size_t decode_merge_smem(const DecodeArgs& a, int max_splits) {
+  return sizeof(float) * (kMergeRows * max_splits + kMergeRows * a.kpad + kMergeRows * a.dc +
+                          256 * kMergeRows);
+}
+
+hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
+  if (a.dc == 0) return hipSuccess;
+  const int len = a.mfma ? a.kpp : a.k;
+  dim3 grid(a.nseq * a.hkv, (len + kPrepOut - 1) / kPrepOut);
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(decode_prep_kernel<uint16_t>, grid, dim3(256), decode_prep_smem(a), s, a);
+  else
+    hipLaunchKernelGGL(decode_prep_kernel<float>, grid, dim3(256), decode_prep_smem(a), s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s) {

@@ -21,6 +21,7 @@ constexpr int kNumCU = 256;         // MI355X compute units
 constexpr int kMaxCoef = 4097;      // decode keeps per-thread coefficient slots
 constexpr int kMaxHeadDim = 256;
 constexpr size_t kAlign = 256;
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
 thread_local std::string g_err;
 
@@ -195,6 +196,29 @@ struct DecPlan {
   size_t off_A, off_part, ws_bytes;
 };
 
+// Row grouping of the MFMA path: `rows` consecutive query heads per item.
+bool mfma_rows_ok(const Shape& sh, int rows, int kpp) {
+  const int G = sh.G;
+  if (rows > 32 || sh.Hq % rows) return false;
+  if (!(rows % G == 0 || G % rows == 0)) return false;
+  const int nheads = rows >= G ? rows / G : 1;
+  const int rph = std::min(rows, G);
+  if (rph > fa::decode_mfma_max_rph(kpp)) return false;
+  const int mb = rows > 16 ? 2 : 1;
+  const int T = fa::decode_mfma_tokens(kpp);
+  const int nt = 64 * fa::decode_mfma_waves(kpp);
+  if (nheads * (sh.Du / 2) > nt || nheads * (sh.Dc / 2) > nt) return false;
+  const int tpp = std::max(1, nt / (nheads * T));
+  if (sh.Du % (2 * tpp) || sh.Dc % (2 * tpp)) return false;
+  fa::DecodeArgs probe;
+  std::memset(&probe, 0, sizeof probe);
+  probe.kpp = kpp;
+  probe.D = sh.D;
+  if (fa::decode_mfma_smem(probe, mb) > kMaxLds) return false;
+  if (kpp <= 512) return true;
+  return kpp <= fa::decode_mfma_max_kpp(mb);
+}
+
 fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   fa::DecodeArgs& a = p->args;
   std::memset(&a, 0, sizeof a);
@@ -208,26 +232,42 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   a.dc = sh.Dc;
   a.k = sh.k;
   a.kpad = (sh.k + 3) / 4 * 4;
+  a.kpp = (2 * (sh.k / 2 + 1) + 31) / 32 * 32;
   a.sink = sh.S;
   a.recent = sh.R;
-  if (sh.G <= fa::kDecRows) {
-    int hg = 1;
-    for (int c = 1; c <= sh.Hkv; ++c)
-      if (sh.Hkv % c == 0 && c * sh.G <= fa::kDecRows) hg = c;
-    a.rows = hg * sh.G;
-    a.ngroups = sh.Hkv / hg;
-  } else {
-    if (sh.G % fa::kDecRows)
-      return fail(FA_ERR_SHAPE, "query heads per KV head (%d) must be <= %d or a multiple of it",
-                  sh.G, fa::kDecRows);
-    a.rows = fa::kDecRows;
-    a.ngroups = sh.Hkv * (sh.G / fa::kDecRows);
+  // MFMA path for 16-bit caches: as many stacked rows as the basis length
+  // pays for (long bases amortise their generation over more rows).
+  int rows = 0;
+  if (sh.dtype == FA_BF16 && sh.Du % 2 == 0 && sh.Dc % 2 == 0) {
+    const int cap = (sh.k >= 512) ? 32 : std::max(4, std::min(sh.G, 8));
+    for (int r = cap; r >= 1; --r)
+      if (mfma_rows_ok(sh, r, a.kpp)) {
+        rows = r;
+        break;
+      }
   }
+  int tile;
+  if (rows > 0) {
+    a.mfma = 1;
+    a.mb = rows > 16 ? 2 : 1;
+    tile = fa::decode_mfma_tokens(a.kpp);
+  } else {
+    a.mfma = 0;
+    tile = fa::kDecTile;
+    rows = 0;
+    for (int r = fa::kDecRows; r >= 1; --r)
+      if (sh.Hq % r == 0 && (r % sh.G == 0 || sh.G % r == 0)) {
+        rows = r;
+        break;
+      }
+  }
+  a.rows = rows;
+  a.ngroups = sh.Hq / rows;
   a.RS = 2 + a.du + a.dc + a.kpad;
   const int64_t work = sh.total_len * a.ngroups;
-  const int64_t target = 2 * kNumCU;
-  int chunk = static_cast<int>(std::max<int64_t>(
-      fa::kDecTile, (work + target - 1) / target / fa::kDecTile * fa::kDecTile));
+  const int64_t target = a.mfma ? kNumCU : 2 * kNumCU;
+  const int chunk = static_cast<int>(
+      std::max<int64_t>(tile, (work + target - 1) / target / tile * tile));
   int item = 0, prow = 0;
   for (int b = 0; b < sh.B; ++b) {
     const int ns = (sh.L[b] + chunk - 1) / chunk;
@@ -243,7 +283,9 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   }
   p->nitems = item;
   p->off_A = 0;
-  p->off_part = align_up(static_cast<size_t>(sh.B) * sh.Hq * a.kpad * sizeof(float));
+  const size_t a_bytes = a.mfma ? static_cast<size_t>(sh.B) * sh.Hq * a.kpp * 2
+                                : static_cast<size_t>(sh.B) * sh.Hq * a.kpad * sizeof(float);
+  p->off_part = align_up(a_bytes);
   p->ws_bytes = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
   return FA_OK;
 }
@@ -410,6 +452,7 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
   a.out = out;
   a.scale = scale;
   a.A = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_A);
+  a.A16 = static_cast<char*>(workspace) + p.off_A;
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_part);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -417,7 +460,7 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
     e = fa::launch_decode_prep(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode prep kernel");
   }
-  e = fa::launch_decode_split(a, p.nitems, s);
+  e = a.mfma ? fa::launch_decode_mfma(a, p.nitems, s) : fa::launch_decode_split(a, p.nitems, s);
   if (e != hipSuccess) return hip_fail(e, "decode split kernel");
   e = fa::launch_decode_merge(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode merge kernel");

@@ -43,8 +43,10 @@ hipError_t launch_edge_gather(const EdgeArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode --
 constexpr int kDecRows = 4;    // query rows per work item (VALU path)
-constexpr int kDecTile = 64;   // tokens per tile
+constexpr int kDecTile = 64;   // tokens per tile (VALU path)
 
+// A work item covers `rows` consecutive query heads of one sequence (query
+// head i reads KV head i / G) and one token range of it.
 struct DecodeArgs {
   int dtype;                   // 0 f32, 1 bf16
   const void* q;
@@ -56,19 +58,28 @@ struct DecodeArgs {
   const float* cv;
   const int32_t* dims;
   float* out;
-  float* A;      // workspace [B][Hq][kpad]: scale * alpha_n * q_C . ck[n]
-  float* part;   // workspace partials [prow][RS]
-  int nseq, hq, hkv, G, D, du, dc, k, kpad, sink, recent;
+  float* A;      // VALU path: [B][Hq][kpad] fp32, basis order
+  void* A16;     // MFMA path: [B][Hq][kpp] fp16, pair order
+  float* part;   // partials [prow][RS]: m, l, o_U[du], o_E[dc], W[kpad]
+  int nseq, hq, hkv, G, D, du, dc, k, kpad, kpp, sink, recent;
+  int mfma;      // 1: decode_mfma kernel, 0: VALU kernel
+  int mb;        // MFMA path: 16-row blocks per item
   int rows;      // query rows per work item
-  int ngroups;   // row groups per sequence
+  int ngroups;   // row groups per sequence (Hq / rows)
   int RS;        // floats per partial row: 2 + du + dc + kpad
   float scale;
-  SeqTable seq;  // item0/nsplit/chunk over (row group, split); prow0 below
+  SeqTable seq;  // item0/nsplit/chunk over (row group, split)
   int32_t prow0[kMaxBatch];  // first partial row of sequence b: sum Hq * nsplit
 };
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
+size_t decode_mfma_smem(const DecodeArgs& a, int mb);
+int decode_mfma_tokens(int kpp);
+int decode_mfma_waves(int kpp);
+int decode_mfma_max_kpp(int mb);
+int decode_mfma_max_rph(int kpp);
 
 }  // namespace fa
