@@ -105,7 +105,7 @@ fa_status_t fa_project_workspace_size(const fa_desc_t *desc, size_t *bytes);
  * retained sink/recent rows of kc (vc) are also gathered into it (skill page,
  * Step 3).  Either matrix may be skipped: pass kc = ck = ke = NULL (or the V
  * trio).  With n_comp_dims = 0 the call does nothing and every pointer may be
- * NULL.  The 16-bit path needs n_comp_dims % 8 == 0 and 16-byte aligned kc/vc;
+ * NULL.  The 16-bit path needs n_comp_dims % 4 == 0 and 8-byte aligned kc/vc;
  * it computes in fp16 operands, so |kc|, |vc| must stay below 65504.
  * desc.dims is not used.
  */
@@ -124,6 +124,7 @@ fa_status_t fa_decode_workspace_size(const fa_desc_t *desc, size_t *bytes);
  *   out[b][i] = sum_t p_t V~[t]      for t = 0 .. L_b-1.
  * The reconstruction is never formed: compressed scores are
  * (scale q_C ck^T) . phi(tau) and compressed values are (sum_tau p phi(tau)) cv.
+ * bf16 caches need 16-byte aligned kx, vx, ke, ve.
  */
 fa_status_t fa_decode(const fa_desc_t *desc, const void *q, const void *kx,
                       const void *vx, const void *ke, const void *ve,

@@ -396,107 +396,137 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 }
 
 // -------------------------------------------------------------- merge ----
-// One block per (sequence, KV head): combine the splits of its G query rows
-// (in chunks of kMergeRows), apply the basis scale and C_V, scatter dims.
+// Pass 1 (decode_merge_vec): one block per (query row, 256-wide slice of the
+// partial vector [o_U | o_E | W]).  Each block recomputes the log-sum-exp
+// weights of the splits, sums its slice over the splits in a fixed order and
+// writes o_U / l to out, o_E and alpha * W to the merge buffer (mrg).
+// Pass 2 (decode_merge_cv): one block per (sequence, KV head) applies C_V to
+// the merged W of its query rows and writes the compressible dims.
 constexpr int kMergeRows = 4;
 
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  extern __shared__ float smem[];
-  const int b = blockIdx.x / a.hkv, h = blockIdx.x % a.hkv;
+__global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];  // [ns] weights
+  __shared__ float red[256];
+  const int row = blockIdx.x;      // b * hq + i
+  const int b = row / a.hq, i = row % a.hq, h = i / a.G;
   const int ns = a.seq.nsplit[b];
   const int M = a.seq.mid[b];
   const bool has_mid = a.dc > 0 && M > 0;
-  const int K = has_mid ? a.k : 0;
-  float* wsp = smem;                           // [kMergeRows][ns]
-  float* Wm = wsp + kMergeRows * ns;           // [kMergeRows][kpad]
-  float* oe = Wm + kMergeRows * a.kpad;        // [kMergeRows][dc]
-  float* red = oe + kMergeRows * a.dc;         // [256][kMergeRows]
-  __shared__ float Linv[kMergeRows];
-  const int tid = threadIdx.x;
+  const int nvec = a.du + a.dc + (has_mid ? a.k : 0);
+  const int idx = blockIdx.y * 256 + threadIdx.x;
+  if (blockIdx.y * 256 >= nvec) return;  // uniform per block
+  const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS;
+  float mx = -INFINITY;
+  for (int s = threadIdx.x; s < ns; s += 256) mx = fmaxf(mx, P[static_cast<int64_t>(s) * a.RS]);
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float lsum = 0.0f;
+  for (int s = threadIdx.x; s < ns; s += 256) {
+    const float m = P[static_cast<int64_t>(s) * a.RS];
+    const float w = (m == -INFINITY) ? 0.0f : __expf(m - mx);
+    smem[s] = w;
+    lsum += w * P[static_cast<int64_t>(s) * a.RS + 1];
+  }
+  red[threadIdx.x] = lsum;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float linv = 1.0f / red[0];
+  float* mrow = a.mrg + static_cast<int64_t>(row) * a.MS;
+  if (blockIdx.y == 0 && threadIdx.x == 0) mrow[a.dc + a.kpad] = linv;
+  if (idx >= nvec) return;
+  const float* Pi = P + 2 + idx;
+  float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+    v0 = fmaf(smem[s], Pi[static_cast<int64_t>(s) * a.RS], v0);
+    v1 = fmaf(smem[s + 1], Pi[static_cast<int64_t>(s + 1) * a.RS], v1);
+    v2 = fmaf(smem[s + 2], Pi[static_cast<int64_t>(s + 2) * a.RS], v2);
+    v3 = fmaf(smem[s + 3], Pi[static_cast<int64_t>(s + 3) * a.RS], v3);
+  }
+  for (; s < ns; ++s) v0 = fmaf(smem[s], Pi[static_cast<int64_t>(s) * a.RS], v0);
+  const float v = (v0 + v1) + (v2 + v3);
+  if (idx < a.du) {
+    const int dd = a.dims[h * a.D + idx];
+    if (dd >= 0 && dd < a.D) a.out[static_cast<int64_t>(row) * a.D + dd] = v * linv;
+  } else if (idx < a.du + a.dc) {
+    mrow[idx - a.du] = v;
+  } else {
+    const int n = idx - a.du - a.dc;
+    mrow[a.dc + n] = v * basis_alpha(n, M);
+  }
+}
 
+__global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  const int b = blockIdx.x / a.hkv, h = blockIdx.x % a.hkv;
+  const int M = a.seq.mid[b];
+  const bool has_mid = a.dc > 0 && M > 0;
+  float* Wm = smem;                            // [kMergeRows][kpad]
+  float* red = Wm + kMergeRows * a.kpad;       // [256][kMergeRows]
+  const int tid = threadIdx.x;
+  const int dcp = (a.dc + 63) / 64 * 64;
+  const int ngrp = max(1, 256 / dcp);
   for (int g0 = 0; g0 < a.G; g0 += kMergeRows) {
     const int ng = min(kMergeRows, a.G - g0);
     __syncthreads();
-    for (int g = tid >> 6; g < ng; g += 4) {
-      const int lane = tid & 63;
-      const int i = h * a.G + g0 + g;
-      const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS;
-      float mx = -INFINITY;
-      for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, P[static_cast<int64_t>(s) * a.RS]);
-      mx = wave_max(mx);
-      float lsum = 0.0f;
-      for (int s = lane; s < ns; s += 64) {
-        const float m = P[static_cast<int64_t>(s) * a.RS];
-        const float w = (m == -INFINITY) ? 0.0f : __expf(m - mx);
-        wsp[g * ns + s] = w;
-        lsum += w * P[static_cast<int64_t>(s) * a.RS + 1];
+    if (has_mid)
+      for (int idx = tid; idx < ng * a.k; idx += 256) {
+        const int g = idx / a.k, n = idx % a.k;
+        const int64_t row = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
+        Wm[g * a.kpad + n] = a.mrg[row * a.MS + a.dc + n];
       }
-      lsum = wave_sum(lsum);
-      if (lane == 0) Linv[g] = 1.0f / lsum;
-    }
     __syncthreads();
-    // weighted sums of o_U, o_E and W over the splits
-    const int nvec = a.du + a.dc + K;
-    for (int idx = tid; idx < nvec; idx += blockDim.x) {
-      for (int g = 0; g < ng; ++g) {
-        const int i = h * a.G + g0 + g;
-        const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS + 2 + idx;
-        const float* w = wsp + g * ns;
-        float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
-        int s = 0;
-        for (; s + 4 <= ns; s += 4) {
-          v0 = fmaf(w[s], P[static_cast<int64_t>(s) * a.RS], v0);
-          v1 = fmaf(w[s + 1], P[static_cast<int64_t>(s + 1) * a.RS], v1);
-          v2 = fmaf(w[s + 2], P[static_cast<int64_t>(s + 2) * a.RS], v2);
-          v3 = fmaf(w[s + 3], P[static_cast<int64_t>(s + 3) * a.RS], v3);
+    for (int c0 = 0; c0 < dcp; c0 += 256) {
+      const int c = c0 + tid % dcp, grp = tid / dcp;
+      float acc[kMergeRows];
+#pragma unroll
+      for (int g = 0; g < kMergeRows; ++g) acc[g] = 0.0f;
+      if (c < a.dc && grp < ngrp && has_mid) {
+        const float* cvb = a.cv + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc + c;
+        int n = grp;
+        for (; n + 3 * ngrp < a.k; n += 4 * ngrp) {  // four independent loads in flight
+          const float x0 = cvb[static_cast<int64_t>(n) * a.dc];
+          const float x1 = cvb[static_cast<int64_t>(n + ngrp) * a.dc];
+          const float x2 = cvb[static_cast<int64_t>(n + 2 * ngrp) * a.dc];
+          const float x3 = cvb[static_cast<int64_t>(n + 3 * ngrp) * a.dc];
+#pragma unroll
+          for (int g = 0; g < kMergeRows; ++g)
+            if (g < ng)
+              acc[g] = fmaf(Wm[g * a.kpad + n], x0,
+                            fmaf(Wm[g * a.kpad + n + ngrp], x1,
+                                 fmaf(Wm[g * a.kpad + n + 2 * ngrp], x2,
+                                      fmaf(Wm[g * a.kpad + n + 3 * ngrp], x3, acc[g]))));
         }
-        for (; s < ns; ++s) v0 = fmaf(w[s], P[static_cast<int64_t>(s) * a.RS], v0);
-        const float v = (v0 + v1) + (v2 + v3);
-        if (idx < a.du) {
-          const int dd = a.dims[h * a.D + idx];
-          if (dd >= 0 && dd < a.D) a.out[(static_cast<int64_t>(b) * a.hq + i) * a.D + dd] = v * Linv[g];
-        } else if (idx < a.du + a.dc) {
-          oe[g * a.dc + idx - a.du] = v;
-        } else {
-          const int n = idx - a.du - a.dc;
-          Wm[g * a.kpad + n] = v * basis_alpha(n, M);
+        for (; n < a.k; n += ngrp) {
+          const float x = cvb[static_cast<int64_t>(n) * a.dc];
+#pragma unroll
+          for (int g = 0; g < kMergeRows; ++g)
+            if (g < ng) acc[g] = fmaf(Wm[g * a.kpad + n], x, acc[g]);
         }
       }
-    }
-    __syncthreads();
-    // compressible dims: edge part + W . C_V; threads (c, n-group)
-    if (a.dc > 0) {
-      const int dcp = (a.dc + 63) / 64 * 64;
-      const int ngrp = max(1, 256 / dcp);
-      for (int c0 = 0; c0 < dcp; c0 += 256) {
-        const int c = c0 + tid % dcp, grp = tid / dcp;
-        float acc[kMergeRows];
 #pragma unroll
-        for (int g = 0; g < kMergeRows; ++g) acc[g] = 0.0f;
-        if (c < a.dc && grp < ngrp && has_mid) {
-          const float* cvb = a.cv + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc + c;
-          for (int n = grp; n < a.k; n += ngrp) {
-            const float v = cvb[static_cast<int64_t>(n) * a.dc];
-#pragma unroll
-            for (int g = 0; g < kMergeRows; ++g)
-              if (g < ng) acc[g] = fmaf(Wm[g * a.kpad + n], v, acc[g]);
-          }
+      for (int g = 0; g < kMergeRows; ++g) red[tid * kMergeRows + g] = acc[g];
+      __syncthreads();
+      if (grp == 0 && c < a.dc) {
+        for (int g = 0; g < ng; ++g) {
+          float sum = 0.0f;
+          for (int q = 0; q < ngrp; ++q) sum += red[(q * dcp + (tid % dcp)) * kMergeRows + g];
+          const int64_t row = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
+          const float* mrow = a.mrg + row * a.MS;
+          const int dd = a.dims[h * a.D + a.du + c];
+          if (dd >= 0 && dd < a.D) a.out[row * a.D + dd] = (sum + mrow[c]) * mrow[a.dc + a.kpad];
         }
-#pragma unroll
-        for (int g = 0; g < kMergeRows; ++g) red[tid * kMergeRows + g] = acc[g];
-        __syncthreads();
-        if (grp == 0 && c < a.dc) {
-          for (int g = 0; g < ng; ++g) {
-            float s = 0.0f;
-            for (int q = 0; q < ngrp; ++q) s += red[(q * dcp + (tid % dcp)) * kMergeRows + g];
-            const int i = h * a.G + g0 + g;
-            const int dd = a.dims[h * a.D + a.du + c];
-            if (dd >= 0 && dd < a.D)
-              a.out[(static_cast<int64_t>(b) * a.hq + i) * a.D + dd] = (s + oe[g * a.dc + c]) * Linv[g];
-          }
-        }
-        __syncthreads();
       }
+      __syncthreads();
     }
   }
 }
@@ -518,9 +548,8 @@ size_t decode_split_smem(const DecodeArgs& a) {
   return sizeof(float) * (kDecRows * a.D + kDecRows * a.kpad + 4 * kDecRows * kDecTile +
                           kDecTile * kDecRows + kDecRows);
 }
-size_t decode_merge_smem(const DecodeArgs& a, int max_splits) {
-  return sizeof(float) * (kMergeRows * max_splits + kMergeRows * a.kpad + kMergeRows * a.dc +
-                          256 * kMergeRows);
+size_t decode_merge_cv_smem(const DecodeArgs& a) {
+  return sizeof(float) * (kMergeRows * a.kpad + 256 * kMergeRows);
 }
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
@@ -551,10 +580,16 @@ hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s) {
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
   int max_splits = 1;
   for (int b = 0; b < a.nseq; ++b) max_splits = max(max_splits, a.seq.nsplit[b]);
-  const size_t sm = decode_merge_smem(a, max_splits);
-  const hipError_t e = allow_lds(decode_merge_kernel, sm);
+  const int nvec = a.du + a.dc + a.k;
+  hipError_t e = allow_lds(decode_merge_vec_kernel, sizeof(float) * max_splits);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.nseq * a.hkv), dim3(256), sm, s, a);
+  hipLaunchKernelGGL(decode_merge_vec_kernel, dim3(a.nseq * a.hq, (nvec + 255) / 256), dim3(256),
+                     sizeof(float) * max_splits, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.dc == 0) return hipSuccess;
+  const size_t sm = decode_merge_cv_smem(a);
+  if ((e = allow_lds(decode_merge_cv_kernel, sm)) != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_cv_kernel, dim3(a.nseq * a.hkv), dim3(256), sm, s, a);
   return hipGetLastError();
 }
 

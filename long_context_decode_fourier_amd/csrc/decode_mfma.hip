@@ -2,21 +2,27 @@
 //
 // Same arithmetic as the VALU kernel in decode.hip (scores and values in
 // coefficient space, online softmax, partials merged by decode_merge), laid out
-// for CDNA4 matrix cores:
+// for CDNA4 matrix cores.  A work item is (sequence, group of up to 32
+// consecutive query heads, token range); its query rows are stacked into the
+// 16-row M blocks of the MFMA.  Per tile of T tokens:
 //
-// * the query rows of a work item (up to 32 query heads that share the
-//   sequence, hence its middle length M and its basis) are stacked into the
-//   M dimension of v_mfma_f32_16x16x32_f16 / 16x16x16_f16;
-// * per tile of T tokens the basis tile phi[t][pos] (unscaled cos/sin, fp16)
-//   is generated once into LDS and shared by every row;
-// * compressed scores S = A phi^T contract over coefficients: each wave owns a
-//   slice of 32-wide coefficient units, keeps its slice of A (scale*alpha*q_C
-//   ck, fp16) in registers, reads phi with 16-byte LDS loads, and the four
-//   waves' partial scores are summed in LDS;
-// * value moments W += P phi contract over tokens: the same LDS tile is read
-//   transposed with ds_read_b64_tr_b16, W stays in registers per wave slice;
-// * exact dims (and the retained edge rows) are dot products per KV head on
-//   VALU with coalesced 16-byte row loads.
+// * the basis tile phi[t][pos] (unscaled cos/sin, fp16) is generated once into
+//   LDS and shared by every row (three-term recurrence along the frequency
+//   index, seeded from exact integer phases every 16 frequencies);
+// * compressed scores  S_c = A phi^T  (fp16 MFMA over coefficients): each wave
+//   owns a slice of 32-wide coefficient units and keeps its slice of A
+//   (scale * alpha * q_C ck, written by decode_prep) in registers; the waves'
+//   partial scores are summed in LDS;
+// * exact scores  S_x = q_U kx^T  (bf16 MFMA over the exact dims) per KV head
+//   with q_U held in registers and kx staged in LDS;
+// * value moments  W += P phi  (fp16 MFMA over tokens, phi read transposed
+//   with ds_read_b64_tr_b16) and exact values  o_U += P vx  (bf16 MFMA, vx read
+//   transposed; P is split into a bf16 head and a bf16 remainder so the
+//   product keeps ~16 bits of P);
+// * kx / vx rows of the next tile are loaded (16-byte loads) while the current
+//   tile computes, then staged through LDS;
+// * the retained edge rows (ke / ve; at most a few tiles per sequence) take a
+//   VALU path with batched loads.
 //
 // Coefficients live in "pair order" inside the kernel: position 2j holds the
 // cosine of frequency j (j = 0 is the constant), 2j+1 the sine; position 1 is
@@ -29,16 +35,16 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
-// Transposed 4 x 16-bit LDS read (see kernel header): lane 4a+e of each
-// 16-lane group receives element e of the chunks addressed by lanes
-// a, a+4, a+8, a+12 of its group.
-__device__ inline half4 lds_read_tr4(const _Float16* p) {
-  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p));
-  return __builtin_bit_cast(half4, r);
+// Transposed 4 x 16-bit LDS read: lane 4a+e of each 16-lane group receives
+// element e of the 8-byte chunks addressed by lanes a, a+4, a+8, a+12 of its
+// group.
+__device__ inline short4v lds_read_tr4(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p));
 }
 
 __device__ inline float wmax(float v, int width) {
@@ -49,23 +55,27 @@ __device__ inline float wsum(float v, int width) {
   for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+__device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// round-to-nearest-even float -> bf16 bits (finite inputs)
+__device__ inline uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
 
-template <int MB, int NW, int MAXU, int T, int RPH>
+// MB: 16-row blocks; NW: waves; MAXU: max 32-wide coefficient units per wave;
+// T: tokens per tile (16 or 32); PF: 16-byte kx (and vx) chunks staged per
+// thread per tile; XPW: max (KV head, 16-dim block) exact-value tiles per
+// wave; RPH: max query rows per KV head (edge-row VALU path).
+template <int MB, int NW, int MAXU, int T, int PF, int XPW, int RPH>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NT = 64 * NW, MR = 16 * MB, NB = T / 16;
   constexpr int SL = (MR * T + NT - 1) / NT;  // softmax (row, token) slots per thread
+  constexpr int KCM = 2;                      // max 32-dim chunks of the exact dims
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int PS = a.kpp + 16;  // LDS row stride in halves; 2*PS = 32 (mod 64) words
-  _Float16* phi = reinterpret_cast<_Float16*>(smem);        // [T][PS]
-  float* qs = reinterpret_cast<float*>(phi + T * PS);        // [MR][D]
-  float* sx = qs + MR * a.D;                                 // [MR][T]
-  float* spart = sx + MR * T;                                // [NW][MR][T]
-  float* pf = spart + NW * MR * T;                           // [MR][T]
-  _Float16* ph = reinterpret_cast<_Float16*>(pf + MR * T);   // [MR][T]
-  float* corr = reinterpret_cast<float*>(ph + MR * T);       // [MR]
-  int* flag = reinterpret_cast<int*>(corr + MR);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
   const int b = seq_of_item(a.seq, a.nseq, blockIdx.x);
   const int local = blockIdx.x - a.seq.item0[b];
   const int ns = a.seq.nsplit[b];
@@ -82,18 +92,86 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int rph = min(rows, a.G);  // query rows per KV head inside the item
   const bool has_mid = a.dc > 0 && M > 0;
   const int du = a.du, dc = a.dc, D = a.D;
+  const int du32 = (du + 31) & ~31;
+  const int KC = du32 / 32;        // exact-dim chunks (<= KCM)
+  const int DUS = du32 + 8;        // LDS row stride of staged kx / vx (halves)
+  const int PS = a.kpp + 16;       // LDS row stride of the basis tile (halves)
 
-  // ---- scaled q rows in dim-split order
-  for (int idx = tid; idx < MR * D; idx += NT) {
-    const int r = idx / D, j = idx % D;
+  _Float16* phi = reinterpret_cast<_Float16*>(smem);             // [T][PS]
+  uint16_t* kxs = reinterpret_cast<uint16_t*>(phi + T * PS);     // [nheads][T][DUS]
+  uint16_t* vxs = kxs + nheads * T * DUS;                         // [nheads][T][DUS]
+  float* sx = reinterpret_cast<float*>(vxs + nheads * T * DUS);   // [MR][T]
+  float* sedge = sx + MR * T;                                     // [MR][T]
+  float* spart = sedge + MR * T;                                  // [NW][MR][T]
+  float* pf = spart + NW * MR * T;                                // [MR][T]
+  _Float16* ph = reinterpret_cast<_Float16*>(pf + MR * T);        // [MR][T]
+  uint16_t* pbh = reinterpret_cast<uint16_t*>(ph + MR * T);       // [MR][T]
+  uint16_t* pbl = pbh + MR * T;                                   // [MR][T]
+  float* qcs = reinterpret_cast<float*>(pbl + MR * T);            // [MR][dc] (edge rows)
+  float* corr = qcs + MR * dc;                                    // [MR]
+  int* flag = reinterpret_cast<int*>(corr + MR);
+
+  // ---- zero the staging rows once: columns [du, DUS) stay zero (finite operands)
+  for (int i = tid; i < 2 * nheads * T * DUS; i += NT) kxs[i] = 0;
+
+  // ---- kx / vx staging: thread -> 16-byte chunks c = tid + NT*i of the tile
+  const int du8 = du / 8;
+  const int nchunk = nheads * T * du8;
+  uint4 pk[PF], pv[PF];
+  auto prefetch = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int c = tid + NT * i;
+      uint4 vk = make_uint4(0u, 0u, 0u, 0u), vv = vk;
+      if (c < nchunk) {
+        const int hh = c / (T * du8), rem = c % (T * du8);
+        const int tt = rem / du8, c8 = rem % du8;
+        const int t = tile + tt;
+        if (t < t_end) {
+          const int64_t off = (row0 + static_cast<int64_t>(h0 + hh) * L + t) * du + 8 * c8;
+          vk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kx) + off);
+          vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.vx) + off);
+        }
+      }
+      pk[i] = vk;
+      pv[i] = vv;
+    }
+  };
+  if (du8 > 0) prefetch(t_begin);
+
+  // ---- q operands: exact dims as bf16 MFMA A operand (per 32-dim chunk),
+  //      compressible dims (scaled, fp32) in LDS for the edge rows
+  bf16x8 Qreg[KCM][MB];
+#pragma unroll
+  for (int kc = 0; kc < KCM; ++kc)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = mb * 16 + l16;
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 32 * kc + 8 * g4 + e;
+        uint16_t bits = 0;
+        if (row < rows && j < du) {
+          const int qi = qi0 + row;
+          const int dd = a.dims[(qi / a.G) * D + j];
+          if (dd >= 0 && dd < D)
+            bits = static_cast<const uint16_t*>(a.q)[(static_cast<int64_t>(b) * a.hq + qi) * D + dd];
+        }
+        v[e] = __builtin_bit_cast(__bf16, bits);
+      }
+      Qreg[kc][mb] = v;
+    }
+  for (int idx = tid; idx < MR * dc; idx += NT) {
+    const int r = idx / dc, c = idx % dc;
     float v = 0.0f;
     if (r < rows) {
       const int qi = qi0 + r;
-      const int dd = a.dims[(qi / a.G) * D + j];
+      const int dd = a.dims[(qi / a.G) * D + du + c];
       if (dd >= 0 && dd < D)
         v = a.scale * bf16_to_f32(static_cast<const uint16_t*>(a.q)[(static_cast<int64_t>(b) * a.hq + qi) * D + dd]);
     }
-    qs[idx] = v;
+    qcs[idx] = v;
   }
 
   // ---- this wave's coefficient units and its slice of A (MFMA A operand)
@@ -107,11 +185,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       half8 v;
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = 0;
-      const int row = mb * 16 + (lane & 15);
+      const int row = mb * 16 + l16;
       if (has_mid && u < nu && row < rows)
         v = *reinterpret_cast<const half8*>(
             static_cast<const _Float16*>(a.A16) +
-            (static_cast<int64_t>(b) * a.hq + qi0 + row) * a.kpp + (u0 + u) * 32 + 8 * (lane >> 4));
+            (static_cast<int64_t>(b) * a.hq + qi0 + row) * a.kpp + (u0 + u) * 32 + 8 * g4);
       Areg[u][mb] = v;
     }
   floatx4 Wacc[MAXU][2][MB];
@@ -122,19 +200,22 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) Wacc[u][n2][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- exact-dim value accumulators: thread -> (head, dim pair)
-  const int du2 = du / 2, dc2 = dc / 2;
-  const int xh = du2 ? tid / du2 : 0, xd = du2 ? tid % du2 : 0;
-  const bool xval = du2 > 0 && tid < nheads * du2;
+  // ---- exact-value tiles of this wave: (KV head, 16-dim block) pairs
+  const int ndb = du32 / 16;
+  floatx4 Uacc[XPW];
+#pragma unroll
+  for (int x = 0; x < XPW; ++x) Uacc[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- edge-row value accumulators (VALU): thread -> (head, comp-dim pair)
+  const int dc2 = dc / 2;
   const int eh = dc2 ? tid / dc2 : 0, ec = dc2 ? tid % dc2 : 0;
   const bool evld = dc2 > 0 && tid < nheads * dc2;
-  const int xrb = (rows >= a.G) ? xh * a.G : 0;
   const int erb = (rows >= a.G) ? eh * a.G : 0;
-  float oU[RPH][2], oE[RPH][2];
+  float oE[RPH][2];
 #pragma unroll
-  for (int r = 0; r < RPH; ++r) oU[r][0] = oU[r][1] = oE[r][0] = oE[r][1] = 0.0f;
+  for (int r = 0; r < RPH; ++r) oE[r][0] = oE[r][1] = 0.0f;
 
-  // ---- softmax slots: thread -> (row, token) for idx = tid and tid + NT
+  // ---- softmax slots: thread -> (row, token) for idx = tid + NT*j
   float m_run[SL], l_run[SL];
 #pragma unroll
   for (int j = 0; j < SL; ++j) {
@@ -150,16 +231,29 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int c_lo = grun * cper, c_hi = min(chunks, c_lo + cper);
   const float invM = has_mid ? 1.0f / static_cast<float>(M) : 0.0f;
 
-  // ---- exact score mapping: thread -> (head, token, part of the dims)
+  // ---- edge-score mapping: thread -> (head, token, part of the comp dims)
   const int npairs = nheads * T;
-  const int tpp = NT / npairs >= 1 ? NT / npairs : 1;  // threads per (head, token)
+  const int tpp = NT / npairs >= 1 ? NT / npairs : 1;
 
-  __syncthreads();
+  __syncthreads();  // staging rows zeroed, qcs ready
 
   for (int tile0 = t_begin; tile0 < t_end; tile0 += T) {
     const int nt = min(T, t_end - tile0);
-    // ================= phase 1: basis tile, exact scores
+    const bool tile_edge = dc > 0 && (M == 0 || tile0 < S || tile0 + nt > S + M);
+    // ================= phase 1: stage this tile, prefetch the next, basis tile
     if (tid == 0) *flag = 0;
+    if (du8 > 0) {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        const int c = tid + NT * i;
+        if (c < nchunk) {
+          const int row = c / du8, c8 = c % du8;  // row = hh * T + tt
+          *reinterpret_cast<uint4*>(kxs + row * DUS + 8 * c8) = pk[i];
+          *reinterpret_cast<uint4*>(vxs + row * DUS + 8 * c8) = pv[i];
+        }
+      }
+      if (tile0 + T < t_end) prefetch(tile0 + T);
+    }
     {
       const int t = tile0 + gt;
       const bool mid = has_mid && t < t_end && t >= S && t < S + M;
@@ -178,7 +272,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         int r0 = phase_mod(4 * c_lo, tau, M);
         const int d16 = phase_mod(16, tau, M);
         for (int c = c_lo; c < c_hi; c += 4) {
-          int r1 = r0 + tau % M;
+          int r1 = r0 + tau;
           if (r1 >= M) r1 -= M;
           const float x0 = static_cast<float>(r0) * invM, x1 = static_cast<float>(r1) * invM;
           float cp = cos_rev(x0), sp_ = sin_rev(x0);
@@ -190,10 +284,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
             z[1] = static_cast<_Float16>(sp_);
             z[2] = static_cast<_Float16>(cc);
             z[3] = static_cast<_Float16>(sc);
-            float cn = fmaf(c2, cc, -cp), sn = fmaf(c2, sc, -sp_);
+            const float cn = fmaf(c2, cc, -cp), sn = fmaf(c2, sc, -sp_);
             z[4] = static_cast<_Float16>(cn);
             z[5] = static_cast<_Float16>(sn);
-            float cm = fmaf(c2, cn, -cc), sm = fmaf(c2, sn, -sc);
+            const float cm = fmaf(c2, cn, -cc), sm = fmaf(c2, sn, -sc);
             z[6] = static_cast<_Float16>(cm);
             z[7] = static_cast<_Float16>(sm);
             *reinterpret_cast<half8*>(dst + 8 * cc4) = z;
@@ -207,51 +301,47 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         }
       }
     }
-    for (int pr = tid / tpp; pr < npairs; pr += NT / tpp) {
-      const int hh = pr / T, tt = pr % T, part = tid % tpp;
-      const int t = tile0 + tt;
-      const int h = h0 + hh;
-      const int rb = (rows >= a.G) ? hh * a.G : 0;
-      float acc[RPH];
+    if (tile_edge) {
+      // compressible part of the exact scores of the retained edge rows
+      for (int pr = tid / tpp; pr < npairs; pr += NT / tpp) {
+        const int hh = pr / T, tt = pr % T, part = tid % tpp;
+        const int t = tile0 + tt;
+        const int rb = (rows >= a.G) ? hh * a.G : 0;
+        float acc[RPH];
 #pragma unroll
-      for (int r = 0; r < RPH; ++r) acc[r] = 0.0f;
-      if (t < t_end) {
-        const int dper = du / tpp, d0 = part * dper;
-        const uint32_t* krow = reinterpret_cast<const uint32_t*>(
-            static_cast<const uint16_t*>(a.kx) + (row0 + static_cast<int64_t>(h) * L + t) * du + d0);
-        for (int d = 0; d < dper; d += 2) {
-          const uint32_t w2 = krow[d >> 1];
-          const float k0 = __uint_as_float(w2 << 16), k1 = __uint_as_float(w2 & 0xFFFF0000u);
-#pragma unroll
-          for (int r = 0; r < RPH; ++r)
-            if (r < rph) acc[r] = fmaf(qs[(rb + r) * D + d0 + d], k0, fmaf(qs[(rb + r) * D + d0 + d + 1], k1, acc[r]));
-        }
-        const bool edge = dc > 0 && (M == 0 || t < S || t >= S + M);
-        if (edge) {
+        for (int r = 0; r < RPH; ++r) acc[r] = 0.0f;
+        if (t < t_end && (M == 0 || t < S || t >= S + M)) {
           const int e = (M == 0 || t < S) ? t : t - M;
           const int cper_ = dc / tpp, c0 = part * cper_;
           const uint32_t* erow = reinterpret_cast<const uint32_t*>(
-              static_cast<const uint16_t*>(a.ke) + ((static_cast<int64_t>(b) * a.hkv + h) * E + e) * dc + c0);
-          for (int c = 0; c < cper_; c += 2) {
-            const uint32_t w2 = erow[c >> 1];
-            const float k0 = __uint_as_float(w2 << 16), k1 = __uint_as_float(w2 & 0xFFFF0000u);
+              static_cast<const uint16_t*>(a.ke) + ((static_cast<int64_t>(b) * a.hkv + h0 + hh) * E + e) * dc + c0);
+          for (int cb = 0; 2 * cb < cper_; cb += 8) {  // batches of 8 independent loads
+            uint32_t ew[8];
 #pragma unroll
-            for (int r = 0; r < RPH; ++r)
-              if (r < rph)
-                acc[r] = fmaf(qs[(rb + r) * D + du + c0 + c], k0, fmaf(qs[(rb + r) * D + du + c0 + c + 1], k1, acc[r]));
+            for (int c = 0; c < 8; ++c) ew[c] = (2 * (cb + c) < cper_) ? erow[cb + c] : 0u;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+              if (2 * (cb + c) < cper_)
+#pragma unroll
+                for (int r = 0; r < RPH; ++r)
+                  if (r < rph) {
+                    const int cc = c0 + 2 * (cb + c);
+                    acc[r] = fmaf(qcs[(rb + r) * dc + cc], lo_bf16(ew[c]),
+                                  fmaf(qcs[(rb + r) * dc + cc + 1], hi_bf16(ew[c]), acc[r]));
+                  }
           }
         }
+#pragma unroll
+        for (int r = 0; r < RPH; ++r) acc[r] = wsum(acc[r], tpp);
+        if (part == 0)
+#pragma unroll
+          for (int r = 0; r < RPH; ++r)
+            if (r < rph) sedge[(rb + r) * T + tt] = acc[r];
       }
-#pragma unroll
-      for (int r = 0; r < RPH; ++r) acc[r] = wsum(acc[r], tpp);
-      if (part == 0)
-#pragma unroll
-        for (int r = 0; r < RPH; ++r)
-          if (r < rph) sx[(rb + r) * T + tt] = (t < t_end) ? acc[r] : -INFINITY;
     }
     __syncthreads();
 
-    // ================= phase 2: compressed score partials (MFMA)
+    // ================= phase 2: compressed score partials, exact scores (MFMA)
     if (has_mid) {
       floatx4 sacc[MB][NB];
 #pragma unroll
@@ -264,7 +354,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const half8 bv = *reinterpret_cast<const half8*>(
-                phi + (nb * 16 + (lane & 15)) * PS + (u0 + u) * 32 + 8 * (lane >> 4));
+                phi + (nb * 16 + l16) * PS + (u0 + u) * 32 + 8 * g4);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
               sacc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Areg[u][mb], bv, sacc[mb][nb], 0, 0, 0);
@@ -277,7 +367,30 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            spart[(wave * MR + mb * 16 + 4 * (lane >> 4) + r) * T + nb * 16 + (lane & 15)] = sacc[mb][nb][r];
+            spart[(wave * MR + mb * 16 + 4 * g4 + r) * T + nb * 16 + l16] = sacc[mb][nb][r];
+    }
+    for (int p = wave; p < nheads * NB; p += NW) {
+      const int hh = p / NB, nb = p % NB;
+      const int rb = (rows >= a.G) ? hh * a.G : 0;
+      const int mb = rb >> 4;
+      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = kxs + (hh * T + nb * 16 + l16) * DUS + 8 * g4;
+#pragma unroll
+      for (int kc = 0; kc < KCM; ++kc) {
+        if (kc < KC) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(krow + 32 * kc);
+          bf16x8 av = Qreg[kc][0];
+          if (MB > 1 && mb == 1) av = Qreg[kc][MB - 1];
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, s, 0, 0, 0);
+        }
+      }
+      const int tt = nb * 16 + l16;
+      const bool valid = tile0 + tt < t_end;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mb * 16 + 4 * g4 + r;
+        if (row >= rb && row < rb + rph) sx[row * T + tt] = valid ? a.scale * s[r] : -INFINITY;
+      }
     }
     __syncthreads();
 
@@ -289,9 +402,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       float s = -INFINITY;
       if (row < rows) {
         s = sx[row * T + tt];
-        if (has_mid && s != -INFINITY) {
+        if (s != -INFINITY) {
+          if (tile_edge) s += sedge[row * T + tt];
+          if (has_mid) {
 #pragma unroll
-          for (int w = 0; w < NW; ++w) s += spart[(w * MR + row) * T + tt];
+            for (int w = 0; w < NW; ++w) s += spart[(w * MR + row) * T + tt];
+          }
         }
       }
       const float m_new = fmaxf(m_run[j], wmax(s, T));
@@ -302,6 +418,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       if (row >= MR) continue;
       pf[row * T + tt] = p;
       ph[row * T + tt] = static_cast<_Float16>(p);
+      const uint16_t hb = bf16_rne(p);
+      pbh[row * T + tt] = hb;
+      pbl[row * T + tt] = bf16_rne(p - __uint_as_float(static_cast<uint32_t>(hb) << 16));
       if (tt == 0) {
         corr[row] = c;
         if (c != 1.0f) *flag = 1;
@@ -309,15 +428,15 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // ================= phase 4: value moments W (MFMA), exact values (VALU)
+    // ================= phase 4: value moments W, exact values (MFMA)
     const bool rescale = *flag != 0;
-    if (has_mid) {
-      if (rescale) {
+    if (rescale) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          float cr[4];
+      for (int mb = 0; mb < MB; ++mb) {
+        float cr[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) cr[r] = corr[mb * 16 + 4 * (lane >> 4) + r];
+        for (int r = 0; r < 4; ++r) cr[r] = corr[mb * 16 + 4 * g4 + r];
+        if (has_mid) {
 #pragma unroll
           for (int u = 0; u < MAXU; ++u)
 #pragma unroll
@@ -325,57 +444,66 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) Wacc[u][n2][mb][r] *= cr[r];
         }
+#pragma unroll
+        for (int x = 0; x < XPW; ++x) {
+          const int p = wave + NW * x;
+          const int rb = (rows >= a.G) ? (p / max(ndb, 1)) * a.G : 0;
+          if ((rb >> 4) == mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Uacc[x][r] *= cr[r];
+        }
       }
-      const int g = lane >> 4, s16 = lane & 15;
+    }
+    if (has_mid) {
 #pragma unroll
       for (int u = 0; u < MAXU; ++u) {
         if (u < nu) {
 #pragma unroll
           for (int n2 = 0; n2 < 2; ++n2) {
-            const int nbase = (u0 + u) * 32 + n2 * 16 + 4 * (s16 & 3);
+            const int nbase = (u0 + u) * 32 + n2 * 16 + 4 * (l16 & 3);
             if constexpr (T == 32) {
-              const half4 lo = lds_read_tr4(phi + (8 * g + (s16 >> 2)) * PS + nbase);
-              const half4 hi = lds_read_tr4(phi + (8 * g + 4 + (s16 >> 2)) * PS + nbase);
-              const half8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              const short4v lo = lds_read_tr4(phi + (8 * g4 + (l16 >> 2)) * PS + nbase);
+              const short4v hi = lds_read_tr4(phi + (8 * g4 + 4 + (l16 >> 2)) * PS + nbase);
+              const half8 bv = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
               for (int mb = 0; mb < MB; ++mb) {
-                const half8 pv = *reinterpret_cast<const half8*>(ph + (mb * 16 + s16) * T + 8 * g);
-                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv, bv, Wacc[u][n2][mb], 0, 0, 0);
+                const half8 pv8 = *reinterpret_cast<const half8*>(ph + (mb * 16 + l16) * T + 8 * g4);
+                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv8, bv, Wacc[u][n2][mb], 0, 0, 0);
               }
             } else {
-              const half4 bv = lds_read_tr4(phi + (4 * g + (s16 >> 2)) * PS + nbase);
+              const half4 bv = __builtin_bit_cast(half4, lds_read_tr4(phi + (4 * g4 + (l16 >> 2)) * PS + nbase));
 #pragma unroll
               for (int mb = 0; mb < MB; ++mb) {
-                const half4 pv = *reinterpret_cast<const half4*>(ph + (mb * 16 + s16) * T + 4 * g);
-                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pv, bv, Wacc[u][n2][mb], 0, 0, 0);
+                const half4 pv4 = *reinterpret_cast<const half4*>(ph + (mb * 16 + l16) * T + 4 * g4);
+                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pv4, bv, Wacc[u][n2][mb], 0, 0, 0);
               }
             }
           }
         }
       }
     }
-    if (xval) {
-      const int h = h0 + xh;
-      if (rescale)
 #pragma unroll
-        for (int r = 0; r < RPH; ++r)
-          if (r < rph) {
-            const float cr = corr[xrb + r];
-            oU[r][0] *= cr;
-            oU[r][1] *= cr;
-          }
-      const uint32_t* vcol = reinterpret_cast<const uint32_t*>(
-          static_cast<const uint16_t*>(a.vx) + (row0 + static_cast<int64_t>(h) * L + tile0) * du + 2 * xd);
-      for (int tt = 0; tt < nt; ++tt) {
-        const uint32_t w2 = vcol[static_cast<int64_t>(tt) * du2];
-        const float v0 = __uint_as_float(w2 << 16), v1 = __uint_as_float(w2 & 0xFFFF0000u);
-#pragma unroll
-        for (int r = 0; r < RPH; ++r)
-          if (r < rph) {
-            const float p = pf[(xrb + r) * T + tt];
-            oU[r][0] = fmaf(p, v0, oU[r][0]);
-            oU[r][1] = fmaf(p, v1, oU[r][1]);
-          }
+    for (int x = 0; x < XPW; ++x) {
+      const int p = wave + NW * x;
+      if (ndb == 0 || p >= nheads * ndb) continue;
+      const int hh = p / ndb, db = p % ndb;
+      const int rb = (rows >= a.G) ? hh * a.G : 0;
+      const int mb = rb >> 4;
+      const uint16_t* vbase = vxs + hh * T * DUS + db * 16 + 4 * (l16 & 3);
+      if constexpr (T == 32) {
+        const short4v lo = lds_read_tr4(vbase + (8 * g4 + (l16 >> 2)) * DUS);
+        const short4v hi = lds_read_tr4(vbase + (8 * g4 + 4 + (l16 >> 2)) * DUS);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 ph8 = *reinterpret_cast<const bf16x8*>(pbh + (mb * 16 + l16) * T + 8 * g4);
+        const bf16x8 pl8 = *reinterpret_cast<const bf16x8*>(pbl + (mb * 16 + l16) * T + 8 * g4);
+        Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph8, bv, Uacc[x], 0, 0, 0);
+        Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl8, bv, Uacc[x], 0, 0, 0);
+      } else {
+        const short4v bv = lds_read_tr4(vbase + (4 * g4 + (l16 >> 2)) * DUS);
+        const short4v ph4 = *reinterpret_cast<const short4v*>(pbh + (mb * 16 + l16) * T + 4 * g4);
+        const short4v pl4 = *reinterpret_cast<const short4v*>(pbl + (mb * 16 + l16) * T + 4 * g4);
+        Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph4, bv, Uacc[x], 0, 0, 0);
+        Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl4, bv, Uacc[x], 0, 0, 0);
       }
     }
     if (evld) {
@@ -388,26 +516,36 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
             oE[r][0] *= cr;
             oE[r][1] *= cr;
           }
-      // edge tokens of this tile: [tile0, S) and [S + M, ...) (all tokens when M = 0)
-      const int lo_end = (M == 0) ? tile0 + nt : min(tile0 + nt, S);
-      const int hi_beg = (M == 0) ? tile0 + nt : max(tile0, S + M);
-      const uint32_t* ecol = reinterpret_cast<const uint32_t*>(
-          static_cast<const uint16_t*>(a.ve) + (static_cast<int64_t>(b) * a.hkv + h) * E * dc + 2 * ec);
-      for (int t = tile0; t < tile0 + nt; ++t) {
-        if (t >= lo_end && t < hi_beg) {
-          t = hi_beg - 1;
-          continue;
-        }
-        const int e = (M == 0 || t < S) ? t : t - M;
-        const uint32_t w2 = ecol[static_cast<int64_t>(e) * dc2];
-        const float v0 = __uint_as_float(w2 << 16), v1 = __uint_as_float(w2 & 0xFFFF0000u);
+      if (tile_edge) {
+        // edge tokens of this tile: [tile0, mid_lo) and [mid_hi, tile0 + nt)
+        const int mid_lo = (M == 0) ? tile0 + nt : max(tile0, min(tile0 + nt, S));
+        const int mid_hi = (M == 0) ? tile0 + nt : max(mid_lo, min(tile0 + nt, S + M));
+        const uint32_t* ecol = reinterpret_cast<const uint32_t*>(
+            static_cast<const uint16_t*>(a.ve) + (static_cast<int64_t>(b) * a.hkv + h) * E * dc + 2 * ec);
+        for (int seg = 0; seg < 2; ++seg) {
+          const int lo = seg == 0 ? tile0 : mid_hi, hi = seg == 0 ? mid_lo : tile0 + nt;
+          for (int t0 = lo; t0 < hi; t0 += 8) {  // batches of 8 independent loads
+            uint32_t w8[8];
 #pragma unroll
-        for (int r = 0; r < RPH; ++r)
-          if (r < rph) {
-            const float p = pf[(erb + r) * T + (t - tile0)];
-            oE[r][0] = fmaf(p, v0, oE[r][0]);
-            oE[r][1] = fmaf(p, v1, oE[r][1]);
+            for (int q = 0; q < 8; ++q) {
+              const int t = t0 + q;
+              const int e = (M == 0 || t < S) ? t : t - M;
+              w8[q] = (t < hi) ? ecol[static_cast<int64_t>(e) * dc2] : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              if (t0 + q >= hi) break;
+              const float v0 = lo_bf16(w8[q]), v1 = hi_bf16(w8[q]);
+#pragma unroll
+              for (int r = 0; r < RPH; ++r)
+                if (r < rph) {
+                  const float p = pf[(erb + r) * T + (t0 + q - tile0)];
+                  oE[r][0] = fmaf(p, v0, oE[r][0]);
+                  oE[r][1] = fmaf(p, v1, oE[r][1]);
+                }
+            }
           }
+        }
       }
     }
     __syncthreads();
@@ -425,14 +563,22 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       P[1] = l_run[j];
     }
   }
-  if (xval)
 #pragma unroll
-    for (int r = 0; r < RPH; ++r)
-      if (r < rph) {
-        float* P = a.part + (prow + static_cast<int64_t>(xrb + r) * ns) * a.RS + 2 + 2 * xd;
-        P[0] = oU[r][0];
-        P[1] = oU[r][1];
-      }
+  for (int x = 0; x < XPW; ++x) {
+    const int p = wave + NW * x;
+    if (ndb == 0 || p >= nheads * ndb) continue;
+    const int hh = p / ndb, db = p % ndb;
+    const int rb = (rows >= a.G) ? hh * a.G : 0;
+    const int mb = rb >> 4;
+    const int d = db * 16 + l16;
+    if (d >= du) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = mb * 16 + 4 * g4 + r;
+      if (row >= rb && row < rb + rph)
+        a.part[(prow + static_cast<int64_t>(row) * ns) * a.RS + 2 + d] = Uacc[x][r];
+    }
+  }
   if (evld)
 #pragma unroll
     for (int r = 0; r < RPH; ++r)
@@ -447,7 +593,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       if (u >= nu) continue;
 #pragma unroll
       for (int n2 = 0; n2 < 2; ++n2) {
-        const int pos = (u0 + u) * 32 + n2 * 16 + (lane & 15);
+        const int pos = (u0 + u) * 32 + n2 * 16 + l16;
         const int j = pos >> 1;
         const int n = (pos & 1) ? (j == 0 ? -1 : 2 * j) : (j == 0 ? 0 : 2 * j - 1);
         if (n < 0 || n >= a.k) continue;
@@ -455,7 +601,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int row = mb * 16 + 4 * (lane >> 4) + r;
+            const int row = mb * 16 + 4 * g4 + r;
             if (row < rows)
               a.part[(prow + static_cast<int64_t>(row) * ns) * a.RS + 2 + du + dc + n] = Wacc[u][n2][mb][r];
           }
@@ -464,9 +610,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-template <int MB, int NW, int MAXU, int T, int RPH>
+template <int MB, int NW, int MAXU, int T, int PF, int XPW, int RPH>
 hipError_t launch_one(const DecodeArgs& a, int nitems, size_t smem, hipStream_t s) {
-  auto k = decode_mfma_kernel<MB, NW, MAXU, T, RPH>;
+  auto k = decode_mfma_kernel<MB, NW, MAXU, T, PF, XPW, RPH>;
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -477,39 +623,47 @@ hipError_t launch_one(const DecodeArgs& a, int nitems, size_t smem, hipStream_t 
   return hipGetLastError();
 }
 
+// Compiled variants, chosen by row blocks and basis length (pair-order
+// positions kpp): short bases take 4 waves, long ones 8 waves so that each
+// wave's slice of A and W stays in registers.
+constexpr MfmaVariant kVariants[] = {
+    // mb nw maxu  t pf xpw rph kpp_min kpp_max
+    {1, 4, 4, 32, 4, 4, 8, 0, 512},
+    {2, 4, 4, 32, 4, 8, 8, 0, 512},
+    {2, 8, 5, 32, 2, 4, 4, 513, 1280},
+    {1, 8, 5, 32, 2, 4, 4, 513, 1280},
+    {1, 8, 9, 16, 1, 4, 4, 1281, 2304},
+};
+
 }  // namespace
 
-// Compiled variants (M blocks, waves, max 32-wide coefficient units per wave,
-// tokens per tile), chosen by basis length:
-//   k <  512: 16 rows, 4 waves, <= 4 units, 32 tokens
-//   k >= 512: 32 rows (<= 1280 positions, 32 tokens) or 16 rows (<= 2304
-//             positions, 16 tokens so the basis tile fits LDS), 8 waves.
-int decode_mfma_tokens(int kpp) { return kpp <= 1280 ? 32 : 16; }
-int decode_mfma_waves(int kpp) { return kpp <= 512 ? 4 : 8; }
-int decode_mfma_max_kpp(int mb) { return mb == 1 ? 2304 : 1280; }
-int decode_mfma_max_rph(int kpp) { return kpp <= 512 ? 8 : 4; }
+const MfmaVariant* decode_mfma_pick(int kpp, int mb) {
+  for (const MfmaVariant& v : kVariants)
+    if (v.mb == mb && kpp >= v.kpp_min && kpp <= v.kpp_max) return &v;
+  return nullptr;
+}
 
-size_t decode_mfma_smem(const DecodeArgs& a, int mb) {
-  const int T = decode_mfma_tokens(a.kpp), MR = 16 * mb, NW = decode_mfma_waves(a.kpp);
-  return static_cast<size_t>(T) * (a.kpp + 16) * 2 +
-         sizeof(float) * (MR * a.D + MR * T + NW * MR * T + MR * T) + 2 * MR * T + 4 * MR + 16;
+size_t decode_mfma_smem(const DecodeArgs& a, const MfmaVariant& v, int nheads) {
+  const int T = v.t, MR = 16 * v.mb;
+  const int dus = ((a.du + 31) & ~31) + 8;
+  return static_cast<size_t>(T) * (a.kpp + 16) * 2 + 2 * static_cast<size_t>(2 * nheads * T * dus) +
+         sizeof(float) * (MR * T * 2 + v.nw * MR * T + MR * T) + 2 * MR * T * 3 +
+         sizeof(float) * (MR * a.dc + MR) + 16;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s) {
   if (nitems == 0) return hipSuccess;
-  const size_t smem = decode_mfma_smem(a, a.mb);
-  const int rph = a.rows < a.G ? a.rows : a.G;
-  if (a.kpp <= 512) {
-    if (a.mb == 1) return launch_one<1, 4, 4, 32, 8>(a, nitems, smem, s);
-    return launch_one<2, 4, 4, 32, 8>(a, nitems, smem, s);
+  const MfmaVariant* v = decode_mfma_pick(a.kpp, a.mb);
+  if (!v) return hipErrorInvalidValue;
+  const int nheads = a.rows >= a.G ? a.rows / a.G : 1;
+  const size_t smem = decode_mfma_smem(a, *v, nheads);
+  switch (v - kVariants) {
+    case 0: return launch_one<1, 4, 4, 32, 4, 4, 8>(a, nitems, smem, s);
+    case 1: return launch_one<2, 4, 4, 32, 4, 8, 8>(a, nitems, smem, s);
+    case 2: return launch_one<2, 8, 5, 32, 2, 4, 4>(a, nitems, smem, s);
+    case 3: return launch_one<1, 8, 5, 32, 2, 4, 4>(a, nitems, smem, s);
+    case 4: return launch_one<1, 8, 9, 16, 1, 4, 4>(a, nitems, smem, s);
   }
-  if (rph > 4) return hipErrorInvalidValue;
-  if (a.mb == 2) {
-    if (a.kpp <= 1280) return launch_one<2, 8, 5, 32, 4>(a, nitems, smem, s);
-    return hipErrorInvalidValue;
-  }
-  if (a.kpp <= 1280) return launch_one<1, 8, 5, 32, 4>(a, nitems, smem, s);
-  if (a.kpp <= 2304) return launch_one<1, 8, 9, 16, 4>(a, nitems, smem, s);
   return hipErrorInvalidValue;
 }
 

@@ -118,7 +118,8 @@ int choose_splits(int tiles, int steps, int slots) {
     const int items = tiles * s;
     const int rounds = (items + slots - 1) / slots;
     const double per_item = static_cast<double>((steps + s - 1) / s);
-    const double cost = rounds * per_item + (s > 1 ? 0.02 * steps : 0.0);  // partial traffic
+    // a split costs about two steps of work: its partial tile is written and read back
+    const double cost = rounds * per_item + 2.0 * (s - 1);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = s;
@@ -146,19 +147,19 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
     a.seq.row0[b] = sh.row0[b];
   }
   if (!p->f16 || a.ncols == 0) return FA_OK;
-  if (sh.Dc % 8) return fail(FA_ERR_SHAPE, "bf16 projection needs n_comp_dims %% 8 == 0 (got %d)", sh.Dc);
+  if (sh.Dc % 4) return fail(FA_ERR_SHAPE, "bf16 projection needs n_comp_dims %% 4 == 0 (got %d)", sh.Dc);
 
-  // Large tiles (256 x 256, one 8-wave block per CU) when they still give at
-  // least one tile per CU's worth of work; else 64 x 128 tiles (4 waves).
+  // Large tiles (256 x 256, one 8-wave block per CU) for large contractions;
+  // else 128 x 64 tiles (2 waves), several blocks per CU.
   double flops = 0.0;
   for (int b = 0; b < sh.B; ++b) flops += 2.0 * sh.M[b] * sh.k * a.ncols;
   const bool big = flops > 1.0e11;
-  a.tk = big ? 256 : 64;
-  a.tn = big ? 256 : 128;
+  a.tk = big ? 256 : 128;
+  a.tn = big ? 256 : 64;
   a.nktiles = (sh.k + a.tk - 1) / a.tk;
   a.nctiles = (a.ncols + a.tn - 1) / a.tn;
   const int tiles = a.nktiles * a.nctiles;
-  const int slots = big ? kNumCU : 2 * kNumCU;
+  const int slots = kNumCU;  // co-resident blocks share a CU's matrix cores
   int64_t total_steps = 0;
   for (int b = 0; b < sh.B; ++b) total_steps += (sh.M[b] + fa::kProjTT - 1) / fa::kProjTT;
   bool any_split = false;
@@ -183,8 +184,11 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
     item += tiles * s;
   }
   p->nitems = item;
-  (void)any_split;
-  p->ws_bytes = align_up(static_cast<size_t>(item) * a.tk * a.tn * sizeof(float));
+  // A sequence without middle still needs its zero coefficients written.
+  bool any_empty = false;
+  for (int b = 0; b < sh.B; ++b) any_empty = any_empty || sh.M[b] == 0;
+  a.direct = (!any_split && !any_empty) ? 1 : 0;
+  p->ws_bytes = a.direct ? 0 : align_up(static_cast<size_t>(item) * a.tk * a.tn * sizeof(float));
   return FA_OK;
 }
 
@@ -193,30 +197,36 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
 struct DecPlan {
   fa::DecodeArgs args;
   int nitems;
-  size_t off_A, off_part, ws_bytes;
+  size_t off_A, off_part, off_mrg, ws_bytes;
 };
 
-// Row grouping of the MFMA path: `rows` consecutive query heads per item.
+// Row grouping of the MFMA path: `rows` consecutive query heads per item,
+// checked against the compiled variant that would run it.
 bool mfma_rows_ok(const Shape& sh, int rows, int kpp) {
   const int G = sh.G;
   if (rows > 32 || sh.Hq % rows) return false;
   if (!(rows % G == 0 || G % rows == 0)) return false;
-  const int nheads = rows >= G ? rows / G : 1;
-  const int rph = std::min(rows, G);
-  if (rph > fa::decode_mfma_max_rph(kpp)) return false;
+  if (rows > 16 && 16 % G) return false;  // each KV head's rows inside one 16-row block
   const int mb = rows > 16 ? 2 : 1;
-  const int T = fa::decode_mfma_tokens(kpp);
-  const int nt = 64 * fa::decode_mfma_waves(kpp);
-  if (nheads * (sh.Du / 2) > nt || nheads * (sh.Dc / 2) > nt) return false;
-  const int tpp = std::max(1, nt / (nheads * T));
-  if (sh.Du % (2 * tpp) || sh.Dc % (2 * tpp)) return false;
+  const fa::MfmaVariant* v = fa::decode_mfma_pick(kpp, mb);
+  if (!v) return false;
+  const int nheads = rows >= G ? rows / G : 1;
+  if (std::min(rows, G) > v->rph) return false;
+  const int nt = 64 * v->nw;
+  const int du32 = (sh.Du + 31) / 32 * 32;
+  if (sh.Du % 8 || du32 > 64) return false;
+  if (nheads * (du32 / 16) > v->xpw * v->nw) return false;
+  if (nheads * (sh.Dc / 2) > nt || sh.Dc % 2) return false;
+  const int tpp = std::max(1, nt / (nheads * v->t));
+  if (sh.Dc % (2 * tpp)) return false;
+  if (nheads * v->t * (sh.Du / 8) > v->pf * nt) return false;
   fa::DecodeArgs probe;
   std::memset(&probe, 0, sizeof probe);
   probe.kpp = kpp;
   probe.D = sh.D;
-  if (fa::decode_mfma_smem(probe, mb) > kMaxLds) return false;
-  if (kpp <= 512) return true;
-  return kpp <= fa::decode_mfma_max_kpp(mb);
+  probe.du = sh.Du;
+  probe.dc = sh.Dc;
+  return fa::decode_mfma_smem(probe, *v, nheads) <= kMaxLds;
 }
 
 fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
@@ -250,7 +260,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   if (rows > 0) {
     a.mfma = 1;
     a.mb = rows > 16 ? 2 : 1;
-    tile = fa::decode_mfma_tokens(a.kpp);
+    tile = fa::decode_mfma_pick(a.kpp, a.mb)->t;
   } else {
     a.mfma = 0;
     tile = fa::kDecTile;
@@ -285,8 +295,10 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   p->off_A = 0;
   const size_t a_bytes = a.mfma ? static_cast<size_t>(sh.B) * sh.Hq * a.kpp * 2
                                 : static_cast<size_t>(sh.B) * sh.Hq * a.kpad * sizeof(float);
+  a.MS = a.dc + a.kpad + 1;
   p->off_part = align_up(a_bytes);
-  p->ws_bytes = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
+  p->off_mrg = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
+  p->ws_bytes = p->off_mrg + align_up(static_cast<size_t>(sh.B) * sh.Hq * a.MS * sizeof(float));
   return FA_OK;
 }
 
@@ -346,7 +358,7 @@ fa_status_t fa_project(const fa_desc_t* desc, const void* kc, const void* vc, fl
   if (vc) { a.x[m] = vc; a.out[m] = cv; ++m; }
   if (p.f16 && a.ncols > 0) {
     for (int i = 0; i < nmat; ++i)
-      if (reinterpret_cast<uintptr_t>(a.x[i]) & 15) return fail(FA_ERR_SHAPE, "kc/vc must be 16-byte aligned");
+      if (reinterpret_cast<uintptr_t>(a.x[i]) & 7) return fail(FA_ERR_SHAPE, "kc/vc must be 8-byte aligned");
     if (p.ws_bytes && (!workspace || workspace_bytes < p.ws_bytes))
       return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
                   workspace ? workspace_bytes : 0);
@@ -418,6 +430,12 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
   DecPlan p;
   st = plan_decode(sh, &p);
   if (st != FA_OK) return st;
+  if (p.args.mfma) {
+    const void* rows16[4] = {kx, vx, ke, ve};
+    for (const void* ptr : rows16)
+      if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 15))
+        return fail(FA_ERR_SHAPE, "bf16 kx, vx, ke, ve must be 16-byte aligned");
+  }
   if (!workspace || workspace_bytes < p.ws_bytes)
     return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
                 workspace ? workspace_bytes : 0);
@@ -454,6 +472,7 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
   a.A = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_A);
   a.A16 = static_cast<char*>(workspace) + p.off_A;
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_part);
+  a.mrg = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_mrg);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (sh.Dc > 0 && sh.any_mid) {

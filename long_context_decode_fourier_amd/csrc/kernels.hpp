@@ -22,7 +22,8 @@ struct ProjArgs {
   int tk, tn;        // tile: coefficient rows x columns (16-bit path)
   int nktiles, nctiles;
   int nseq;
-  float* partial;    // [items][tk][tn] (16-bit path)
+  float* partial;    // [items][tk][tn] (16-bit path, when not direct)
+  int direct;        // every sequence has one split: the kernel writes ck / cv
   SeqTable seq;      // item0/nsplit: items = tiles * nsplit; chunk = positions per split
 };
 
@@ -61,12 +62,14 @@ struct DecodeArgs {
   float* A;      // VALU path: [B][Hq][kpad] fp32, basis order
   void* A16;     // MFMA path: [B][Hq][kpp] fp16, pair order
   float* part;   // partials [prow][RS]: m, l, o_U[du], o_E[dc], W[kpad]
+  float* mrg;    // merged rows [B*Hq][MS]: o_E[dc], alpha*W[kpad], 1/l
   int nseq, hq, hkv, G, D, du, dc, k, kpad, kpp, sink, recent;
   int mfma;      // 1: decode_mfma kernel, 0: VALU kernel
   int mb;        // MFMA path: 16-row blocks per item
   int rows;      // query rows per work item
   int ngroups;   // row groups per sequence (Hq / rows)
   int RS;        // floats per partial row: 2 + du + dc + kpad
+  int MS;        // floats per merged row: dc + kpad + 1
   float scale;
   SeqTable seq;  // item0/nsplit/chunk over (row group, split)
   int32_t prow0[kMaxBatch];  // first partial row of sequence b: sum Hq * nsplit
@@ -76,10 +79,18 @@ hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
-size_t decode_mfma_smem(const DecodeArgs& a, int mb);
-int decode_mfma_tokens(int kpp);
-int decode_mfma_waves(int kpp);
-int decode_mfma_max_kpp(int mb);
-int decode_mfma_max_rph(int kpp);
+// A compiled variant of the MFMA decode kernel.
+struct MfmaVariant {
+  int mb;       // 16-row blocks
+  int nw;       // waves per workgroup
+  int maxu;     // max 32-wide coefficient units per wave
+  int t;        // tokens per tile
+  int pf;       // 16-byte kx/vx chunks staged per thread per tile
+  int xpw;      // max (KV head, 16-dim block) exact-value tiles per wave
+  int rph;      // max query rows per KV head
+  int kpp_min, kpp_max;
+};
+const MfmaVariant* decode_mfma_pick(int kpp, int mb);
+size_t decode_mfma_smem(const DecodeArgs& a, const MfmaVariant& v, int nheads);
 
 }  // namespace fa

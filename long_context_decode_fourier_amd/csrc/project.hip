@@ -50,16 +50,27 @@ __device__ inline ProjItem proj_item(const ProjArgs& a, int item) {
 }
 
 // Wave grid WR x WC; each wave owns RB x CB blocks of 32 x 32 outputs.
+//
+// Cache tile staging: thread (cg, tg) loads 4 consecutive columns (8 bytes)
+// of 8 consecutive positions, converts bf16 -> fp16 and packs each column's 8
+// positions into one 16-byte LDS store.  LDS holds column-major blocks of 8
+// positions with a 144-byte column stride; the block index is XOR-swizzled
+// with (col >> 3) & 7, which keeps the stores (8 lanes, 8 column groups) and
+// the MFMA operand reads (8 lanes, 8 consecutive columns) on distinct 16-byte
+// bank slots.  The next step's loads are issued before the MFMA loop of the
+// current step.
+__device__ inline int xt_off(int col, int tblock) {
+  return col * kLdsStride + ((tblock ^ ((col >> 3) & 7)) << 3);
+}
+
 template <int WR, int WC, int RB, int CB>
 __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
   constexpr int kThreads = 64 * WR * WC;
   constexpr int TK = WR * RB * 32;
   constexpr int TN = WC * CB * 32;
-  constexpr int kColGroups = TN / 8;
+  constexpr int kColGroups = TN / 4;
   constexpr int kPosGroups = kThreads / kColGroups;
-  constexpr int kPosPerThread = kProjTT / kPosGroups;
-  static_assert(kPosPerThread * kPosGroups == kProjTT, "tile/thread mismatch");
-  static_assert(kPosPerThread == 4, "loader packs 4 positions per column");
+  static_assert(kPosGroups * 8 == kProjTT, "8 positions per thread cover the step");
 
   __shared__ __attribute__((aligned(16))) _Float16 xt[TN * kLdsStride];
 
@@ -70,17 +81,18 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
   const int L = a.seq.len[it.b];
   const int64_t row0 = a.seq.row0[it.b];
 
-  // ---- loader: 8 consecutive columns x 4 positions per thread
-  const int cg = tid % kColGroups, pg = tid / kColGroups;
-  const int col0 = it.ctile * TN + cg * 8;
-  const bool col_ok = col0 < a.ncols;  // Dc % 8 == 0: the 8 columns share (mat, h)
-  const uint16_t* xbase = nullptr;
+  // ---- loader: 4 consecutive columns x 8 positions per thread
+  const int cg = tid % kColGroups, tg = tid / kColGroups;
+  const int col0 = it.ctile * TN + cg * 4;
+  const bool col_ok = col0 < a.ncols;  // Dc % 4 == 0: the 4 columns share (mat, h)
+  const uint16_t* xbase = static_cast<const uint16_t*>(a.x[0]);
   if (col_ok) {
     const int blk = col0 / a.dc, c0 = col0 % a.dc;
     const int mat = blk / a.hkv, h = blk % a.hkv;
-    xbase = static_cast<const uint16_t*>(a.x[mat]) +
+    xbase = static_cast<const uint16_t*>(mat ? a.x[1] : a.x[0]) +
             (row0 + static_cast<int64_t>(h) * L + a.sink) * a.dc + c0;
   }
+  uint2 raw[8];
 
   // ---- basis generator state, one coefficient row per lane and row block
   const float invM = 1.0f / static_cast<float>(M);
@@ -109,29 +121,39 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tau = it.t_begin + tg * 8 + i;
+    raw[i] = (col_ok && tau < it.t_end)
+                 ? *reinterpret_cast<const uint2*>(xbase + static_cast<int64_t>(tau) * a.dc)
+                 : make_uint2(0u, 0u);
+  }
   for (int step = it.t_begin; step < it.t_end; step += kProjTT) {
-    uint4 raw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tau = step + pg * 4 + i;
-      if (col_ok && tau < it.t_end)
-        raw[i] = *reinterpret_cast<const uint4*>(xbase + static_cast<int64_t>(tau) * a.dc);
-      else
-        raw[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
     __syncthreads();  // the previous step's MFMA reads of xt are done
+    {
+      half8 v0, v1, v2, v3;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      half4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = (j < 2) ? raw[i].x : (j < 4) ? raw[i].y : (j < 6) ? raw[i].z : raw[i].w;
-        const uint32_t bits = (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
-        v[i] = static_cast<_Float16>(__uint_as_float(bits));
+      for (int i = 0; i < 8; ++i) {
+        v0[i] = static_cast<_Float16>(__uint_as_float(raw[i].x << 16));
+        v1[i] = static_cast<_Float16>(__uint_as_float(raw[i].x & 0xFFFF0000u));
+        v2[i] = static_cast<_Float16>(__uint_as_float(raw[i].y << 16));
+        v3[i] = static_cast<_Float16>(__uint_as_float(raw[i].y & 0xFFFF0000u));
       }
-      *reinterpret_cast<half4*>(&xt[(cg * 8 + j) * kLdsStride + pg * 4]) = v;
+      *reinterpret_cast<half8*>(&xt[xt_off(cg * 4 + 0, tg)]) = v0;
+      *reinterpret_cast<half8*>(&xt[xt_off(cg * 4 + 1, tg)]) = v1;
+      *reinterpret_cast<half8*>(&xt[xt_off(cg * 4 + 2, tg)]) = v2;
+      *reinterpret_cast<half8*>(&xt[xt_off(cg * 4 + 3, tg)]) = v3;
     }
     __syncthreads();
+    if (step + kProjTT < it.t_end) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tau = step + kProjTT + tg * 8 + i;
+        raw[i] = (col_ok && tau < it.t_end)
+                     ? *reinterpret_cast<const uint2*>(xbase + static_cast<int64_t>(tau) * a.dc)
+                     : make_uint2(0u, 0u);
+      }
+    }
 
     float yp[RB], yc[RB];
 #pragma unroll
@@ -163,7 +185,7 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const half8 bv = *reinterpret_cast<const half8*>(
-            &xt[(wc * (CB * 32) + cb * 32 + (lane & 31)) * kLdsStride + 32 * (lane >> 5) + 8 * s]);
+            &xt[xt_off(wc * (CB * 32) + cb * 32 + (lane & 31), 4 * (lane >> 5) + s)]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rb], bv, acc[rb][cb], 0, 0, 0);
@@ -176,6 +198,26 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
     }
   }
 
+  if (a.direct) {
+    // single split: scale by the basis normalisation and scatter to ck / cv
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = it.ktile * TK + wr * (RB * 32) + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = it.ctile * TN + wc * (CB * 32) + cb * 32 + (lane & 31);
+          if (n < a.k && col < a.ncols) {
+            const int f = basis_freq(n);
+            const float alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
+                                                       : sqrtf(2.0f / static_cast<float>(M));
+            const int blk = col / a.dc, c = col % a.dc, mat = blk / a.hkv, h = blk % a.hkv;
+            (mat ? a.out[1] : a.out[0])[((static_cast<int64_t>(it.b) * a.hkv + h) * a.k + n) * a.dc + c] = alpha * acc[rb][cb][r];
+          }
+        }
+    return;
+  }
   float* P = a.partial + static_cast<int64_t>(blockIdx.x) * TK * TN;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -319,23 +361,24 @@ __global__ __launch_bounds__(256) void edge_gather_kernel(EdgeArgs a) {
 }  // namespace
 
 // Tile configurations of the 16-bit kernel: 256 x 256 (8 waves) for large
-// problems, 64 x 128 (4 waves) when large tiles would leave CUs idle.
+// problems, 128 x 64 (2 waves) when large tiles would leave CUs idle.
 bool project_tile_supported(int tk, int tn) {
-  return (tk == 256 && tn == 256) || (tk == 64 && tn == 128);
+  return (tk == 256 && tn == 256) || (tk == 128 && tn == 64);
 }
 
 hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
   if (nitems == 0) return hipSuccess;
   if (a.tk == 256 && a.tn == 256)
     hipLaunchKernelGGL((project_f16_kernel<4, 2, 2, 4>), dim3(nitems), dim3(512), 0, s, a);
-  else if (a.tk == 64 && a.tn == 128)
-    hipLaunchKernelGGL((project_f16_kernel<2, 2, 1, 2>), dim3(nitems), dim3(256), 0, s, a);
+  else if (a.tk == 128 && a.tn == 64)
+    hipLaunchKernelGGL((project_f16_kernel<2, 1, 2, 2>), dim3(nitems), dim3(128), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_project_reduce(const ProjArgs& a, hipStream_t s) {
+  if (a.direct) return hipSuccess;
   const int blocks = a.nseq * a.nktiles * a.nctiles * a.tk;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(project_reduce_kernel, dim3(blocks), dim3(256), 0, s, a);
