@@ -85,6 +85,29 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.hkv, h = bh % a.hkv;
   const int M = a.seq.mid[b];
+  if (a.mfma && blockIdx.y == 0) {
+    // MFMA path: this KV head's query rows in dims order, so that the split
+    // kernel loads them contiguously (exact dims bf16, compressible dims fp32)
+    const int du32 = (a.du + 31) & ~31;
+    const int w = du32 + a.dc;
+    for (int idx = threadIdx.x; idx < a.G * w; idx += blockDim.x) {
+      const int g = idx / w, j = idx % w;
+      const int64_t i = static_cast<int64_t>(b) * a.hq + h * a.G + g;
+      if (j < du32) {
+        uint16_t bits = 0;
+        if (j < a.du) {
+          const int d = a.dims[h * a.D + j];
+          if (d >= 0 && d < a.D) bits = static_cast<const uint16_t*>(a.q)[i * a.D + d];
+        }
+        static_cast<uint16_t*>(a.Q16)[i * du32 + j] = bits;
+      } else {
+        const int c = j - du32;
+        const int d = a.dims[h * a.D + a.du + c];
+        a.QC[i * a.dc + c] = (d >= 0 && d < a.D) ? a.scale * ld<T>(a.q, i * a.D + d) : 0.0f;
+      }
+    }
+  }
+  if (!a.prep_a) return;
   const int o = threadIdx.x % kPrepOut, part = threadIdx.x / kPrepOut;
   const int pos = blockIdx.y * kPrepOut + o;
   const int len = a.mfma ? a.kpp : a.k;
@@ -553,8 +576,8 @@ size_t decode_merge_cv_smem(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
-  if (a.dc == 0) return hipSuccess;
-  const int len = a.mfma ? a.kpp : a.k;
+  if (!a.prep_a && !a.mfma) return hipSuccess;
+  const int len = a.prep_a ? (a.mfma ? a.kpp : a.k) : 1;
   dim3 grid(a.nseq * a.hkv, (len + kPrepOut - 1) / kPrepOut);
   if (a.dtype == 1)
     hipLaunchKernelGGL(decode_prep_kernel<uint16_t>, grid, dim3(256), decode_prep_smem(a), s, a);

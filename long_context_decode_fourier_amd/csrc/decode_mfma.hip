@@ -55,6 +55,33 @@ __device__ inline float wsum(float v, int width) {
   for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// All-reduce over aligned groups of W = 16 or 32 lanes: DPP rotations inside
+// each 16-lane row, then one swizzle (xor 16) across the two rows of a
+// 32-lane half.
+template <int CTRL> __device__ inline float dpp_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float swz_xor16(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+template <int W> __device__ inline float group_max(float v) {
+  static_assert(W == 16 || W == 32, "group width");
+  v = fmaxf(v, dpp_ror<0x128>(v));
+  v = fmaxf(v, dpp_ror<0x124>(v));
+  v = fmaxf(v, dpp_ror<0x122>(v));
+  v = fmaxf(v, dpp_ror<0x121>(v));
+  if constexpr (W == 32) v = fmaxf(v, swz_xor16(v));
+  return v;
+}
+template <int W> __device__ inline float group_sum(float v) {
+  static_assert(W == 16 || W == 32, "group width");
+  v += dpp_ror<0x128>(v);
+  v += dpp_ror<0x124>(v);
+  v += dpp_ror<0x122>(v);
+  v += dpp_ror<0x121>(v);
+  if constexpr (W == 32) v += swz_xor16(v);
+  return v;
+}
 __device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 // round-to-nearest-even float -> bf16 bits (finite inputs)
@@ -72,6 +99,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NT = 64 * NW, MR = 16 * MB, NB = T / 16;
   constexpr int SL = (MR * T + NT - 1) / NT;  // softmax (row, token) slots per thread
   constexpr int KCM = 2;                      // max 32-dim chunks of the exact dims
+  constexpr int kNoChunk = 1 << 29;           // staging slot without a chunk
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -114,24 +142,36 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   // ---- zero the staging rows once: columns [du, DUS) stay zero (finite operands)
   for (int i = tid; i < 2 * nheads * T * DUS; i += NT) kxs[i] = 0;
 
-  // ---- kx / vx staging: thread -> 16-byte chunks c = tid + NT*i of the tile
+  // ---- kx / vx staging: thread -> 16-byte chunks c = tid + NT*i of the tile;
+  //      the chunk -> (KV head, token, 8 dims) map is the same for every tile
   const int du8 = du / 8;
   const int nchunk = nheads * T * du8;
+  int64_t st_src[PF];  // element offset of the chunk in the tile starting at t_begin
+  int st_tt[PF];       // token within the tile (kNoChunk: no chunk)
+  int st_lds[PF];      // LDS offset (halves) in kxs / vxs
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int c = tid + NT * i;
+    st_tt[i] = kNoChunk;
+    st_src[i] = 0;
+    st_lds[i] = 0;
+    if (du8 > 0 && c < nchunk) {
+      const int row = c / du8, c8 = c % du8;  // row = hh * T + tt
+      const int hh = row / T, tt = row % T;
+      st_tt[i] = tt;
+      st_src[i] = (row0 + static_cast<int64_t>(h0 + hh) * L + t_begin + tt) * du + 8 * c8;
+      st_lds[i] = row * DUS + 8 * c8;
+    }
+  }
   uint4 pk[PF], pv[PF];
   auto prefetch = [&](int tile) {
+    const int64_t shift = static_cast<int64_t>(tile - t_begin) * du;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const int c = tid + NT * i;
       uint4 vk = make_uint4(0u, 0u, 0u, 0u), vv = vk;
-      if (c < nchunk) {
-        const int hh = c / (T * du8), rem = c % (T * du8);
-        const int tt = rem / du8, c8 = rem % du8;
-        const int t = tile + tt;
-        if (t < t_end) {
-          const int64_t off = (row0 + static_cast<int64_t>(h0 + hh) * L + t) * du + 8 * c8;
-          vk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kx) + off);
-          vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.vx) + off);
-        }
+      if (tile + st_tt[i] < t_end) {
+        vk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kx) + st_src[i] + shift);
+        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.vx) + st_src[i] + shift);
       }
       pk[i] = vk;
       pv[i] = vv;
@@ -139,39 +179,26 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   };
   if (du8 > 0) prefetch(t_begin);
 
-  // ---- q operands: exact dims as bf16 MFMA A operand (per 32-dim chunk),
-  //      compressible dims (scaled, fp32) in LDS for the edge rows
+  // ---- q operands (permuted by decode_prep): exact dims as bf16 MFMA A
+  //      operand per 32-dim chunk, compressible dims (scaled fp32) in LDS for
+  //      the edge rows
   bf16x8 Qreg[KCM][MB];
 #pragma unroll
   for (int kc = 0; kc < KCM; ++kc)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int row = mb * 16 + l16;
-      bf16x8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 32 * kc + 8 * g4 + e;
-        uint16_t bits = 0;
-        if (row < rows && j < du) {
-          const int qi = qi0 + row;
-          const int dd = a.dims[(qi / a.G) * D + j];
-          if (dd >= 0 && dd < D)
-            bits = static_cast<const uint16_t*>(a.q)[(static_cast<int64_t>(b) * a.hq + qi) * D + dd];
-        }
-        v[e] = __builtin_bit_cast(__bf16, bits);
-      }
-      Qreg[kc][mb] = v;
+      uint4 bits = make_uint4(0u, 0u, 0u, 0u);
+      if (row < rows && kc < KC)
+        bits = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q16) +
+                                               (static_cast<int64_t>(b) * a.hq + qi0 + row) * du32 +
+                                               32 * kc + 8 * g4);
+      Qreg[kc][mb] = __builtin_bit_cast(bf16x8, bits);
     }
-  for (int idx = tid; idx < MR * dc; idx += NT) {
-    const int r = idx / dc, c = idx % dc;
-    float v = 0.0f;
-    if (r < rows) {
-      const int qi = qi0 + r;
-      const int dd = a.dims[(qi / a.G) * D + du + c];
-      if (dd >= 0 && dd < D)
-        v = a.scale * bf16_to_f32(static_cast<const uint16_t*>(a.q)[(static_cast<int64_t>(b) * a.hq + qi) * D + dd]);
-    }
-    qcs[idx] = v;
+  {
+    const float* qsrc = a.QC + (static_cast<int64_t>(b) * a.hq + qi0) * dc;
+#pragma unroll 4
+    for (int idx = tid; idx < MR * dc; idx += NT) qcs[idx] = (idx < rows * dc) ? qsrc[idx] : 0.0f;
   }
 
   // ---- this wave's coefficient units and its slice of A (MFMA A operand)
@@ -230,6 +257,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int cper = (chunks + kRuns - 1) / kRuns;
   const int c_lo = grun * cper, c_hi = min(chunks, c_lo + cper);
   const float invM = has_mid ? 1.0f / static_cast<float>(M) : 0.0f;
+  // integer phases of this thread's token (tau = t - sink, taken mod M):
+  // tau itself, 4 c_lo tau (first pair of its run) and 16 tau (run step),
+  // advanced by T tokens per tile
+  int ph_tau = 0, ph_r0 = 0, ph_d16 = 0, inc_tau = 0, inc_r0 = 0, inc_d16 = 0;
+  if (has_mid) {
+    int tau0 = (t_begin + gt - S) % M;
+    if (tau0 < 0) tau0 += M;
+    ph_tau = tau0;
+    ph_r0 = phase_mod(4 * c_lo, tau0, M);
+    ph_d16 = phase_mod(16, tau0, M);
+    inc_tau = T % M;
+    inc_r0 = phase_mod(4 * c_lo, T, M);
+    inc_d16 = phase_mod(16, T, M);
+  }
 
   // ---- edge-score mapping: thread -> (head, token, part of the comp dims)
   const int npairs = nheads * T;
@@ -245,11 +286,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     if (du8 > 0) {
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
-        const int c = tid + NT * i;
-        if (c < nchunk) {
-          const int row = c / du8, c8 = c % du8;  // row = hh * T + tt
-          *reinterpret_cast<uint4*>(kxs + row * DUS + 8 * c8) = pk[i];
-          *reinterpret_cast<uint4*>(vxs + row * DUS + 8 * c8) = pv[i];
+        if (st_tt[i] != kNoChunk) {
+          *reinterpret_cast<uint4*>(kxs + st_lds[i]) = pk[i];
+          *reinterpret_cast<uint4*>(vxs + st_lds[i]) = pv[i];
         }
       }
       if (tile0 + T < t_end) prefetch(tile0 + T);
@@ -266,11 +305,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
           *reinterpret_cast<half8*>(dst + 8 * c) = z;
         }
       } else {
-        const int tau = t - S;
+        const int tau = ph_tau;  // t - sink (a middle token: 0 <= t - sink < M)
         const float c2 = 2.0f * cos_rev(static_cast<float>(tau) * invM);
         // runs of 4 chunks (16 pairs) are seeded from exact phases
-        int r0 = phase_mod(4 * c_lo, tau, M);
-        const int d16 = phase_mod(16, tau, M);
+        int r0 = ph_r0;
+        const int d16 = ph_d16;
         for (int c = c_lo; c < c_hi; c += 4) {
           int r1 = r0 + tau;
           if (r1 >= M) r1 -= M;
@@ -299,6 +338,14 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
           r0 += d16;
           if (r0 >= M) r0 -= M;
         }
+      }
+      if (has_mid) {
+        ph_tau += inc_tau;
+        if (ph_tau >= M) ph_tau -= M;
+        ph_r0 += inc_r0;
+        if (ph_r0 >= M) ph_r0 -= M;
+        ph_d16 += inc_d16;
+        if (ph_d16 >= M) ph_d16 -= M;
       }
     }
     if (tile_edge) {
@@ -410,10 +457,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
           }
         }
       }
-      const float m_new = fmaxf(m_run[j], wmax(s, T));
+      const float m_new = fmaxf(m_run[j], group_max<T>(s));
       const float c = (m_new == -INFINITY || m_run[j] == m_new) ? 1.0f : __expf(m_run[j] - m_new);
       const float p = (s == -INFINITY) ? 0.0f : __expf(s - m_new);
-      l_run[j] = l_run[j] * c + wsum(p, T);
+      l_run[j] = l_run[j] * c + group_sum<T>(p);
       m_run[j] = m_new;
       if (row >= MR) continue;
       pf[row * T + tt] = p;

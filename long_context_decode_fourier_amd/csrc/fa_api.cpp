@@ -46,6 +46,7 @@ struct Shape {
   int L[fa::kMaxBatch], M[fa::kMaxBatch];
   int64_t row0[fa::kMaxBatch];
   int64_t total_len;
+  int max_len;
   bool any_mid;
 };
 
@@ -78,6 +79,7 @@ fa_status_t validate(const fa_desc_t* d, Shape* sh) {
   sh->R = d->recent;
   sh->k = d->n_coef;
   sh->total_len = 0;
+  sh->max_len = 0;
   sh->any_mid = false;
   for (int b = 0; b < sh->B; ++b) {
     const int L = d->seq_len[b];
@@ -90,6 +92,7 @@ fa_status_t validate(const fa_desc_t* d, Shape* sh) {
     sh->M[b] = static_cast<int>(M);
     sh->row0[b] = static_cast<int64_t>(sh->Hkv) * sh->total_len;
     sh->total_len += L;
+    sh->max_len = std::max(sh->max_len, L);
     sh->any_mid = sh->any_mid || M > 0;
   }
   return FA_OK;
@@ -159,7 +162,9 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
   a.nktiles = (sh.k + a.tk - 1) / a.tk;
   a.nctiles = (a.ncols + a.tn - 1) / a.tn;
   const int tiles = a.nktiles * a.nctiles;
-  const int slots = kNumCU;  // co-resident blocks share a CU's matrix cores
+  // Co-resident blocks: one 8-wave block per CU for large tiles; small
+  // 2-wave blocks are latency-bound, so four per CU overlap their steps.
+  const int slots = big ? kNumCU : 4 * kNumCU;
   int64_t total_steps = 0;
   for (int b = 0; b < sh.B; ++b) total_steps += (sh.M[b] + fa::kProjTT - 1) / fa::kProjTT;
   bool any_split = false;
@@ -197,7 +202,7 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
 struct DecPlan {
   fa::DecodeArgs args;
   int nitems;
-  size_t off_A, off_part, off_mrg, ws_bytes;
+  size_t off_A, off_q16, off_qc, off_part, off_mrg, ws_bytes;
 };
 
 // Row grouping of the MFMA path: `rows` consecutive query heads per item,
@@ -274,10 +279,30 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   a.rows = rows;
   a.ngroups = sh.Hq / rows;
   a.RS = 2 + a.du + a.dc + a.kpad;
+  // Token chunk per item: the smallest multiple of the tile for which the
+  // items fit one round of `target` co-resident blocks (ragged batches round
+  // each sequence up, so the even share alone can spill into a second round).
   const int64_t work = sh.total_len * a.ngroups;
   const int64_t target = a.mfma ? kNumCU : 2 * kNumCU;
-  const int chunk = static_cast<int>(
-      std::max<int64_t>(tile, (work + target - 1) / target / tile * tile));
+  int chunk = static_cast<int>(std::max<int64_t>(tile, (work + target - 1) / target / tile * tile));
+  auto count_items = [&](int c) {
+    int64_t n = 0;
+    for (int b = 0; b < sh.B; ++b) n += (sh.L[b] + c - 1) / c;
+    return n * a.ngroups;
+  };
+  if (count_items(chunk) > target) {
+    // smallest multiple of the tile in (chunk, max_len] that fits (item count
+    // falls as the chunk grows); keep the even share if none does
+    const int64_t top = (static_cast<int64_t>(sh.max_len) + tile - 1) / tile;
+    if (count_items(static_cast<int>(top * tile)) <= target) {
+      int64_t lo = chunk / tile, hi = top;  // count(lo) > target >= count(hi)
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) / 2;
+        if (count_items(static_cast<int>(mid * tile)) <= target) hi = mid; else lo = mid;
+      }
+      chunk = static_cast<int>(hi * tile);
+    }
+  }
   int item = 0, prow = 0;
   for (int b = 0; b < sh.B; ++b) {
     const int ns = (sh.L[b] + chunk - 1) / chunk;
@@ -296,7 +321,12 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   const size_t a_bytes = a.mfma ? static_cast<size_t>(sh.B) * sh.Hq * a.kpp * 2
                                 : static_cast<size_t>(sh.B) * sh.Hq * a.kpad * sizeof(float);
   a.MS = a.dc + a.kpad + 1;
-  p->off_part = align_up(a_bytes);
+  a.prep_a = (sh.Dc > 0 && sh.any_mid) ? 1 : 0;
+  const size_t rows_total = static_cast<size_t>(sh.B) * sh.Hq;
+  const size_t du32 = static_cast<size_t>((sh.Du + 31) / 32 * 32);
+  p->off_q16 = align_up(a_bytes);
+  p->off_qc = p->off_q16 + (a.mfma ? align_up(rows_total * du32 * 2) : 0);
+  p->off_part = p->off_qc + (a.mfma ? align_up(rows_total * sh.Dc * sizeof(float)) : 0);
   p->off_mrg = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
   p->ws_bytes = p->off_mrg + align_up(static_cast<size_t>(sh.B) * sh.Hq * a.MS * sizeof(float));
   return FA_OK;
@@ -471,14 +501,14 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
   a.scale = scale;
   a.A = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_A);
   a.A16 = static_cast<char*>(workspace) + p.off_A;
+  a.Q16 = static_cast<char*>(workspace) + p.off_q16;
+  a.QC = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_qc);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_part);
   a.mrg = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_mrg);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (sh.Dc > 0 && sh.any_mid) {
-    e = fa::launch_decode_prep(a, s);
-    if (e != hipSuccess) return hip_fail(e, "decode prep kernel");
-  }
+  e = fa::launch_decode_prep(a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode prep kernel");
   e = a.mfma ? fa::launch_decode_mfma(a, p.nitems, s) : fa::launch_decode_split(a, p.nitems, s);
   if (e != hipSuccess) return hip_fail(e, "decode split kernel");
   e = fa::launch_decode_merge(a, s);

@@ -61,6 +61,9 @@ struct DecodeArgs {
   float* out;
   float* A;      // VALU path: [B][Hq][kpad] fp32, basis order
   void* A16;     // MFMA path: [B][Hq][kpp] fp16, pair order
+  void* Q16;     // MFMA path: [B][Hq][du32] bf16, q at the exact dims (dims order, zero pad)
+  float* QC;     // MFMA path: [B][Hq][dc] fp32, scale * q at the compressible dims
+  int prep_a;    // decode_prep computes A (Dc > 0 and some sequence has middle tokens)
   float* part;   // partials [prow][RS]: m, l, o_U[du], o_E[dc], W[kpad]
   float* mrg;    // merged rows [B*Hq][MS]: o_E[dc], alpha*W[kpad], 1/l
   int nseq, hq, hkv, G, D, du, dc, k, kpad, kpp, sink, recent;

@@ -20,6 +20,8 @@
 //
 // fp32 inputs take a VALU kernel with correctly rounded phases (sincospi per
 // value) and compensated summation, which keeps coefficients within 1e-5.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace fa {
@@ -231,25 +233,37 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
       }
 }
 
-// Fixed-order sum of the split partials of one tile row, scaled by the basis
-// normalisation, scattered to ck / cv.  Sequences without middle get zeros.
+// Fixed-order sum of the split partials of each tile element, scaled by the
+// basis normalisation, scattered to ck / cv.  One thread per 4 consecutive
+// tile columns: grid-stride over (sequence, tile, row, column quad).
+// Sequences without middle get zeros.
 __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a) {
-  const int tk = a.tk, tn = a.tn;
+  const int tk = a.tk, tn = a.tn, tn4 = tn / 4;
   const int tiles = a.nktiles * a.nctiles;
-  int g = blockIdx.x;
-  const int nl = g % tk;
-  g /= tk;
-  const int tile = g % tiles, b = g / tiles;
-  const int kt = tile / a.nctiles, ct = tile % a.nctiles;
-  const int n = kt * tk + nl;
-  for (int cl = threadIdx.x; cl < tn; cl += blockDim.x) {
-    const int col = ct * tn + cl;
-    if (n >= a.k || col >= a.ncols) continue;
+  const int64_t per_seq = static_cast<int64_t>(tiles) * tk * tn4;
+  const int64_t total = per_seq * a.nseq;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int b = static_cast<int>(g / per_seq);
+    int64_t r = g - b * per_seq;
+    const int q4 = static_cast<int>(r % tn4);
+    r /= tn4;
+    const int nl = static_cast<int>(r % tk);
+    const int tile = static_cast<int>(r / tk);
+    const int kt = tile / a.nctiles, ct = tile % a.nctiles;
+    const int n = kt * tk + nl;
+    const int col0 = ct * tn + 4 * q4;
+    if (n >= a.k || col0 >= a.ncols) continue;
     const int ns = a.seq.nsplit[b];
-    const float* P = a.partial +
-                     (static_cast<int64_t>(a.seq.item0[b] + tile * ns) * tk + nl) * tn + cl;
-    float sum = 0.0f;
-    for (int sp = 0; sp < ns; ++sp) sum += P[static_cast<int64_t>(sp) * tk * tn];
+    const float* P = a.partial + (static_cast<int64_t>(a.seq.item0[b] + tile * ns) * tk + nl) * tn + 4 * q4;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < ns; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(sp) * tk * tn);
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
     const int M = a.seq.mid[b];
     float alpha = 0.0f;
     if (M > 0) {
@@ -257,8 +271,13 @@ __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a) {
       alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
                                      : sqrtf(2.0f / static_cast<float>(M));
     }
-    const int blk = col / a.dc, c = col % a.dc, mat = blk / a.hkv, h = blk % a.hkv;
-    a.out[mat][((static_cast<int64_t>(b) * a.hkv + h) * a.k + n) * a.dc + c] = alpha * sum;
+    // Dc % 4 == 0: the 4 columns share (matrix, KV head)
+    const int blk = col0 / a.dc, c = col0 % a.dc, mat = blk / a.hkv, h = blk % a.hkv;
+    float* o = (mat ? a.out[1] : a.out[0]) + ((static_cast<int64_t>(b) * a.hkv + h) * a.k + n) * a.dc + c;
+    o[0] = alpha * sum.x;
+    o[1] = alpha * sum.y;
+    o[2] = alpha * sum.z;
+    o[3] = alpha * sum.w;
   }
 }
 
@@ -379,8 +398,9 @@ hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
 
 hipError_t launch_project_reduce(const ProjArgs& a, hipStream_t s) {
   if (a.direct) return hipSuccess;
-  const int blocks = a.nseq * a.nktiles * a.nctiles * a.tk;
-  if (blocks == 0) return hipSuccess;
+  const int64_t quads = static_cast<int64_t>(a.nseq) * a.nktiles * a.nctiles * a.tk * (a.tn / 4);
+  if (quads == 0) return hipSuccess;
+  const int blocks = static_cast<int>(std::min<int64_t>((quads + 255) / 256, 8 * 2048));
   hipLaunchKernelGGL(project_reduce_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
