@@ -104,6 +104,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="input copies (0: enough to beat the LLC)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy kernel over MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -117,6 +119,16 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        # torch elementwise negation: reads and writes exactly n * 4 bytes
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4}))
+        return
     fb.lib()
     cfg = wl.CONFIGS[args.workload]
     w = wl.make(cfg)
