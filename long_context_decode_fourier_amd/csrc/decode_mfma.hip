@@ -4,30 +4,39 @@
 // coefficient space, online softmax, partials merged by decode_merge), laid out
 // for CDNA4 matrix cores.  A work item is (sequence, group of up to 32
 // consecutive query heads, token range); its query rows are stacked into the
-// 16-row M blocks of the MFMA.  Per tile of T tokens:
+// 16-row M blocks of the MFMA.  Tiles hold 16 tokens.
 //
-// * the basis tile phi[t][pos] (unscaled cos/sin, fp16) is generated once into
-//   LDS and shared by every row (three-term recurrence along the frequency
-//   index, seeded from exact integer phases every 16 frequencies);
-// * compressed scores  S_c = A phi^T  (fp16 MFMA over coefficients): each wave
-//   owns a slice of 32-wide coefficient units and keeps its slice of A
-//   (scale * alpha * q_C ck, written by decode_prep) in registers; the waves'
-//   partial scores are summed in LDS;
-// * exact scores  S_x = q_U kx^T  (bf16 MFMA over the exact dims) per KV head
-//   with q_U held in registers and kx staged in LDS;
-// * value moments  W += P phi  (fp16 MFMA over tokens, phi read transposed
-//   with ds_read_b64_tr_b16) and exact values  o_U += P vx  (bf16 MFMA, vx read
-//   transposed; P is split into a bf16 head and a bf16 remainder so the
-//   product keeps ~16 bits of P);
-// * kx / vx rows of the next tile are loaded (16-byte loads) while the current
-//   tile computes, then staged through LDS;
-// * the retained edge rows (ke / ve; at most a few tiles per sequence) take a
-//   VALU path with batched loads.
+// Per tile:
+//
+// [A] basis and scores.  Every wave owns a slice of 32-wide coefficient units
+//     and generates its slice of the basis tile directly as the MFMA operand
+//     (lane = token, 8 consecutive pair-order positions = 4 frequencies): each
+//     lane seeds e^{i f x}, e^{i x} and e^{i 16 x} from exact integer phases
+//     (phases advance by 16 tokens per tile, so nothing drifts), builds its 4
+//     frequencies by rotation and recurrence, and steps 16 frequencies per unit
+//     with the three-term recurrence.  The wave's compressed score partials
+//     S_c = A phi^T (fp16 MFMA, A = scale alpha q_C ck in registers) go to LDS,
+//     and its basis slice is written to a wave-private LDS slice for [C].
+//     Exact-dim scores q_U kx^T run on bf16 MFMA with kx loaded from HBM
+//     straight into the operand layout (no LDS).  Edge tokens (sink, recent)
+//     add their compressible part on VALU.
+// [B] online softmax over the tile (one thread per row and token, DPP
+//     reductions); P goes to LDS as fp16 (for W), bf16 head + remainder (for
+//     the exact values) and fp32 (edge values).
+// [C] value moments W += P phi (fp16 MFMA, the wave's basis slice read back
+//     transposed with ds_read_b64_tr_b16), exact values o_U += P vx (bf16 MFMA,
+//     vx staged in a double-buffered LDS tile and read transposed), edge values
+//     on VALU.
+//
+// Two barriers per tile: after [A] and after [B].  The loop is rotated so that
+// [C] of one tile and [A] of the next share a segment: the W and o_U MFMAs of
+// tile i overlap the basis generation of tile i+1.
 //
 // Coefficients live in "pair order" inside the kernel: position 2j holds the
 // cosine of frequency j (j = 0 is the constant), 2j+1 the sine; position 1 is
-// unused.  A is written in that order by decode_prep, W is converted back to
-// the basis order when the partials are stored.
+// unused (its basis value sin(0) is 0).  A is written in that order by
+// decode_prep, W is converted back to the basis order when the partials are
+// stored.
 #include "kernels.hpp"
 
 namespace fa {
@@ -47,39 +56,26 @@ __device__ inline short4v lds_read_tr4(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p));
 }
 
-__device__ inline float wmax(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ inline float wsum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-// All-reduce over aligned groups of W = 16 or 32 lanes: DPP rotations inside
-// each 16-lane row, then one swizzle (xor 16) across the two rows of a
-// 32-lane half.
+// All-reduce over aligned groups of 16 lanes: DPP rotations inside a row.
 template <int CTRL> __device__ inline float dpp_ror(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ inline float swz_xor16(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-}
-template <int W> __device__ inline float group_max(float v) {
-  static_assert(W == 16 || W == 32, "group width");
+__device__ inline float row16_max(float v) {
   v = fmaxf(v, dpp_ror<0x128>(v));
   v = fmaxf(v, dpp_ror<0x124>(v));
   v = fmaxf(v, dpp_ror<0x122>(v));
   v = fmaxf(v, dpp_ror<0x121>(v));
-  if constexpr (W == 32) v = fmaxf(v, swz_xor16(v));
   return v;
 }
-template <int W> __device__ inline float group_sum(float v) {
-  static_assert(W == 16 || W == 32, "group width");
+__device__ inline float row16_sum(float v) {
   v += dpp_ror<0x128>(v);
   v += dpp_ror<0x124>(v);
   v += dpp_ror<0x122>(v);
   v += dpp_ror<0x121>(v);
-  if constexpr (W == 32) v += swz_xor16(v);
+  return v;
+}
+__device__ inline float wsum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 __device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -89,20 +85,32 @@ __device__ inline uint16_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
+// Two floats to packed fp16 (round to nearest even), one instruction.
+__device__ inline uint32_t pack_f16(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
+}
+__device__ inline int add_mod(int x, int d, int M) {
+  x += d;
+  return x >= M ? x - M : x;
+}
 
 // MB: 16-row blocks; NW: waves; MAXU: max 32-wide coefficient units per wave;
-// T: tokens per tile (16 or 32); PF: 16-byte kx (and vx) chunks staged per
-// thread per tile; XPW: max (KV head, 16-dim block) exact-value tiles per
-// wave; RPH: max query rows per KV head (edge-row VALU path).
-template <int MB, int NW, int MAXU, int T, int PF, int XPW, int RPH>
+// PF: 16-byte vx chunks staged per thread per tile; XP: max KV heads per wave
+// (exact scores); XU: max (KV head, 16-dim block) exact-value tiles per wave;
+// RPH: max query rows per KV head (edge-row VALU path).
+template <int MB, int NW, int MAXU, int PF, int XP, int XU, int RPH>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NT = 64 * NW, MR = 16 * MB, NB = T / 16;
-  constexpr int SL = (MR * T + NT - 1) / NT;  // softmax (row, token) slots per thread
-  constexpr int KCM = 2;                      // max 32-dim chunks of the exact dims
-  constexpr int kNoChunk = 1 << 29;           // staging slot without a chunk
+  constexpr int T = kMfmaTile, TP = kMfmaTile + 4;
+  constexpr int NT = 64 * NW, MR = 16 * MB;
+  constexpr int KCM = 2;             // max 32-dim chunks of the exact dims
+  constexpr int kNoChunk = 1 << 29;  // staging slot without a chunk
+  static_assert(MR * T <= NT, "one softmax slot per thread");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g4 = lane >> 4, l16 = lane & 15;
   const int b = seq_of_item(a.seq, a.nseq, blockIdx.x);
   const int local = blockIdx.x - a.seq.item0[b];
@@ -119,36 +127,32 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int nheads = rows >= a.G ? rows / a.G : 1;
   const int rph = min(rows, a.G);  // query rows per KV head inside the item
   const bool has_mid = a.dc > 0 && M > 0;
-  const int du = a.du, dc = a.dc, D = a.D;
+  const int du = a.du, dc = a.dc;
   const int du32 = (du + 31) & ~31;
-  const int KC = du32 / 32;        // exact-dim chunks (<= KCM)
-  const int DUS = du32 + 8;        // LDS row stride of staged kx / vx (halves)
-  const int PS = a.kpp + 16;       // LDS row stride of the basis tile (halves)
+  const int KC = du32 / 32;  // exact-dim chunks (<= KCM)
+  const int ndb = du32 / 16;
 
-  _Float16* phi = reinterpret_cast<_Float16*>(smem);             // [T][PS]
-  uint16_t* kxs = reinterpret_cast<uint16_t*>(phi + T * PS);     // [nheads][T][DUS]
-  uint16_t* vxs = kxs + nheads * T * DUS;                         // [nheads][T][DUS]
-  float* sx = reinterpret_cast<float*>(vxs + nheads * T * DUS);   // [MR][T]
-  float* sedge = sx + MR * T;                                     // [MR][T]
-  float* spart = sedge + MR * T;                                  // [NW][MR][T]
-  float* pf = spart + NW * MR * T;                                // [MR][T]
-  _Float16* ph = reinterpret_cast<_Float16*>(pf + MR * T);        // [MR][T]
-  uint16_t* pbh = reinterpret_cast<uint16_t*>(ph + MR * T);       // [MR][T]
-  uint16_t* pbl = pbh + MR * T;                                   // [MR][T]
-  float* qcs = reinterpret_cast<float*>(pbl + MR * T);            // [MR][dc] (edge rows)
-  float* corr = qcs + MR * dc;                                    // [MR]
-  int* flag = reinterpret_cast<int*>(corr + MR);
+  const MfmaLds lo = mfma_lds(MB, NW, a.kpp, nheads, du, dc);
+  const int PS = lo.ps, DUS = lo.dus;
+  _Float16* phi = reinterpret_cast<_Float16*>(smem + lo.phi);   // [T][PS]
+  uint16_t* vxs = reinterpret_cast<uint16_t*>(smem + lo.vxs);   // [2][nheads][T][DUS]
+  float* spart = reinterpret_cast<float*>(smem + lo.spart);     // [NW][MR][TP]
+  float* sx = reinterpret_cast<float*>(smem + lo.sx);           // [MR][TP]
+  float* sedge = reinterpret_cast<float*>(smem + lo.sedge);     // [MR][TP]
+  float* pf = reinterpret_cast<float*>(smem + lo.pf);           // [MR][TP]
+  _Float16* ph = reinterpret_cast<_Float16*>(smem + lo.ph);     // [MR][TP]
+  uint16_t* pbh = reinterpret_cast<uint16_t*>(smem + lo.pbh);   // [MR][TP]
+  uint16_t* pbl = reinterpret_cast<uint16_t*>(smem + lo.pbl);   // [MR][TP]
+  float* corr = reinterpret_cast<float*>(smem + lo.corr);       // [MR]
+  float* qcs = reinterpret_cast<float*>(smem + lo.qcs);         // [MR][dc]
 
-  // ---- zero the staging rows once: columns [du, DUS) stay zero (finite operands)
-  for (int i = tid; i < 2 * nheads * T * DUS; i += NT) kxs[i] = 0;
-
-  // ---- kx / vx staging: thread -> 16-byte chunks c = tid + NT*i of the tile;
-  //      the chunk -> (KV head, token, 8 dims) map is the same for every tile
+  // ---- vx staging: thread -> 16-byte chunks c = tid + NT*i of a tile; the
+  //      chunk -> (KV head, token, 8 dims) map is the same for every tile
   const int du8 = du / 8;
   const int nchunk = nheads * T * du8;
   int64_t st_src[PF];  // element offset of the chunk in the tile starting at t_begin
   int st_tt[PF];       // token within the tile (kNoChunk: no chunk)
-  int st_lds[PF];      // LDS offset (halves) in kxs / vxs
+  int st_lds[PF];      // LDS offset (elements) inside one vxs buffer
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
     const int c = tid + NT * i;
@@ -163,24 +167,51 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       st_lds[i] = row * DUS + 8 * c8;
     }
   }
-  uint4 pk[PF], pv[PF];
-  auto prefetch = [&](int tile) {
+  uint4 pv[PF];
+  auto prefetch_v = [&](int tile) {
     const int64_t shift = static_cast<int64_t>(tile - t_begin) * du;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      uint4 vk = make_uint4(0u, 0u, 0u, 0u), vv = vk;
-      if (tile + st_tt[i] < t_end) {
-        vk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kx) + st_src[i] + shift);
-        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.vx) + st_src[i] + shift);
-      }
-      pk[i] = vk;
-      pv[i] = vv;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (tile + st_tt[i] < t_end)
+        v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.vx) + st_src[i] + shift);
+      pv[i] = v;
     }
   };
-  if (du8 > 0) prefetch(t_begin);
+  auto stage_v = [&](int buf) {
+    uint16_t* dst = vxs + buf * nheads * T * DUS;
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      if (st_tt[i] != kNoChunk) *reinterpret_cast<uint4*>(dst + st_lds[i]) = pv[i];
+  };
+
+  // ---- kx as the B operand of the exact-score MFMA, loaded from HBM:
+  //      lane -> (token l16, dims 32 kc + 8 g4 .. +7) of KV head wave + NW x
+  int64_t kx_src[XP];
+  uint4 kreg[XP][KCM];
+#pragma unroll
+  for (int x = 0; x < XP; ++x)
+    kx_src[x] = (row0 + static_cast<int64_t>(h0 + wave + NW * x) * L + t_begin + l16) * du + 8 * g4;
+  auto prefetch_k = [&](int tile) {
+    const int64_t shift = static_cast<int64_t>(tile - t_begin) * du;
+    const bool tok_ok = tile + l16 < t_end;
+#pragma unroll
+    for (int x = 0; x < XP; ++x)
+#pragma unroll
+      for (int kc = 0; kc < KCM; ++kc) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tok_ok && wave + NW * x < nheads && kc < KC && 32 * kc + 8 * g4 < du)
+          v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kx) + kx_src[x] + shift + 32 * kc);
+        kreg[x][kc] = v;
+      }
+  };
+  if (du8 > 0) {
+    prefetch_k(t_begin);
+    prefetch_v(t_begin);
+  }
 
   // ---- q operands (permuted by decode_prep): exact dims as bf16 MFMA A
-  //      operand per 32-dim chunk, compressible dims (scaled fp32) in LDS for
+  //      operand per 32-dim chunk; compressible dims (scaled fp32) in LDS for
   //      the edge rows
   bf16x8 Qreg[KCM][MB];
 #pragma unroll
@@ -226,12 +257,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     for (int n2 = 0; n2 < 2; ++n2)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) Wacc[u][n2][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // ---- exact-value tiles of this wave: (KV head, 16-dim block) pairs
-  const int ndb = du32 / 16;
-  floatx4 Uacc[XPW];
+  floatx4 Uacc[XU];
 #pragma unroll
-  for (int x = 0; x < XPW; ++x) Uacc[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int x = 0; x < XU; ++x) Uacc[x] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // ---- edge-row value accumulators (VALU): thread -> (head, comp-dim pair)
   const int dc2 = dc / 2;
@@ -242,114 +270,137 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int r = 0; r < RPH; ++r) oE[r][0] = oE[r][1] = 0.0f;
 
-  // ---- softmax slots: thread -> (row, token) for idx = tid + NT*j
-  float m_run[SL], l_run[SL];
-#pragma unroll
-  for (int j = 0; j < SL; ++j) {
-    m_run[j] = -INFINITY;
-    l_run[j] = 0.0f;
-  }
+  // ---- softmax slot: thread -> (row, token); threads beyond MR * T idle
+  const int s_row = tid / T, s_tt = tid % T;
+  float m_run = -INFINITY, l_run = 0.0f;
 
-  // ---- basis generation mapping: thread -> (token, run of pair chunks)
-  constexpr int kRuns = NT / T;              // runs per token
-  const int gt = tid % T, grun = tid / T;
-  const int chunks = a.kpp / 8;              // 4 pairs (8 halves) per chunk
-  const int cper = (chunks + kRuns - 1) / kRuns;
-  const int c_lo = grun * cper, c_hi = min(chunks, c_lo + cper);
+  // ---- basis generator: lane -> token l16 of the tile and frequencies
+  //      16 u + 4 g4 + j (j < 4) of its wave's units.  Integer phases (mod M)
+  //      of tau, 16 tau and f0 tau (f0 = 16 u0 + 4 g4) for this lane's token,
+  //      advanced by 16 tokens per tile.
   const float invM = has_mid ? 1.0f / static_cast<float>(M) : 0.0f;
-  // integer phases of this thread's token (tau = t - sink, taken mod M):
-  // tau itself, 4 c_lo tau (first pair of its run) and 16 tau (run step),
-  // advanced by T tokens per tile
-  int ph_tau = 0, ph_r0 = 0, ph_d16 = 0, inc_tau = 0, inc_r0 = 0, inc_d16 = 0;
+  const int f0 = 16 * u0 + 4 * g4;
+  int ph_tau = 0, ph_16 = 0, ph_f0 = 0, inc_tau = 0, inc_16 = 0, inc_f0 = 0;
   if (has_mid) {
-    int tau0 = (t_begin + gt - S) % M;
+    int tau0 = (t_begin + l16 - S) % M;
     if (tau0 < 0) tau0 += M;
     ph_tau = tau0;
-    ph_r0 = phase_mod(4 * c_lo, tau0, M);
-    ph_d16 = phase_mod(16, tau0, M);
+    ph_16 = phase_mod(16, tau0, M);
+    ph_f0 = phase_mod(f0, tau0, M);
     inc_tau = T % M;
-    inc_r0 = phase_mod(4 * c_lo, T, M);
-    inc_d16 = phase_mod(16, T, M);
+    inc_16 = phase_mod(16, T, M);
+    inc_f0 = phase_mod(f0, T, M);
   }
 
   // ---- edge-score mapping: thread -> (head, token, part of the comp dims)
   const int npairs = nheads * T;
-  const int tpp = NT / npairs >= 1 ? NT / npairs : 1;
+  const int tpp = edge_tpp(NT, npairs);
 
-  __syncthreads();  // staging rows zeroed, qcs ready
-
-  for (int tile0 = t_begin; tile0 < t_end; tile0 += T) {
+  // =================================================================== [A]
+  auto phase_a = [&](int tile0) {
     const int nt = min(T, t_end - tile0);
     const bool tile_edge = dc > 0 && (M == 0 || tile0 < S || tile0 + nt > S + M);
-    // ================= phase 1: stage this tile, prefetch the next, basis tile
-    if (tid == 0) *flag = 0;
+    if (has_mid) {
+      const int t = tile0 + l16;
+      const bool mid = t < t_end && t >= S && t < S + M;
+      // seeds of this lane's token: e^{i f0 x}, e^{i x}, e^{i 16 x}, x = 2 pi tau / M
+      const float x0 = static_cast<float>(ph_f0) * invM;
+      const float x1 = static_cast<float>(ph_tau) * invM;
+      const float x16 = static_cast<float>(ph_16) * invM;
+      // a lane whose token is not a middle token seeds zeros: all its values are 0
+      const float c0 = mid ? cos_rev(x0) : 0.0f, s0 = mid ? sin_rev(x0) : 0.0f;
+      const float c1 = cos_rev(x1), s1 = sin_rev(x1);
+      const float c16 = cos_rev(x16), s16 = sin_rev(x16);
+      const float tc1 = 2.0f * c1, tc16 = 2.0f * c16;
+      // two register sets alternate between even and odd units
+      float ca[4], sa[4], cb[4], sb[4];
+      ca[0] = c0;
+      sa[0] = s0;
+      ca[1] = fmaf(c0, c1, -s0 * s1);
+      sa[1] = fmaf(s0, c1, c0 * s1);
+      ca[2] = fmaf(tc1, ca[1], -ca[0]);
+      sa[2] = fmaf(tc1, sa[1], -sa[0]);
+      ca[3] = fmaf(tc1, ca[2], -ca[1]);
+      sa[3] = fmaf(tc1, sa[2], -sa[1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cb[j] = sb[j] = 0.0f;
+      floatx4 sacc[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) sacc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      _Float16* dst = phi + l16 * PS + u0 * 32 + 8 * g4;
+#pragma unroll
+      for (int u = 0; u < MAXU; ++u) {
+        if (u < nu) {
+          if (u == 1) {  // unit u0+1: rotate by 16 frequencies
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              cb[j] = fmaf(ca[j], c16, -sa[j] * s16);
+              sb[j] = fmaf(sa[j], c16, ca[j] * s16);
+            }
+          } else if (u > 1) {  // three-term recurrence, step 16 frequencies
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (u & 1) {
+                cb[j] = fmaf(tc16, ca[j], -cb[j]);
+                sb[j] = fmaf(tc16, sa[j], -sb[j]);
+              } else {
+                ca[j] = fmaf(tc16, cb[j], -ca[j]);
+                sa[j] = fmaf(tc16, sb[j], -sa[j]);
+              }
+            }
+          }
+          const float* zc = (u & 1) ? cb : ca;
+          const float* zs = (u & 1) ? sb : sa;
+          const uint4 bits = make_uint4(pack_f16(zc[0], zs[0]), pack_f16(zc[1], zs[1]),
+                                        pack_f16(zc[2], zs[2]), pack_f16(zc[3], zs[3]));
+          const half8 bv = __builtin_bit_cast(half8, bits);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Areg[u][mb], bv, sacc[mb], 0, 0, 0);
+          *reinterpret_cast<uint4*>(dst + 32 * u) = bits;
+        }
+      }
+      // this wave's partial scores: lane -> token l16, rows 4 g4 + r
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) spart[(wave * MR + mb * 16 + 4 * g4 + r) * TP + l16] = sacc[mb][r];
+      ph_tau = add_mod(ph_tau, inc_tau, M);
+      ph_16 = add_mod(ph_16, inc_16, M);
+      ph_f0 = add_mod(ph_f0, inc_f0, M);
+    }
+    // exact-dim scores of this wave's KV heads
     if (du8 > 0) {
 #pragma unroll
-      for (int i = 0; i < PF; ++i) {
-        if (st_tt[i] != kNoChunk) {
-          *reinterpret_cast<uint4*>(kxs + st_lds[i]) = pk[i];
-          *reinterpret_cast<uint4*>(vxs + st_lds[i]) = pv[i];
-        }
-      }
-      if (tile0 + T < t_end) prefetch(tile0 + T);
-    }
-    {
-      const int t = tile0 + gt;
-      const bool mid = has_mid && t < t_end && t >= S && t < S + M;
-      _Float16* dst = phi + gt * PS;
-      if (!mid) {
-        for (int c = c_lo; c < c_hi; ++c) {
-          half8 z;
+      for (int x = 0; x < XP; ++x) {
+        const int hh = wave + NW * x;
+        if (hh < nheads) {
+          const int rb = (rows >= a.G) ? hh * a.G : 0;
+          const int mb = rb >> 4;
+          floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) z[e] = 0;
-          *reinterpret_cast<half8*>(dst + 8 * c) = z;
-        }
-      } else {
-        const int tau = ph_tau;  // t - sink (a middle token: 0 <= t - sink < M)
-        const float c2 = 2.0f * cos_rev(static_cast<float>(tau) * invM);
-        // runs of 4 chunks (16 pairs) are seeded from exact phases
-        int r0 = ph_r0;
-        const int d16 = ph_d16;
-        for (int c = c_lo; c < c_hi; c += 4) {
-          int r1 = r0 + tau;
-          if (r1 >= M) r1 -= M;
-          const float x0 = static_cast<float>(r0) * invM, x1 = static_cast<float>(r1) * invM;
-          float cp = cos_rev(x0), sp_ = sin_rev(x0);
-          float cc = cos_rev(x1), sc = sin_rev(x1);
-          const int cend = min(c + 4, c_hi);
-          for (int cc4 = c; cc4 < cend; ++cc4) {
-            half8 z;
-            z[0] = static_cast<_Float16>(cp);
-            z[1] = static_cast<_Float16>(sp_);
-            z[2] = static_cast<_Float16>(cc);
-            z[3] = static_cast<_Float16>(sc);
-            const float cn = fmaf(c2, cc, -cp), sn = fmaf(c2, sc, -sp_);
-            z[4] = static_cast<_Float16>(cn);
-            z[5] = static_cast<_Float16>(sn);
-            const float cm = fmaf(c2, cn, -cc), sm = fmaf(c2, sn, -sc);
-            z[6] = static_cast<_Float16>(cm);
-            z[7] = static_cast<_Float16>(sm);
-            *reinterpret_cast<half8*>(dst + 8 * cc4) = z;
-            cp = fmaf(c2, cm, -cn);
-            sp_ = fmaf(c2, sm, -sn);
-            cc = fmaf(c2, cp, -cm);
-            sc = fmaf(c2, sp_, -sm);
+          for (int kc = 0; kc < KCM; ++kc)
+            if (kc < KC) {
+              const bf16x8 av = (MB > 1 && mb == 1) ? Qreg[kc][MB - 1] : Qreg[kc][0];
+              s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, kreg[x][kc]), s, 0, 0, 0);
+            }
+          const bool valid = tile0 + l16 < t_end;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = mb * 16 + 4 * g4 + r;
+            if (row >= rb && row < rb + rph) sx[row * TP + l16] = valid ? a.scale * s[r] : -INFINITY;
           }
-          r0 += d16;
-          if (r0 >= M) r0 -= M;
         }
       }
-      if (has_mid) {
-        ph_tau += inc_tau;
-        if (ph_tau >= M) ph_tau -= M;
-        ph_r0 += inc_r0;
-        if (ph_r0 >= M) ph_r0 -= M;
-        ph_d16 += inc_d16;
-        if (ph_d16 >= M) ph_d16 -= M;
+    } else {
+      // no exact dims: every row's exact part is 0 (or -inf past the end)
+      for (int idx = tid; idx < MR * T; idx += NT) {
+        const int row = idx / T, tt = idx % T;
+        sx[row * TP + tt] = (tile0 + tt < t_end) ? 0.0f : -INFINITY;
       }
     }
     if (tile_edge) {
-      // compressible part of the exact scores of the retained edge rows
+      // compressible part of the scores of the retained edge rows
       for (int pr = tid / tpp; pr < npairs; pr += NT / tpp) {
         const int hh = pr / T, tt = pr % T, part = tid % tpp;
         const int t = tile0 + tt;
@@ -359,9 +410,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         for (int r = 0; r < RPH; ++r) acc[r] = 0.0f;
         if (t < t_end && (M == 0 || t < S || t >= S + M)) {
           const int e = (M == 0 || t < S) ? t : t - M;
-          const int cper_ = dc / tpp, c0 = part * cper_;
+          const int cper_ = dc / tpp, cb0 = part * cper_;
           const uint32_t* erow = reinterpret_cast<const uint32_t*>(
-              static_cast<const uint16_t*>(a.ke) + ((static_cast<int64_t>(b) * a.hkv + h0 + hh) * E + e) * dc + c0);
+              static_cast<const uint16_t*>(a.ke) + ((static_cast<int64_t>(b) * a.hkv + h0 + hh) * E + e) * dc + cb0);
           for (int cb = 0; 2 * cb < cper_; cb += 8) {  // batches of 8 independent loads
             uint32_t ew[8];
 #pragma unroll
@@ -372,7 +423,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < RPH; ++r)
                   if (r < rph) {
-                    const int cc = c0 + 2 * (cb + c);
+                    const int cc = cb0 + 2 * (cb + c);
                     acc[r] = fmaf(qcs[(rb + r) * dc + cc], lo_bf16(ew[c]),
                                   fmaf(qcs[(rb + r) * dc + cc + 1], hi_bf16(ew[c]), acc[r]));
                   }
@@ -383,186 +434,126 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         if (part == 0)
 #pragma unroll
           for (int r = 0; r < RPH; ++r)
-            if (r < rph) sedge[(rb + r) * T + tt] = acc[r];
+            if (r < rph) sedge[(rb + r) * TP + tt] = acc[r];
       }
     }
-    __syncthreads();
+    // next tile's kx and vx: issued last, so that no wait above covers them
+    if (du8 > 0 && tile0 + T < t_end) {
+      prefetch_k(tile0 + T);
+      prefetch_v(tile0 + T);
+    }
+  };
 
-    // ================= phase 2: compressed score partials, exact scores (MFMA)
-    if (has_mid) {
-      floatx4 sacc[MB][NB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sacc[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < MAXU; ++u) {
-        if (u < nu) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const half8 bv = *reinterpret_cast<const half8*>(
-                phi + (nb * 16 + l16) * PS + (u0 + u) * 32 + 8 * g4);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              sacc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Areg[u][mb], bv, sacc[mb][nb], 0, 0, 0);
-          }
-        }
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            spart[(wave * MR + mb * 16 + 4 * g4 + r) * T + nb * 16 + l16] = sacc[mb][nb][r];
-    }
-    for (int p = wave; p < nheads * NB; p += NW) {
-      const int hh = p / NB, nb = p % NB;
-      const int rb = (rows >= a.G) ? hh * a.G : 0;
-      const int mb = rb >> 4;
-      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = kxs + (hh * T + nb * 16 + l16) * DUS + 8 * g4;
-#pragma unroll
-      for (int kc = 0; kc < KCM; ++kc) {
-        if (kc < KC) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(krow + 32 * kc);
-          bf16x8 av = Qreg[kc][0];
-          if (MB > 1 && mb == 1) av = Qreg[kc][MB - 1];
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, s, 0, 0, 0);
-        }
-      }
-      const int tt = nb * 16 + l16;
-      const bool valid = tile0 + tt < t_end;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = mb * 16 + 4 * g4 + r;
-        if (row >= rb && row < rb + rph) sx[row * T + tt] = valid ? a.scale * s[r] : -INFINITY;
-      }
-    }
-    __syncthreads();
-
-    // ================= phase 3: online softmax over the tile
-#pragma unroll
-    for (int j = 0; j < SL; ++j) {
-      const int idx = tid + NT * j;
-      const int row = idx / T, tt = idx % T;  // row >= MR: idle slot
+  // =================================================================== [B]
+  auto phase_b = [&](int tile0) {
+    const int nt = min(T, t_end - tile0);
+    const bool tile_edge = dc > 0 && (M == 0 || tile0 < S || tile0 + nt > S + M);
+    if (s_row < MR) {
       float s = -INFINITY;
-      if (row < rows) {
-        s = sx[row * T + tt];
+      if (s_row < rows) {
+        s = sx[s_row * TP + s_tt];
         if (s != -INFINITY) {
-          if (tile_edge) s += sedge[row * T + tt];
+          if (tile_edge) s += sedge[s_row * TP + s_tt];
           if (has_mid) {
 #pragma unroll
-            for (int w = 0; w < NW; ++w) s += spart[(w * MR + row) * T + tt];
+            for (int w = 0; w < NW; ++w) s += spart[(w * MR + s_row) * TP + s_tt];
           }
         }
       }
-      const float m_new = fmaxf(m_run[j], group_max<T>(s));
-      const float c = (m_new == -INFINITY || m_run[j] == m_new) ? 1.0f : __expf(m_run[j] - m_new);
+      const float m_new = fmaxf(m_run, row16_max(s));
+      const float c = (m_new == -INFINITY || m_run == m_new) ? 1.0f : __expf(m_run - m_new);
       const float p = (s == -INFINITY) ? 0.0f : __expf(s - m_new);
-      l_run[j] = l_run[j] * c + group_sum<T>(p);
-      m_run[j] = m_new;
-      if (row >= MR) continue;
-      pf[row * T + tt] = p;
-      ph[row * T + tt] = static_cast<_Float16>(p);
+      l_run = l_run * c + row16_sum(p);
+      m_run = m_new;
+      const int o = s_row * TP + s_tt;
+      pf[o] = p;
+      ph[o] = static_cast<_Float16>(p);
       const uint16_t hb = bf16_rne(p);
-      pbh[row * T + tt] = hb;
-      pbl[row * T + tt] = bf16_rne(p - __uint_as_float(static_cast<uint32_t>(hb) << 16));
-      if (tt == 0) {
-        corr[row] = c;
-        if (c != 1.0f) *flag = 1;
-      }
+      pbh[o] = hb;
+      pbl[o] = bf16_rne(p - __uint_as_float(static_cast<uint32_t>(hb) << 16));
+      if (s_tt == 0) corr[s_row] = c;
     }
-    __syncthreads();
+  };
 
-    // ================= phase 4: value moments W, exact values (MFMA)
-    const bool rescale = *flag != 0;
-    if (rescale) {
+  // =================================================================== [C]
+  auto phase_c = [&](int tile0, int buf) {
+    const int nt = min(T, t_end - tile0);
+    const bool tile_edge = dc > 0 && (M == 0 || tile0 < S || tile0 + nt > S + M);
+    // rescale the running sums of the rows whose maximum moved (wave-uniform test)
+    {
+      float cr[MB][4];
+      bool any = false;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        float cr[4];
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cr[r] = corr[mb * 16 + 4 * g4 + r];
-        if (has_mid) {
-#pragma unroll
-          for (int u = 0; u < MAXU; ++u)
-#pragma unroll
-            for (int n2 = 0; n2 < 2; ++n2)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) Wacc[u][n2][mb][r] *= cr[r];
+        for (int r = 0; r < 4; ++r) {
+          cr[mb][r] = corr[mb * 16 + 4 * g4 + r];
+          any = any || cr[mb][r] != 1.0f;
         }
+      if (__any(any)) {
 #pragma unroll
-        for (int x = 0; x < XPW; ++x) {
-          const int p = wave + NW * x;
-          const int rb = (rows >= a.G) ? (p / max(ndb, 1)) * a.G : 0;
-          if ((rb >> 4) == mb)
+        for (int mb = 0; mb < MB; ++mb) {
+          if (has_mid) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Uacc[x][r] *= cr[r];
+            for (int u = 0; u < MAXU; ++u)
+#pragma unroll
+              for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Wacc[u][n2][mb][r] *= cr[mb][r];
+          }
+#pragma unroll
+          for (int x = 0; x < XU; ++x) {
+            const int q = wave + NW * x;
+            const int rb = (rows >= a.G) ? (q / max(ndb, 1)) * a.G : 0;
+            if ((rb >> 4) == mb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) Uacc[x][r] *= cr[mb][r];
+          }
         }
       }
     }
     if (has_mid) {
+      half4 pv4[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) pv4[mb] = *reinterpret_cast<const half4*>(ph + (mb * 16 + l16) * TP + 4 * g4);
 #pragma unroll
       for (int u = 0; u < MAXU; ++u) {
         if (u < nu) {
 #pragma unroll
           for (int n2 = 0; n2 < 2; ++n2) {
             const int nbase = (u0 + u) * 32 + n2 * 16 + 4 * (l16 & 3);
-            if constexpr (T == 32) {
-              const short4v lo = lds_read_tr4(phi + (8 * g4 + (l16 >> 2)) * PS + nbase);
-              const short4v hi = lds_read_tr4(phi + (8 * g4 + 4 + (l16 >> 2)) * PS + nbase);
-              const half8 bv = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const half4 bv = __builtin_bit_cast(half4, lds_read_tr4(phi + (4 * g4 + (l16 >> 2)) * PS + nbase));
 #pragma unroll
-              for (int mb = 0; mb < MB; ++mb) {
-                const half8 pv8 = *reinterpret_cast<const half8*>(ph + (mb * 16 + l16) * T + 8 * g4);
-                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv8, bv, Wacc[u][n2][mb], 0, 0, 0);
-              }
-            } else {
-              const half4 bv = __builtin_bit_cast(half4, lds_read_tr4(phi + (4 * g4 + (l16 >> 2)) * PS + nbase));
-#pragma unroll
-              for (int mb = 0; mb < MB; ++mb) {
-                const half4 pv4 = *reinterpret_cast<const half4*>(ph + (mb * 16 + l16) * T + 4 * g4);
-                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pv4, bv, Wacc[u][n2][mb], 0, 0, 0);
-              }
-            }
+            for (int mb = 0; mb < MB; ++mb)
+              Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pv4[mb], bv, Wacc[u][n2][mb], 0, 0, 0);
           }
         }
       }
     }
+    const uint16_t* vbuf = vxs + buf * nheads * T * DUS;
 #pragma unroll
-    for (int x = 0; x < XPW; ++x) {
-      const int p = wave + NW * x;
-      if (ndb == 0 || p >= nheads * ndb) continue;
-      const int hh = p / ndb, db = p % ndb;
+    for (int x = 0; x < XU; ++x) {
+      const int q = wave + NW * x;
+      if (ndb == 0 || q >= nheads * ndb) continue;
+      const int hh = q / ndb, db = q % ndb;
       const int rb = (rows >= a.G) ? hh * a.G : 0;
       const int mb = rb >> 4;
-      const uint16_t* vbase = vxs + hh * T * DUS + db * 16 + 4 * (l16 & 3);
-      if constexpr (T == 32) {
-        const short4v lo = lds_read_tr4(vbase + (8 * g4 + (l16 >> 2)) * DUS);
-        const short4v hi = lds_read_tr4(vbase + (8 * g4 + 4 + (l16 >> 2)) * DUS);
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 ph8 = *reinterpret_cast<const bf16x8*>(pbh + (mb * 16 + l16) * T + 8 * g4);
-        const bf16x8 pl8 = *reinterpret_cast<const bf16x8*>(pbl + (mb * 16 + l16) * T + 8 * g4);
-        Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph8, bv, Uacc[x], 0, 0, 0);
-        Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl8, bv, Uacc[x], 0, 0, 0);
-      } else {
-        const short4v bv = lds_read_tr4(vbase + (4 * g4 + (l16 >> 2)) * DUS);
-        const short4v ph4 = *reinterpret_cast<const short4v*>(pbh + (mb * 16 + l16) * T + 4 * g4);
-        const short4v pl4 = *reinterpret_cast<const short4v*>(pbl + (mb * 16 + l16) * T + 4 * g4);
-        Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph4, bv, Uacc[x], 0, 0, 0);
-        Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl4, bv, Uacc[x], 0, 0, 0);
-      }
+      const uint16_t* vbase = vbuf + hh * T * DUS + db * 16 + 4 * (l16 & 3);
+      const short4v bv = lds_read_tr4(vbase + (4 * g4 + (l16 >> 2)) * DUS);
+      const short4v ph4 = *reinterpret_cast<const short4v*>(pbh + (mb * 16 + l16) * TP + 4 * g4);
+      const short4v pl4 = *reinterpret_cast<const short4v*>(pbl + (mb * 16 + l16) * TP + 4 * g4);
+      Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph4, bv, Uacc[x], 0, 0, 0);
+      Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl4, bv, Uacc[x], 0, 0, 0);
     }
     if (evld) {
       const int h = h0 + eh;
-      if (rescale)
 #pragma unroll
-        for (int r = 0; r < RPH; ++r)
-          if (r < rph) {
-            const float cr = corr[erb + r];
-            oE[r][0] *= cr;
-            oE[r][1] *= cr;
-          }
+      for (int r = 0; r < RPH; ++r)
+        if (r < rph) {
+          const float cr = corr[erb + r];
+          oE[r][0] *= cr;
+          oE[r][1] *= cr;
+        }
       if (tile_edge) {
         // edge tokens of this tile: [tile0, mid_lo) and [mid_hi, tile0 + nt)
         const int mid_lo = (M == 0) ? tile0 + nt : max(tile0, min(tile0 + nt, S));
@@ -570,23 +561,23 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         const uint32_t* ecol = reinterpret_cast<const uint32_t*>(
             static_cast<const uint16_t*>(a.ve) + (static_cast<int64_t>(b) * a.hkv + h) * E * dc + 2 * ec);
         for (int seg = 0; seg < 2; ++seg) {
-          const int lo = seg == 0 ? tile0 : mid_hi, hi = seg == 0 ? mid_lo : tile0 + nt;
-          for (int t0 = lo; t0 < hi; t0 += 8) {  // batches of 8 independent loads
+          const int lo_t = seg == 0 ? tile0 : mid_hi, hi_t = seg == 0 ? mid_lo : tile0 + nt;
+          for (int t0 = lo_t; t0 < hi_t; t0 += 8) {  // batches of 8 independent loads
             uint32_t w8[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
               const int t = t0 + q;
               const int e = (M == 0 || t < S) ? t : t - M;
-              w8[q] = (t < hi) ? ecol[static_cast<int64_t>(e) * dc2] : 0u;
+              w8[q] = (t < hi_t) ? ecol[static_cast<int64_t>(e) * dc2] : 0u;
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-              if (t0 + q >= hi) break;
+              if (t0 + q >= hi_t) break;
               const float v0 = lo_bf16(w8[q]), v1 = hi_bf16(w8[q]);
 #pragma unroll
               for (int r = 0; r < RPH; ++r)
                 if (r < rph) {
-                  const float p = pf[(erb + r) * T + (t0 + q - tile0)];
+                  const float p = pf[(erb + r) * TP + (t0 + q - tile0)];
                   oE[r][0] = fmaf(p, v0, oE[r][0]);
                   oE[r][1] = fmaf(p, v1, oE[r][1]);
                 }
@@ -595,26 +586,40 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         }
       }
     }
+  };
+
+  // ---- pipeline: [A](0) | { [B](i) | [C](i) [A](i+1) } ...
+  // Every prologue load completes here, so that no wait inside the loop (for
+  // A, q or the first tile) also waits for the loop's own prefetches.
+  __builtin_amdgcn_s_waitcnt(0);
+  const int ntiles = (t_end - t_begin + T - 1) / T;
+  if (du8 > 0) stage_v(0);
+  phase_a(t_begin);
+  __syncthreads();
+  for (int i = 0; i < ntiles; ++i) {
+    const int tile0 = t_begin + i * T;
+    phase_b(tile0);
+    __syncthreads();
+    phase_c(tile0, i & 1);
+    if (i + 1 < ntiles) {
+      if (du8 > 0) stage_v((i + 1) & 1);
+      phase_a(tile0 + T);
+    }
     __syncthreads();
   }
 
   // ================= partials
   const int64_t prow = static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(qi0) * ns + sp;
-#pragma unroll
-  for (int j = 0; j < SL; ++j) {
-    const int idx = tid + NT * j;
-    const int row = idx / T, tt = idx % T;
-    if (tt == 0 && row < rows) {
-      float* P = a.part + (prow + static_cast<int64_t>(row) * ns) * a.RS;
-      P[0] = m_run[j];
-      P[1] = l_run[j];
-    }
+  if (s_row < rows && s_tt == 0) {
+    float* P = a.part + (prow + static_cast<int64_t>(s_row) * ns) * a.RS;
+    P[0] = m_run;
+    P[1] = l_run;
   }
 #pragma unroll
-  for (int x = 0; x < XPW; ++x) {
-    const int p = wave + NW * x;
-    if (ndb == 0 || p >= nheads * ndb) continue;
-    const int hh = p / ndb, db = p % ndb;
+  for (int x = 0; x < XU; ++x) {
+    const int q = wave + NW * x;
+    if (ndb == 0 || q >= nheads * ndb) continue;
+    const int hh = q / ndb, db = q % ndb;
     const int rb = (rows >= a.G) ? hh * a.G : 0;
     const int mb = rb >> 4;
     const int d = db * 16 + l16;
@@ -657,9 +662,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-template <int MB, int NW, int MAXU, int T, int PF, int XPW, int RPH>
+template <int MB, int NW, int MAXU, int PF, int XP, int XU, int RPH>
 hipError_t launch_one(const DecodeArgs& a, int nitems, size_t smem, hipStream_t s) {
-  auto k = decode_mfma_kernel<MB, NW, MAXU, T, PF, XPW, RPH>;
+  auto k = decode_mfma_kernel<MB, NW, MAXU, PF, XP, XU, RPH>;
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -671,18 +676,45 @@ hipError_t launch_one(const DecodeArgs& a, int nitems, size_t smem, hipStream_t 
 }
 
 // Compiled variants, chosen by row blocks and basis length (pair-order
-// positions kpp): short bases take 4 waves, long ones 8 waves so that each
-// wave's slice of A and W stays in registers.
+// positions kpp): each wave's slice of A and W stays in registers.
 constexpr MfmaVariant kVariants[] = {
-    // mb nw maxu  t pf xpw rph kpp_min kpp_max
-    {1, 4, 4, 32, 4, 4, 8, 0, 512},
-    {2, 4, 4, 32, 4, 8, 8, 0, 512},
-    {2, 8, 5, 32, 2, 4, 4, 513, 1280},
-    {1, 8, 5, 32, 2, 4, 4, 513, 1280},
-    {1, 8, 9, 16, 1, 4, 4, 1281, 2304},
+    // mb nw maxu pf xp xu rph kpp_min kpp_max
+    {1, 8, 2, 4, 2, 8, 8, 0, 512},
+    {2, 8, 2, 2, 1, 4, 8, 0, 512},
+    {2, 8, 5, 1, 1, 2, 4, 513, 1280},
+    {1, 8, 5, 2, 2, 4, 8, 513, 1280},
+    {1, 8, 9, 1, 1, 2, 4, 1281, 2304},
 };
 
 }  // namespace
+
+// LDS carve-up shared by the kernel and the host-side size check.
+__host__ __device__ MfmaLds mfma_lds(int mb, int nw, int kpp, int nheads, int du, int dc) {
+  const int T = kMfmaTile, MR = 16 * mb, TP = kMfmaTile + 4;
+  const int du32 = (du + 31) & ~31;
+  MfmaLds o;
+  int off = 0;
+  auto take = [&off](int bytes) {
+    const int r = off;
+    off += (bytes + 15) & ~15;
+    return r;
+  };
+  o.ps = kpp + 16;
+  o.dus = du32 + 16;
+  o.phi = take(T * o.ps * 2);
+  o.vxs = take(du32 ? 2 * nheads * T * o.dus * 2 : 0);
+  o.spart = take(nw * MR * TP * 4);
+  o.sx = take(MR * TP * 4);
+  o.sedge = take(MR * TP * 4);
+  o.pf = take(MR * TP * 4);
+  o.ph = take(MR * TP * 2);
+  o.pbh = take(MR * TP * 2);
+  o.pbl = take(MR * TP * 2);
+  o.corr = take(MR * 4);
+  o.qcs = take(MR * dc * 4);
+  o.total = off;
+  return o;
+}
 
 const MfmaVariant* decode_mfma_pick(int kpp, int mb) {
   for (const MfmaVariant& v : kVariants)
@@ -691,11 +723,7 @@ const MfmaVariant* decode_mfma_pick(int kpp, int mb) {
 }
 
 size_t decode_mfma_smem(const DecodeArgs& a, const MfmaVariant& v, int nheads) {
-  const int T = v.t, MR = 16 * v.mb;
-  const int dus = ((a.du + 31) & ~31) + 8;
-  return static_cast<size_t>(T) * (a.kpp + 16) * 2 + 2 * static_cast<size_t>(2 * nheads * T * dus) +
-         sizeof(float) * (MR * T * 2 + v.nw * MR * T + MR * T) + 2 * MR * T * 3 +
-         sizeof(float) * (MR * a.dc + MR) + 16;
+  return static_cast<size_t>(mfma_lds(v.mb, v.nw, a.kpp, nheads, a.du, a.dc).total);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s) {
@@ -705,11 +733,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s) {
   const int nheads = a.rows >= a.G ? a.rows / a.G : 1;
   const size_t smem = decode_mfma_smem(a, *v, nheads);
   switch (v - kVariants) {
-    case 0: return launch_one<1, 4, 4, 32, 4, 4, 8>(a, nitems, smem, s);
-    case 1: return launch_one<2, 4, 4, 32, 4, 8, 8>(a, nitems, smem, s);
-    case 2: return launch_one<2, 8, 5, 32, 2, 4, 4>(a, nitems, smem, s);
-    case 3: return launch_one<1, 8, 5, 32, 2, 4, 4>(a, nitems, smem, s);
-    case 4: return launch_one<1, 8, 9, 16, 1, 4, 4>(a, nitems, smem, s);
+    case 0: return launch_one<1, 8, 2, 4, 2, 8, 8>(a, nitems, smem, s);
+    case 1: return launch_one<2, 8, 2, 2, 1, 4, 8>(a, nitems, smem, s);
+    case 2: return launch_one<2, 8, 5, 1, 1, 2, 4>(a, nitems, smem, s);
+    case 3: return launch_one<1, 8, 5, 2, 2, 4, 8>(a, nitems, smem, s);
+    case 4: return launch_one<1, 8, 9, 1, 1, 2, 4>(a, nitems, smem, s);
   }
   return hipErrorInvalidValue;
 }

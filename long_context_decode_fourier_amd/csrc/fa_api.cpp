@@ -215,23 +215,18 @@ bool mfma_rows_ok(const Shape& sh, int rows, int kpp) {
   const int mb = rows > 16 ? 2 : 1;
   const fa::MfmaVariant* v = fa::decode_mfma_pick(kpp, mb);
   if (!v) return false;
+  const int T = fa::kMfmaTile;
   const int nheads = rows >= G ? rows / G : 1;
   if (std::min(rows, G) > v->rph) return false;
   const int nt = 64 * v->nw;
   const int du32 = (sh.Du + 31) / 32 * 32;
   if (sh.Du % 8 || du32 > 64) return false;
-  if (nheads * (du32 / 16) > v->xpw * v->nw) return false;
-  if (nheads * (sh.Dc / 2) > nt || sh.Dc % 2) return false;
-  const int tpp = std::max(1, nt / (nheads * v->t));
-  if (sh.Dc % (2 * tpp)) return false;
-  if (nheads * v->t * (sh.Du / 8) > v->pf * nt) return false;
-  fa::DecodeArgs probe;
-  std::memset(&probe, 0, sizeof probe);
-  probe.kpp = kpp;
-  probe.D = sh.D;
-  probe.du = sh.Du;
-  probe.dc = sh.Dc;
-  return fa::decode_mfma_smem(probe, *v, nheads) <= kMaxLds;
+  if (nheads > v->xp * v->nw) return false;                   // exact-score heads per wave
+  if (nheads * (du32 / 16) > v->xu * v->nw) return false;     // exact-value tiles per wave
+  if (nheads * T * (sh.Du / 8) > v->pf * nt) return false;    // staged vx chunks per thread
+  if (nheads * (sh.Dc / 2) > nt || sh.Dc % 2) return false;   // edge-value threads
+  if (sh.Dc % (2 * fa::edge_tpp(nt, nheads * T))) return false;
+  return fa::mfma_lds(v->mb, v->nw, kpp, nheads, sh.Du, sh.Dc).total <= kMaxLds;
 }
 
 fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
@@ -254,8 +249,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   // pays for (long bases amortise their generation over more rows).
   int rows = 0;
   if (sh.dtype == FA_BF16 && sh.Du % 2 == 0 && sh.Dc % 2 == 0) {
-    const int cap = (sh.k >= 512) ? 32 : std::max(4, std::min(sh.G, 8));
-    for (int r = cap; r >= 1; --r)
+    for (int r = 32; r >= 1; --r)
       if (mfma_rows_ok(sh, r, a.kpp)) {
         rows = r;
         break;
@@ -265,7 +259,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   if (rows > 0) {
     a.mfma = 1;
     a.mb = rows > 16 ? 2 : 1;
-    tile = fa::decode_mfma_pick(a.kpp, a.mb)->t;
+    tile = fa::kMfmaTile;
   } else {
     a.mfma = 0;
     tile = fa::kDecTile;

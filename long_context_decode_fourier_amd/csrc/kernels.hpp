@@ -82,17 +82,30 @@ hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
-// A compiled variant of the MFMA decode kernel.
+// MFMA decode kernel: tokens per tile, compiled variants and LDS carve-up.
+constexpr int kMfmaTile = 16;
 struct MfmaVariant {
   int mb;       // 16-row blocks
   int nw;       // waves per workgroup
   int maxu;     // max 32-wide coefficient units per wave
-  int t;        // tokens per tile
-  int pf;       // 16-byte kx/vx chunks staged per thread per tile
-  int xpw;      // max (KV head, 16-dim block) exact-value tiles per wave
+  int pf;       // 16-byte vx chunks staged per thread per tile
+  int xp;       // max KV heads per wave (exact scores)
+  int xu;       // max (KV head, 16-dim block) exact-value tiles per wave
   int rph;      // max query rows per KV head
   int kpp_min, kpp_max;
 };
+struct MfmaLds {
+  int ps, dus;  // row strides (halves) of the basis tile and the staged vx rows
+  int phi, vxs, spart, sx, sedge, pf, ph, pbh, pbl, corr, qcs, total;  // byte offsets
+};
+__host__ __device__ MfmaLds mfma_lds(int mb, int nw, int kpp, int nheads, int du, int dc);
+// Threads per (KV head, token) pair in the edge-score path: the largest power
+// of two <= threads / pairs (at least 1).
+__host__ __device__ inline int edge_tpp(int threads, int pairs) {
+  int t = 1;
+  while (2 * t * pairs <= threads) t *= 2;
+  return t;
+}
 const MfmaVariant* decode_mfma_pick(int kpp, int mb);
 size_t decode_mfma_smem(const DecodeArgs& a, const MfmaVariant& v, int nheads);
 
