@@ -423,8 +423,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // partial vector [o_U | o_E | W]).  Each block recomputes the log-sum-exp
 // weights of the splits, sums its slice over the splits in a fixed order and
 // writes o_U / l to out, o_E and alpha * W to the merge buffer (mrg).
-// Pass 2 (decode_merge_cv): one block per (sequence, KV head) applies C_V to
-// the merged W of its query rows and writes the compressible dims.
+// Pass 2 (decode_merge_cv): one block per (sequence, KV head, 32 compressible
+// dims) applies C_V to the merged W of the head's query rows and writes those
+// dims of out.
 constexpr int kMergeRows = 4;
 
 __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
@@ -467,16 +468,16 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   if (blockIdx.y == 0 && threadIdx.x == 0) mrow[a.dc + a.kpad] = linv;
   if (idx >= nvec) return;
   const float* Pi = P + 2 + idx;
-  float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    v0 = fmaf(smem[s], Pi[static_cast<int64_t>(s) * a.RS], v0);
-    v1 = fmaf(smem[s + 1], Pi[static_cast<int64_t>(s + 1) * a.RS], v1);
-    v2 = fmaf(smem[s + 2], Pi[static_cast<int64_t>(s + 2) * a.RS], v2);
-    v3 = fmaf(smem[s + 3], Pi[static_cast<int64_t>(s + 3) * a.RS], v3);
+  // fixed-order sum over the splits, 8 loads in flight
+  float v = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (s0 + j < ns) ? Pi[static_cast<int64_t>(s0 + j) * a.RS] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < ns) v = fmaf(smem[s0 + j], x[j], v);
   }
-  for (; s < ns; ++s) v0 = fmaf(smem[s], Pi[static_cast<int64_t>(s) * a.RS], v0);
-  const float v = (v0 + v1) + (v2 + v3);
   if (idx < a.du) {
     const int dd = a.dims[h * a.D + idx];
     if (dd >= 0 && dd < a.D) a.out[static_cast<int64_t>(row) * a.D + dd] = v * linv;
@@ -488,16 +489,27 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   }
 }
 
+// Pass 2 body: one block per (sequence, KV head, 32-column slice of the
+// compressible dims) computes O_C[g][c] = sum_n (alpha W)[g][n] cv[n][c] for
+// the head's query rows, kMergeRows rows at a time.  Thread (column quad cq,
+// n-lane nl) reads 4 consecutive columns of the cv rows n = nl + 32 j with
+// kCvBatch loads in flight; the 32 n-lanes are summed in a fixed order.
+constexpr int kCvCols = 32;
+constexpr int kCvLanes = 32;
+constexpr int kCvBatch = 8;
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   const int b = blockIdx.x / a.hkv, h = blockIdx.x % a.hkv;
   const int M = a.seq.mid[b];
   const bool has_mid = a.dc > 0 && M > 0;
-  float* Wm = smem;                            // [kMergeRows][kpad]
-  float* red = Wm + kMergeRows * a.kpad;       // [256][kMergeRows]
+  float* Wm = smem;                                   // [kMergeRows][kpad]
+  float* red = Wm + kMergeRows * a.kpad;              // [kCvLanes][kMergeRows][kCvCols]
   const int tid = threadIdx.x;
-  const int dcp = (a.dc + 63) / 64 * 64;
-  const int ngrp = max(1, 256 / dcp);
+  const int cq = tid % (kCvCols / 4), nl = tid / (kCvCols / 4);
+  const int c = blockIdx.y * kCvCols + 4 * cq;
+  const float* cvb = a.cv + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc;
   for (int g0 = 0; g0 < a.G; g0 += kMergeRows) {
     const int ng = min(kMergeRows, a.G - g0);
     __syncthreads();
@@ -508,48 +520,61 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
         Wm[g * a.kpad + n] = a.mrg[row * a.MS + a.dc + n];
       }
     __syncthreads();
-    for (int c0 = 0; c0 < dcp; c0 += 256) {
-      const int c = c0 + tid % dcp, grp = tid / dcp;
-      float acc[kMergeRows];
+    float acc[kMergeRows][4];
 #pragma unroll
-      for (int g = 0; g < kMergeRows; ++g) acc[g] = 0.0f;
-      if (c < a.dc && grp < ngrp && has_mid) {
-        const float* cvb = a.cv + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc + c;
-        int n = grp;
-        for (; n + 3 * ngrp < a.k; n += 4 * ngrp) {  // four independent loads in flight
-          const float x0 = cvb[static_cast<int64_t>(n) * a.dc];
-          const float x1 = cvb[static_cast<int64_t>(n + ngrp) * a.dc];
-          const float x2 = cvb[static_cast<int64_t>(n + 2 * ngrp) * a.dc];
-          const float x3 = cvb[static_cast<int64_t>(n + 3 * ngrp) * a.dc];
+    for (int g = 0; g < kMergeRows; ++g) acc[g][0] = acc[g][1] = acc[g][2] = acc[g][3] = 0.0f;
+    if (has_mid && c < a.dc) {
+      for (int n0 = nl; n0 < a.k; n0 += kCvLanes * kCvBatch) {
+        float4 x[kCvBatch];
+#pragma unroll
+        for (int j = 0; j < kCvBatch; ++j) {
+          const int n = n0 + kCvLanes * j;
+          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (n < a.k) {
+            const float* src = cvb + static_cast<int64_t>(n) * a.dc + c;
+            if (VEC) {
+              v = *reinterpret_cast<const float4*>(src);
+            } else {
+              v.x = src[0];
+              if (c + 1 < a.dc) v.y = src[1];
+              if (c + 2 < a.dc) v.z = src[2];
+              if (c + 3 < a.dc) v.w = src[3];
+            }
+          }
+          x[j] = v;
+        }
+#pragma unroll
+        for (int j = 0; j < kCvBatch; ++j) {
+          const int n = n0 + kCvLanes * j;
+          if (n >= a.k) break;
 #pragma unroll
           for (int g = 0; g < kMergeRows; ++g)
-            if (g < ng)
-              acc[g] = fmaf(Wm[g * a.kpad + n], x0,
-                            fmaf(Wm[g * a.kpad + n + ngrp], x1,
-                                 fmaf(Wm[g * a.kpad + n + 2 * ngrp], x2,
-                                      fmaf(Wm[g * a.kpad + n + 3 * ngrp], x3, acc[g]))));
-        }
-        for (; n < a.k; n += ngrp) {
-          const float x = cvb[static_cast<int64_t>(n) * a.dc];
-#pragma unroll
-          for (int g = 0; g < kMergeRows; ++g)
-            if (g < ng) acc[g] = fmaf(Wm[g * a.kpad + n], x, acc[g]);
+            if (g < ng) {
+              const float w = Wm[g * a.kpad + n];
+              acc[g][0] = fmaf(w, x[j].x, acc[g][0]);
+              acc[g][1] = fmaf(w, x[j].y, acc[g][1]);
+              acc[g][2] = fmaf(w, x[j].z, acc[g][2]);
+              acc[g][3] = fmaf(w, x[j].w, acc[g][3]);
+            }
         }
       }
+    }
 #pragma unroll
-      for (int g = 0; g < kMergeRows; ++g) red[tid * kMergeRows + g] = acc[g];
-      __syncthreads();
-      if (grp == 0 && c < a.dc) {
-        for (int g = 0; g < ng; ++g) {
-          float sum = 0.0f;
-          for (int q = 0; q < ngrp; ++q) sum += red[(q * dcp + (tid % dcp)) * kMergeRows + g];
-          const int64_t row = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
-          const float* mrow = a.mrg + row * a.MS;
-          const int dd = a.dims[h * a.D + a.du + c];
-          if (dd >= 0 && dd < a.D) a.out[row * a.D + dd] = (sum + mrow[c]) * mrow[a.dc + a.kpad];
-        }
+    for (int g = 0; g < kMergeRows; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(nl * kMergeRows + g) * kCvCols + 4 * cq + e] = acc[g][e];
+    __syncthreads();
+    if (tid < ng * kCvCols) {
+      const int g = tid / kCvCols, col = tid % kCvCols;
+      const int cc = blockIdx.y * kCvCols + col;
+      if (cc < a.dc) {
+        float sum = 0.0f;
+        for (int q = 0; q < kCvLanes; ++q) sum += red[(q * kMergeRows + g) * kCvCols + col];
+        const int64_t row = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
+        const float* mrow = a.mrg + row * a.MS;
+        const int dd = a.dims[h * a.D + a.du + cc];
+        if (dd >= 0 && dd < a.D) a.out[row * a.D + dd] = (sum + mrow[cc]) * mrow[a.dc + a.kpad];
       }
-      __syncthreads();
     }
   }
 }
@@ -572,7 +597,7 @@ size_t decode_split_smem(const DecodeArgs& a) {
                           kDecTile * kDecRows + kDecRows);
 }
 size_t decode_merge_cv_smem(const DecodeArgs& a) {
-  return sizeof(float) * (kMergeRows * a.kpad + 256 * kMergeRows);
+  return sizeof(float) * (kMergeRows * a.kpad + kCvLanes * kMergeRows * kCvCols);
 }
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
@@ -611,8 +636,15 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dc == 0) return hipSuccess;
   const size_t sm = decode_merge_cv_smem(a);
-  if ((e = allow_lds(decode_merge_cv_kernel, sm)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_cv_kernel, dim3(a.nseq * a.hkv), dim3(256), sm, s, a);
+  const dim3 grid(a.nseq * a.hkv, (a.dc + kCvCols - 1) / kCvCols);
+  const bool vec = a.dc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.cv) & 15) == 0;
+  if (vec) {
+    if ((e = allow_lds(decode_merge_cv_kernel<true>, sm)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_cv_kernel<true>, grid, dim3(256), sm, s, a);
+  } else {
+    if ((e = allow_lds(decode_merge_cv_kernel<false>, sm)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_cv_kernel<false>, grid, dim3(256), sm, s, a);
+  }
   return hipGetLastError();
 }
 
