@@ -24,6 +24,8 @@
 // (e^{i theta_j tau} times e^{i 2 pi tau / M}) and along tau by rotation with
 // e^{i 2 pi j / M}; both are re-anchored from exact integer phases through
 // sincospi, which keeps fp32 results within 1e-5 of the exact value.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace fa {
@@ -33,6 +35,14 @@ template <typename T> __device__ inline float ld(const void* p, int64_t i) {
   return load_f32<T>(static_cast<const T*>(p), i);
 }
 
+// Sum over each aligned group of 16 lanes (DPP rotations inside a row).
+__device__ inline float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
+  return v;
+}
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -73,57 +83,203 @@ __device__ inline int pair_pos_to_n(int pos, int k) {
 // --------------------------------------------------------------- prep ----
 // A[b][i][n] = scale * alpha_n * sum_c q[b][i][comp_c] ck[b,h][n][c], one
 // block per (sequence, KV head, 32 outputs); 8 threads split the c sum.
-constexpr int kPrepOut = 32;
-constexpr int kPrepParts = 8;
-constexpr int kPrepRows = 8;
+// On the MFMA path the first block of each (sequence, KV head) also writes the
+// head's query rows at the exact dims in dims order (bf16) and computes the
+// edge split: plain softmax attention of those rows over the retained sink and
+// recent tokens (all dims exact), stored as split nsplit-1 of each row.
+constexpr int kPrepPos = 128;   // coefficient positions per A-part block
+constexpr int kPrepPass = 4;    // 64-column passes over the compressible dims (dc <= 256)
+constexpr int kPrepRows = 8;    // query rows per pass over q_C
 
-template <typename T>
+// Edge split of the query rows of (sequence b, KV head h); 16-bit caches.
+// The retained rows (exact dims from kx / vx, compressible dims from ke / ve)
+// are first copied to LDS with every load of a thread in flight at once, then
+// scores, softmax and values run from LDS.
+// smem: q of the G rows in dims order, scaled [G][D] fp32 | probabilities
+// [G][ne] fp32 | K rows [ne][D] bf16 | V rows [ne][D] bf16.
+__device__ void edge_split_attention(const DecodeArgs& a, int b, int h, float* sm) {
+  const int L = a.seq.len[b], M = a.seq.mid[b];
+  const int S = a.sink, E = a.sink + a.recent;
+  const int ne = (M > 0) ? E : L;  // retained tokens (all of them without a middle)
+  const int D = a.D, du = a.du, dc = a.dc, G = a.G;
+  const int ns = a.seq.nsplit[b];
+  const int64_t row0 = a.seq.row0[b];
+  float* qs = sm;                                              // [G][D]
+  float* ps = qs + G * D;                                      // [G][ne]
+  uint16_t* ks = reinterpret_cast<uint16_t*>(ps + G * E);      // [ne][D]
+  uint16_t* vs = ks + E * D;                                   // [ne][D]
+  const int tid = threadIdx.x, nt = blockDim.x;
+  __syncthreads();
+  // exact dims: 8-dim chunks (du % 8 == 0 on this path), t = e or e + M
+  const int du8 = du / 8, dc2 = dc / 2;
+  const uint16_t* kxh = static_cast<const uint16_t*>(a.kx) + (row0 + static_cast<int64_t>(h) * L) * du;
+  const uint16_t* vxh = static_cast<const uint16_t*>(a.vx) + (row0 + static_cast<int64_t>(h) * L) * du;
+  const uint32_t* keh = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.ke) +
+                                                           (static_cast<int64_t>(b) * a.hkv + h) * E * dc);
+  const uint32_t* veh = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.ve) +
+                                                           (static_cast<int64_t>(b) * a.hkv + h) * E * dc);
+  for (int i0 = tid; i0 < ne * du8; i0 += 8 * nt) {
+    uint4 kv[8], vv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * nt;
+      kv[u] = vv[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < ne * du8) {
+        const int e = i / du8, c8 = i % du8;
+        const int t = (M > 0 && e >= S) ? e + M : e;
+        kv[u] = *reinterpret_cast<const uint4*>(kxh + static_cast<int64_t>(t) * du + 8 * c8);
+        vv[u] = *reinterpret_cast<const uint4*>(vxh + static_cast<int64_t>(t) * du + 8 * c8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * nt;
+      if (i < ne * du8) {
+        const int e = i / du8, c8 = i % du8;
+        uint32_t* kd = reinterpret_cast<uint32_t*>(ks + e * D + 8 * c8);
+        uint32_t* vd = reinterpret_cast<uint32_t*>(vs + e * D + 8 * c8);
+        kd[0] = kv[u].x; kd[1] = kv[u].y; kd[2] = kv[u].z; kd[3] = kv[u].w;
+        vd[0] = vv[u].x; vd[1] = vv[u].y; vd[2] = vv[u].z; vd[3] = vv[u].w;
+      }
+    }
+  }
+  // compressible dims: 2-dim words (dc % 2 == 0 on this path)
+  for (int i0 = tid; i0 < ne * dc2; i0 += 8 * nt) {
+    uint32_t kw[8], vw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * nt;
+      kw[u] = vw[u] = 0u;
+      if (i < ne * dc2) {
+        kw[u] = keh[i];
+        vw[u] = veh[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * nt;
+      if (i < ne * dc2) {
+        const int e = i / dc2, c2 = i % dc2;
+        *reinterpret_cast<uint32_t*>(ks + e * D + du + 2 * c2) = kw[u];
+        *reinterpret_cast<uint32_t*>(vs + e * D + du + 2 * c2) = vw[u];
+      }
+    }
+  }
+  for (int idx = tid; idx < G * D; idx += nt) {
+    const int g = idx / D, j = idx % D;
+    const int d = a.dims[h * D + j];
+    const int64_t i = static_cast<int64_t>(b) * a.hq + h * G + g;
+    qs[idx] = (d >= 0 && d < D) ? a.scale * bf16_to_f32(static_cast<const uint16_t*>(a.q)[i * D + d]) : 0.0f;
+  }
+  __syncthreads();
+  // scores: thread -> (token e, row g); D is even
+  for (int idx = tid; idx < ne * G; idx += nt) {
+    const int e = idx / G, g = idx % G;
+    const float* qg = qs + g * D;
+    const uint32_t* kr = reinterpret_cast<const uint32_t*>(ks + e * D);
+    float s0 = 0.0f, s1 = 0.0f;
+    for (int j2 = 0; j2 < D / 2; ++j2) {
+      const uint32_t w = kr[j2];
+      s0 = fmaf(qg[2 * j2], __uint_as_float(w << 16), s0);
+      s1 = fmaf(qg[2 * j2 + 1], __uint_as_float(w & 0xFFFF0000u), s1);
+    }
+    ps[g * ne + e] = s0 + s1;
+  }
+  __syncthreads();
+  // softmax of each row: one wave per row
+  const int lane = tid & 63, nwv = nt >> 6;
+  for (int g = tid >> 6; g < G; g += nwv) {
+    float m = -INFINITY;
+    for (int e = lane; e < ne; e += 64) m = fmaxf(m, ps[g * ne + e]);
+    m = wave_max(m);
+    float l = 0.0f;
+    for (int e = lane; e < ne; e += 64) {
+      const float p = (m == -INFINITY) ? 0.0f : __expf(ps[g * ne + e] - m);
+      ps[g * ne + e] = p;
+      l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G + g) * ns + ns - 1) * a.RS;
+      P[0] = m;
+      P[1] = l;
+    }
+  }
+  __syncthreads();
+  // values: thread -> (row g, dim j: exact dims then compressible dims)
+  for (int idx = tid; idx < G * D; idx += nt) {
+    const int g = idx / D, j = idx % D;
+    const float* pg = ps + g * ne;
+    float acc = 0.0f;
+    for (int e = 0; e < ne; ++e) acc = fmaf(pg[e], bf16_to_f32(vs[e * D + j]), acc);
+    // partial layout [m, l, o_U(du), o_E(dc), W]: dim j of the row sits at 2 + j
+    a.part[(static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G + g) * ns + ns - 1) * a.RS + 2 + j] = acc;
+  }
+}
+
+// A-part: block (b, h, chunk of kPrepPos coefficient positions); each wave
+// takes 32 positions, 4 at a time (16 lanes per ck row, 4 columns per lane and
+// 64-column pass), with every row load of the wave in flight at once; the 16
+// lanes of a row are summed with DPP rotations.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
-  float* qc = smem;                               // [kPrepRows][dc]
-  float* red = smem + kPrepRows * a.dc;           // [kPrepParts][kPrepRows][kPrepOut]
   const int bh = blockIdx.x;
   const int b = bh / a.hkv, h = bh % a.hkv;
   const int M = a.seq.mid[b];
   if (a.mfma && blockIdx.y == 0) {
-    // MFMA path: this KV head's query rows in dims order, so that the split
-    // kernel loads them contiguously (exact dims bf16, compressible dims fp32)
+    // MFMA path: this KV head's query rows at the exact dims in dims order
+    // (bf16, zero padded to 32), loaded contiguously by the split kernel
     const int du32 = (a.du + 31) & ~31;
-    const int w = du32 + a.dc;
-    for (int idx = threadIdx.x; idx < a.G * w; idx += blockDim.x) {
-      const int g = idx / w, j = idx % w;
+    for (int idx = threadIdx.x; idx < a.G * du32; idx += blockDim.x) {
+      const int g = idx / du32, j = idx % du32;
       const int64_t i = static_cast<int64_t>(b) * a.hq + h * a.G + g;
-      if (j < du32) {
-        uint16_t bits = 0;
-        if (j < a.du) {
-          const int d = a.dims[h * a.D + j];
-          if (d >= 0 && d < a.D) bits = static_cast<const uint16_t*>(a.q)[i * a.D + d];
-        }
-        static_cast<uint16_t*>(a.Q16)[i * du32 + j] = bits;
-      } else {
-        const int c = j - du32;
-        const int d = a.dims[h * a.D + a.du + c];
-        a.QC[i * a.dc + c] = (d >= 0 && d < a.D) ? a.scale * ld<T>(a.q, i * a.D + d) : 0.0f;
+      uint16_t bits = 0;
+      if (j < a.du) {
+        const int d = a.dims[h * a.D + j];
+        if (d >= 0 && d < a.D) bits = static_cast<const uint16_t*>(a.q)[i * a.D + d];
       }
+      static_cast<uint16_t*>(a.Q16)[i * du32 + j] = bits;
     }
+    if (a.edge_split) edge_split_attention(a, b, h, smem);
+    return;
   }
   if (!a.prep_a) return;
-  const int o = threadIdx.x % kPrepOut, part = threadIdx.x / kPrepOut;
-  const int pos = blockIdx.y * kPrepOut + o;
+  float* qc = smem;  // [kPrepRows][dc]
+  const int chunk = blockIdx.y - (a.mfma ? 1 : 0);
   const int len = a.mfma ? a.kpp : a.k;
-  const int n = (pos >= len) ? -1 : (a.mfma ? pair_pos_to_n(pos, a.k) : pos);
-  const int cper = (a.dc + kPrepParts - 1) / kPrepParts;
-  const int c0 = part * cper, c1 = min(a.dc, c0 + cper);
-  // coefficient loads first: they do not depend on q
-  float ckr[32];
-  const float* ckrow = a.ck + ((static_cast<int64_t>(b) * a.hkv + h) * a.k + max(n, 0)) * a.dc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
+  const int npass = (a.dc + 63) / 64;
+  const float* ckh = a.ck + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc;
+  // this lane's ck rows: positions pos0 + 4 s + g4 (s < 8) of its wave
+  const int pos0 = chunk * kPrepPos + wave * 32;
+  float4 ckv[8][kPrepPass];
 #pragma unroll
-  for (int c = 0; c < 32; ++c) ckr[c] = (n >= 0 && M > 0 && c0 + c < c1) ? ckrow[c0 + c] : 0.0f;
-  const float alpha = (n >= 0 && M > 0) ? basis_alpha(n, M) : 0.0f;
+  for (int st = 0; st < 8; ++st) {
+    const int pos = pos0 + 4 * st + g4;
+    const int n = (pos >= len) ? -1 : (a.mfma ? pair_pos_to_n(pos, a.k) : pos);
+#pragma unroll
+    for (int ps = 0; ps < kPrepPass; ++ps) {
+      const int c = 64 * ps + 4 * l16;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ps < npass && n >= 0 && M > 0 && c < a.dc) {
+        const float* src = ckh + static_cast<int64_t>(n) * a.dc + c;
+        if (VEC) {
+          v = *reinterpret_cast<const float4*>(src);
+        } else {
+          v.x = src[0];
+          if (c + 1 < a.dc) v.y = src[1];
+          if (c + 2 < a.dc) v.z = src[2];
+          if (c + 3 < a.dc) v.w = src[3];
+        }
+      }
+      ckv[st][ps] = v;
+    }
+  }
   for (int g0 = 0; g0 < a.G; g0 += kPrepRows) {
     const int ng = min(kPrepRows, a.G - g0);
     __syncthreads();
-    for (int idx = threadIdx.x; idx < ng * a.dc; idx += blockDim.x) {
+    for (int idx = tid; idx < ng * a.dc; idx += blockDim.x) {
       const int g = idx / a.dc, c = idx % a.dc;
       const int d = a.dims[h * a.D + a.du + c];
       const int i = h * a.G + g0 + g;
@@ -132,28 +288,34 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
                              : 0.0f;
     }
     __syncthreads();
-    float acc[kPrepRows];
 #pragma unroll
-    for (int g = 0; g < kPrepRows; ++g) acc[g] = 0.0f;
+    for (int st = 0; st < 8; ++st) {
+      const int pos = pos0 + 4 * st + g4;
+      const int n = (pos >= len) ? -1 : (a.mfma ? pair_pos_to_n(pos, a.k) : pos);
+      const float alpha = (n >= 0 && M > 0) ? basis_alpha(n, M) : 0.0f;
 #pragma unroll
-    for (int c = 0; c < 32; ++c)
-      if (c0 + c < c1)
+      for (int g = 0; g < kPrepRows; ++g) {
+        if (g >= ng) break;
+        float acc = 0.0f;
 #pragma unroll
-        for (int g = 0; g < kPrepRows; ++g)
-          if (g < ng) acc[g] = fmaf(qc[g * a.dc + c0 + c], ckr[c], acc[g]);
-#pragma unroll
-    for (int g = 0; g < kPrepRows; ++g) red[(part * kPrepRows + g) * kPrepOut + o] = acc[g];
-    __syncthreads();
-    if (part == 0 && pos < len) {
-      for (int g = 0; g < ng; ++g) {
-        float s = 0.0f;
-#pragma unroll
-        for (int p = 0; p < kPrepParts; ++p) s += red[(p * kPrepRows + g) * kPrepOut + o];
-        const int64_t i = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
-        if (a.mfma)
-          static_cast<_Float16*>(a.A16)[i * a.kpp + pos] = static_cast<_Float16>(alpha * s);
-        else
-          a.A[i * a.kpad + pos] = alpha * s;
+        for (int ps = 0; ps < kPrepPass; ++ps) {
+          const int c = 64 * ps + 4 * l16;
+          if (ps < npass && c < a.dc) {
+            const float* qg = qc + g * a.dc + c;
+            acc = fmaf(qg[0], ckv[st][ps].x, acc);
+            if (c + 1 < a.dc) acc = fmaf(qg[1], ckv[st][ps].y, acc);
+            if (c + 2 < a.dc) acc = fmaf(qg[2], ckv[st][ps].z, acc);
+            if (c + 3 < a.dc) acc = fmaf(qg[3], ckv[st][ps].w, acc);
+          }
+        }
+        acc = row16_sum(acc);
+        if (l16 == 0 && pos < len) {
+          const int64_t i = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
+          if (a.mfma)
+            static_cast<_Float16*>(a.A16)[i * a.kpp + pos] = static_cast<_Float16>(alpha * acc);
+          else
+            a.A[i * a.kpad + pos] = alpha * acc;
+        }
       }
     }
   }
@@ -468,15 +630,22 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   if (blockIdx.y == 0 && threadIdx.x == 0) mrow[a.dc + a.kpad] = linv;
   if (idx >= nvec) return;
   const float* Pi = P + 2 + idx;
+  // splits that hold this entry: with an edge split (the last one), o_E comes
+  // from it alone and W from the other splits alone
+  int s_lo = 0, s_hi = ns;
+  if (a.edge_split && idx >= a.du) {
+    if (idx < a.du + a.dc) s_lo = ns - 1;
+    else s_hi = ns - 1;
+  }
   // fixed-order sum over the splits, 8 loads in flight
   float v = 0.0f;
-  for (int s0 = 0; s0 < ns; s0 += 8) {
+  for (int s0 = s_lo; s0 < s_hi; s0 += 8) {
     float x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (s0 + j < ns) ? Pi[static_cast<int64_t>(s0 + j) * a.RS] : 0.0f;
+    for (int j = 0; j < 8; ++j) x[j] = (s0 + j < s_hi) ? Pi[static_cast<int64_t>(s0 + j) * a.RS] : 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (s0 + j < ns) v = fmaf(smem[s0 + j], x[j], v);
+      if (s0 + j < s_hi) v = fmaf(smem[s0 + j], x[j], v);
   }
   if (idx < a.du) {
     const int dd = a.dims[h * a.D + idx];
@@ -590,7 +759,13 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 }  // namespace
 
 size_t decode_prep_smem(const DecodeArgs& a) {
-  return sizeof(float) * (kPrepRows * a.dc + kPrepParts * kPrepRows * kPrepOut);
+  size_t n = sizeof(float) * kPrepRows * a.dc;
+  if (a.edge_split) n = std::max(n, decode_edge_smem(a));
+  return n;
+}
+size_t decode_edge_smem(const DecodeArgs& a) {
+  const size_t E = static_cast<size_t>(a.sink) + a.recent;  // upper bound of the retained tokens
+  return sizeof(float) * (static_cast<size_t>(a.G) * a.D + a.G * E) + 2 * sizeof(uint16_t) * E * a.D;
 }
 size_t decode_split_smem(const DecodeArgs& a) {
   return sizeof(float) * (kDecRows * a.D + kDecRows * a.kpad + 4 * kDecRows * kDecTile +
@@ -602,12 +777,23 @@ size_t decode_merge_cv_smem(const DecodeArgs& a) {
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
   if (!a.prep_a && !a.mfma) return hipSuccess;
-  const int len = a.prep_a ? (a.mfma ? a.kpp : a.k) : 1;
-  dim3 grid(a.nseq * a.hkv, (len + kPrepOut - 1) / kPrepOut);
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(decode_prep_kernel<uint16_t>, grid, dim3(256), decode_prep_smem(a), s, a);
-  else
-    hipLaunchKernelGGL(decode_prep_kernel<float>, grid, dim3(256), decode_prep_smem(a), s, a);
+  const int len = a.mfma ? a.kpp : a.k;
+  const int chunks = a.prep_a ? (len + kPrepPos - 1) / kPrepPos : 0;
+  dim3 grid(a.nseq * a.hkv, chunks + (a.mfma ? 1 : 0));
+  const size_t sm = decode_prep_smem(a);
+  const bool vec = a.dc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.ck) & 15) == 0;
+  hipError_t e;
+#define FA_PREP(T, V)                                                              \
+  do {                                                                             \
+    if ((e = allow_lds(decode_prep_kernel<T, V>, sm)) != hipSuccess) return e;    \
+    hipLaunchKernelGGL((decode_prep_kernel<T, V>), grid, dim3(256), sm, s, a);     \
+  } while (0)
+  if (a.dtype == 1) {
+    if (vec) FA_PREP(uint16_t, true); else FA_PREP(uint16_t, false);
+  } else {
+    if (vec) FA_PREP(float, true); else FA_PREP(float, false);
+  }
+#undef FA_PREP
   return hipGetLastError();
 }
 

@@ -3,8 +3,10 @@
 // Same arithmetic as the VALU kernel in decode.hip (scores and values in
 // coefficient space, online softmax, partials merged by decode_merge), laid out
 // for CDNA4 matrix cores.  A work item is (sequence, group of up to 32
-// consecutive query heads, token range); its query rows are stacked into the
-// 16-row M blocks of the MFMA.  Tiles hold 16 tokens.
+// consecutive query heads, range of middle tokens); its query rows are stacked
+// into the 16-row M blocks of the MFMA.  Tiles hold 16 tokens.  The retained
+// sink and recent tokens form one more split of every row, computed by
+// decode_prep, so this kernel sees middle tokens only.
 //
 // Per tile:
 //
@@ -18,15 +20,13 @@
 //     S_c = A phi^T (fp16 MFMA, A = scale alpha q_C ck in registers) go to LDS,
 //     and its basis slice is written to a wave-private LDS slice for [C].
 //     Exact-dim scores q_U kx^T run on bf16 MFMA with kx loaded from HBM
-//     straight into the operand layout (no LDS).  Edge tokens (sink, recent)
-//     add their compressible part on VALU.
+//     straight into the operand layout (no LDS).
 // [B] online softmax over the tile (one thread per row and token, DPP
-//     reductions); P goes to LDS as fp16 (for W), bf16 head + remainder (for
-//     the exact values) and fp32 (edge values).
+//     reductions); P goes to LDS as fp16 (for W) and as a bf16 head plus
+//     remainder (for the exact values).
 // [C] value moments W += P phi (fp16 MFMA, the wave's basis slice read back
-//     transposed with ds_read_b64_tr_b16), exact values o_U += P vx (bf16 MFMA,
-//     vx staged in a double-buffered LDS tile and read transposed), edge values
-//     on VALU.
+//     transposed with ds_read_b64_tr_b16) and exact values o_U += P vx (bf16
+//     MFMA, vx staged in a double-buffered LDS tile and read transposed).
 //
 // Two barriers per tile: after [A] and after [B].  The loop is rotated so that
 // [C] of one tile and [A] of the next share a segment: the W and o_U MFMAs of
@@ -98,9 +98,8 @@ __device__ inline int add_mod(int x, int d, int M) {
 
 // MB: 16-row blocks; NW: waves; MAXU: max 32-wide coefficient units per wave;
 // PF: 16-byte vx chunks staged per thread per tile; XP: max KV heads per wave
-// (exact scores); XU: max (KV head, 16-dim block) exact-value tiles per wave;
-// RPH: max query rows per KV head (edge-row VALU path).
-template <int MB, int NW, int MAXU, int PF, int XP, int XU, int RPH>
+// (exact scores); XU: max (KV head, 16-dim block) exact-value tiles per wave.
+template <int MB, int NW, int MAXU, int PF, int XP, int XU>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int T = kMfmaTile, TP = kMfmaTile + 4;
   constexpr int NT = 64 * NW, MR = 16 * MB;
@@ -114,19 +113,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int g4 = lane >> 4, l16 = lane & 15;
   const int b = seq_of_item(a.seq, a.nseq, blockIdx.x);
   const int local = blockIdx.x - a.seq.item0[b];
-  const int ns = a.seq.nsplit[b];
-  const int rg = local / ns, sp = local % ns;
+  const int ns = a.seq.nsplit[b];  // middle splits + the edge split
+  const int nsm = ns - 1;
+  const int rg = local / nsm, sp = local % nsm;
   const int L = a.seq.len[b], M = a.seq.mid[b];
-  const int S = a.sink, E = a.sink + a.recent;
-  const int t_begin = sp * a.seq.chunk[b];
-  const int t_end = min(L, t_begin + a.seq.chunk[b]);
+  const int S = a.sink;
+  const int t_begin = S + sp * a.seq.chunk[b];
+  const int t_end = min(S + M, t_begin + a.seq.chunk[b]);
   const int64_t row0 = a.seq.row0[b];
   const int rows = a.rows;
   const int qi0 = rg * rows;
   const int h0 = qi0 / a.G;
   const int nheads = rows >= a.G ? rows / a.G : 1;
   const int rph = min(rows, a.G);  // query rows per KV head inside the item
-  const bool has_mid = a.dc > 0 && M > 0;
+  const bool has_mid = a.dc > 0;  // items exist only for sequences with middle tokens
   const int du = a.du, dc = a.dc;
   const int du32 = (du + 31) & ~31;
   const int KC = du32 / 32;  // exact-dim chunks (<= KCM)
@@ -138,13 +138,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   uint16_t* vxs = reinterpret_cast<uint16_t*>(smem + lo.vxs);   // [2][nheads][T][DUS]
   float* spart = reinterpret_cast<float*>(smem + lo.spart);     // [NW][MR][TP]
   float* sx = reinterpret_cast<float*>(smem + lo.sx);           // [MR][TP]
-  float* sedge = reinterpret_cast<float*>(smem + lo.sedge);     // [MR][TP]
-  float* pf = reinterpret_cast<float*>(smem + lo.pf);           // [MR][TP]
   _Float16* ph = reinterpret_cast<_Float16*>(smem + lo.ph);     // [MR][TP]
   uint16_t* pbh = reinterpret_cast<uint16_t*>(smem + lo.pbh);   // [MR][TP]
   uint16_t* pbl = reinterpret_cast<uint16_t*>(smem + lo.pbl);   // [MR][TP]
   float* corr = reinterpret_cast<float*>(smem + lo.corr);       // [MR]
-  float* qcs = reinterpret_cast<float*>(smem + lo.qcs);         // [MR][dc]
 
   // ---- vx staging: thread -> 16-byte chunks c = tid + NT*i of a tile; the
   //      chunk -> (KV head, token, 8 dims) map is the same for every tile
@@ -210,9 +207,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     prefetch_v(t_begin);
   }
 
-  // ---- q operands (permuted by decode_prep): exact dims as bf16 MFMA A
-  //      operand per 32-dim chunk; compressible dims (scaled fp32) in LDS for
-  //      the edge rows
+  // ---- q at the exact dims (permuted by decode_prep): bf16 MFMA A operand
+  //      per 32-dim chunk
   bf16x8 Qreg[KCM][MB];
 #pragma unroll
   for (int kc = 0; kc < KCM; ++kc)
@@ -226,12 +222,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
                                                32 * kc + 8 * g4);
       Qreg[kc][mb] = __builtin_bit_cast(bf16x8, bits);
     }
-  {
-    const float* qsrc = a.QC + (static_cast<int64_t>(b) * a.hq + qi0) * dc;
-#pragma unroll 4
-    for (int idx = tid; idx < MR * dc; idx += NT) qcs[idx] = (idx < rows * dc) ? qsrc[idx] : 0.0f;
-  }
-
   // ---- this wave's coefficient units and its slice of A (MFMA A operand)
   const int U = a.kpp / 32;
   const int u0 = (U * wave) / NW, nu = (U * (wave + 1)) / NW - u0;
@@ -261,15 +251,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int x = 0; x < XU; ++x) Uacc[x] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- edge-row value accumulators (VALU): thread -> (head, comp-dim pair)
-  const int dc2 = dc / 2;
-  const int eh = dc2 ? tid / dc2 : 0, ec = dc2 ? tid % dc2 : 0;
-  const bool evld = dc2 > 0 && tid < nheads * dc2;
-  const int erb = (rows >= a.G) ? eh * a.G : 0;
-  float oE[RPH][2];
-#pragma unroll
-  for (int r = 0; r < RPH; ++r) oE[r][0] = oE[r][1] = 0.0f;
-
   // ---- softmax slot: thread -> (row, token); threads beyond MR * T idle
   const int s_row = tid / T, s_tt = tid % T;
   float m_run = -INFINITY, l_run = 0.0f;
@@ -292,17 +273,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     inc_f0 = phase_mod(f0, T, M);
   }
 
-  // ---- edge-score mapping: thread -> (head, token, part of the comp dims)
-  const int npairs = nheads * T;
-  const int tpp = edge_tpp(NT, npairs);
-
   // =================================================================== [A]
   auto phase_a = [&](int tile0) {
-    const int nt = min(T, t_end - tile0);
-    const bool tile_edge = dc > 0 && (M == 0 || tile0 < S || tile0 + nt > S + M);
     if (has_mid) {
-      const int t = tile0 + l16;
-      const bool mid = t < t_end && t >= S && t < S + M;
+      const bool mid = tile0 + l16 < t_end;
       // seeds of this lane's token: e^{i f0 x}, e^{i x}, e^{i 16 x}, x = 2 pi tau / M
       const float x0 = static_cast<float>(ph_f0) * invM;
       const float x1 = static_cast<float>(ph_tau) * invM;
@@ -399,44 +373,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         sx[row * TP + tt] = (tile0 + tt < t_end) ? 0.0f : -INFINITY;
       }
     }
-    if (tile_edge) {
-      // compressible part of the scores of the retained edge rows
-      for (int pr = tid / tpp; pr < npairs; pr += NT / tpp) {
-        const int hh = pr / T, tt = pr % T, part = tid % tpp;
-        const int t = tile0 + tt;
-        const int rb = (rows >= a.G) ? hh * a.G : 0;
-        float acc[RPH];
-#pragma unroll
-        for (int r = 0; r < RPH; ++r) acc[r] = 0.0f;
-        if (t < t_end && (M == 0 || t < S || t >= S + M)) {
-          const int e = (M == 0 || t < S) ? t : t - M;
-          const int cper_ = dc / tpp, cb0 = part * cper_;
-          const uint32_t* erow = reinterpret_cast<const uint32_t*>(
-              static_cast<const uint16_t*>(a.ke) + ((static_cast<int64_t>(b) * a.hkv + h0 + hh) * E + e) * dc + cb0);
-          for (int cb = 0; 2 * cb < cper_; cb += 8) {  // batches of 8 independent loads
-            uint32_t ew[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) ew[c] = (2 * (cb + c) < cper_) ? erow[cb + c] : 0u;
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-              if (2 * (cb + c) < cper_)
-#pragma unroll
-                for (int r = 0; r < RPH; ++r)
-                  if (r < rph) {
-                    const int cc = cb0 + 2 * (cb + c);
-                    acc[r] = fmaf(qcs[(rb + r) * dc + cc], lo_bf16(ew[c]),
-                                  fmaf(qcs[(rb + r) * dc + cc + 1], hi_bf16(ew[c]), acc[r]));
-                  }
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < RPH; ++r) acc[r] = wsum(acc[r], tpp);
-        if (part == 0)
-#pragma unroll
-          for (int r = 0; r < RPH; ++r)
-            if (r < rph) sedge[(rb + r) * TP + tt] = acc[r];
-      }
-    }
     // next tile's kx and vx: issued last, so that no wait above covers them
     if (du8 > 0 && tile0 + T < t_end) {
       prefetch_k(tile0 + T);
@@ -445,15 +381,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   };
 
   // =================================================================== [B]
-  auto phase_b = [&](int tile0) {
-    const int nt = min(T, t_end - tile0);
-    const bool tile_edge = dc > 0 && (M == 0 || tile0 < S || tile0 + nt > S + M);
+  auto phase_b = [&]() {
     if (s_row < MR) {
       float s = -INFINITY;
       if (s_row < rows) {
         s = sx[s_row * TP + s_tt];
         if (s != -INFINITY) {
-          if (tile_edge) s += sedge[s_row * TP + s_tt];
           if (has_mid) {
 #pragma unroll
             for (int w = 0; w < NW; ++w) s += spart[(w * MR + s_row) * TP + s_tt];
@@ -466,7 +399,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       l_run = l_run * c + row16_sum(p);
       m_run = m_new;
       const int o = s_row * TP + s_tt;
-      pf[o] = p;
       ph[o] = static_cast<_Float16>(p);
       const uint16_t hb = bf16_rne(p);
       pbh[o] = hb;
@@ -476,9 +408,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   };
 
   // =================================================================== [C]
-  auto phase_c = [&](int tile0, int buf) {
-    const int nt = min(T, t_end - tile0);
-    const bool tile_edge = dc > 0 && (M == 0 || tile0 < S || tile0 + nt > S + M);
+  auto phase_c = [&](int buf) {
     // rescale the running sums of the rows whose maximum moved (wave-uniform test)
     {
       float cr[MB][4];
@@ -545,47 +475,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph4, bv, Uacc[x], 0, 0, 0);
       Uacc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl4, bv, Uacc[x], 0, 0, 0);
     }
-    if (evld) {
-      const int h = h0 + eh;
-#pragma unroll
-      for (int r = 0; r < RPH; ++r)
-        if (r < rph) {
-          const float cr = corr[erb + r];
-          oE[r][0] *= cr;
-          oE[r][1] *= cr;
-        }
-      if (tile_edge) {
-        // edge tokens of this tile: [tile0, mid_lo) and [mid_hi, tile0 + nt)
-        const int mid_lo = (M == 0) ? tile0 + nt : max(tile0, min(tile0 + nt, S));
-        const int mid_hi = (M == 0) ? tile0 + nt : max(mid_lo, min(tile0 + nt, S + M));
-        const uint32_t* ecol = reinterpret_cast<const uint32_t*>(
-            static_cast<const uint16_t*>(a.ve) + (static_cast<int64_t>(b) * a.hkv + h) * E * dc + 2 * ec);
-        for (int seg = 0; seg < 2; ++seg) {
-          const int lo_t = seg == 0 ? tile0 : mid_hi, hi_t = seg == 0 ? mid_lo : tile0 + nt;
-          for (int t0 = lo_t; t0 < hi_t; t0 += 8) {  // batches of 8 independent loads
-            uint32_t w8[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const int t = t0 + q;
-              const int e = (M == 0 || t < S) ? t : t - M;
-              w8[q] = (t < hi_t) ? ecol[static_cast<int64_t>(e) * dc2] : 0u;
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              if (t0 + q >= hi_t) break;
-              const float v0 = lo_bf16(w8[q]), v1 = hi_bf16(w8[q]);
-#pragma unroll
-              for (int r = 0; r < RPH; ++r)
-                if (r < rph) {
-                  const float p = pf[(erb + r) * TP + (t0 + q - tile0)];
-                  oE[r][0] = fmaf(p, v0, oE[r][0]);
-                  oE[r][1] = fmaf(p, v1, oE[r][1]);
-                }
-            }
-          }
-        }
-      }
-    }
   };
 
   // ---- pipeline: [A](0) | { [B](i) | [C](i) [A](i+1) } ...
@@ -598,9 +487,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   __syncthreads();
   for (int i = 0; i < ntiles; ++i) {
     const int tile0 = t_begin + i * T;
-    phase_b(tile0);
+    phase_b();
     __syncthreads();
-    phase_c(tile0, i & 1);
+    phase_c(i & 1);
     if (i + 1 < ntiles) {
       if (du8 > 0) stage_v((i + 1) & 1);
       phase_a(tile0 + T);
@@ -631,14 +520,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         a.part[(prow + static_cast<int64_t>(row) * ns) * a.RS + 2 + d] = Uacc[x][r];
     }
   }
-  if (evld)
-#pragma unroll
-    for (int r = 0; r < RPH; ++r)
-      if (r < rph) {
-        float* P = a.part + (prow + static_cast<int64_t>(erb + r) * ns) * a.RS + 2 + du + 2 * ec;
-        P[0] = oE[r][0];
-        P[1] = oE[r][1];
-      }
   if (has_mid) {
 #pragma unroll
     for (int u = 0; u < MAXU; ++u) {
@@ -662,9 +543,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-template <int MB, int NW, int MAXU, int PF, int XP, int XU, int RPH>
+template <int MB, int NW, int MAXU, int PF, int XP, int XU>
 hipError_t launch_one(const DecodeArgs& a, int nitems, size_t smem, hipStream_t s) {
-  auto k = decode_mfma_kernel<MB, NW, MAXU, PF, XP, XU, RPH>;
+  auto k = decode_mfma_kernel<MB, NW, MAXU, PF, XP, XU>;
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -678,12 +559,12 @@ hipError_t launch_one(const DecodeArgs& a, int nitems, size_t smem, hipStream_t 
 // Compiled variants, chosen by row blocks and basis length (pair-order
 // positions kpp): each wave's slice of A and W stays in registers.
 constexpr MfmaVariant kVariants[] = {
-    // mb nw maxu pf xp xu rph kpp_min kpp_max
-    {1, 8, 2, 4, 2, 8, 8, 0, 512},
-    {2, 8, 2, 2, 1, 4, 8, 0, 512},
-    {2, 8, 5, 1, 1, 2, 4, 513, 1280},
-    {1, 8, 5, 2, 2, 4, 8, 513, 1280},
-    {1, 8, 9, 1, 1, 2, 4, 1281, 2304},
+    // mb nw maxu pf xp xu kpp_min kpp_max
+    {1, 8, 2, 4, 2, 8, 0, 512},
+    {2, 8, 2, 2, 1, 4, 0, 512},
+    {2, 8, 5, 1, 1, 2, 513, 1280},
+    {1, 8, 5, 2, 2, 4, 513, 1280},
+    {1, 8, 9, 1, 1, 2, 1281, 2304},
 };
 
 }  // namespace
@@ -705,13 +586,10 @@ __host__ __device__ MfmaLds mfma_lds(int mb, int nw, int kpp, int nheads, int du
   o.vxs = take(du32 ? 2 * nheads * T * o.dus * 2 : 0);
   o.spart = take(nw * MR * TP * 4);
   o.sx = take(MR * TP * 4);
-  o.sedge = take(MR * TP * 4);
-  o.pf = take(MR * TP * 4);
   o.ph = take(MR * TP * 2);
   o.pbh = take(MR * TP * 2);
   o.pbl = take(MR * TP * 2);
   o.corr = take(MR * 4);
-  o.qcs = take(MR * dc * 4);
   o.total = off;
   return o;
 }
@@ -733,11 +611,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s) {
   const int nheads = a.rows >= a.G ? a.rows / a.G : 1;
   const size_t smem = decode_mfma_smem(a, *v, nheads);
   switch (v - kVariants) {
-    case 0: return launch_one<1, 8, 2, 4, 2, 8, 8>(a, nitems, smem, s);
-    case 1: return launch_one<2, 8, 2, 2, 1, 4, 8>(a, nitems, smem, s);
-    case 2: return launch_one<2, 8, 5, 1, 1, 2, 4>(a, nitems, smem, s);
-    case 3: return launch_one<1, 8, 5, 2, 2, 4, 8>(a, nitems, smem, s);
-    case 4: return launch_one<1, 8, 9, 1, 1, 2, 4>(a, nitems, smem, s);
+    case 0: return launch_one<1, 8, 2, 4, 2, 8>(a, nitems, smem, s);
+    case 1: return launch_one<2, 8, 2, 2, 1, 4>(a, nitems, smem, s);
+    case 2: return launch_one<2, 8, 5, 1, 1, 2>(a, nitems, smem, s);
+    case 3: return launch_one<1, 8, 5, 2, 2, 4>(a, nitems, smem, s);
+    case 4: return launch_one<1, 8, 9, 1, 1, 2>(a, nitems, smem, s);
   }
   return hipErrorInvalidValue;
 }

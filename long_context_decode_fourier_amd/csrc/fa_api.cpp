@@ -202,7 +202,7 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
 struct DecPlan {
   fa::DecodeArgs args;
   int nitems;
-  size_t off_A, off_q16, off_qc, off_part, off_mrg, ws_bytes;
+  size_t off_A, off_q16, off_part, off_mrg, ws_bytes;
 };
 
 // Row grouping of the MFMA path: `rows` consecutive query heads per item,
@@ -217,15 +217,12 @@ bool mfma_rows_ok(const Shape& sh, int rows, int kpp) {
   if (!v) return false;
   const int T = fa::kMfmaTile;
   const int nheads = rows >= G ? rows / G : 1;
-  if (std::min(rows, G) > v->rph) return false;
   const int nt = 64 * v->nw;
   const int du32 = (sh.Du + 31) / 32 * 32;
   if (sh.Du % 8 || du32 > 64) return false;
   if (nheads > v->xp * v->nw) return false;                   // exact-score heads per wave
   if (nheads * (du32 / 16) > v->xu * v->nw) return false;     // exact-value tiles per wave
   if (nheads * T * (sh.Du / 8) > v->pf * nt) return false;    // staged vx chunks per thread
-  if (nheads * (sh.Dc / 2) > nt || sh.Dc % 2) return false;   // edge-value threads
-  if (sh.Dc % (2 * fa::edge_tpp(nt, nheads * T))) return false;
   return fa::mfma_lds(v->mb, v->nw, kpp, nheads, sh.Du, sh.Dc).total <= kMaxLds;
 }
 
@@ -248,7 +245,9 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   // MFMA path for 16-bit caches: as many stacked rows as the basis length
   // pays for (long bases amortise their generation over more rows).
   int rows = 0;
-  if (sh.dtype == FA_BF16 && sh.Du % 2 == 0 && sh.Dc % 2 == 0) {
+  fa::DecodeArgs probe = a;  // the edge split (decode_prep) must fit its LDS
+  probe.edge_split = 1;
+  if (sh.dtype == FA_BF16 && sh.Du % 2 == 0 && sh.Dc % 2 == 0 && fa::decode_edge_smem(probe) <= kMaxLds) {
     for (int r = 32; r >= 1; --r)
       if (mfma_rows_ok(sh, r, a.kpp)) {
         rows = r;
@@ -273,21 +272,30 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   a.rows = rows;
   a.ngroups = sh.Hq / rows;
   a.RS = 2 + a.du + a.dc + a.kpad;
+  // MFMA path: the split kernel covers the middle tokens [S, S+M) and
+  // decode_prep adds one split per row for the sink and recent tokens.
+  a.edge_split = a.mfma;
+  auto span = [&](int b) { return a.edge_split ? sh.M[b] : sh.L[b]; };
   // Token chunk per item: the smallest multiple of the tile for which the
   // items fit one round of `target` co-resident blocks (ragged batches round
   // each sequence up, so the even share alone can spill into a second round).
-  const int64_t work = sh.total_len * a.ngroups;
+  int64_t work = 0;
+  int max_span = 0;
+  for (int b = 0; b < sh.B; ++b) {
+    work += static_cast<int64_t>(span(b)) * a.ngroups;
+    max_span = std::max(max_span, span(b));
+  }
   const int64_t target = a.mfma ? kNumCU : 2 * kNumCU;
   int chunk = static_cast<int>(std::max<int64_t>(tile, (work + target - 1) / target / tile * tile));
   auto count_items = [&](int c) {
     int64_t n = 0;
-    for (int b = 0; b < sh.B; ++b) n += (sh.L[b] + c - 1) / c;
+    for (int b = 0; b < sh.B; ++b) n += (span(b) + c - 1) / c;
     return n * a.ngroups;
   };
-  if (count_items(chunk) > target) {
-    // smallest multiple of the tile in (chunk, max_len] that fits (item count
-    // falls as the chunk grows); keep the even share if none does
-    const int64_t top = (static_cast<int64_t>(sh.max_len) + tile - 1) / tile;
+  if (max_span > 0 && count_items(chunk) > target) {
+    // smallest multiple of the tile in (chunk, max_span] that fits (item
+    // count falls as the chunk grows); keep the even share if none does
+    const int64_t top = (static_cast<int64_t>(max_span) + tile - 1) / tile;
     if (count_items(static_cast<int>(top * tile)) <= target) {
       int64_t lo = chunk / tile, hi = top;  // count(lo) > target >= count(hi)
       while (hi - lo > 1) {
@@ -299,7 +307,8 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   }
   int item = 0, prow = 0;
   for (int b = 0; b < sh.B; ++b) {
-    const int ns = (sh.L[b] + chunk - 1) / chunk;
+    const int nsm = (span(b) + chunk - 1) / chunk;  // splits handled by the split kernel
+    const int ns = nsm + a.edge_split;
     a.seq.len[b] = sh.L[b];
     a.seq.mid[b] = sh.M[b];
     a.seq.row0[b] = sh.row0[b];
@@ -307,7 +316,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
     a.seq.nsplit[b] = ns;
     a.seq.chunk[b] = chunk;
     a.prow0[b] = prow;
-    item += ns * a.ngroups;
+    item += nsm * a.ngroups;
     prow += ns * sh.Hq;
   }
   p->nitems = item;
@@ -319,8 +328,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   const size_t rows_total = static_cast<size_t>(sh.B) * sh.Hq;
   const size_t du32 = static_cast<size_t>((sh.Du + 31) / 32 * 32);
   p->off_q16 = align_up(a_bytes);
-  p->off_qc = p->off_q16 + (a.mfma ? align_up(rows_total * du32 * 2) : 0);
-  p->off_part = p->off_qc + (a.mfma ? align_up(rows_total * sh.Dc * sizeof(float)) : 0);
+  p->off_part = p->off_q16 + (a.mfma ? align_up(rows_total * du32 * 2) : 0);
   p->off_mrg = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
   p->ws_bytes = p->off_mrg + align_up(static_cast<size_t>(sh.B) * sh.Hq * a.MS * sizeof(float));
   return FA_OK;
@@ -496,7 +504,6 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
   a.A = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_A);
   a.A16 = static_cast<char*>(workspace) + p.off_A;
   a.Q16 = static_cast<char*>(workspace) + p.off_q16;
-  a.QC = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_qc);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_part);
   a.mrg = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_mrg);
   hipStream_t s = static_cast<hipStream_t>(stream);

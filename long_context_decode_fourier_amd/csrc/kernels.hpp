@@ -62,23 +62,25 @@ struct DecodeArgs {
   float* A;      // VALU path: [B][Hq][kpad] fp32, basis order
   void* A16;     // MFMA path: [B][Hq][kpp] fp16, pair order
   void* Q16;     // MFMA path: [B][Hq][du32] bf16, q at the exact dims (dims order, zero pad)
-  float* QC;     // MFMA path: [B][Hq][dc] fp32, scale * q at the compressible dims
   int prep_a;    // decode_prep computes A (Dc > 0 and some sequence has middle tokens)
   float* part;   // partials [prow][RS]: m, l, o_U[du], o_E[dc], W[kpad]
   float* mrg;    // merged rows [B*Hq][MS]: o_E[dc], alpha*W[kpad], 1/l
   int nseq, hq, hkv, G, D, du, dc, k, kpad, kpp, sink, recent;
   int mfma;      // 1: decode_mfma kernel, 0: VALU kernel
+  int edge_split;  // 1: split nsplit-1 of every row holds the sink/recent tokens
+                   //    (decode_prep); the other splits cover middle tokens only
   int mb;        // MFMA path: 16-row blocks per item
   int rows;      // query rows per work item
   int ngroups;   // row groups per sequence (Hq / rows)
   int RS;        // floats per partial row: 2 + du + dc + kpad
   int MS;        // floats per merged row: dc + kpad + 1
   float scale;
-  SeqTable seq;  // item0/nsplit/chunk over (row group, split)
+  SeqTable seq;  // item0 / nsplit (splits per row, edge split included) / chunk
   int32_t prow0[kMaxBatch];  // first partial row of sequence b: sum Hq * nsplit
 };
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s);
+size_t decode_edge_smem(const DecodeArgs& a);  // LDS of the edge split (decode_prep)
 hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
@@ -91,21 +93,13 @@ struct MfmaVariant {
   int pf;       // 16-byte vx chunks staged per thread per tile
   int xp;       // max KV heads per wave (exact scores)
   int xu;       // max (KV head, 16-dim block) exact-value tiles per wave
-  int rph;      // max query rows per KV head
   int kpp_min, kpp_max;
 };
 struct MfmaLds {
   int ps, dus;  // row strides (halves) of the basis tile and the staged vx rows
-  int phi, vxs, spart, sx, sedge, pf, ph, pbh, pbl, corr, qcs, total;  // byte offsets
+  int phi, vxs, spart, sx, ph, pbh, pbl, corr, total;  // byte offsets
 };
 __host__ __device__ MfmaLds mfma_lds(int mb, int nw, int kpp, int nheads, int du, int dc);
-// Threads per (KV head, token) pair in the edge-score path: the largest power
-// of two <= threads / pairs (at least 1).
-__host__ __device__ inline int edge_tpp(int threads, int pairs) {
-  int t = 1;
-  while (2 * t * pairs <= threads) t *= 2;
-  return t;
-}
 const MfmaVariant* decode_mfma_pick(int kpp, int mb);
 size_t decode_mfma_smem(const DecodeArgs& a, const MfmaVariant& v, int nheads);
 
