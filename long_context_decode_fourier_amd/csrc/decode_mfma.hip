@@ -21,9 +21,12 @@
 //     and its basis slice is written to a wave-private LDS slice for [C].
 //     Exact-dim scores q_U kx^T run on bf16 MFMA with kx loaded from HBM
 //     straight into the operand layout (no LDS).
-// [B] online softmax over the tile (one thread per row and token, DPP
-//     reductions); P goes to LDS as fp16 (for W) and as a bf16 head plus
-//     remainder (for the exact values).
+// [B] online softmax over the tile (one thread per row and token).  A row's
+//     reference maximum moves only when a score exceeds it by more than
+//     kLazyMax, so probabilities stay below e^kLazyMax (exact in value: m and
+//     l share the reference) and the accumulators are rarely rescaled; the
+//     sum l is kept per lane and reduced once at the end.  P goes to LDS as
+//     fp16 (for W) and as a bf16 head plus remainder (for the exact values).
 // [C] value moments W += P phi (fp16 MFMA, the wave's basis slice read back
 //     transposed with ds_read_b64_tr_b16) and exact values o_U += P vx (bf16
 //     MFMA, vx staged in a double-buffered LDS tile and read transposed).
@@ -85,6 +88,10 @@ __device__ inline uint16_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
+// Softmax reference maximum: moved only when a score exceeds it by more than
+// this (probabilities stay below e^8 ~ 3e3, well inside fp16 and bf16 range).
+constexpr float kLazyMax = 8.0f;
+
 // Two floats to packed fp16 (round to nearest even), one instruction.
 __device__ inline uint32_t pack_f16(float lo, float hi) {
   uint32_t r;
@@ -273,10 +280,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     inc_f0 = phase_mod(f0, T, M);
   }
 
-  // =================================================================== [A]
-  auto phase_a = [&](int tile0) {
+  // ============================================ [C] value moments + [A] basis
+  // One pass over this wave's units does, per unit, the value-moment MFMAs of
+  // the previous tile (do_w: W += P phi, phi read back transposed) and then
+  // the basis, score MFMA and LDS store of tile tile0 (do_a).  The transposed
+  // reads of a unit precede its stores in program order, so one basis buffer
+  // serves both tiles, and the basis VALU work of one tile interleaves with
+  // the MFMA and LDS work of the other.
+  auto fused = [&](bool do_w, bool do_a, int tile0) {
     if (has_mid) {
-      const bool mid = tile0 + l16 < t_end;
+      half4 pv4[MB];
+      if (do_w) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) pv4[mb] = *reinterpret_cast<const half4*>(ph + (mb * 16 + l16) * TP + 4 * g4);
+      }
+      const bool mid = do_a && tile0 + l16 < t_end;
       // seeds of this lane's token: e^{i f0 x}, e^{i x}, e^{i 16 x}, x = 2 pi tau / M
       const float x0 = static_cast<float>(ph_f0) * invM;
       const float x1 = static_cast<float>(ph_tau) * invM;
@@ -305,6 +323,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < MAXU; ++u) {
         if (u < nu) {
+          if (do_w) {
+#pragma unroll
+            for (int n2 = 0; n2 < 2; ++n2) {
+              const int nbase = (u0 + u) * 32 + n2 * 16 + 4 * (l16 & 3);
+              const half4 bv = __builtin_bit_cast(half4, lds_read_tr4(phi + (4 * g4 + (l16 >> 2)) * PS + nbase));
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb)
+                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pv4[mb], bv, Wacc[u][n2][mb], 0, 0, 0);
+            }
+          }
+          if (!do_a) continue;
           if (u == 1) {  // unit u0+1: rotate by 16 frequencies
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -334,15 +363,18 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
           *reinterpret_cast<uint4*>(dst + 32 * u) = bits;
         }
       }
-      // this wave's partial scores: lane -> token l16, rows 4 g4 + r
+      if (do_a) {
+        // this wave's partial scores: lane -> token l16, rows 4 g4 + r
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) spart[(wave * MR + mb * 16 + 4 * g4 + r) * TP + l16] = sacc[mb][r];
-      ph_tau = add_mod(ph_tau, inc_tau, M);
-      ph_16 = add_mod(ph_16, inc_16, M);
-      ph_f0 = add_mod(ph_f0, inc_f0, M);
+          for (int r = 0; r < 4; ++r) spart[(wave * MR + mb * 16 + 4 * g4 + r) * TP + l16] = sacc[mb][r];
+        ph_tau = add_mod(ph_tau, inc_tau, M);
+        ph_16 = add_mod(ph_16, inc_16, M);
+        ph_f0 = add_mod(ph_f0, inc_f0, M);
+      }
     }
+    if (!do_a) return;
     // exact-dim scores of this wave's KV heads
     if (du8 > 0) {
 #pragma unroll
@@ -382,7 +414,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 
   // =================================================================== [B]
   auto phase_b = [&]() {
-    if (s_row < MR) {
+    if (s_row < MR) {  // whole waves (MR * T is a multiple of 64)
       float s = -INFINITY;
       if (s_row < rows) {
         s = sx[s_row * TP + s_tt];
@@ -393,11 +425,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
           }
         }
       }
-      const float m_new = fmaxf(m_run, row16_max(s));
-      const float c = (m_new == -INFINITY || m_run == m_new) ? 1.0f : __expf(m_run - m_new);
-      const float p = (s == -INFINITY) ? 0.0f : __expf(s - m_new);
-      l_run = l_run * c + row16_sum(p);
-      m_run = m_new;
+      float c = 1.0f;
+      if (__any(s > m_run + kLazyMax)) {  // some row of this wave moves its reference
+        const float m_tile = row16_max(s);
+        if (m_tile > m_run + kLazyMax) {
+          c = (m_run == -INFINITY) ? 0.0f : __expf(m_run - m_tile);
+          m_run = m_tile;
+          l_run *= c;
+        }
+      }
+      const float p = (s == -INFINITY) ? 0.0f : __expf(s - m_run);
+      l_run += p;  // this lane's share of the row sum
       const int o = s_row * TP + s_tt;
       ph[o] = static_cast<_Float16>(p);
       const uint16_t hb = bf16_rne(p);
@@ -408,58 +446,41 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   };
 
   // =================================================================== [C]
-  auto phase_c = [&](int buf) {
-    // rescale the running sums of the rows whose maximum moved (wave-uniform test)
-    {
-      float cr[MB][4];
-      bool any = false;
+  // rescale the running sums of the rows whose reference moved (wave-uniform test)
+  auto rescale = [&]() {
+    float cr[MB][4];
+    bool any = false;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          cr[mb][r] = corr[mb * 16 + 4 * g4 + r];
-          any = any || cr[mb][r] != 1.0f;
+      for (int r = 0; r < 4; ++r) {
+        cr[mb][r] = corr[mb * 16 + 4 * g4 + r];
+        any = any || cr[mb][r] != 1.0f;
+      }
+    if (__any(any)) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if (has_mid) {
+#pragma unroll
+          for (int u = 0; u < MAXU; ++u)
+#pragma unroll
+            for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) Wacc[u][n2][mb][r] *= cr[mb][r];
         }
-      if (__any(any)) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          if (has_mid) {
+        for (int x = 0; x < XU; ++x) {
+          const int q = wave + NW * x;
+          const int rb = (rows >= a.G) ? (q / max(ndb, 1)) * a.G : 0;
+          if ((rb >> 4) == mb)
 #pragma unroll
-            for (int u = 0; u < MAXU; ++u)
-#pragma unroll
-              for (int n2 = 0; n2 < 2; ++n2)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Wacc[u][n2][mb][r] *= cr[mb][r];
-          }
-#pragma unroll
-          for (int x = 0; x < XU; ++x) {
-            const int q = wave + NW * x;
-            const int rb = (rows >= a.G) ? (q / max(ndb, 1)) * a.G : 0;
-            if ((rb >> 4) == mb)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) Uacc[x][r] *= cr[mb][r];
-          }
+            for (int r = 0; r < 4; ++r) Uacc[x][r] *= cr[mb][r];
         }
       }
     }
-    if (has_mid) {
-      half4 pv4[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) pv4[mb] = *reinterpret_cast<const half4*>(ph + (mb * 16 + l16) * TP + 4 * g4);
-#pragma unroll
-      for (int u = 0; u < MAXU; ++u) {
-        if (u < nu) {
-#pragma unroll
-          for (int n2 = 0; n2 < 2; ++n2) {
-            const int nbase = (u0 + u) * 32 + n2 * 16 + 4 * (l16 & 3);
-            const half4 bv = __builtin_bit_cast(half4, lds_read_tr4(phi + (4 * g4 + (l16 >> 2)) * PS + nbase));
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pv4[mb], bv, Wacc[u][n2][mb], 0, 0, 0);
-          }
-        }
-      }
-    }
+  };
+  // exact values o_U += P vx of the tile staged in vxs[buf]
+  auto values_u = [&](int buf) {
     const uint16_t* vbuf = vxs + buf * nheads * T * DUS;
 #pragma unroll
     for (int x = 0; x < XU; ++x) {
@@ -477,32 +498,35 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- pipeline: [A](0) | { [B](i) | [C](i) [A](i+1) } ...
+  // ---- pipeline: [A](0) | { [B](i) | [C](i) fused with [A](i+1) } ...
   // Every prologue load completes here, so that no wait inside the loop (for
   // A, q or the first tile) also waits for the loop's own prefetches.
   __builtin_amdgcn_s_waitcnt(0);
   const int ntiles = (t_end - t_begin + T - 1) / T;
   if (du8 > 0) stage_v(0);
-  phase_a(t_begin);
+  fused(false, true, t_begin);
   __syncthreads();
   for (int i = 0; i < ntiles; ++i) {
     const int tile0 = t_begin + i * T;
+    const bool next = i + 1 < ntiles;
     phase_b();
     __syncthreads();
-    phase_c(i & 1);
-    if (i + 1 < ntiles) {
-      if (du8 > 0) stage_v((i + 1) & 1);
-      phase_a(tile0 + T);
-    }
+    rescale();
+    if (next && du8 > 0) stage_v((i + 1) & 1);
+    fused(true, next, tile0 + T);
+    values_u(i & 1);
     __syncthreads();
   }
 
   // ================= partials
   const int64_t prow = static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(qi0) * ns + sp;
-  if (s_row < rows && s_tt == 0) {
-    float* P = a.part + (prow + static_cast<int64_t>(s_row) * ns) * a.RS;
-    P[0] = m_run;
-    P[1] = l_run;
+  if (s_row < MR) {
+    const float l_row = row16_sum(l_run);
+    if (s_row < rows && s_tt == 0) {
+      float* P = a.part + (prow + static_cast<int64_t>(s_row) * ns) * a.RS;
+      P[0] = m_run;
+      P[1] = l_row;
+    }
   }
 #pragma unroll
   for (int x = 0; x < XU; ++x) {
@@ -580,7 +604,11 @@ __host__ __device__ MfmaLds mfma_lds(int mb, int nw, int kpp, int nheads, int du
     off += (bytes + 15) & ~15;
     return r;
   };
-  o.ps = kpp + 16;
+  // basis-tile row stride = 80 (mod 128) halves = 8 (mod 32) dwords: the
+  // 16-byte stores of 16 rows x 4 column chunks and the transposed 8-byte
+  // reads of 4 rows x 4 chunks spread evenly over the LDS banks (strides of
+  // 48, 80 and 112 mod 128 measure alike; 0 and 32 mod 128 conflict)
+  o.ps = kpp + ((80 - kpp % 128) + 128) % 128;
   o.dus = du32 + 16;
   o.phi = take(T * o.ps * 2);
   o.vxs = take(du32 ? 2 * nheads * T * o.dus * 2 : 0);
