@@ -52,6 +52,13 @@ template <> __device__ inline float load_f32<uint16_t>(const uint16_t* p, int64_
 __device__ inline float sin_rev(float x) { return __builtin_amdgcn_sinf(x); }
 __device__ inline float cos_rev(float x) { return __builtin_amdgcn_cosf(x); }
 
+// Two floats to packed fp16 (round to nearest even), one instruction.
+__device__ inline uint32_t pack_f16(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
+}
+
 // (f * tau) mod M, exact, for f, tau >= 0 (64-bit product).
 __device__ inline int phase_mod(int f, int tau, int M) {
   return static_cast<int>((static_cast<uint64_t>(f) * static_cast<uint64_t>(tau)) %

@@ -92,12 +92,6 @@ __device__ inline uint16_t bf16_rne(float x) {
 // this (probabilities stay below e^8 ~ 3e3, well inside fp16 and bf16 range).
 constexpr float kLazyMax = 8.0f;
 
-// Two floats to packed fp16 (round to nearest even), one instruction.
-__device__ inline uint32_t pack_f16(float lo, float hi) {
-  uint32_t r;
-  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-  return r;
-}
 __device__ inline int add_mod(int x, int d, int M) {
   x += d;
   return x >= M ? x - M : x;

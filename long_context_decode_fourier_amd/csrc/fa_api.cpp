@@ -189,6 +189,7 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
     item += tiles * s;
   }
   p->nitems = item;
+  a.nitems = item;
   // A sequence without middle still needs its zero coefficients written.
   bool any_empty = false;
   for (int b = 0; b < sh.B; ++b) any_empty = any_empty || sh.M[b] == 0;

@@ -22,6 +22,7 @@ struct ProjArgs {
   int tk, tn;        // tile: coefficient rows x columns (16-bit path)
   int nktiles, nctiles;
   int nseq;
+  int nitems;        // work items (16-bit path)
   float* partial;    // [items][tk][tn] (16-bit path, when not direct)
   int direct;        // every sequence has one split: the kernel writes ck / cv
   SeqTable seq;      // item0/nsplit: items = tiles * nsplit; chunk = positions per split

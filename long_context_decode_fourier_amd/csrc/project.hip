@@ -35,20 +35,34 @@ constexpr int kLdsStride = kProjTT + 8;  // halves per LDS column (padding sprea
 
 struct ProjItem {
   int b, ktile, ctile, t_begin, t_end, M;
+  int slot;  // partial-tile slot: item0[b] + (ktile * nctiles + ctile) * nsplit + split
 };
 
-__device__ inline ProjItem proj_item(const ProjArgs& a, int item) {
+// XCD-aware schedule.  Blocks are dispatched round-robin over the 8 XCDs
+// (block p runs on XCD p % 8), each with its own L2.  Items are numbered so
+// that the coefficient tiles reading the same cache slice (same column tile
+// and token range) are consecutive, and consecutive items go to the same XCD:
+// block p takes item (p % 8) * per + p / 8.  Returns false for the few padding
+// blocks of the last round.
+constexpr int kXcds = 8;
+__device__ inline bool proj_item(const ProjArgs& a, int nitems, int block, ProjItem* out) {
+  const int per = (nitems + kXcds - 1) / kXcds;
+  const int item = (block % kXcds) * per + block / kXcds;
+  if (item >= nitems) return false;
   ProjItem it;
   it.b = seq_of_item(a.seq, a.nseq, item);
   const int local = item - a.seq.item0[it.b];
   const int ns = a.seq.nsplit[it.b];
-  const int tile = local / ns, sp = local % ns;
-  it.ktile = tile / a.nctiles;
-  it.ctile = tile % a.nctiles;
+  it.ktile = local % a.nktiles;                 // fastest: coefficient tiles of one slice
+  const int group = local / a.nktiles;          // (column tile, split)
+  it.ctile = group / ns;
+  const int sp = group % ns;
   it.M = a.seq.mid[it.b];
   it.t_begin = sp * a.seq.chunk[it.b];
   it.t_end = min(it.M, it.t_begin + a.seq.chunk[it.b]);
-  return it;
+  it.slot = a.seq.item0[it.b] + (it.ktile * a.nctiles + it.ctile) * ns + sp;
+  *out = it;
+  return true;
 }
 
 // Wave grid WR x WC; each wave owns RB x CB blocks of 32 x 32 outputs.
@@ -59,8 +73,9 @@ __device__ inline ProjItem proj_item(const ProjArgs& a, int item) {
 // positions with a 144-byte column stride; the block index is XOR-swizzled
 // with (col >> 3) & 7, which keeps the stores (8 lanes, 8 column groups) and
 // the MFMA operand reads (8 lanes, 8 consecutive columns) on distinct 16-byte
-// bank slots.  The next step's loads are issued before the MFMA loop of the
-// current step.
+// bank slots.  The tile is double-buffered: the next step's loads are issued
+// before the MFMA loop of the current step and stored to the other buffer
+// after it, so one barrier per step suffices.
 __device__ inline int xt_off(int col, int tblock) {
   return col * kLdsStride + ((tblock ^ ((col >> 3) & 7)) << 3);
 }
@@ -74,9 +89,10 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
   constexpr int kPosGroups = kThreads / kColGroups;
   static_assert(kPosGroups * 8 == kProjTT, "8 positions per thread cover the step");
 
-  __shared__ __attribute__((aligned(16))) _Float16 xt[TN * kLdsStride];
+  __shared__ __attribute__((aligned(16))) _Float16 xts[2][TN * kLdsStride];
 
-  const ProjItem it = proj_item(a, blockIdx.x);
+  ProjItem it;
+  if (!proj_item(a, a.nitems, blockIdx.x, &it)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC;
   const int M = it.M;
@@ -123,43 +139,58 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
+  auto load_raw = [&](int step) {
+    const uint16_t* src = xbase + static_cast<int64_t>(step + tg * 8) * a.dc;
+    if (col_ok && step + kProjTT <= it.t_end) {  // full step: no per-position test
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int tau = it.t_begin + tg * 8 + i;
-    raw[i] = (col_ok && tau < it.t_end)
-                 ? *reinterpret_cast<const uint2*>(xbase + static_cast<int64_t>(tau) * a.dc)
-                 : make_uint2(0u, 0u);
-  }
-  for (int step = it.t_begin; step < it.t_end; step += kProjTT) {
-    __syncthreads();  // the previous step's MFMA reads of xt are done
-    {
-      half8 v0, v1, v2, v3;
+      for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(i) * a.dc);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v0[i] = static_cast<_Float16>(__uint_as_float(raw[i].x << 16));
-        v1[i] = static_cast<_Float16>(__uint_as_float(raw[i].x & 0xFFFF0000u));
-        v2[i] = static_cast<_Float16>(__uint_as_float(raw[i].y << 16));
-        v3[i] = static_cast<_Float16>(__uint_as_float(raw[i].y & 0xFFFF0000u));
-      }
-      *reinterpret_cast<half8*>(&xt[xt_off(cg * 4 + 0, tg)]) = v0;
-      *reinterpret_cast<half8*>(&xt[xt_off(cg * 4 + 1, tg)]) = v1;
-      *reinterpret_cast<half8*>(&xt[xt_off(cg * 4 + 2, tg)]) = v2;
-      *reinterpret_cast<half8*>(&xt[xt_off(cg * 4 + 3, tg)]) = v3;
-    }
-    __syncthreads();
-    if (step + kProjTT < it.t_end) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tau = step + kProjTT + tg * 8 + i;
-        raw[i] = (col_ok && tau < it.t_end)
-                     ? *reinterpret_cast<const uint2*>(xbase + static_cast<int64_t>(tau) * a.dc)
+      for (int i = 0; i < 8; ++i)
+        raw[i] = (col_ok && step + tg * 8 + i < it.t_end)
+                     ? *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(i) * a.dc)
                      : make_uint2(0u, 0u);
-      }
     }
+  };
+  auto store_raw = [&](_Float16* xt) {
+    // bf16 -> fp32 -> fp16 (exact for |x| in [2^-14, 65504]), one column of 8
+    // positions per 16-byte store
+    uint4 c[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float a0 = __uint_as_float(raw[i].x << 16), a1 = __uint_as_float(raw[i + 1].x << 16);
+      const float b0 = __uint_as_float(raw[i].x & 0xFFFF0000u), b1 = __uint_as_float(raw[i + 1].x & 0xFFFF0000u);
+      const float c0 = __uint_as_float(raw[i].y << 16), c1 = __uint_as_float(raw[i + 1].y << 16);
+      const float d0 = __uint_as_float(raw[i].y & 0xFFFF0000u), d1 = __uint_as_float(raw[i + 1].y & 0xFFFF0000u);
+      (&c[0].x)[i / 2] = pack_f16(a0, a1);
+      (&c[1].x)[i / 2] = pack_f16(b0, b1);
+      (&c[2].x)[i / 2] = pack_f16(c0, c1);
+      (&c[3].x)[i / 2] = pack_f16(d0, d1);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&xt[xt_off(cg * 4 + q, tg)]) = c[q];
+  };
 
+  load_raw(it.t_begin);
+  store_raw(xts[0]);
+  __syncthreads();
+  int buf = 0;
+  for (int step = it.t_begin; step < it.t_end; step += kProjTT) {
+    const bool more = step + kProjTT < it.t_end;
+    if (more) load_raw(step + kProjTT);
+    const _Float16* xt = xts[buf];
+    auto read_b = [&](int s, half8* bv) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        bv[cb] = *reinterpret_cast<const half8*>(
+            &xt[xt_off(wc * (CB * 32) + cb * 32 + (lane & 31), 4 * (lane >> 5) + s)]);
+    };
+    half8 bcur[CB], bnxt[CB];
+    read_b(0, bcur);
     float yp[RB], yc[RB];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (s < 3) read_b(s + 1, bnxt);  // operands of the next sub-step in flight
       half8 av[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -181,23 +212,28 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
         }
         yp[rb] = v[6];
         yc[rb] = v[7];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) av[rb][e] = static_cast<_Float16>(v[e]);
+        const uint4 bits = make_uint4(pack_f16(v[0], v[1]), pack_f16(v[2], v[3]),
+                                      pack_f16(v[4], v[5]), pack_f16(v[6], v[7]));
+        av[rb] = __builtin_bit_cast(half8, bits);
       }
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const half8 bv = *reinterpret_cast<const half8*>(
-            &xt[xt_off(wc * (CB * 32) + cb * 32 + (lane & 31), 4 * (lane >> 5) + s)]);
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rb], bv, acc[rb][cb], 0, 0, 0);
-      }
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rb], bcur[cb], acc[rb][cb], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) bcur[cb] = bnxt[cb];
+      // the next step's tile goes to the other buffer (last read in the
+      // previous step, before its barrier) between this step's MFMAs
+      if (s == 1 && more) store_raw(xts[buf ^ 1]);
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       ph[rb] += d64[rb];
       if (ph[rb] >= M) ph[rb] -= M;
     }
+    __syncthreads();
+    buf ^= 1;
   }
 
   if (a.direct) {
@@ -220,7 +256,7 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
         }
     return;
   }
-  float* P = a.partial + static_cast<int64_t>(blockIdx.x) * TK * TN;
+  float* P = a.partial + static_cast<int64_t>(it.slot) * TK * TN;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -387,10 +423,11 @@ bool project_tile_supported(int tk, int tn) {
 
 hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
   if (nitems == 0) return hipSuccess;
+  const int blocks = (nitems + kXcds - 1) / kXcds * kXcds;
   if (a.tk == 256 && a.tn == 256)
-    hipLaunchKernelGGL((project_f16_kernel<4, 2, 2, 4>), dim3(nitems), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((project_f16_kernel<4, 2, 2, 4>), dim3(blocks), dim3(512), 0, s, a);
   else if (a.tk == 128 && a.tn == 64)
-    hipLaunchKernelGGL((project_f16_kernel<2, 1, 2, 2>), dim3(nitems), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((project_f16_kernel<2, 1, 2, 2>), dim3(blocks), dim3(128), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
