@@ -52,11 +52,14 @@ template <> __device__ inline float load_f32<uint16_t>(const uint16_t* p, int64_
 __device__ inline float sin_rev(float x) { return __builtin_amdgcn_sinf(x); }
 __device__ inline float cos_rev(float x) { return __builtin_amdgcn_cosf(x); }
 
-// Two floats to packed fp16 (round to nearest even), one instruction.
+// Two floats to packed fp16 (round to nearest even).  A vector conversion
+// (v_cvt_pk_f16_f32 on gfx950) that the compiler schedules and hazard-checks
+// like any other instruction.
+typedef float pk_float2 __attribute__((ext_vector_type(2)));
+typedef _Float16 pk_half2 __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_f16(float lo, float hi) {
-  uint32_t r;
-  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-  return r;
+  const pk_half2 h = __builtin_convertvector((pk_float2){lo, hi}, pk_half2);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // (f * tau) mod M, exact, for f, tau >= 0 (64-bit product).

@@ -185,13 +185,11 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
         bv[cb] = *reinterpret_cast<const half8*>(
             &xt[xt_off(wc * (CB * 32) + cb * 32 + (lane & 31), 4 * (lane >> 5) + s)]);
     };
-    half8 bcur[CB], bnxt[CB];
-    read_b(0, bcur);
+    // basis operand of sub-step s (16 positions): lane -> coefficient row,
+    // 8 consecutive positions; runs of 16 positions are seeded from exact
+    // phases, the rest follows the three-term recurrence
     float yp[RB], yc[RB];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) read_b(s + 1, bnxt);  // operands of the next sub-step in flight
-      half8 av[RB];
+    auto gen_a = [&](int s, half8* av) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         float v[8];
@@ -216,16 +214,34 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
                                       pack_f16(v[4], v[5]), pack_f16(v[6], v[7]));
         av[rb] = __builtin_bit_cast(half8, bits);
       }
+    };
+    // software pipeline over the 4 sub-steps: the operands of sub-step s+1
+    // (LDS reads, basis VALU) are produced while sub-step s's MFMAs run
+    half8 bcur[CB], bnxt[CB], acur[RB], anxt[RB];
+    read_b(0, bcur);
+    gen_a(0, acur);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+        read_b(s + 1, bnxt);
+        gen_a(s + 1, anxt);
+      }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rb], bcur[cb], acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[rb], bcur[cb], acc[rb][cb], 0, 0, 0);
+      if (s < 3) {
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) bcur[cb] = bnxt[cb];
+        for (int cb = 0; cb < CB; ++cb) bcur[cb] = bnxt[cb];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acur[rb] = anxt[rb];
+      }
       // the next step's tile goes to the other buffer (last read in the
-      // previous step, before its barrier) between this step's MFMAs
-      if (s == 1 && more) store_raw(xts[buf ^ 1]);
+      // previous step, before its barrier) between this step's MFMAs; after
+      // the last step the store repeats data nobody reads, which keeps the
+      // sub-step loop one basic block
+      if (s == 1) store_raw(xts[buf ^ 1]);
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
