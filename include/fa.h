@@ -124,6 +124,9 @@ fa_status_t fa_decode_workspace_size(const fa_desc_t *desc, size_t *bytes);
  *   out[b][i] = sum_t p_t V~[t]      for t = 0 .. L_b-1.
  * The reconstruction is never formed: compressed scores are
  * (scale q_C ck^T) . phi(tau) and compressed values are (sum_tau p phi(tau)) cv.
+ * Required pointers: q, out, desc.dims; kx and vx when Du > 0; ke and ve when
+ * Dc > 0 and sink + recent > 0; ck and cv when Dc > 0 and some sequence has
+ * middle tokens (others may be NULL, FA_ERR_NULL otherwise).
  * bf16 caches need 16-byte aligned kx, vx, ke, ve.
  */
 fa_status_t fa_decode(const fa_desc_t *desc, const void *q, const void *kx,

@@ -22,6 +22,7 @@ constexpr int kMaxCoef = 4097;      // decode keeps per-thread coefficient slots
 constexpr int kMaxHeadDim = 256;
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kMinTiles = 7;            // preferred tiles per decode item (MFMA path)
 
 thread_local std::string g_err;
 
@@ -249,11 +250,22 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   fa::DecodeArgs probe = a;  // the edge split (decode_prep) must fit its LDS
   probe.edge_split = 1;
   if (sh.dtype == FA_BF16 && sh.Du % 2 == 0 && sh.Dc % 2 == 0 && fa::decode_edge_smem(probe) <= kMaxLds) {
-    for (int r = 32; r >= 1; --r)
-      if (mfma_rows_ok(sh, r, a.kpp)) {
+    // Largest row group whose items still get kMinTiles tiles each (per-item
+    // fixed costs and the split count of the merge favour long items); if
+    // none does, the largest valid group.
+    int64_t mid_tokens = 0;
+    for (int b = 0; b < sh.B; ++b) mid_tokens += sh.M[b];
+    int fallback = 0;
+    for (int r = 32; r >= 1; --r) {
+      if (!mfma_rows_ok(sh, r, a.kpp)) continue;
+      if (!fallback) fallback = r;
+      const int64_t per_item = mid_tokens * (sh.Hq / r) / kNumCU;
+      if (per_item >= static_cast<int64_t>(kMinTiles) * fa::kMfmaTile) {
         rows = r;
         break;
       }
+    }
+    if (!rows) rows = fallback;
   }
   int tile;
   if (rows > 0) {
@@ -456,7 +468,8 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
   if (!q || !out) return fail(FA_ERR_NULL, "q and out are required");
   if (!desc->dims) return fail(FA_ERR_NULL, "desc.dims is NULL");
   if (sh.Du > 0 && (!kx || !vx)) return fail(FA_ERR_NULL, "kx and vx are required when Du > 0");
-  if (sh.Dc > 0 && (!ke || !ve)) return fail(FA_ERR_NULL, "ke and ve are required when Dc > 0");
+  if (sh.Dc > 0 && sh.S + sh.R > 0 && (!ke || !ve))
+    return fail(FA_ERR_NULL, "ke and ve are required when Dc > 0 and sink + recent > 0");
   if (sh.Dc > 0 && sh.any_mid && (!ck || !cv))
     return fail(FA_ERR_NULL, "ck and cv are required when a sequence has middle tokens");
   if (!(scale == scale)) return fail(FA_ERR_SHAPE, "scale is NaN");

@@ -166,6 +166,17 @@ SMALL = {
                                 n_comp=64, n_coef=41), [700]),
     "bf16_many_tiles": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=8, head_dim=128,
                              n_comp=96, n_coef=513), [5000, 2345]),
+    # retention windows other than 32 + 64: none at all (the edge split is
+    # empty), sink only, recent only (with a sequence that is all window), and
+    # a window longer than one pass of the block's threads
+    "bf16_no_window": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                            n_comp=32, n_coef=65, sink=0, recent=0), [300, 129]),
+    "bf16_sink_only": (dict(dtype="bf16", batch=1, n_q_heads=4, n_kv_heads=4, head_dim=64,
+                            n_comp=32, n_coef=33, sink=16, recent=0), [250]),
+    "bf16_recent_only": (dict(dtype="bf16", batch=2, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                              n_comp=16, n_coef=17, sink=0, recent=24), [260, 24]),
+    "bf16_long_window": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                              n_comp=32, n_coef=101, sink=100, recent=200), [1000, 250]),
 }
 
 
