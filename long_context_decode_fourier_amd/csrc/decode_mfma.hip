@@ -40,6 +40,8 @@
 // unused (its basis value sin(0) is 0).  A is written in that order by
 // decode_prep, W is converted back to the basis order when the partials are
 // stored.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace fa {
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KCM = 2;             // max 32-dim chunks of the exact dims
   constexpr int kNoChunk = 1 << 29;  // staging slot without a chunk
   static_assert(MR * T <= NT, "one softmax slot per thread");
+  static_assert((NW & (NW - 1)) == 0, "power-of-two wave count (partial-score tree)");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -281,7 +284,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   // reads of a unit precede its stores in program order, so one basis buffer
   // serves both tiles, and the basis VALU work of one tile interleaves with
   // the MFMA and LDS work of the other.
-  auto fused = [&](bool do_w, bool do_a, int tile0) {
+  // do_w / do_a are compile-time flags (std::integral_constant), so that the
+  // unit loop holds no branch on them
+  auto fused = [&](auto do_w_c, auto do_a_c, int tile0) {
+    constexpr bool do_w = decltype(do_w_c)::value;
+    constexpr bool do_a = decltype(do_a_c)::value;
     if (has_mid) {
       half4 pv4[MB];
       if (do_w) {
@@ -314,17 +321,30 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) sacc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
       _Float16* dst = phi + l16 * PS + u0 * 32 + 8 * g4;
+      // W operands of the previous tile, read one unit ahead so that the LDS
+      // latency overlaps a unit's basis arithmetic (a unit's slot is
+      // overwritten only after its reads; the read past the last unit repeats
+      // the last unit, which keeps it unconditional)
+      const _Float16* wsrc = phi + (4 * g4 + (l16 >> 2)) * PS + u0 * 32 + 4 * (l16 & 3);
+      half4 bw[2][2];
+      if (do_w) {
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) bw[0][n2] = __builtin_bit_cast(half4, lds_read_tr4(wsrc + n2 * 16));
+      }
 #pragma unroll
       for (int u = 0; u < MAXU; ++u) {
         if (u < nu) {
           if (do_w) {
 #pragma unroll
-            for (int n2 = 0; n2 < 2; ++n2) {
-              const int nbase = (u0 + u) * 32 + n2 * 16 + 4 * (l16 & 3);
-              const half4 bv = __builtin_bit_cast(half4, lds_read_tr4(phi + (4 * g4 + (l16 >> 2)) * PS + nbase));
+            for (int n2 = 0; n2 < 2; ++n2)
 #pragma unroll
               for (int mb = 0; mb < MB; ++mb)
-                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pv4[mb], bv, Wacc[u][n2][mb], 0, 0, 0);
+                Wacc[u][n2][mb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pv4[mb], bw[u & 1][n2], Wacc[u][n2][mb], 0, 0, 0);
+            if (u + 1 < MAXU) {
+              const int un = min(u + 1, nu - 1);
+#pragma unroll
+              for (int n2 = 0; n2 < 2; ++n2)
+                bw[(u + 1) & 1][n2] = __builtin_bit_cast(half4, lds_read_tr4(wsrc + un * 32 + n2 * 16));
             }
           }
           if (!do_a) continue;
@@ -368,7 +388,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         ph_f0 = add_mod(ph_f0, inc_f0, M);
       }
     }
-    if (!do_a) return;
+  };
+
+  // exact-dim scores of tile tile0 (kx prefetched one segment earlier), then
+  // the loads of the next tile: issued first in their segment, so that the
+  // MFMA and load latencies overlap the long basis pass
+  auto exact_a = [&](int tile0) {
     // exact-dim scores of this wave's KV heads
     if (du8 > 0) {
 #pragma unroll
@@ -411,12 +436,19 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     if (s_row < MR) {  // whole waves (MR * T is a multiple of 64)
       float s = -INFINITY;
       if (s_row < rows) {
-        s = sx[s_row * TP + s_tt];
-        if (s != -INFINITY) {
-          if (has_mid) {
+        // all reads issued before the first use; the partials of a token past
+        // the end are 0, so its -inf exact score passes through the sum
+        const float e = sx[s_row * TP + s_tt];
+        s = e;
+        if (has_mid) {
+          float pw[NW];
 #pragma unroll
-            for (int w = 0; w < NW; ++w) s += spart[(w * MR + s_row) * TP + s_tt];
-          }
+          for (int w = 0; w < NW; ++w) pw[w] = spart[(w * MR + s_row) * TP + s_tt];
+#pragma unroll
+          for (int h = NW / 2; h >= 1; h /= 2)
+#pragma unroll
+            for (int w = 0; w < h; ++w) pw[w] += pw[w + h];
+          s += pw[0];
         }
       }
       float c = 1.0f;
@@ -498,17 +530,30 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   const int ntiles = (t_end - t_begin + T - 1) / T;
   if (du8 > 0) stage_v(0);
-  fused(false, true, t_begin);
+  using kOn = std::integral_constant<bool, true>;
+  using kOff = std::integral_constant<bool, false>;
+  exact_a(t_begin);
+  fused(kOff(), kOn(), t_begin);
   __syncthreads();
-  for (int i = 0; i < ntiles; ++i) {
+  // tiles 0 .. ntiles-2 also prepare the next tile; the last one only
+  // finishes its own
+  for (int i = 0; i + 1 < ntiles; ++i) {
     const int tile0 = t_begin + i * T;
-    const bool next = i + 1 < ntiles;
     phase_b();
     __syncthreads();
     rescale();
-    if (next && du8 > 0) stage_v((i + 1) & 1);
-    fused(true, next, tile0 + T);
+    if (du8 > 0) stage_v((i + 1) & 1);
     values_u(i & 1);
+    exact_a(tile0 + T);
+    fused(kOn(), kOn(), tile0 + T);
+    __syncthreads();
+  }
+  if (ntiles > 0) {
+    phase_b();
+    __syncthreads();
+    rescale();
+    values_u((ntiles - 1) & 1);
+    fused(kOn(), kOff(), 0);
     __syncthreads();
   }
 
