@@ -79,12 +79,6 @@ __device__ inline float row16_sum(float v) {
   v += dpp_ror<0x121>(v);
   return v;
 }
-__device__ inline float wsum(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 // round-to-nearest-even float -> bf16 bits (finite inputs)
 __device__ inline uint16_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);

@@ -164,8 +164,9 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
   a.nctiles = (a.ncols + a.tn - 1) / a.tn;
   const int tiles = a.nktiles * a.nctiles;
   // Co-resident blocks: one 8-wave block per CU for large tiles; small
-  // 2-wave blocks are latency-bound, so four per CU overlap their steps.
-  const int slots = big ? kNumCU : 4 * kNumCU;
+  // 2-wave blocks are latency-bound, so six per CU (three waves per SIMD, the
+  // kernel's register-limited occupancy) overlap their steps.
+  const int slots = big ? kNumCU : 6 * kNumCU;
   int64_t total_steps = 0;
   for (int b = 0; b < sh.B; ++b) total_steps += (sh.M[b] + fa::kProjTT - 1) / fa::kProjTT;
   bool any_split = false;
@@ -411,22 +412,10 @@ fa_status_t fa_project(const fa_desc_t* desc, const void* kc, const void* vc, fl
       return fail(FA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
     a.partial = static_cast<float*>(workspace);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
+  // retained rows of the matrices whose edge outputs were given
+  fa::EdgeArgs ea;
+  std::memset(&ea, 0, sizeof ea);
   if (sh.Dc > 0) {
-    if (p.f16) {
-      e = fa::launch_project_f16(a, p.nitems, s);
-      if (e != hipSuccess) return hip_fail(e, "project kernel");
-      e = fa::launch_project_reduce(a, s);
-      if (e != hipSuccess) return hip_fail(e, "project reduce kernel");
-    } else {
-      e = fa::launch_project_f32(a, s);
-      if (e != hipSuccess) return hip_fail(e, "project f32 kernel");
-    }
-  }
-  if ((ke || ve) && sh.Dc > 0) {
-    fa::EdgeArgs ea;
-    std::memset(&ea, 0, sizeof ea);
     int n = 0;
     if (ke) { ea.x[n] = kc; ea.e[n] = ke; ++n; }
     if (ve) { ea.x[n] = vc; ea.e[n] = ve; ++n; }
@@ -441,6 +430,25 @@ fa_status_t fa_project(const fa_desc_t* desc, const void* kc, const void* vc, fl
       ea.seq.len[b] = sh.L[b];
       ea.seq.row0[b] = sh.row0[b];
     }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  bool edges_done = false;
+  if (sh.Dc > 0) {
+    if (p.f16) {
+      e = fa::launch_project_f16(a, p.nitems, s);
+      if (e != hipSuccess) return hip_fail(e, "project kernel");
+      if (!a.direct) {
+        e = fa::launch_project_reduce(a, ea, s);
+        if (e != hipSuccess) return hip_fail(e, "project reduce kernel");
+        edges_done = true;
+      }
+    } else {
+      e = fa::launch_project_f32(a, s);
+      if (e != hipSuccess) return hip_fail(e, "project f32 kernel");
+    }
+  }
+  if (ea.nmat > 0 && !edges_done) {
     e = fa::launch_edge_gather(ea, s);
     if (e != hipSuccess) return hip_fail(e, "edge gather kernel");
   }

@@ -28,10 +28,9 @@ struct ProjArgs {
   SeqTable seq;      // item0/nsplit: items = tiles * nsplit; chunk = positions per split
 };
 
-// Supported tiles (tk x tn): 256 x 256 and 64 x 128.
+// Supported tiles (tk x tn): 256 x 256, 128 x 128 and 128 x 64.
 bool project_tile_supported(int tk, int tn);
 hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s);
-hipError_t launch_project_reduce(const ProjArgs& a, hipStream_t s);
 hipError_t launch_project_f32(const ProjArgs& a, hipStream_t s);
 
 // Gather of the sink/recent rows of kc (vc) into ke (ve).
@@ -42,6 +41,9 @@ struct EdgeArgs {
   SeqTable seq;
 };
 hipError_t launch_edge_gather(const EdgeArgs& a, hipStream_t s);
+// Split-partial reduction of the 16-bit path; with ea.nmat > 0 it also copies
+// the retained rows (then no separate gather is launched).
+hipError_t launch_project_reduce(const ProjArgs& a, const EdgeArgs& ea, hipStream_t s);
 
 // ---------------------------------------------------------------- decode --
 constexpr int kDecRows = 4;    // query rows per work item (VALU path)

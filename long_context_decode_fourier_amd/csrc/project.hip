@@ -13,10 +13,11 @@
 // values in [-1, 1] keep 11 significant bits (bf16 would keep 8, which costs
 // an order of magnitude in coefficient accuracy).  Accumulation is fp32.
 //
-// Basis values along a lane's run of 16 consecutive positions come from the
+// Basis values along a lane's run of 32 consecutive positions come from the
 // three-term recurrence y(t+1) = 2 cos(theta) y(t) - y(t-1), seeded with two
 // exact values from the integer phase (f*tau mod M) and the hardware sin unit;
-// the run length bounds the recurrence's error growth (about 1e-5).
+// the run length bounds the recurrence's error growth (about 3e-5 absolute,
+// a tenth of the fp16 rounding of the operand).
 //
 // fp32 inputs take a VALU kernel with correctly rounded phases (sincospi per
 // value) and compensated summation, which keeps coefficients within 1e-5.
@@ -81,13 +82,14 @@ __device__ inline int xt_off(int col, int tblock) {
 }
 
 template <int WR, int WC, int RB, int CB>
-__global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
+__global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a) {
   constexpr int kThreads = 64 * WR * WC;
   constexpr int TK = WR * RB * 32;
   constexpr int TN = WC * CB * 32;
   constexpr int kColGroups = TN / 4;
   constexpr int kPosGroups = kThreads / kColGroups;
-  static_assert(kPosGroups * 8 == kProjTT, "8 positions per thread cover the step");
+  constexpr int NPG = kProjTT / (8 * kPosGroups);  // 8-position groups per thread
+  static_assert(NPG >= 1 && NPG * kPosGroups * 8 == kProjTT, "the loader threads cover the step");
 
   __shared__ __attribute__((aligned(16))) _Float16 xts[2][TN * kLdsStride];
 
@@ -99,7 +101,8 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
   const int L = a.seq.len[it.b];
   const int64_t row0 = a.seq.row0[it.b];
 
-  // ---- loader: 4 consecutive columns x 8 positions per thread
+  // ---- loader: 4 consecutive columns x NPG groups of 8 positions per thread
+  //      (groups tg, tg + kPosGroups, ...)
   const int cg = tid % kColGroups, tg = tid / kColGroups;
   const int col0 = it.ctile * TN + cg * 4;
   const bool col_ok = col0 < a.ncols;  // Dc % 4 == 0: the 4 columns share (mat, h)
@@ -110,12 +113,12 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
     xbase = static_cast<const uint16_t*>(mat ? a.x[1] : a.x[0]) +
             (row0 + static_cast<int64_t>(h) * L + a.sink) * a.dc + c0;
   }
-  uint2 raw[8];
+  uint2 raw[NPG][8];
 
   // ---- basis generator state, one coefficient row per lane and row block
   const float invM = 1.0f / static_cast<float>(M);
   float c2[RB], off[RB];
-  int fr[RB], ph[RB], d16[RB], d64[RB];
+  int fr[RB], ph[RB], d64[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int n = it.ktile * TK + wr * (RB * 32) + rb * 32 + (lane & 31);
@@ -127,7 +130,6 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
     off[rb] = basis_is_cos(ne) ? 0.25f : 0.0f;  // cos(2 pi x) = sin(2 pi (x + 1/4))
     fr[rb] = f;
     ph[rb] = phase_mod(f, it.t_begin + 32 * (lane >> 5), M);
-    d16[rb] = phase_mod(f, 16, M);
     d64[rb] = phase_mod(f, kProjTT, M);
   }
 
@@ -140,35 +142,44 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
   auto load_raw = [&](int step) {
-    const uint16_t* src = xbase + static_cast<int64_t>(step + tg * 8) * a.dc;
-    if (col_ok && step + kProjTT <= it.t_end) {  // full step: no per-position test
 #pragma unroll
-      for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(i) * a.dc);
-    } else {
+    for (int j = 0; j < NPG; ++j) {
+      const int p0 = step + (tg + kPosGroups * j) * 8;
+      const uint16_t* src = xbase + static_cast<int64_t>(p0) * a.dc;
+      if (col_ok && step + kProjTT <= it.t_end) {  // full step: no per-position test
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        raw[i] = (col_ok && step + tg * 8 + i < it.t_end)
-                     ? *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(i) * a.dc)
-                     : make_uint2(0u, 0u);
+        for (int i = 0; i < 8; ++i) raw[j][i] = *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(i) * a.dc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          raw[j][i] = (col_ok && p0 + i < it.t_end)
+                          ? *reinterpret_cast<const uint2*>(src + static_cast<int64_t>(i) * a.dc)
+                          : make_uint2(0u, 0u);
+      }
     }
   };
   auto store_raw = [&](_Float16* xt) {
     // bf16 -> fp32 -> fp16 (exact for |x| in [2^-14, 65504]), one column of 8
     // positions per 16-byte store
-    uint4 c[4];
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const float a0 = __uint_as_float(raw[i].x << 16), a1 = __uint_as_float(raw[i + 1].x << 16);
-      const float b0 = __uint_as_float(raw[i].x & 0xFFFF0000u), b1 = __uint_as_float(raw[i + 1].x & 0xFFFF0000u);
-      const float c0 = __uint_as_float(raw[i].y << 16), c1 = __uint_as_float(raw[i + 1].y << 16);
-      const float d0 = __uint_as_float(raw[i].y & 0xFFFF0000u), d1 = __uint_as_float(raw[i + 1].y & 0xFFFF0000u);
-      (&c[0].x)[i / 2] = pack_f16(a0, a1);
-      (&c[1].x)[i / 2] = pack_f16(b0, b1);
-      (&c[2].x)[i / 2] = pack_f16(c0, c1);
-      (&c[3].x)[i / 2] = pack_f16(d0, d1);
+    for (int j = 0; j < NPG; ++j) {
+      uint4 c[4];
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const uint2 r0 = raw[j][i], r1 = raw[j][i + 1];
+        const float a0 = __uint_as_float(r0.x << 16), a1 = __uint_as_float(r1.x << 16);
+        const float b0 = __uint_as_float(r0.x & 0xFFFF0000u), b1 = __uint_as_float(r1.x & 0xFFFF0000u);
+        const float c0 = __uint_as_float(r0.y << 16), c1 = __uint_as_float(r1.y << 16);
+        const float d0 = __uint_as_float(r0.y & 0xFFFF0000u), d1 = __uint_as_float(r1.y & 0xFFFF0000u);
+        (&c[0].x)[i / 2] = pack_f16(a0, a1);
+        (&c[1].x)[i / 2] = pack_f16(b0, b1);
+        (&c[2].x)[i / 2] = pack_f16(c0, c1);
+        (&c[3].x)[i / 2] = pack_f16(d0, d1);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint4*>(&xt[xt_off(cg * 4 + q, tg + kPosGroups * j)]) = c[q];
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&xt[xt_off(cg * 4 + q, tg)]) = c[q];
   };
 
   load_raw(it.t_begin);
@@ -186,16 +197,16 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
             &xt[xt_off(wc * (CB * 32) + cb * 32 + (lane & 31), 4 * (lane >> 5) + s)]);
     };
     // basis operand of sub-step s (16 positions): lane -> coefficient row,
-    // 8 consecutive positions; runs of 16 positions are seeded from exact
-    // phases, the rest follows the three-term recurrence
+    // 8 consecutive positions (lane half h covers positions 32 h + 8 s ..
+    // +7 of the step, so its 4 sub-steps are one run of 32 positions, seeded
+    // from exact phases at sub-step 0 and continued by the recurrence)
     float yp[RB], yc[RB];
     auto gen_a = [&](int s, half8* av) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         float v[8];
-        if ((s & 1) == 0) {
-          int r0 = ph[rb];
-          if (s == 2) { r0 += d16[rb]; if (r0 >= M) r0 -= M; }
+        if (s == 0) {
+          const int r0 = ph[rb];
           int r1 = r0 + fr[rb];
           if (r1 >= M) r1 -= M;
           v[0] = sin_rev(fmaf(static_cast<float>(r0), invM, off[rb]));
@@ -238,10 +249,21 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
         for (int rb = 0; rb < RB; ++rb) acur[rb] = anxt[rb];
       }
       // the next step's tile goes to the other buffer (last read in the
-      // previous step, before its barrier) between this step's MFMAs; after
-      // the last step the store repeats data nobody reads, which keeps the
-      // sub-step loop one basic block
-      if (s == 1) store_raw(xts[buf ^ 1]);
+      // previous step, before its barrier) after this step's last MFMAs, so
+      // that its loads have the whole step to arrive; after the last step the
+      // store repeats data nobody reads, which keeps the sub-step loop one
+      // basic block
+      if (s == 3) {
+        // the raw rows pass through an empty asm statement here, which keeps
+        // their conversion (and the wait for their loads) at the end of the
+        // step; hoisted into the early sub-steps, it would wait for loads
+        // issued moments before
+#pragma unroll
+        for (int j = 0; j < NPG; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(raw[j][i].x), "+v"(raw[j][i].y));
+        store_raw(xts[buf ^ 1]);
+      }
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -285,11 +307,51 @@ __global__ __launch_bounds__(64 * WR * WC) void project_f16_kernel(ProjArgs a) {
       }
 }
 
+// Retained rows (sink, then recent; all rows when L <= sink + recent) of
+// kc (vc), copied to ke (ve) in 16-, 8- or 4-byte words: grid-stride over
+// (sequence, matrix, KV head, retained row, word).
+__device__ inline void edge_copy(const EdgeArgs& a, int64_t first, int64_t stride) {
+  const int E = a.sink + a.recent;
+  const int nbytes = a.dc * a.elem_bytes;
+  const int wsz = (nbytes % 16 == 0) ? 16 : ((nbytes % 8 == 0) ? 8 : 4);
+  const int nw = nbytes / wsz;
+  const int64_t per_seq = static_cast<int64_t>(a.nmat) * a.hkv * E * nw;
+  const int64_t total = per_seq * a.nseq;
+  for (int64_t g = first; g < total; g += stride) {
+    const int b = static_cast<int>(g / per_seq);
+    int64_t r = g - b * per_seq;
+    const int w = static_cast<int>(r % nw);
+    r /= nw;
+    const int e = static_cast<int>(r % E);
+    r /= E;
+    const int h = static_cast<int>(r % a.hkv);
+    const int mat = static_cast<int>(r / a.hkv);
+    const int L = a.seq.len[b];
+    int t;
+    if (L <= E) {
+      if (e >= L) continue;
+      t = e;
+    } else {
+      t = (e < a.sink) ? e : L - E + e;
+    }
+    const char* src = static_cast<const char*>(a.x[mat]) +
+                      (a.seq.row0[b] + static_cast<int64_t>(h) * L + t) * nbytes + w * wsz;
+    char* dst = static_cast<char*>(a.e[mat]) +
+                ((static_cast<int64_t>(b) * a.hkv + h) * E + e) * nbytes + w * wsz;
+    if (wsz == 16)
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    else if (wsz == 8)
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    else
+      *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+  }
+}
+
 // Fixed-order sum of the split partials of each tile element, scaled by the
 // basis normalisation, scattered to ck / cv.  One thread per 4 consecutive
 // tile columns: grid-stride over (sequence, tile, row, column quad).
 // Sequences without middle get zeros.
-__global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a) {
+__global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a, EdgeArgs ea) {
   const int tk = a.tk, tn = a.tn, tn4 = tn / 4;
   const int tiles = a.nktiles * a.nctiles;
   const int64_t per_seq = static_cast<int64_t>(tiles) * tk * tn4;
@@ -331,6 +393,10 @@ __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a) {
     o[2] = alpha * sum.z;
     o[3] = alpha * sum.w;
   }
+  // the retained rows ride along (no launch of their own)
+  if (ea.nmat > 0)
+    edge_copy(ea, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+              static_cast<int64_t>(gridDim.x) * blockDim.x);
 }
 
 // fp32 inputs: one block per (sequence, matrix, KV head, 8 coefficients).
@@ -398,35 +464,15 @@ __global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
   }
 }
 
-// Retained rows (sink, then recent; all rows when L <= sink + recent).
 __global__ __launch_bounds__(256) void edge_gather_kernel(EdgeArgs a) {
-  const int E = a.sink + a.recent;
-  int g = blockIdx.x;  // (b, mat, h, edge row)
-  const int e = g % E;
-  g /= E;
-  const int h = g % a.hkv;
-  g /= a.hkv;
-  const int mat = g % a.nmat, b = g / a.nmat;
-  const int L = a.seq.len[b];
-  int t;
-  if (L <= E) {
-    if (e >= L) return;
-    t = e;
-  } else {
-    t = (e < a.sink) ? e : L - E + e;
-  }
-  const int64_t src_row = a.seq.row0[b] + static_cast<int64_t>(h) * L + t;
-  const int64_t dst_row = (static_cast<int64_t>(b) * a.hkv + h) * E + e;
+  edge_copy(a, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+            static_cast<int64_t>(gridDim.x) * blockDim.x);
+}
+
+int64_t edge_words(const EdgeArgs& a) {
   const int nbytes = a.dc * a.elem_bytes;
-  const char* src = static_cast<const char*>(a.x[mat]) + src_row * nbytes;
-  char* dst = static_cast<char*>(a.e[mat]) + dst_row * nbytes;
-  if ((nbytes & 3) == 0) {
-    for (int i = threadIdx.x; i < nbytes / 4; i += blockDim.x)
-      reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
-  } else {
-    for (int i = threadIdx.x; i < nbytes / 2; i += blockDim.x)
-      reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(src)[i];
-  }
+  const int wsz = (nbytes % 16 == 0) ? 16 : ((nbytes % 8 == 0) ? 8 : 4);
+  return static_cast<int64_t>(a.nseq) * a.nmat * a.hkv * (a.sink + a.recent) * (nbytes / wsz);
 }
 
 }  // namespace
@@ -434,7 +480,7 @@ __global__ __launch_bounds__(256) void edge_gather_kernel(EdgeArgs a) {
 // Tile configurations of the 16-bit kernel: 256 x 256 (8 waves) for large
 // problems, 128 x 64 (2 waves) when large tiles would leave CUs idle.
 bool project_tile_supported(int tk, int tn) {
-  return (tk == 256 && tn == 256) || (tk == 128 && tn == 64);
+  return (tk == 256 && tn == 256) || (tk == 128 && tn == 128) || (tk == 128 && tn == 64);
 }
 
 hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
@@ -442,6 +488,8 @@ hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
   const int blocks = (nitems + kXcds - 1) / kXcds * kXcds;
   if (a.tk == 256 && a.tn == 256)
     hipLaunchKernelGGL((project_f16_kernel<4, 2, 2, 4>), dim3(blocks), dim3(512), 0, s, a);
+  else if (a.tk == 128 && a.tn == 128)
+    hipLaunchKernelGGL((project_f16_kernel<2, 1, 2, 4>), dim3(blocks), dim3(128), 0, s, a);
   else if (a.tk == 128 && a.tn == 64)
     hipLaunchKernelGGL((project_f16_kernel<2, 1, 2, 2>), dim3(blocks), dim3(128), 0, s, a);
   else
@@ -449,12 +497,13 @@ hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_project_reduce(const ProjArgs& a, hipStream_t s) {
+hipError_t launch_project_reduce(const ProjArgs& a, const EdgeArgs& ea, hipStream_t s) {
   if (a.direct) return hipSuccess;
   const int64_t quads = static_cast<int64_t>(a.nseq) * a.nktiles * a.nctiles * a.tk * (a.tn / 4);
-  if (quads == 0) return hipSuccess;
-  const int blocks = static_cast<int>(std::min<int64_t>((quads + 255) / 256, 8 * 2048));
-  hipLaunchKernelGGL(project_reduce_kernel, dim3(blocks), dim3(256), 0, s, a);
+  const int64_t work = std::max(quads, ea.nmat > 0 ? edge_words(ea) : 0);
+  if (work == 0) return hipSuccess;
+  const int blocks = static_cast<int>(std::min<int64_t>((work + 255) / 256, 8 * 2048));
+  hipLaunchKernelGGL(project_reduce_kernel, dim3(blocks), dim3(256), 0, s, a, ea);
   return hipGetLastError();
 }
 
@@ -467,9 +516,10 @@ hipError_t launch_project_f32(const ProjArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_edge_gather(const EdgeArgs& a, hipStream_t s) {
-  const int blocks = a.nseq * a.nmat * a.hkv * (a.sink + a.recent);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(edge_gather_kernel, dim3(blocks), dim3(64), 0, s, a);
+  const int64_t words = edge_words(a);
+  if (words == 0) return hipSuccess;
+  const int blocks = static_cast<int>(std::min<int64_t>((words + 255) / 256, 8 * 2048));
+  hipLaunchKernelGGL(edge_gather_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
