@@ -81,111 +81,287 @@ __device__ inline int pair_pos_to_n(int pos, int k) {
 }
 
 // --------------------------------------------------------------- prep ----
-// A[b][i][n] = scale * alpha_n * sum_c q[b][i][comp_c] ck[b,h][n][c], one
-// block per (sequence, KV head, 32 outputs); 8 threads split the c sum.
-// On the MFMA path the first block of each (sequence, KV head) also writes the
-// head's query rows at the exact dims in dims order (bf16) and computes the
-// edge split: plain softmax attention of those rows over the retained sink and
-// recent tokens (all dims exact), stored as split nsplit-1 of each row.
-constexpr int kPrepPos = 128;   // coefficient positions per A-part block
-constexpr int kPrepPass = 4;    // 64-column passes over the compressible dims (dc <= 256)
-constexpr int kPrepRows = 8;    // query rows per pass over q_C
+// A[b][i][n] = scale * alpha_n * sum_c q[b][i][comp_c] ck[b,h][n][c].  One
+// kernel with two kinds of block:
+//  - edge blocks (MFMA path, one per (sequence, KV head)): the head's query
+//    rows at the exact dims in dims order (bf16, for the split kernel) and
+//    the edge split: plain softmax attention of those rows over the retained
+//    sink and recent tokens (all dims exact), stored as split nsplit-1;
+//  - A blocks (sequence, KV head, kPrepPos coefficient positions).
+// Every block issues all of its global loads before it waits for any, and
+// the dims permutation of q is applied from LDS, so a block costs one memory
+// round trip plus its arithmetic.
+constexpr int kPrepPos = 64;  // coefficient positions per A block
 
-// Edge split of the query rows of (sequence b, KV head h); 16-bit caches.
-// The retained rows (exact dims from kx / vx, compressible dims from ke / ve)
-// are first copied to LDS with every load of a thread in flight at once, then
-// scores, softmax and values run from LDS.
-// smem: q of the G rows in dims order, scaled [G][D] fp32 | probabilities
-// [G][ne] fp32 | K rows [ne][D] bf16 | V rows [ne][D] bf16.
-__device__ void edge_split_attention(const DecodeArgs& a, int b, int h, float* sm) {
+// Stage the G query rows of (b, h) (scaled, as fp32) and the dims table in LDS.
+// Loads of a round are all issued before the first store.
+template <typename T>
+__device__ inline void stage_q(const DecodeArgs& a, int b, int h, float* qraw, int* dl) {
+  const int G = a.G, D = a.D, n = G * D, nt = blockDim.x;
+  const int64_t q0 = (static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(h) * G) * D;
+  constexpr int kQ = 8;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kQ * nt) {
+    float v[kQ];
+#pragma unroll
+    for (int u = 0; u < kQ; ++u) v[u] = (i0 + u * nt < n) ? ld<T>(a.q, q0 + i0 + u * nt) : 0.0f;
+    const int dj = (i0 < D) ? a.dims[h * D + i0] : 0;  // first round covers the dims (D <= 256)
+#pragma unroll
+    for (int u = 0; u < kQ; ++u)
+      if (i0 + u * nt < n) qraw[i0 + u * nt] = a.scale * v[u];
+    if (i0 < D) dl[i0] = dj;
+  }
+}
+
+// A block.  Rows n = [r0, r0 + 64) of ck[b,h] (those the block's positions
+// use) are copied to LDS with coalesced loads (row stride dc + 4 floats, so
+// the 16-byte reads of 8 consecutive rows hit distinct banks); thread
+// (position p = tid % 64, row group tid / 64) then forms the dot products
+// of its rows g = tid / 64 + 4 j with q_C broadcast from LDS.
+template <typename T, bool VEC>
+__device__ void prep_a_block(const DecodeArgs& a, int b, int h, int chunk, float* sm) {
+  const int G = a.G, D = a.D, dc = a.dc, du = a.du;
+  const int M = a.seq.mid[b];
+  const int len = a.mfma ? a.kpp : a.k;
+  const int p0 = chunk * kPrepPos;
+  // pair order: position p >= 2 uses row p - 1, position 0 row 0
+  const int r0 = a.mfma ? max(0, p0 - 1) : p0;
+  const int CS = dc + 4;
+  float* ckl = sm;                       // [64][CS]
+  float* qraw = ckl + kPrepPos * CS;     // [G][D]
+  float* qc = qraw + G * D;              // [G][dc]
+  int* dl = reinterpret_cast<int*>(qc + G * dc);  // [D]
+  const float* src = a.ck + ((static_cast<int64_t>(b) * a.hkv + h) * a.k + r0) * dc;
+  const int nrows = max(0, min(kPrepPos, a.k - r0));
+  const int tid = threadIdx.x;
+  if (VEC) {
+    const int dc4 = dc / 4, n4 = nrows * dc4;
+    constexpr int kB = 16;  // float4 loads in flight per thread (dc <= 256)
+    float4 v[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int i = tid + u * 256;
+      v[u] = (i < n4) ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    stage_q<T>(a, b, h, qraw, dl);
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int i = tid + u * 256;
+      if (i < n4) *reinterpret_cast<float4*>(ckl + (i / dc4) * CS + 4 * (i % dc4)) = v[u];
+    }
+  } else {
+    stage_q<T>(a, b, h, qraw, dl);
+    for (int i = tid; i < nrows * dc; i += 256) ckl[(i / dc) * CS + i % dc] = src[i];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * dc; idx += 256) {
+    const int g = idx / dc, c = idx % dc;
+    const int d = dl[du + c];
+    qc[idx] = (d >= 0 && d < D) ? qraw[g * D + d] : 0.0f;
+  }
+  __syncthreads();
+  const int p = tid & 63, pos = p0 + p;
+  if (pos >= len) return;
+  const int n = a.mfma ? pair_pos_to_n(pos, a.k) : pos;
+  const bool live = n >= 0 && n < a.k && M > 0;
+  const float alpha = live ? basis_alpha(n, M) : 0.0f;
+  const float* crow = ckl + (live ? n - r0 : 0) * CS;
+  for (int g = tid >> 6; g < G; g += 4) {
+    const float* qg = qc + g * dc;
+    float acc0 = 0.0f, acc1 = 0.0f;
+    if (live) {
+      int c = 0;
+      if (VEC) {  // dc % 4 == 0: rows and q_C are 16-byte aligned
+        for (; c + 8 <= dc; c += 8) {
+          const float4 x0 = *reinterpret_cast<const float4*>(crow + c);
+          const float4 x1 = *reinterpret_cast<const float4*>(crow + c + 4);
+          const float4 q0 = *reinterpret_cast<const float4*>(qg + c);
+          const float4 q1 = *reinterpret_cast<const float4*>(qg + c + 4);
+          acc0 = fmaf(q0.x, x0.x, acc0); acc0 = fmaf(q0.y, x0.y, acc0);
+          acc0 = fmaf(q0.z, x0.z, acc0); acc0 = fmaf(q0.w, x0.w, acc0);
+          acc1 = fmaf(q1.x, x1.x, acc1); acc1 = fmaf(q1.y, x1.y, acc1);
+          acc1 = fmaf(q1.z, x1.z, acc1); acc1 = fmaf(q1.w, x1.w, acc1);
+        }
+      }
+      for (; c < dc; ++c) acc0 = fmaf(qg[c], crow[c], acc0);
+    }
+    const float v = alpha * (acc0 + acc1);
+    const int64_t i = static_cast<int64_t>(b) * a.hq + h * G + g;
+    if (a.mfma)
+      static_cast<_Float16*>(a.A16)[i * a.kpp + pos] = static_cast<_Float16>(v);
+    else
+      a.A[i * a.kpad + pos] = v;
+  }
+}
+
+// Edge block (16-bit caches).  The retained rows of K and V (exact dims from
+// kx / vx, compressible dims from ke / ve, in dims order) are loaded with
+// every load in flight at once; K goes to LDS, V waits in registers and
+// takes K's place once the scores are formed.
+// smem: rows [E][D + 8] bf16 | q [G][D] fp32 raw | q [G][D] fp32 in dims
+// order | probabilities [G][E] fp32 | dims [D] int.
+constexpr int kEdgeLoads = 8;  // 8-byte or 16-byte chunks per thread and matrix
+
+// KR: query rows per lane group in the scores and values (1, or 4 when G >= 4).
+template <int KR>
+__device__ void prep_edge_block(const DecodeArgs& a, int b, int h, float* sm) {
   const int L = a.seq.len[b], M = a.seq.mid[b];
   const int S = a.sink, E = a.sink + a.recent;
   const int ne = (M > 0) ? E : L;  // retained tokens (all of them without a middle)
   const int D = a.D, du = a.du, dc = a.dc, G = a.G;
   const int ns = a.seq.nsplit[b];
-  const int64_t row0 = a.seq.row0[b];
-  float* qs = sm;                                              // [G][D]
-  float* ps = qs + G * D;                                      // [G][ne]
-  uint16_t* ks = reinterpret_cast<uint16_t*>(ps + G * E);      // [ne][D]
-  uint16_t* vs = ks + E * D;                                   // [ne][D]
+  const int RSD = D + 8;  // halves per LDS row
+  uint16_t* rows = reinterpret_cast<uint16_t*>(sm);
+  float* qraw = sm + (E * RSD) / 2;
+  float* qs = qraw + G * D;
+  float* ps = qs + G * D;
+  int* dl = reinterpret_cast<int*>(ps + G * E);
   const int tid = threadIdx.x, nt = blockDim.x;
-  __syncthreads();
-  // exact dims: 8-dim chunks (du % 8 == 0 on this path), t = e or e + M
-  const int du8 = du / 8, dc2 = dc / 2;
+  const int64_t row0 = a.seq.row0[b];
   const uint16_t* kxh = static_cast<const uint16_t*>(a.kx) + (row0 + static_cast<int64_t>(h) * L) * du;
   const uint16_t* vxh = static_cast<const uint16_t*>(a.vx) + (row0 + static_cast<int64_t>(h) * L) * du;
-  const uint32_t* keh = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.ke) +
-                                                           (static_cast<int64_t>(b) * a.hkv + h) * E * dc);
-  const uint32_t* veh = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.ve) +
-                                                           (static_cast<int64_t>(b) * a.hkv + h) * E * dc);
-  for (int i0 = tid; i0 < ne * du8; i0 += 8 * nt) {
-    uint4 kv[8], vv[8];
+  const uint16_t* keh = static_cast<const uint16_t*>(a.ke) + (static_cast<int64_t>(b) * a.hkv + h) * E * dc;
+  const uint16_t* veh = static_cast<const uint16_t*>(a.ve) + (static_cast<int64_t>(b) * a.hkv + h) * E * dc;
+  // chunk w of a row: CW halves; exact dims first, then compressible dims
+  const bool wide = (du % 8 == 0) && (dc % 8 == 0);
+  const int CW = wide ? 8 : 2;
+  const int nu = du / CW, nc = dc / CW, per_row = nu + nc;
+  const int nchunk = ne * per_row;
+  auto chunk_src = [&](const uint16_t* xh, const uint16_t* eh, int i) {
+    const int e = i / per_row, w = i % per_row;
+    if (w < nu) {
+      const int t = (M > 0 && e >= S) ? e + M : e;
+      return xh + static_cast<int64_t>(t) * du + w * CW;
+    }
+    return eh + static_cast<int64_t>(e) * dc + (w - nu) * CW;
+  };
+  auto chunk_dst = [&](int i) {
+    const int e = i / per_row, w = i % per_row;
+    return rows + e * RSD + w * CW;
+  };
+  uint4 kv[kEdgeLoads], vv[kEdgeLoads];
+  for (int i0 = 0; i0 < nchunk; i0 += kEdgeLoads * nt) {
+    // K and V chunks of this round, all in flight
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * nt;
+    for (int u = 0; u < kEdgeLoads; ++u) {
+      const int i = i0 + tid + u * nt;
       kv[u] = vv[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (i < ne * du8) {
-        const int e = i / du8, c8 = i % du8;
-        const int t = (M > 0 && e >= S) ? e + M : e;
-        kv[u] = *reinterpret_cast<const uint4*>(kxh + static_cast<int64_t>(t) * du + 8 * c8);
-        vv[u] = *reinterpret_cast<const uint4*>(vxh + static_cast<int64_t>(t) * du + 8 * c8);
+      if (i < nchunk) {
+        if (wide) {
+          kv[u] = *reinterpret_cast<const uint4*>(chunk_src(kxh, keh, i));
+          vv[u] = *reinterpret_cast<const uint4*>(chunk_src(vxh, veh, i));
+        } else {
+          kv[u].x = *reinterpret_cast<const uint32_t*>(chunk_src(kxh, keh, i));
+          vv[u].x = *reinterpret_cast<const uint32_t*>(chunk_src(vxh, veh, i));
+        }
       }
     }
+    if (i0 == 0) stage_q<uint16_t>(a, b, h, qraw, dl);
+    if (i0 + kEdgeLoads * nt >= nchunk) break;  // the last round's V stays in registers
+    // more rounds than registers (large heads): V goes through LDS later
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * nt;
-      if (i < ne * du8) {
-        const int e = i / du8, c8 = i % du8;
-        uint32_t* kd = reinterpret_cast<uint32_t*>(ks + e * D + 8 * c8);
-        uint32_t* vd = reinterpret_cast<uint32_t*>(vs + e * D + 8 * c8);
-        kd[0] = kv[u].x; kd[1] = kv[u].y; kd[2] = kv[u].z; kd[3] = kv[u].w;
-        vd[0] = vv[u].x; vd[1] = vv[u].y; vd[2] = vv[u].z; vd[3] = vv[u].w;
+    for (int u = 0; u < kEdgeLoads; ++u) {
+      const int i = i0 + tid + u * nt;
+      if (i < nchunk) {
+        if (wide) *reinterpret_cast<uint4*>(chunk_dst(i)) = kv[u];
+        else *reinterpret_cast<uint32_t*>(chunk_dst(i)) = kv[u].x;
       }
     }
   }
-  // compressible dims: 2-dim words (dc % 2 == 0 on this path)
-  for (int i0 = tid; i0 < ne * dc2; i0 += 8 * nt) {
-    uint32_t kw[8], vw[8];
+  if (nchunk == 0) stage_q<uint16_t>(a, b, h, qraw, dl);
+  const int last0 = (nchunk > 0) ? ((nchunk - 1) / (kEdgeLoads * nt)) * (kEdgeLoads * nt) : 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * nt;
-      kw[u] = vw[u] = 0u;
-      if (i < ne * dc2) {
-        kw[u] = keh[i];
-        vw[u] = veh[i];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * nt;
-      if (i < ne * dc2) {
-        const int e = i / dc2, c2 = i % dc2;
-        *reinterpret_cast<uint32_t*>(ks + e * D + du + 2 * c2) = kw[u];
-        *reinterpret_cast<uint32_t*>(vs + e * D + du + 2 * c2) = vw[u];
-      }
+  for (int u = 0; u < kEdgeLoads; ++u) {
+    const int i = last0 + tid + u * nt;
+    if (i < nchunk) {
+      if (wide) *reinterpret_cast<uint4*>(chunk_dst(i)) = kv[u];
+      else *reinterpret_cast<uint32_t*>(chunk_dst(i)) = kv[u].x;
     }
   }
+  __syncthreads();
+  // q in dims order, scaled; the exact-dim part also as bf16 for the split kernel
+  const int du32 = (du + 31) & ~31;
   for (int idx = tid; idx < G * D; idx += nt) {
     const int g = idx / D, j = idx % D;
-    const int d = a.dims[h * D + j];
+    const int d = dl[j];
+    qs[idx] = (d >= 0 && d < D) ? qraw[g * D + d] : 0.0f;
+  }
+  for (int idx = tid; idx < G * du32; idx += nt) {
+    const int g = idx / du32, j = idx % du32;
     const int64_t i = static_cast<int64_t>(b) * a.hq + h * G + g;
-    qs[idx] = (d >= 0 && d < D) ? a.scale * bf16_to_f32(static_cast<const uint16_t*>(a.q)[i * D + d]) : 0.0f;
-  }
-  __syncthreads();
-  // scores: thread -> (token e, row g); D is even
-  for (int idx = tid; idx < ne * G; idx += nt) {
-    const int e = idx / G, g = idx % G;
-    const float* qg = qs + g * D;
-    const uint32_t* kr = reinterpret_cast<const uint32_t*>(ks + e * D);
-    float s0 = 0.0f, s1 = 0.0f;
-    for (int j2 = 0; j2 < D / 2; ++j2) {
-      const uint32_t w = kr[j2];
-      s0 = fmaf(qg[2 * j2], __uint_as_float(w << 16), s0);
-      s1 = fmaf(qg[2 * j2 + 1], __uint_as_float(w & 0xFFFF0000u), s1);
+    uint16_t bits = 0;
+    if (j < du) {
+      const int d = dl[j];
+      if (d >= 0 && d < D) bits = static_cast<const uint16_t*>(a.q)[i * D + d];
     }
-    ps[g * ne + e] = s0 + s1;
+    static_cast<uint16_t*>(a.Q16)[i * du32 + j] = bits;
   }
   __syncthreads();
+  // scores: a group of 16 lanes per (token e, block of KR rows), 8
+  // dims per lane and 128-dim pass (2 dims per lane and pass without 16-byte
+  // rows): the K chunk is read once for the block's rows, whose 16 partial
+  // dots are then summed with DPP rotations
+  const int l16 = tid & 15, grp = tid >> 4, ngrp = nt >> 4;
+  const int nrb = (G + KR - 1) / KR;
+  const int npair = ne * nrb;
+  for (int pr0 = 0; pr0 < npair; pr0 += ngrp) {
+    const int pr = pr0 + grp;
+    const bool ok = pr < npair;
+    const int e = ok ? pr / nrb : 0, g0 = ok ? (pr % nrb) * KR : 0;
+    const uint16_t* kr = rows + e * RSD;
+    float acc[KR];
+#pragma unroll
+    for (int r = 0; r < KR; ++r) acc[r] = 0.0f;
+    if (wide) {
+      for (int d0 = 8 * l16; d0 < D; d0 += 128) {
+        const uint4 w = *reinterpret_cast<const uint4*>(kr + d0);
+        const float k0 = __uint_as_float(w.x << 16), k1 = __uint_as_float(w.x & 0xFFFF0000u);
+        const float k2 = __uint_as_float(w.y << 16), k3 = __uint_as_float(w.y & 0xFFFF0000u);
+        const float k4 = __uint_as_float(w.z << 16), k5 = __uint_as_float(w.z & 0xFFFF0000u);
+        const float k6 = __uint_as_float(w.w << 16), k7 = __uint_as_float(w.w & 0xFFFF0000u);
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+          const float* qg = qs + min(g0 + r, G - 1) * D + d0;
+          const float4 qa = *reinterpret_cast<const float4*>(qg);
+          const float4 qb = *reinterpret_cast<const float4*>(qg + 4);
+          float v = acc[r];
+          v = fmaf(qa.x, k0, v); v = fmaf(qa.y, k1, v); v = fmaf(qa.z, k2, v); v = fmaf(qa.w, k3, v);
+          v = fmaf(qb.x, k4, v); v = fmaf(qb.y, k5, v); v = fmaf(qb.z, k6, v); v = fmaf(qb.w, k7, v);
+          acc[r] = v;
+        }
+      }
+    } else {
+      for (int d0 = 2 * l16; d0 < D; d0 += 32) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(kr + d0);
+        const float k0 = __uint_as_float(w << 16), k1 = __uint_as_float(w & 0xFFFF0000u);
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+          const float* qg = qs + min(g0 + r, G - 1) * D + d0;
+          acc[r] = fmaf(qg[1], k1, fmaf(qg[0], k0, acc[r]));
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < KR; ++r) acc[r] = row16_sum(acc[r]);
+    if (ok && l16 == 0)
+#pragma unroll
+      for (int r = 0; r < KR; ++r)
+        if (g0 + r < G) ps[(g0 + r) * ne + e] = acc[r];
+  }
+  __syncthreads();
+  // V replaces K in LDS (the last round from registers, earlier rounds reloaded)
+  for (int i0 = 0; i0 < last0; i0 += nt) {
+    const int i = i0 + tid;
+    if (wide) *reinterpret_cast<uint4*>(chunk_dst(i)) = *reinterpret_cast<const uint4*>(chunk_src(vxh, veh, i));
+    else *reinterpret_cast<uint32_t*>(chunk_dst(i)) = *reinterpret_cast<const uint32_t*>(chunk_src(vxh, veh, i));
+  }
+#pragma unroll
+  for (int u = 0; u < kEdgeLoads; ++u) {
+    const int i = last0 + tid + u * nt;
+    if (i < nchunk) {
+      if (wide) *reinterpret_cast<uint4*>(chunk_dst(i)) = vv[u];
+      else *reinterpret_cast<uint32_t*>(chunk_dst(i)) = vv[u].x;
+    }
+  }
   // softmax of each row: one wave per row
   const int lane = tid & 63, nwv = nt >> 6;
   for (int g = tid >> 6; g < G; g += nwv) {
@@ -194,9 +370,9 @@ __device__ void edge_split_attention(const DecodeArgs& a, int b, int h, float* s
     m = wave_max(m);
     float l = 0.0f;
     for (int e = lane; e < ne; e += 64) {
-      const float p = (m == -INFINITY) ? 0.0f : __expf(ps[g * ne + e] - m);
-      ps[g * ne + e] = p;
-      l += p;
+      const float pe = (m == -INFINITY) ? 0.0f : __expf(ps[g * ne + e] - m);
+      ps[g * ne + e] = pe;
+      l += pe;
     }
     l = wave_sum(l);
     if (lane == 0) {
@@ -206,119 +382,79 @@ __device__ void edge_split_attention(const DecodeArgs& a, int b, int h, float* s
     }
   }
   __syncthreads();
-  // values: thread -> (row g, dim j: exact dims then compressible dims)
-  for (int idx = tid; idx < G * D; idx += nt) {
-    const int g = idx / D, j = idx % D;
-    const float* pg = ps + g * ne;
-    float acc = 0.0f;
-    for (int e = 0; e < ne; ++e) acc = fmaf(pg[e], bf16_to_f32(vs[e * D + j]), acc);
-    // partial layout [m, l, o_U(du), o_E(dc), W]: dim j of the row sits at 2 + j
-    a.part[(static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G + g) * ns + ns - 1) * a.RS + 2 + j] = acc;
+  // values: a group of 16 lanes per (8-dim chunk, block of KR rows),
+  // tokens split over the lanes (e = lane, lane + 16, ...): each V chunk is
+  // read once for the block's rows; the 16 partial sums are added with DPP
+  // rotations (a thread per (row, dim) without 16-byte rows)
+  float* P0 = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G) * ns + ns - 1) * a.RS + 2;
+  const int64_t prs = static_cast<int64_t>(ns) * a.RS;  // partial-row stride of consecutive rows g
+  if (wide) {
+    const int nch = D / 8, nunit = nch * nrb;
+    for (int u0 = 0; u0 < nunit; u0 += ngrp) {
+      const int un = u0 + grp;
+      const bool ok = un < nunit;
+      const int c8 = ok ? un % nch : 0, g0 = ok ? (un / nch) * KR : 0;
+      float acc[KR][8];
+#pragma unroll
+      for (int r = 0; r < KR; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[r][j] = 0.0f;
+      for (int e = l16; e < ne; e += 16) {
+        const uint4 w = *reinterpret_cast<const uint4*>(rows + e * RSD + 8 * c8);
+        const float v0 = __uint_as_float(w.x << 16), v1 = __uint_as_float(w.x & 0xFFFF0000u);
+        const float v2 = __uint_as_float(w.y << 16), v3 = __uint_as_float(w.y & 0xFFFF0000u);
+        const float v4 = __uint_as_float(w.z << 16), v5 = __uint_as_float(w.z & 0xFFFF0000u);
+        const float v6 = __uint_as_float(w.w << 16), v7 = __uint_as_float(w.w & 0xFFFF0000u);
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+          const float pe = ps[min(g0 + r, G - 1) * ne + e];
+          acc[r][0] = fmaf(pe, v0, acc[r][0]); acc[r][1] = fmaf(pe, v1, acc[r][1]);
+          acc[r][2] = fmaf(pe, v2, acc[r][2]); acc[r][3] = fmaf(pe, v3, acc[r][3]);
+          acc[r][4] = fmaf(pe, v4, acc[r][4]); acc[r][5] = fmaf(pe, v5, acc[r][5]);
+          acc[r][6] = fmaf(pe, v6, acc[r][6]); acc[r][7] = fmaf(pe, v7, acc[r][7]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < KR; ++r)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[r][j] = row16_sum(acc[r][j]);
+      if (ok && l16 < 8) {
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+          float v = acc[r][0];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) v = (l16 == j) ? acc[r][j] : v;
+          // partial layout [m, l, o_U(du), o_E(dc), W]: dim j of the row sits at 2 + j
+          if (g0 + r < G) P0[(g0 + r) * prs + 8 * c8 + l16] = v;
+        }
+      }
+    }
+  } else {
+    for (int idx = tid; idx < G * D; idx += nt) {
+      const int g = idx / D, j = idx % D;
+      const float* pg = ps + g * ne;
+      float acc = 0.0f;
+      for (int e = 0; e < ne; ++e) acc = fmaf(pg[e], bf16_to_f32(rows[e * RSD + j]), acc);
+      P0[g * prs + j] = acc;
+    }
   }
 }
 
-// A-part: block (b, h, chunk of kPrepPos coefficient positions); each wave
-// takes 32 positions, 4 at a time (16 lanes per ck row, 4 columns per lane and
-// 64-column pass), with every row load of the wave in flight at once; the 16
-// lanes of a row are summed with DPP rotations.
+// Blocks [0, nedge) are edge blocks (MFMA path), the rest A blocks.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a, int nedge, int chunks) {
   extern __shared__ float smem[];
-  const int bh = blockIdx.x;
-  const int b = bh / a.hkv, h = bh % a.hkv;
-  const int M = a.seq.mid[b];
-  if (a.mfma && blockIdx.y == 0) {
-    // MFMA path: this KV head's query rows at the exact dims in dims order
-    // (bf16, zero padded to 32), loaded contiguously by the split kernel
-    const int du32 = (a.du + 31) & ~31;
-    for (int idx = threadIdx.x; idx < a.G * du32; idx += blockDim.x) {
-      const int g = idx / du32, j = idx % du32;
-      const int64_t i = static_cast<int64_t>(b) * a.hq + h * a.G + g;
-      uint16_t bits = 0;
-      if (j < a.du) {
-        const int d = a.dims[h * a.D + j];
-        if (d >= 0 && d < a.D) bits = static_cast<const uint16_t*>(a.q)[i * a.D + d];
-      }
-      static_cast<uint16_t*>(a.Q16)[i * du32 + j] = bits;
+  int blk = blockIdx.x;
+  if (blk < nedge) {
+    if (a.edge_split) {
+      if (a.G >= 4) prep_edge_block<4>(a, blk / a.hkv, blk % a.hkv, smem);
+      else prep_edge_block<1>(a, blk / a.hkv, blk % a.hkv, smem);
     }
-    if (a.edge_split) edge_split_attention(a, b, h, smem);
     return;
   }
-  if (!a.prep_a) return;
-  float* qc = smem;  // [kPrepRows][dc]
-  const int chunk = blockIdx.y - (a.mfma ? 1 : 0);
-  const int len = a.mfma ? a.kpp : a.k;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
-  const int npass = (a.dc + 63) / 64;
-  const float* ckh = a.ck + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc;
-  // this lane's ck rows: positions pos0 + 4 s + g4 (s < 8) of its wave
-  const int pos0 = chunk * kPrepPos + wave * 32;
-  float4 ckv[8][kPrepPass];
-#pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const int pos = pos0 + 4 * st + g4;
-    const int n = (pos >= len) ? -1 : (a.mfma ? pair_pos_to_n(pos, a.k) : pos);
-#pragma unroll
-    for (int ps = 0; ps < kPrepPass; ++ps) {
-      const int c = 64 * ps + 4 * l16;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ps < npass && n >= 0 && M > 0 && c < a.dc) {
-        const float* src = ckh + static_cast<int64_t>(n) * a.dc + c;
-        if (VEC) {
-          v = *reinterpret_cast<const float4*>(src);
-        } else {
-          v.x = src[0];
-          if (c + 1 < a.dc) v.y = src[1];
-          if (c + 2 < a.dc) v.z = src[2];
-          if (c + 3 < a.dc) v.w = src[3];
-        }
-      }
-      ckv[st][ps] = v;
-    }
-  }
-  for (int g0 = 0; g0 < a.G; g0 += kPrepRows) {
-    const int ng = min(kPrepRows, a.G - g0);
-    __syncthreads();
-    for (int idx = tid; idx < ng * a.dc; idx += blockDim.x) {
-      const int g = idx / a.dc, c = idx % a.dc;
-      const int d = a.dims[h * a.D + a.du + c];
-      const int i = h * a.G + g0 + g;
-      qc[g * a.dc + c] = (d >= 0 && d < a.D)
-                             ? a.scale * ld<T>(a.q, (static_cast<int64_t>(b) * a.hq + i) * a.D + d)
-                             : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int pos = pos0 + 4 * st + g4;
-      const int n = (pos >= len) ? -1 : (a.mfma ? pair_pos_to_n(pos, a.k) : pos);
-      const float alpha = (n >= 0 && M > 0) ? basis_alpha(n, M) : 0.0f;
-#pragma unroll
-      for (int g = 0; g < kPrepRows; ++g) {
-        if (g >= ng) break;
-        float acc = 0.0f;
-#pragma unroll
-        for (int ps = 0; ps < kPrepPass; ++ps) {
-          const int c = 64 * ps + 4 * l16;
-          if (ps < npass && c < a.dc) {
-            const float* qg = qc + g * a.dc + c;
-            acc = fmaf(qg[0], ckv[st][ps].x, acc);
-            if (c + 1 < a.dc) acc = fmaf(qg[1], ckv[st][ps].y, acc);
-            if (c + 2 < a.dc) acc = fmaf(qg[2], ckv[st][ps].z, acc);
-            if (c + 3 < a.dc) acc = fmaf(qg[3], ckv[st][ps].w, acc);
-          }
-        }
-        acc = row16_sum(acc);
-        if (l16 == 0 && pos < len) {
-          const int64_t i = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
-          if (a.mfma)
-            static_cast<_Float16*>(a.A16)[i * a.kpp + pos] = static_cast<_Float16>(alpha * acc);
-          else
-            a.A[i * a.kpad + pos] = alpha * acc;
-        }
-      }
-    }
-  }
+  blk -= nedge;
+  const int bh = blk / chunks, chunk = blk % chunks;
+  prep_a_block<T, VEC>(a, bh / a.hkv, bh % a.hkv, chunk, smem);
 }
 
 // -------------------------------------------------------------- split ----
@@ -758,14 +894,18 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 
 }  // namespace
 
-size_t decode_prep_smem(const DecodeArgs& a) {
-  size_t n = sizeof(float) * kPrepRows * a.dc;
-  if (a.edge_split) n = std::max(n, decode_edge_smem(a));
-  return n;
+size_t decode_prep_a_smem(const DecodeArgs& a) {
+  return sizeof(float) * (static_cast<size_t>(kPrepPos) * (a.dc + 4) + static_cast<size_t>(a.G) * a.D +
+                          static_cast<size_t>(a.G) * a.dc + a.D);
 }
 size_t decode_edge_smem(const DecodeArgs& a) {
   const size_t E = static_cast<size_t>(a.sink) + a.recent;  // upper bound of the retained tokens
-  return sizeof(float) * (static_cast<size_t>(a.G) * a.D + a.G * E) + 2 * sizeof(uint16_t) * E * a.D;
+  return sizeof(uint16_t) * E * (a.D + 8) + sizeof(float) * (2 * static_cast<size_t>(a.G) * a.D + a.G * E + a.D);
+}
+size_t decode_prep_smem(const DecodeArgs& a) {
+  size_t n = a.prep_a ? decode_prep_a_smem(a) : 0;
+  if (a.edge_split) n = std::max(n, decode_edge_smem(a));
+  return n;
 }
 size_t decode_split_smem(const DecodeArgs& a) {
   return sizeof(float) * (kDecRows * a.D + kDecRows * a.kpad + 4 * kDecRows * kDecTile +
@@ -776,17 +916,19 @@ size_t decode_merge_cv_smem(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
-  if (!a.prep_a && !a.mfma) return hipSuccess;
+  const int nedge = a.mfma ? a.nseq * a.hkv : 0;
   const int len = a.mfma ? a.kpp : a.k;
   const int chunks = a.prep_a ? (len + kPrepPos - 1) / kPrepPos : 0;
-  dim3 grid(a.nseq * a.hkv, chunks + (a.mfma ? 1 : 0));
+  const int blocks = nedge + a.nseq * a.hkv * chunks;
+  if (blocks == 0) return hipSuccess;
   const size_t sm = decode_prep_smem(a);
   const bool vec = a.dc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.ck) & 15) == 0;
   hipError_t e;
-#define FA_PREP(T, V)                                                              \
-  do {                                                                             \
-    if ((e = allow_lds(decode_prep_kernel<T, V>, sm)) != hipSuccess) return e;    \
-    hipLaunchKernelGGL((decode_prep_kernel<T, V>), grid, dim3(256), sm, s, a);     \
+#define FA_PREP(T, V)                                                                        \
+  do {                                                                                       \
+    if ((e = allow_lds(decode_prep_kernel<T, V>, sm)) != hipSuccess) return e;              \
+    hipLaunchKernelGGL((decode_prep_kernel<T, V>), dim3(blocks), dim3(256), sm, s, a, nedge, \
+                       max(chunks, 1));                                                      \
   } while (0)
   if (a.dtype == 1) {
     if (vec) FA_PREP(uint16_t, true); else FA_PREP(uint16_t, false);
