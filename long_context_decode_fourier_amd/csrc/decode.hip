@@ -728,7 +728,6 @@ constexpr int kMergeRows = 4;
 
 __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   extern __shared__ float smem[];  // [ns] weights
-  __shared__ float red[256];
   const int row = blockIdx.x;      // b * hq + i
   const int b = row / a.hq, i = row % a.hq, h = i / a.G;
   const int ns = a.seq.nsplit[b];
@@ -738,30 +737,21 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   const int idx = blockIdx.y * 256 + threadIdx.x;
   if (blockIdx.y * 256 >= nvec) return;  // uniform per block
   const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS;
+  // every wave forms the split weights itself (wave reductions, no block
+  // barrier); wave 0 publishes them for the sums below
+  const int lane = threadIdx.x & 63;
   float mx = -INFINITY;
-  for (int s = threadIdx.x; s < ns; s += 256) mx = fmaxf(mx, P[static_cast<int64_t>(s) * a.RS]);
-  red[threadIdx.x] = mx;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
-    __syncthreads();
-  }
-  mx = red[0];
-  __syncthreads();
+  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, P[static_cast<int64_t>(s) * a.RS]);
+  mx = wave_max(mx);
   float lsum = 0.0f;
-  for (int s = threadIdx.x; s < ns; s += 256) {
+  for (int s = lane; s < ns; s += 64) {
     const float m = P[static_cast<int64_t>(s) * a.RS];
     const float w = (m == -INFINITY) ? 0.0f : __expf(m - mx);
-    smem[s] = w;
+    if (threadIdx.x < 64) smem[s] = w;
     lsum += w * P[static_cast<int64_t>(s) * a.RS + 1];
   }
-  red[threadIdx.x] = lsum;
+  const float linv = 1.0f / wave_sum(lsum);
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  const float linv = 1.0f / red[0];
   float* mrow = a.mrg + static_cast<int64_t>(row) * a.MS;
   if (blockIdx.y == 0 && threadIdx.x == 0) mrow[a.dc + a.kpad] = linv;
   if (idx >= nvec) return;
@@ -773,14 +763,14 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     if (idx < a.du + a.dc) s_lo = ns - 1;
     else s_hi = ns - 1;
   }
-  // fixed-order sum over the splits, 8 loads in flight
+  // fixed-order sum over the splits, 16 loads in flight
   float v = 0.0f;
-  for (int s0 = s_lo; s0 < s_hi; s0 += 8) {
-    float x[8];
+  for (int s0 = s_lo; s0 < s_hi; s0 += 16) {
+    float x[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (s0 + j < s_hi) ? Pi[static_cast<int64_t>(s0 + j) * a.RS] : 0.0f;
+    for (int j = 0; j < 16; ++j) x[j] = (s0 + j < s_hi) ? Pi[static_cast<int64_t>(s0 + j) * a.RS] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 16; ++j)
       if (s0 + j < s_hi) v = fmaf(smem[s0 + j], x[j], v);
   }
   if (idx < a.du) {
@@ -794,14 +784,17 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   }
 }
 
-// Pass 2 body: one block per (sequence, KV head, 32-column slice of the
+// Pass 2 body: one block per (sequence, KV head, 8-column slice of the
 // compressible dims) computes O_C[g][c] = sum_n (alpha W)[g][n] cv[n][c] for
 // the head's query rows, kMergeRows rows at a time.  Thread (column quad cq,
-// n-lane nl) reads 4 consecutive columns of the cv rows n = nl + 32 j with
-// kCvBatch loads in flight; the 32 n-lanes are summed in a fixed order.
-constexpr int kCvCols = 32;
-constexpr int kCvLanes = 32;
-constexpr int kCvBatch = 8;
+// n-lane nl) reads 4 consecutive columns of the cv rows n = nl + 128 j and
+// the matching (alpha W)[g][n], up to kCvBatch rows of both in flight; the
+// 128 n-lanes are summed in a fixed order (16-lane partial sums, then the 8
+// partials).
+constexpr int kCvCols = 8;
+constexpr int kCvLanes = 128;
+constexpr int kCvBatch = 16;
+constexpr int kCvQ = kMergeRows * kCvCols;  // (row, column) pairs of a pass
 
 template <bool VEC>
 __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
@@ -809,21 +802,15 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
   const int b = blockIdx.x / a.hkv, h = blockIdx.x % a.hkv;
   const int M = a.seq.mid[b];
   const bool has_mid = a.dc > 0 && M > 0;
-  float* Wm = smem;                                   // [kMergeRows][kpad]
-  float* red = Wm + kMergeRows * a.kpad;              // [kCvLanes][kMergeRows][kCvCols]
+  float* red = smem;                         // [kCvLanes][kCvQ]
+  float* red2 = red + kCvLanes * kCvQ;       // [8][kCvQ]
   const int tid = threadIdx.x;
-  const int cq = tid % (kCvCols / 4), nl = tid / (kCvCols / 4);
+  const int cq = tid & 1, nl = tid >> 1;
   const int c = blockIdx.y * kCvCols + 4 * cq;
   const float* cvb = a.cv + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc;
   for (int g0 = 0; g0 < a.G; g0 += kMergeRows) {
     const int ng = min(kMergeRows, a.G - g0);
-    __syncthreads();
-    if (has_mid)
-      for (int idx = tid; idx < ng * a.k; idx += 256) {
-        const int g = idx / a.k, n = idx % a.k;
-        const int64_t row = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
-        Wm[g * a.kpad + n] = a.mrg[row * a.MS + a.dc + n];
-      }
+    const float* wrow = a.mrg + (static_cast<int64_t>(b) * a.hq + h * a.G + g0) * a.MS + a.dc;
     __syncthreads();
     float acc[kMergeRows][4];
 #pragma unroll
@@ -831,9 +818,13 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
     if (has_mid && c < a.dc) {
       for (int n0 = nl; n0 < a.k; n0 += kCvLanes * kCvBatch) {
         float4 x[kCvBatch];
+        float wv[kCvBatch][kMergeRows];
 #pragma unroll
         for (int j = 0; j < kCvBatch; ++j) {
           const int n = n0 + kCvLanes * j;
+#pragma unroll
+          for (int g = 0; g < kMergeRows; ++g)
+            wv[j][g] = (n < a.k && g < ng) ? wrow[static_cast<int64_t>(g) * a.MS + n] : 0.0f;
           float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
           if (n < a.k) {
             const float* src = cvb + static_cast<int64_t>(n) * a.dc + c;
@@ -855,7 +846,7 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
 #pragma unroll
           for (int g = 0; g < kMergeRows; ++g)
             if (g < ng) {
-              const float w = Wm[g * a.kpad + n];
+              const float w = wv[j][g];
               acc[g][0] = fmaf(w, x[j].x, acc[g][0]);
               acc[g][1] = fmaf(w, x[j].y, acc[g][1]);
               acc[g][2] = fmaf(w, x[j].z, acc[g][2]);
@@ -867,14 +858,21 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < kMergeRows; ++g)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[(nl * kMergeRows + g) * kCvCols + 4 * cq + e] = acc[g][e];
+      for (int e = 0; e < 4; ++e) red[nl * kCvQ + g * kCvCols + 4 * cq + e] = acc[g][e];
+    __syncthreads();
+    {  // 8 partial sums of 16 n-lanes each: thread (part, pair)
+      const int q = tid % kCvQ, part = tid / kCvQ;
+      float sum = 0.0f;
+      for (int l = 0; l < kCvLanes / 8; ++l) sum += red[(part * (kCvLanes / 8) + l) * kCvQ + q];
+      red2[part * kCvQ + q] = sum;
+    }
     __syncthreads();
     if (tid < ng * kCvCols) {
       const int g = tid / kCvCols, col = tid % kCvCols;
       const int cc = blockIdx.y * kCvCols + col;
       if (cc < a.dc) {
         float sum = 0.0f;
-        for (int q = 0; q < kCvLanes; ++q) sum += red[(q * kMergeRows + g) * kCvCols + col];
+        for (int part = 0; part < 8; ++part) sum += red2[part * kCvQ + tid];
         const int64_t row = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
         const float* mrow = a.mrg + row * a.MS;
         const int dd = a.dims[h * a.D + a.du + cc];
@@ -912,7 +910,8 @@ size_t decode_split_smem(const DecodeArgs& a) {
                           kDecTile * kDecRows + kDecRows);
 }
 size_t decode_merge_cv_smem(const DecodeArgs& a) {
-  return sizeof(float) * (kMergeRows * a.kpad + kCvLanes * kMergeRows * kCvCols);
+  (void)a;
+  return sizeof(float) * (kCvLanes * kCvQ + 8 * kCvQ);
 }
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
