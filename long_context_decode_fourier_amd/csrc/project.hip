@@ -399,11 +399,13 @@ __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a, EdgeArg
               static_cast<int64_t>(gridDim.x) * blockDim.x);
 }
 
-// fp32 inputs: one block per (sequence, matrix, KV head, 8 coefficients).
+// fp32 inputs: one block per (sequence, matrix, KV head, kF32Coefs
+// coefficients; few per block, so that small problems still spread over many
+// CUs).
 // Thread (c, lane-of-8 positions) sums phi_n(tau) x[tau][c] over its residue
 // class of tau with Kahan compensation; the 8 partial sums are added in a
 // fixed tree.  The basis value is computed from the exact integer phase.
-constexpr int kF32Coefs = 8;
+constexpr int kF32Coefs = 2;
 
 __global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
   __shared__ float red[8][kF32Coefs][32];
