@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="input copies (0: enough to beat the LLC)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one HIP graph per call and input copy (default: launch every call from the host, "
+                         "which measures faster on this ROCm)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy kernel over MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -164,23 +167,52 @@ def main():
             fb.project(desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], ws_p)
     stream = torch.cuda.current_stream()
 
+    def call_project(s, st):
+        fb.project(desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], ws_p, st)
+
+    def call_decode(s, st):
+        fb.decode(desc, s["q"], s.get("kx"), s.get("vx"), s["ke"], s["ve"], s["ck"], s["cv"],
+                  scale, s["out"], ws_d, st)
+
+    graphs = None  # per input copy: (project graph, decode graph)
+
     def step(i, ev=None):
         s = sets[i % copies]
         if ev is not None:
             ev[0].record(stream)
         if "project" in steps:
-            fb.project(desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], ws_p, stream)
+            if graphs: graphs[i % copies][0].replay()
+            else: call_project(s, stream)
         if ev is not None:
             ev[1].record(stream)
         if "decode" in steps:
-            fb.decode(desc, s["q"], s.get("kx"), s.get("vx"), s["ke"], s["ve"], s["ck"], s["cv"],
-                      scale, s["out"], ws_d, stream)
+            if graphs: graphs[i % copies][1].replay()
+            else: call_decode(s, stream)
         if ev is not None:
             ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.graph:
+        # the step as HIP graphs: the calls are captured once per input copy
+        # (the library makes no allocation, memset or host sync)
+        side = torch.cuda.Stream()
+        graphs = []
+        for s in sets:
+            pair = []
+            for fn, name in ((call_project, "project"), (call_decode, "decode")):
+                g = None
+                if name in steps:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=side):
+                        fn(s, torch.cuda.current_stream())
+                pair.append(g)
+            graphs.append(tuple(pair))
+        torch.cuda.synchronize()
+        for i in range(max(args.warmup, copies)):
+            step(i)
+        torch.cuda.synchronize()
 
     # timed region: whole-step throughput
     t0 = time.perf_counter()
@@ -242,6 +274,7 @@ def main():
                    "n_q_heads": c.n_q_heads, "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
                    "n_comp_dims": c.n_comp, "n_coef": c.n_coef, "sink": c.sink,
                    "recent": c.recent, "input_copies": copies},
+        "launch": "hip graph replay (one graph per call and input copy)" if args.graph else "eager",
         "roofline": roof,
         "cpu_baseline": cpu,
         "calls": extra,
