@@ -97,6 +97,9 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
   if (!proj_item(a, a.nitems, blockIdx.x, &it)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / WC, wc = wave % WC;
+  // a wave whose coefficient rows all lie past k (the padding of the last
+  // k-tile) only loads and converts the cache tile
+  const bool active = it.ktile * TK + wr * (RB * 32) < a.k;
   const int M = it.M;
   const int L = a.seq.len[it.b];
   const int64_t row0 = a.seq.row0[it.b];
@@ -228,43 +231,41 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
     };
     // software pipeline over the 4 sub-steps: the operands of sub-step s+1
     // (LDS reads, basis VALU) are produced while sub-step s's MFMAs run
-    half8 bcur[CB], bnxt[CB], acur[RB], anxt[RB];
-    read_b(0, bcur);
-    gen_a(0, acur);
+    if (active) {
+      half8 bcur[CB], bnxt[CB], acur[RB], anxt[RB];
+      read_b(0, bcur);
+      gen_a(0, acur);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) {
-        read_b(s + 1, bnxt);
-        gen_a(s + 1, anxt);
-      }
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) {
+          read_b(s + 1, bnxt);
+          gen_a(s + 1, anxt);
+        }
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[rb], bcur[cb], acc[rb][cb], 0, 0, 0);
-      if (s < 3) {
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[rb], bcur[cb], acc[rb][cb], 0, 0, 0);
+        if (s < 3) {
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) bcur[cb] = bnxt[cb];
+          for (int cb = 0; cb < CB; ++cb) bcur[cb] = bnxt[cb];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acur[rb] = anxt[rb];
-      }
-      // the next step's tile goes to the other buffer (last read in the
-      // previous step, before its barrier) after this step's last MFMAs, so
-      // that its loads have the whole step to arrive; after the last step the
-      // store repeats data nobody reads, which keeps the sub-step loop one
-      // basic block
-      if (s == 3) {
-        // the raw rows pass through an empty asm statement here, which keeps
-        // their conversion (and the wait for their loads) at the end of the
-        // step; hoisted into the early sub-steps, it would wait for loads
-        // issued moments before
-#pragma unroll
-        for (int j = 0; j < NPG; ++j)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(raw[j][i].x), "+v"(raw[j][i].y));
-        store_raw(xts[buf ^ 1]);
+          for (int rb = 0; rb < RB; ++rb) acur[rb] = anxt[rb];
+        }
       }
     }
+    // the next step's tile goes to the other buffer (last read in the
+    // previous step, before its barrier) after this step's MFMAs, so that its
+    // loads have the whole step to arrive; after the last step the store
+    // repeats data nobody reads.  The raw rows pass through an empty asm
+    // statement here, which keeps their conversion (and the wait for their
+    // loads) at the end of the step: hoisted into the early sub-steps, it
+    // would wait for loads issued moments before.
+#pragma unroll
+    for (int j = 0; j < NPG; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(raw[j][i].x), "+v"(raw[j][i].y));
+    store_raw(xts[buf ^ 1]);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       ph[rb] += d64[rb];
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
       for (int r = 0; r < 16; ++r) {
         const int nl = wr * (RB * 32) + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int cl = wc * (CB * 32) + cb * 32 + (lane & 31);
-        P[nl * TN + cl] = acc[rb][cb][r];
+        if (it.ktile * TK + nl < a.k) P[nl * TN + cl] = acc[rb][cb][r];  // the reduce reads rows < k only
       }
 }
 
