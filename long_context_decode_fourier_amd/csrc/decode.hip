@@ -96,7 +96,7 @@ constexpr int kPrepPos = 64;  // coefficient positions per A block
 // Stage the G query rows of (b, h) (scaled, as fp32) and the dims table in LDS.
 // Loads of a round are all issued before the first store.
 template <typename T>
-__device__ inline void stage_q(const DecodeArgs& a, int b, int h, float* qraw, int* dl) {
+__device__ inline void stage_q(const DecodeArgs& a, int b, int h, float* qraw, int* dl, float mul) {
   const int G = a.G, D = a.D, n = G * D, nt = blockDim.x;
   const int64_t q0 = (static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(h) * G) * D;
   constexpr int kQ = 8;
@@ -107,7 +107,7 @@ __device__ inline void stage_q(const DecodeArgs& a, int b, int h, float* qraw, i
     const int dj = (i0 < D) ? a.dims[h * D + i0] : 0;  // first round covers the dims (D <= 256)
 #pragma unroll
     for (int u = 0; u < kQ; ++u)
-      if (i0 + u * nt < n) qraw[i0 + u * nt] = a.scale * v[u];
+      if (i0 + u * nt < n) qraw[i0 + u * nt] = mul * v[u];
     if (i0 < D) dl[i0] = dj;
   }
 }
@@ -118,7 +118,7 @@ __device__ inline void stage_q(const DecodeArgs& a, int b, int h, float* qraw, i
 // (position p = tid % 64, row group tid / 64) then forms the dot products
 // of its rows g = tid / 64 + 4 j with q_C broadcast from LDS.
 template <typename T, bool VEC>
-__device__ void prep_a_block(const DecodeArgs& a, int b, int h, int chunk, float* sm) {
+__device__ __forceinline__ void prep_a_block(const DecodeArgs& a, int b, int h, int chunk, float* sm) {
   const int G = a.G, D = a.D, dc = a.dc, du = a.du;
   const int M = a.seq.mid[b];
   const int len = a.mfma ? a.kpp : a.k;
@@ -142,14 +142,14 @@ __device__ void prep_a_block(const DecodeArgs& a, int b, int h, int chunk, float
       const int i = tid + u * 256;
       v[u] = (i < n4) ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    stage_q<T>(a, b, h, qraw, dl);
+    stage_q<T>(a, b, h, qraw, dl, a.scale);
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       const int i = tid + u * 256;
       if (i < n4) *reinterpret_cast<float4*>(ckl + (i / dc4) * CS + 4 * (i % dc4)) = v[u];
     }
   } else {
-    stage_q<T>(a, b, h, qraw, dl);
+    stage_q<T>(a, b, h, qraw, dl, a.scale);
     for (int i = tid; i < nrows * dc; i += 256) ckl[(i / dc) * CS + i % dc] = src[i];
   }
   __syncthreads();
@@ -203,7 +203,7 @@ constexpr int kEdgeLoads = 8;  // 8-byte or 16-byte chunks per thread and matrix
 
 // KR: query rows per lane group in the scores and values (1, or 4 when G >= 4).
 template <int KR>
-__device__ void prep_edge_block(const DecodeArgs& a, int b, int h, float* sm) {
+__device__ __forceinline__ void prep_edge_block(const DecodeArgs& a, int b, int h, float* sm) {
   const int L = a.seq.len[b], M = a.seq.mid[b];
   const int S = a.sink, E = a.sink + a.recent;
   const int ne = (M > 0) ? E : L;  // retained tokens (all of them without a middle)
@@ -255,7 +255,7 @@ __device__ void prep_edge_block(const DecodeArgs& a, int b, int h, float* sm) {
         }
       }
     }
-    if (i0 == 0) stage_q<uint16_t>(a, b, h, qraw, dl);
+    if (i0 == 0) stage_q<uint16_t>(a, b, h, qraw, dl, a.scale);
     if (i0 + kEdgeLoads * nt >= nchunk) break;  // the last round's V stays in registers
     // more rounds than registers (large heads): V goes through LDS later
 #pragma unroll
@@ -267,7 +267,7 @@ __device__ void prep_edge_block(const DecodeArgs& a, int b, int h, float* sm) {
       }
     }
   }
-  if (nchunk == 0) stage_q<uint16_t>(a, b, h, qraw, dl);
+  if (nchunk == 0) stage_q<uint16_t>(a, b, h, qraw, dl, a.scale);
   const int last0 = (nchunk > 0) ? ((nchunk - 1) / (kEdgeLoads * nt)) * (kEdgeLoads * nt) : 0;
 #pragma unroll
   for (int u = 0; u < kEdgeLoads; ++u) {
@@ -440,6 +440,192 @@ __device__ void prep_edge_block(const DecodeArgs& a, int b, int h, float* sm) {
   }
 }
 
+// Edge block on MFMA (16-byte rows, D % 32 == 0, G <= 16): scores
+// S = q K^T with v_mfma_f32_16x16x32_bf16 (q and K are bf16, exact products;
+// the scale is applied to the fp32 result), values O = P V with
+// v_mfma_f32_16x16x16bf16_1k on P split into bf16 hi + lo (about 16 bits of
+// p), V read transposed from LDS.  Token blocks of 16 (ne rounded up; the
+// padding tokens get a score of -inf and zero V rows).
+// smem: rows [E16][D + 8] bf16 | q [G][D] fp32 raw | q [G][D + 8] bf16 in
+// dims order | scores / probabilities [G][E16] fp32 | dims [D] int.
+typedef __bf16 ebf16x8 __attribute__((ext_vector_type(8)));
+typedef short eshort4 __attribute__((ext_vector_type(4)));
+typedef float efloat4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) eshort4 elds_short4;
+
+// Transposed 4 x 16-bit LDS read: lane 4c+e of each 16-lane group receives
+// element e of the 8-byte chunks addressed by lanes c, c+4, c+8, c+12.
+__device__ inline eshort4 edge_tr4(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((elds_short4*)(p));
+}
+__device__ inline uint16_t edge_bf16_rne(float x) {  // finite inputs
+  const uint32_t u = __float_as_uint(x);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__host__ __device__ inline size_t edge_mfma_smem_bytes(int E, int G, int D) {
+  const size_t E16 = (static_cast<size_t>(E) + 15) & ~static_cast<size_t>(15);
+  const size_t qb = (static_cast<size_t>(G) * (D + 8) + 7) & ~static_cast<size_t>(7);  // halves
+  return 2 * E16 * (D + 8) + 4 * static_cast<size_t>(G) * D + 2 * qb + 4 * static_cast<size_t>(G) * E16 + 4 * D;
+}
+
+__device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b, int h, float* sm) {
+  const int L = a.seq.len[b], M = a.seq.mid[b];
+  const int S = a.sink, E = a.sink + a.recent;
+  const int ne = (M > 0) ? E : L;
+  const int D = a.D, du = a.du, dc = a.dc, G = a.G;
+  const int ns = a.seq.nsplit[b];
+  const int E16 = (E + 15) & ~15, RSE = D + 8, QS = D + 8;
+  uint16_t* rows = reinterpret_cast<uint16_t*>(sm);
+  float* qraw = sm + (E16 * RSE) / 2;
+  uint16_t* qb = reinterpret_cast<uint16_t*>(qraw + G * D);
+  float* ps = reinterpret_cast<float*>(qb + ((G * QS + 7) & ~7));
+  int* dl = reinterpret_cast<int*>(ps + G * E16);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, nwv = nt >> 6, l16 = lane & 15, g4 = lane >> 4;
+  const int64_t row0 = a.seq.row0[b];
+  const uint16_t* kxh = static_cast<const uint16_t*>(a.kx) + (row0 + static_cast<int64_t>(h) * L) * du;
+  const uint16_t* vxh = static_cast<const uint16_t*>(a.vx) + (row0 + static_cast<int64_t>(h) * L) * du;
+  const uint16_t* keh = static_cast<const uint16_t*>(a.ke) + (static_cast<int64_t>(b) * a.hkv + h) * E * dc;
+  const uint16_t* veh = static_cast<const uint16_t*>(a.ve) + (static_cast<int64_t>(b) * a.hkv + h) * E * dc;
+  const int nu = du / 8, per_row = nu + dc / 8;  // 16-byte chunks: exact dims first
+  const int nchunk = ne * per_row;
+  auto chunk_src = [&](const uint16_t* xh, const uint16_t* eh, int i) {
+    const int e = i / per_row, w = i % per_row;
+    if (w < nu) {
+      const int t = (M > 0 && e >= S) ? e + M : e;
+      return xh + static_cast<int64_t>(t) * du + w * 8;
+    }
+    return eh + static_cast<int64_t>(e) * dc + (w - nu) * 8;
+  };
+  auto chunk_dst = [&](int i) { return rows + (i / per_row) * RSE + (i % per_row) * 8; };
+  // every load in flight: K to LDS, the last round of V kept in registers
+  uint4 kv[kEdgeLoads], vv[kEdgeLoads];
+  for (int i0 = 0; i0 < nchunk; i0 += kEdgeLoads * nt) {
+#pragma unroll
+    for (int u = 0; u < kEdgeLoads; ++u) {
+      const int i = i0 + tid + u * nt;
+      kv[u] = vv[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < nchunk) {
+        kv[u] = *reinterpret_cast<const uint4*>(chunk_src(kxh, keh, i));
+        vv[u] = *reinterpret_cast<const uint4*>(chunk_src(vxh, veh, i));
+      }
+    }
+    if (i0 == 0) stage_q<uint16_t>(a, b, h, qraw, dl, 1.0f);
+    if (i0 + kEdgeLoads * nt >= nchunk) break;
+#pragma unroll
+    for (int u = 0; u < kEdgeLoads; ++u) {
+      const int i = i0 + tid + u * nt;
+      if (i < nchunk) *reinterpret_cast<uint4*>(chunk_dst(i)) = kv[u];
+    }
+  }
+  if (nchunk == 0) stage_q<uint16_t>(a, b, h, qraw, dl, 1.0f);
+  const int last0 = (nchunk > 0) ? ((nchunk - 1) / (kEdgeLoads * nt)) * (kEdgeLoads * nt) : 0;
+#pragma unroll
+  for (int u = 0; u < kEdgeLoads; ++u) {
+    const int i = last0 + tid + u * nt;
+    if (i < nchunk) *reinterpret_cast<uint4*>(chunk_dst(i)) = kv[u];
+  }
+  __syncthreads();
+  // q in dims order as bf16 (exact: the raw q values are bf16), and the
+  // exact-dim part as the split kernel's operand
+  const int du32 = (du + 31) & ~31;
+  for (int idx = tid; idx < G * D; idx += nt) {
+    const int g = idx / D, j = idx % D;
+    const int d = dl[j];
+    qb[g * QS + j] = (d >= 0 && d < D) ? static_cast<uint16_t>(__float_as_uint(qraw[g * D + d]) >> 16) : 0;
+  }
+  for (int idx = tid; idx < G * du32; idx += nt) {
+    const int g = idx / du32, j = idx % du32;
+    const int64_t i = static_cast<int64_t>(b) * a.hq + h * G + g;
+    uint16_t bits = 0;
+    if (j < du) {
+      const int d = dl[j];
+      if (d >= 0 && d < D) bits = static_cast<const uint16_t*>(a.q)[i * D + d];
+    }
+    static_cast<uint16_t*>(a.Q16)[i * du32 + j] = bits;
+  }
+  __syncthreads();
+  // scores: wave -> token blocks of 16; lane (l16 = token, g4) -> rows 4 g4 + r
+  for (int eb = wave; eb < E16 / 16; eb += nwv) {
+    efloat4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < D / 32; ++kc) {
+      uint4 qa = make_uint4(0u, 0u, 0u, 0u);
+      if (l16 < G) qa = *reinterpret_cast<const uint4*>(qb + l16 * QS + kc * 32 + 8 * g4);
+      const uint4 kb = *reinterpret_cast<const uint4*>(rows + (eb * 16 + l16) * RSE + kc * 32 + 8 * g4);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(ebf16x8, qa), __builtin_bit_cast(ebf16x8, kb),
+                                                    acc, 0, 0, 0);
+    }
+    const int e = eb * 16 + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * g4 + r;
+      if (g < G) ps[g * E16 + e] = (e < ne) ? a.scale * acc[r] : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // V replaces K (the last round from registers, earlier rounds reloaded);
+  // padding rows [ne, E16) are zero
+  for (int i0 = 0; i0 < last0; i0 += nt) {
+    const int i = i0 + tid;
+    *reinterpret_cast<uint4*>(chunk_dst(i)) = *reinterpret_cast<const uint4*>(chunk_src(vxh, veh, i));
+  }
+#pragma unroll
+  for (int u = 0; u < kEdgeLoads; ++u) {
+    const int i = last0 + tid + u * nt;
+    if (i < nchunk) *reinterpret_cast<uint4*>(chunk_dst(i)) = vv[u];
+  }
+  for (int i = tid; i < (E16 - ne) * (D / 8); i += nt)
+    *reinterpret_cast<uint4*>(rows + (ne + i / (D / 8)) * RSE + (i % (D / 8)) * 8) = make_uint4(0u, 0u, 0u, 0u);
+  // softmax of each row (one wave per row); probabilities of padding tokens are 0
+  for (int g = wave; g < G; g += nwv) {
+    float m = -INFINITY;
+    for (int e = lane; e < ne; e += 64) m = fmaxf(m, ps[g * E16 + e]);
+    m = wave_max(m);
+    float l = 0.0f;
+    for (int e = lane; e < E16; e += 64) {
+      const float pe = (e >= ne || m == -INFINITY) ? 0.0f : __expf(ps[g * E16 + e] - m);
+      ps[g * E16 + e] = pe;
+      l += pe;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G + g) * ns + ns - 1) * a.RS;
+      P[0] = m;
+      P[1] = l;
+    }
+  }
+  __syncthreads();
+  // values: wave -> 16-dim blocks; A = P (rows l16, tokens 4 g4 .. +3) as
+  // bf16 hi + lo, B = V read transposed (tokens 4 g4 .. +3 of dim l16)
+  float* P0 = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G) * ns + ns - 1) * a.RS + 2;
+  const int64_t prs = static_cast<int64_t>(ns) * a.RS;
+  for (int nb = wave; nb < D / 16; nb += nwv) {
+    efloat4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < E16 / 16; ++kt) {
+      float4 p4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (l16 < G) p4 = *reinterpret_cast<const float4*>(ps + l16 * E16 + kt * 16 + 4 * g4);
+      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+      eshort4 hi4, lo4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint16_t hb = edge_bf16_rne(pv[j]);
+        hi4[j] = static_cast<short>(hb);
+        lo4[j] = static_cast<short>(edge_bf16_rne(pv[j] - __uint_as_float(static_cast<uint32_t>(hb) << 16)));
+      }
+      const eshort4 vb = edge_tr4(rows + (kt * 16 + 4 * g4 + (l16 >> 2)) * RSE + nb * 16 + 4 * (l16 & 3));
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi4, vb, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo4, vb, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * g4 + r;
+      // partial layout [m, l, o_U(du), o_E(dc), W]: dim j of the row sits at 2 + j
+      if (g < G) P0[g * prs + nb * 16 + l16] = acc[r];
+    }
+  }
+}
+
 // Blocks [0, nedge) are edge blocks (MFMA path), the rest A blocks.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a, int nedge, int chunks) {
@@ -447,8 +633,12 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a, int nedg
   int blk = blockIdx.x;
   if (blk < nedge) {
     if (a.edge_split) {
-      if (a.G >= 4) prep_edge_block<4>(a, blk / a.hkv, blk % a.hkv, smem);
-      else prep_edge_block<1>(a, blk / a.hkv, blk % a.hkv, smem);
+      if (a.du % 8 == 0 && a.dc % 8 == 0 && a.D % 32 == 0 && a.G <= 16)
+        prep_edge_block_mfma(a, blk / a.hkv, blk % a.hkv, smem);
+      else if (a.G >= 4)
+        prep_edge_block<4>(a, blk / a.hkv, blk % a.hkv, smem);
+      else
+        prep_edge_block<1>(a, blk / a.hkv, blk % a.hkv, smem);
     }
     return;
   }
@@ -898,7 +1088,9 @@ size_t decode_prep_a_smem(const DecodeArgs& a) {
 }
 size_t decode_edge_smem(const DecodeArgs& a) {
   const size_t E = static_cast<size_t>(a.sink) + a.recent;  // upper bound of the retained tokens
-  return sizeof(uint16_t) * E * (a.D + 8) + sizeof(float) * (2 * static_cast<size_t>(a.G) * a.D + a.G * E + a.D);
+  const size_t valu = sizeof(uint16_t) * E * (a.D + 8) +
+                      sizeof(float) * (2 * static_cast<size_t>(a.G) * a.D + a.G * E + a.D);
+  return std::max(valu, edge_mfma_smem_bytes(a.sink + a.recent, a.G, a.D));
 }
 size_t decode_prep_smem(const DecodeArgs& a) {
   size_t n = a.prep_a ? decode_prep_a_smem(a) : 0;
