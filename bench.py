@@ -73,6 +73,33 @@ def measured_traffic(workload, kernel):
     return e.get("bytes_per_launch")
 
 
+def box_peaks(torch):
+    """Achieved streaming-copy bandwidth and fp16 GEMM rate on this GPU."""
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+    n = (2 << 30) // 4  # 2 GiB read + 2 GiB written
+    src = torch.empty(n, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 20)
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda", dtype=torch.float16)
+    b = torch.randn(m, m, device="cuda", dtype=torch.float16)
+    t_mm = timed(lambda: torch.matmul(a, b), 20)
+    return {"copy_GBps": 2 * n * 4 / t_copy / 1e9, "copy_frac_of_8TBps": 2 * n * 4 / t_copy / 8e12,
+            "fp16_gemm_TFLOPs": 2.0 * m ** 3 / t_mm / 1e12, "fp16_gemm_frac_of_2.5PF": 2.0 * m ** 3 / t_mm / 2.5e15,
+            "gemm": "torch.matmul fp16 %dx%dx%d" % (m, m, m), "copy": "torch copy_ of 2 GiB fp32"}
+
+
 def cpu_baseline(w, scale, seconds):
     """The oracle (fp64 numpy) on the same workload, repeated ~`seconds`."""
     from oracle import batch as ob
@@ -107,6 +134,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay one HIP graph per call and input copy (default: launch every call from the host, "
                          "which measures faster on this ROCm)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure what the box reaches: a streaming copy (HBM GB/s) and a large fp16 "
+                         "GEMM (hipBLASLt through torch, MFMA TFLOP/s), as context for the roofline fractions")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy kernel over MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -122,6 +152,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.peaks:
+        print(json.dumps(box_peaks(torch)))
+        return
     if args.calibrate_copy:
         # torch elementwise negation: reads and writes exactly n * 4 bytes
         n = args.calibrate_copy * (1 << 20) // 4
@@ -251,6 +284,17 @@ def main():
         roof = {"kernel": "fa_project", "bound": "mfma", "achieved": ach,
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_F16_PEAK_TFLOPS,
                 "traffic": measured_traffic(args.workload, "fa_project")}
+
+    # context: the same achieved rate against what the box reaches outside the
+    # library (streaming copy / hipBLASLt GEMM, measured by bench.py --peaks)
+    try:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "box_peaks.json")) as f:
+            bp = json.load(f)
+        box = bp["copy_GBps"] if roof["unit"] == "GB/s" else bp["fp16_gemm_TFLOPs"]
+        roof["box_peak"] = box
+        roof["frac_of_box_peak"] = roof["achieved"] / box
+    except (OSError, ValueError, KeyError):
+        pass
 
     cpu = None
     if not args.no_cpu_baseline:
