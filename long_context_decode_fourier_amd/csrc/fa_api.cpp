@@ -153,20 +153,19 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
   if (!p->f16 || a.ncols == 0) return FA_OK;
   if (sh.Dc % 4) return fail(FA_ERR_SHAPE, "bf16 projection needs n_comp_dims %% 4 == 0 (got %d)", sh.Dc);
 
-  // Large tiles (256 x 256, one 8-wave block per CU) for large contractions;
-  // else 128 x 64 tiles (2 waves), several blocks per CU.
+  // Large square tiles (256 x 256) for large contractions; else tall tiles
+  // (512 coefficient rows x 64 columns), which load and convert each cache
+  // value once for all the coefficients of a small k.  Both are 8-wave
+  // blocks, one per CU.
   double flops = 0.0;
   for (int b = 0; b < sh.B; ++b) flops += 2.0 * sh.M[b] * sh.k * a.ncols;
   const bool big = flops > 1.0e11;
-  a.tk = big ? 256 : 128;
+  a.tk = big ? 256 : 512;
   a.tn = big ? 256 : 64;
   a.nktiles = (sh.k + a.tk - 1) / a.tk;
   a.nctiles = (a.ncols + a.tn - 1) / a.tn;
   const int tiles = a.nktiles * a.nctiles;
-  // Co-resident blocks: one 8-wave block per CU for large tiles; small
-  // 2-wave blocks are latency-bound, so six per CU (three waves per SIMD, the
-  // kernel's register-limited occupancy) overlap their steps.
-  const int slots = big ? kNumCU : 6 * kNumCU;
+  const int slots = kNumCU;
   int64_t total_steps = 0;
   for (int b = 0; b < sh.B; ++b) total_steps += (sh.M[b] + fa::kProjTT - 1) / fa::kProjTT;
   bool any_split = false;

@@ -28,8 +28,7 @@ struct ProjArgs {
   SeqTable seq;      // item0/nsplit: items = tiles * nsplit; chunk = positions per split
 };
 
-// Supported tiles (tk x tn): 256 x 256, 128 x 128 and 128 x 64.
-bool project_tile_supported(int tk, int tn);
+// Supported tiles (tk x tn): 256 x 256 and 512 x 64 (tall).
 hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s);
 hipError_t launch_project_f32(const ProjArgs& a, hipStream_t s);
 

@@ -22,6 +22,7 @@
 // fp32 inputs take a VALU kernel with correctly rounded phases (sincospi per
 // value) and compensated summation, which keeps coefficients within 1e-5.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -308,6 +309,231 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
       }
 }
 
+// Tall tiles for few coefficients: the 8 waves of a block are stacked along
+// the coefficient rows (wave w owns rows 64 w .. 64 w + 63 of a 512-row tile)
+// and share one cache tile of 64 columns, so each cache value is loaded and
+// converted once per block and each basis row is generated by one wave.  A
+// block per CU; to keep enough bytes in flight for HBM, the cache rows are
+// prefetched D steps ahead into registers.  Every load is unconditional (a
+// position past the item's end reads the last valid row and is zeroed when it
+// is staged), so the waits for a step count the loads of the later steps
+// instead of draining them.
+//
+// Loader: thread (cg = tid % 16, pp = tid / 16) owns columns 4 cg .. 4 cg + 3
+// at positions 2 pp and 2 pp + 1 of a step and stores each column's pair as
+// one 4-byte word of the column-major LDS layout of project_f16_kernel.
+constexpr int kTallWaves = 8;
+constexpr int kTallTN = 64;
+
+template <int RB, int D>
+__global__ __launch_bounds__(64 * kTallWaves, 2) void project_tall_kernel(ProjArgs a) {
+  constexpr int CB = kTallTN / 32;
+  constexpr int TK = kTallWaves * RB * 32;
+  static_assert((kTallTN / 4) * (kProjTT / 2) == 64 * kTallWaves, "one column quad x position pair per thread");
+  static_assert(D == 2 || D == 4, "the unrolled step loop keeps slots and LDS buffer parity static");
+
+  __shared__ __attribute__((aligned(16))) _Float16 xts[2][kTallTN * kLdsStride];
+
+  ProjItem it;
+  if (!proj_item(a, a.nitems, blockIdx.x, &it)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool active = it.ktile * TK + wave * (RB * 32) < a.k;
+  const int M = it.M;
+  const int L = a.seq.len[it.b];
+  const int64_t row0 = a.seq.row0[it.b];
+
+  // ---- loader (a column past ncols reads column 0 and is zeroed)
+  const int cg = tid & 15, pp = tid >> 4;
+  const int col0 = it.ctile * kTallTN + cg * 4;
+  const bool col_ok = col0 < a.ncols;
+  const int colc = col_ok ? col0 : 0;
+  const int blk = colc / a.dc, c0 = colc % a.dc;
+  const int mat = blk / a.hkv, h = blk % a.hkv;
+  const uint16_t* xb = static_cast<const uint16_t*>(mat ? a.x[1] : a.x[0]) +
+                       (row0 + static_cast<int64_t>(h) * L + a.sink) * a.dc + c0;
+  const int last = it.t_end - 1;
+  uint2 raw[D][2];
+  auto load = [&](int i, uint2 (&r)[2]) {
+    const int q = it.t_begin + i * kProjTT + 2 * pp;
+    r[0] = *reinterpret_cast<const uint2*>(xb + static_cast<int64_t>(min(q, last)) * a.dc);
+    r[1] = *reinterpret_cast<const uint2*>(xb + static_cast<int64_t>(min(q + 1, last)) * a.dc);
+  };
+  // bf16 -> fp32 -> fp16 (exact for |x| in [2^-14, 65504]); positions past
+  // the item's end (and columns past ncols) become zeros
+  auto stage = [&](int i, const uint2 (&r)[2], _Float16* xt) {
+    const int q = it.t_begin + i * kProjTT + 2 * pp;
+    const uint32_t m0 = (col_ok && q <= last) ? 0xFFFFFFFFu : 0u;
+    const uint32_t m1 = (col_ok && q + 1 <= last) ? 0xFFFFFFFFu : 0u;
+    const uint32_t ax = r[0].x & m0, ay = r[0].y & m0, bx = r[1].x & m1, by = r[1].y & m1;
+    uint32_t w[4];
+    w[0] = pack_f16(__uint_as_float(ax << 16), __uint_as_float(bx << 16));
+    w[1] = pack_f16(__uint_as_float(ax & 0xFFFF0000u), __uint_as_float(bx & 0xFFFF0000u));
+    w[2] = pack_f16(__uint_as_float(ay << 16), __uint_as_float(by << 16));
+    w[3] = pack_f16(__uint_as_float(ay & 0xFFFF0000u), __uint_as_float(by & 0xFFFF0000u));
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      *reinterpret_cast<uint32_t*>(&xt[xt_off(cg * 4 + qq, pp >> 2) + 2 * (pp & 3)]) = w[qq];
+  };
+
+  // ---- basis generator state, one coefficient row per lane and row block
+  const float invM = 1.0f / static_cast<float>(M);
+  float c2[RB], off[RB];
+  int fr[RB], ph[RB], d64[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int n = it.ktile * TK + wave * (RB * 32) + rb * 32 + (lane & 31);
+    const int ne = min(n, a.k - 1);
+    const int f = basis_freq(ne) % M;
+    float sn, cs;
+    sincos_phase(f, M, &sn, &cs);
+    c2[rb] = 2.0f * cs;
+    off[rb] = basis_is_cos(ne) ? 0.25f : 0.0f;
+    fr[rb] = f;
+    ph[rb] = phase_mod(f, it.t_begin + 32 * (lane >> 5), M);
+    d64[rb] = phase_mod(f, kProjTT, M);
+  }
+  floatx16 acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
+
+  // basis operand of sub-step s (same runs as project_f16_kernel: seeded at
+  // s = 0 from the exact phases of the step, continued by the recurrence)
+  float yp[RB], yc[RB];
+  auto gen_a = [&](int s, half8* av) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float v[8];
+      if (s == 0) {
+        const int r0 = ph[rb];
+        int r1 = r0 + fr[rb];
+        if (r1 >= M) r1 -= M;
+        v[0] = sin_rev(fmaf(static_cast<float>(r0), invM, off[rb]));
+        v[1] = sin_rev(fmaf(static_cast<float>(r1), invM, off[rb]));
+#pragma unroll
+        for (int e = 2; e < 8; ++e) v[e] = fmaf(c2[rb], v[e - 1], -v[e - 2]);
+      } else {
+        v[0] = fmaf(c2[rb], yc[rb], -yp[rb]);
+        v[1] = fmaf(c2[rb], v[0], -yc[rb]);
+#pragma unroll
+        for (int e = 2; e < 8; ++e) v[e] = fmaf(c2[rb], v[e - 1], -v[e - 2]);
+      }
+      yp[rb] = v[6];
+      yc[rb] = v[7];
+      const uint4 bits = make_uint4(pack_f16(v[0], v[1]), pack_f16(v[2], v[3]),
+                                    pack_f16(v[4], v[5]), pack_f16(v[6], v[7]));
+      av[rb] = __builtin_bit_cast(half8, bits);
+    }
+  };
+
+  // one step of MFMAs on the staged tile xt (the sub-step pipeline of
+  // project_f16_kernel), then the basis phases move on by one step
+  auto compute = [&](const _Float16* xt) {
+    auto read_b = [&](int s, half8* bv) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        bv[cb] = *reinterpret_cast<const half8*>(&xt[xt_off(cb * 32 + (lane & 31), 4 * (lane >> 5) + s)]);
+    };
+    if (active) {
+      half8 bcur[CB], bnxt[CB], acur[RB], anxt[RB];
+      read_b(0, bcur);
+      gen_a(0, acur);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) {
+          read_b(s + 1, bnxt);
+          gen_a(s + 1, anxt);
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(acur[rb], bcur[cb], acc[rb][cb], 0, 0, 0);
+        if (s < 3) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) bcur[cb] = bnxt[cb];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acur[rb] = anxt[rb];
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ph[rb] += d64[rb];
+      if (ph[rb] >= M) ph[rb] -= M;
+    }
+  };
+
+  // Step i's rows sit in raw[i % D] from D steps before they are staged;
+  // step i is staged into buffer i & 1 one step before its MFMAs, and its
+  // slot is refilled with step i + D at once.  Stages and loads past the last
+  // step touch only valid rows and a buffer nobody reads.
+  const int nsteps = (it.t_end - it.t_begin + kProjTT - 1) / kProjTT;
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, raw[d]);
+  stage(0, raw[0], xts[0]);
+  load(D, raw[0]);
+  __syncthreads();
+  // (whole rounds of D steps first: a loop with an early exit would merge
+  // its exit path into the loop head and make every wait there a full drain)
+  auto step = [&](int i, auto dc) {
+    constexpr int d = decltype(dc)::value;
+    compute(xts[d & 1]);
+    stage(i + 1, raw[(d + 1) % D], xts[(d + 1) & 1]);
+    load(i + 1 + D, raw[(d + 1) % D]);
+    __syncthreads();
+  };
+  int i0 = 0;
+  for (; i0 + D <= nsteps; i0 += D) {
+    step(i0, std::integral_constant<int, 0>());
+    step(i0 + 1, std::integral_constant<int, 1>());
+    if constexpr (D > 2) {
+      step(i0 + 2, std::integral_constant<int, 2>());
+      step(i0 + 3, std::integral_constant<int, 3>());
+    }
+  }
+  if (i0 < nsteps) step(i0, std::integral_constant<int, 0>());
+  if (i0 + 1 < nsteps) step(i0 + 1, std::integral_constant<int, 1>());
+  if constexpr (D > 2) {
+    if (i0 + 2 < nsteps) step(i0 + 2, std::integral_constant<int, 2>());
+  }
+
+  if (a.direct) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = it.ktile * TK + wave * (RB * 32) + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = it.ctile * kTallTN + cb * 32 + (lane & 31);
+          if (n < a.k && col < a.ncols) {
+            const int f = basis_freq(n);
+            const float alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
+                                                       : sqrtf(2.0f / static_cast<float>(M));
+            const int cblk = col / a.dc, c = col % a.dc, cmat = cblk / a.hkv, ch = cblk % a.hkv;
+            (cmat ? a.out[1] : a.out[0])[((static_cast<int64_t>(it.b) * a.hkv + ch) * a.k + n) * a.dc + c] =
+                alpha * acc[rb][cb][r];
+          }
+        }
+    return;
+  }
+  float* P = a.partial + static_cast<int64_t>(it.slot) * TK * kTallTN;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int nl = wave * (RB * 32) + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int cl = cb * 32 + (lane & 31);
+        if (it.ktile * TK + nl < a.k) P[nl * kTallTN + cl] = acc[rb][cb][r];
+      }
+}
+
 // Retained rows (sink, then recent; all rows when L <= sink + recent) of
 // kc (vc), copied to ke (ve) in 16-, 8- or 4-byte words: grid-stride over
 // (sequence, matrix, KV head, retained row, word).
@@ -349,31 +575,24 @@ __device__ inline void edge_copy(const EdgeArgs& a, int64_t first, int64_t strid
 }
 
 // Fixed-order sum of the split partials of each tile element, scaled by the
-// basis normalisation, scattered to ck / cv.  One thread per 4 consecutive
-// tile columns: grid-stride over (sequence, tile, row, column quad).
-// Sequences without middle get zeros.
+// basis normalisation, scattered to ck / cv.  Block (chunk, tile, sequence)
+// covers 256 / (tn / 4) rows of a tile, one thread per 4 consecutive columns
+// (tn / 4 divides 256).  Sequences without middle get zeros.
 __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a, EdgeArgs ea) {
-  const int tk = a.tk, tn = a.tn, tn4 = tn / 4;
-  const int tiles = a.nktiles * a.nctiles;
-  const int64_t per_seq = static_cast<int64_t>(tiles) * tk * tn4;
-  const int64_t total = per_seq * a.nseq;
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
-       g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int b = static_cast<int>(g / per_seq);
-    int64_t r = g - b * per_seq;
-    const int q4 = static_cast<int>(r % tn4);
-    r /= tn4;
-    const int nl = static_cast<int>(r % tk);
-    const int tile = static_cast<int>(r / tk);
-    const int kt = tile / a.nctiles, ct = tile % a.nctiles;
-    const int n = kt * tk + nl;
-    const int col0 = ct * tn + 4 * q4;
-    if (n >= a.k || col0 >= a.ncols) continue;
+  const int tn4 = a.tn / 4, rows = 256 / tn4;
+  const int b = blockIdx.z, tile = blockIdx.y;
+  const int nl = blockIdx.x * rows + static_cast<int>(threadIdx.x) / tn4;
+  const int q4 = static_cast<int>(threadIdx.x) % tn4;
+  const int kt = tile / a.nctiles, ct = tile % a.nctiles;
+  const int n = kt * a.tk + nl;
+  const int col0 = ct * a.tn + 4 * q4;
+  if (nl < a.tk && n < a.k && col0 < a.ncols) {
     const int ns = a.seq.nsplit[b];
-    const float* P = a.partial + (static_cast<int64_t>(a.seq.item0[b] + tile * ns) * tk + nl) * tn + 4 * q4;
+    const float* P = a.partial + (static_cast<int64_t>(a.seq.item0[b] + tile * ns) * a.tk + nl) * a.tn + 4 * q4;
+    const int64_t stride = static_cast<int64_t>(a.tk) * a.tn;
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int sp = 0; sp < ns; ++sp) {
-      const float4 v = *reinterpret_cast<const float4*>(P + static_cast<int64_t>(sp) * tk * tn);
+      const float4 v = *reinterpret_cast<const float4*>(P + sp * stride);
       sum.x += v.x;
       sum.y += v.y;
       sum.z += v.z;
@@ -386,18 +605,17 @@ __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a, EdgeArg
       alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
                                      : sqrtf(2.0f / static_cast<float>(M));
     }
-    // Dc % 4 == 0: the 4 columns share (matrix, KV head)
+    // Dc % 4 == 0: the 4 columns share (matrix, KV head) and are 16-byte aligned
     const int blk = col0 / a.dc, c = col0 % a.dc, mat = blk / a.hkv, h = blk % a.hkv;
     float* o = (mat ? a.out[1] : a.out[0]) + ((static_cast<int64_t>(b) * a.hkv + h) * a.k + n) * a.dc + c;
-    o[0] = alpha * sum.x;
-    o[1] = alpha * sum.y;
-    o[2] = alpha * sum.z;
-    o[3] = alpha * sum.w;
+    *reinterpret_cast<float4*>(o) = make_float4(alpha * sum.x, alpha * sum.y, alpha * sum.z, alpha * sum.w);
   }
   // the retained rows ride along (no launch of their own)
-  if (ea.nmat > 0)
-    edge_copy(ea, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
-              static_cast<int64_t>(gridDim.x) * blockDim.x);
+  if (ea.nmat > 0) {
+    const int64_t flat = (static_cast<int64_t>(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    edge_copy(ea, flat * blockDim.x + threadIdx.x,
+              static_cast<int64_t>(gridDim.x) * gridDim.y * gridDim.z * blockDim.x);
+  }
 }
 
 // fp32 inputs: one block per (sequence, matrix, KV head, kF32Coefs
@@ -480,21 +698,15 @@ int64_t edge_words(const EdgeArgs& a) {
 
 }  // namespace
 
-// Tile configurations of the 16-bit kernel: 256 x 256 (8 waves) for large
-// problems, 128 x 64 (2 waves) when large tiles would leave CUs idle.
-bool project_tile_supported(int tk, int tn) {
-  return (tk == 256 && tn == 256) || (tk == 128 && tn == 128) || (tk == 128 && tn == 64);
-}
-
+// Tile configurations of the 16-bit path: 256 x 256 square tiles for large
+// contractions, 512 x 64 tall tiles otherwise (both 8-wave blocks).
 hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
   if (nitems == 0) return hipSuccess;
   const int blocks = (nitems + kXcds - 1) / kXcds * kXcds;
   if (a.tk == 256 && a.tn == 256)
     hipLaunchKernelGGL((project_f16_kernel<4, 2, 2, 4>), dim3(blocks), dim3(512), 0, s, a);
-  else if (a.tk == 128 && a.tn == 128)
-    hipLaunchKernelGGL((project_f16_kernel<2, 1, 2, 4>), dim3(blocks), dim3(128), 0, s, a);
-  else if (a.tk == 128 && a.tn == 64)
-    hipLaunchKernelGGL((project_f16_kernel<2, 1, 2, 2>), dim3(blocks), dim3(128), 0, s, a);
+  else if (a.tk == kTallWaves * 64 && a.tn == kTallTN)
+    hipLaunchKernelGGL((project_tall_kernel<2, 4>), dim3(blocks), dim3(64 * kTallWaves), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -502,11 +714,13 @@ hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
 
 hipError_t launch_project_reduce(const ProjArgs& a, const EdgeArgs& ea, hipStream_t s) {
   if (a.direct) return hipSuccess;
-  const int64_t quads = static_cast<int64_t>(a.nseq) * a.nktiles * a.nctiles * a.tk * (a.tn / 4);
-  const int64_t work = std::max(quads, ea.nmat > 0 ? edge_words(ea) : 0);
-  if (work == 0) return hipSuccess;
-  const int blocks = static_cast<int>(std::min<int64_t>((work + 255) / 256, 8 * 2048));
-  hipLaunchKernelGGL(project_reduce_kernel, dim3(blocks), dim3(256), 0, s, a, ea);
+  const int tn4 = a.tn / 4;
+  if (tn4 <= 0 || 256 % tn4 != 0) return hipErrorInvalidValue;
+  const int rows = 256 / tn4;
+  const int tiles = a.nktiles * a.nctiles;
+  if (a.nseq <= 0 || tiles <= 0) return hipSuccess;
+  const dim3 grid((a.tk + rows - 1) / rows, tiles, a.nseq);
+  hipLaunchKernelGGL(project_reduce_kernel, grid, dim3(256), 0, s, a, ea);
   return hipGetLastError();
 }
 
