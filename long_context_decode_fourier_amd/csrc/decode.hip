@@ -736,7 +736,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         for (int r = 0; r < R; ++r) {
           if (r >= a.rows) break;
           const int64_t base = (row0 + static_cast<int64_t>(kh[r]) * L + t) * a.du;
-          for (int d = d0; d < d1; ++d) acc[r] = fmaf(qs[r * a.D + d], ld<T>(a.kx, base + d), acc[r]);
+          // batches of 8 loads in flight (the index is clamped, not branched on)
+          for (int dd = d0; dd < d1; dd += 8) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = ld<T>(a.kx, base + min(dd + i, d1 - 1));
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (dd + i < d1) acc[r] = fmaf(qs[r * a.D + dd + i], v[i], acc[r]);
+          }
         }
         if (comp) {
           const bool edge = (M == 0) || t < S || t >= S + M;
@@ -747,8 +755,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             for (int r = 0; r < R; ++r) {
               if (r >= a.rows) break;
               const int64_t base = ((static_cast<int64_t>(b) * a.hkv + kh[r]) * E + e) * a.dc;
-              for (int c = c0; c < c1; ++c)
-                acc[r] = fmaf(qs[r * a.D + a.du + c], ld<T>(a.ke, base + c), acc[r]);
+              for (int cc = c0; cc < c1; cc += 8) {
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = ld<T>(a.ke, base + min(cc + i, c1 - 1));
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                  if (cc + i < c1) acc[r] = fmaf(qs[r * a.D + a.du + cc + i], v[i], acc[r]);
+              }
             }
           } else {
             const int tau = t - S;
@@ -809,10 +823,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       const int r = idx / a.du, d = idx % a.du;
       float o = oacc[j] * corr[r];
       const int64_t base = (row0 + static_cast<int64_t>(kh[r]) * L + tile0) * a.du + d;
-      for (int tl = 0; tl < nt; ++tl) o = fmaf(ps[tl * R + r], ld<T>(a.vx, base + static_cast<int64_t>(tl) * a.du), o);
+      // batches of 16 tokens' loads in flight (clamped index, no branch)
+      for (int t0 = 0; t0 < nt; t0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = ld<T>(a.vx, base + static_cast<int64_t>(min(t0 + i, nt - 1)) * a.du);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (t0 + i < nt) o = fmaf(ps[(t0 + i) * R + r], v[i], o);
+      }
       oacc[j] = o;
     }
     if (comp) {
+      // only tiles that hold retained tokens read ve
+      const bool any_edge = M == 0 || tile0 < S || tile0 + nt > S + M;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int idx = tid + 256 * j;
@@ -820,13 +844,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const int r = idx / a.dc, c = idx % a.dc;
         float o = eacc[j] * corr[r];
         const int64_t base = (static_cast<int64_t>(b) * a.hkv + kh[r]) * E * a.dc + c;
-        for (int tl = 0; tl < nt; ++tl) {
-          const int t = tile0 + tl;
-          if (M == 0 || t < S || t >= S + M) {
-            const int e = (M == 0 || t < S) ? t : t - M;
-            o = fmaf(ps[tl * R + r], ld<T>(a.ve, base + static_cast<int64_t>(e) * a.dc), o);
+        if (any_edge)
+          for (int t0 = 0; t0 < nt; t0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int t = tile0 + min(t0 + i, nt - 1);
+              const bool edge = M == 0 || t < S || t >= S + M;
+              const int e = !edge ? 0 : ((M == 0 || t < S) ? t : t - M);
+              v[i] = ld<T>(a.ve, base + static_cast<int64_t>(e) * a.dc);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int t = tile0 + t0 + i;
+              if (t0 + i < nt && (M == 0 || t < S || t >= S + M)) o = fmaf(ps[(t0 + i) * R + r], v[i], o);
+            }
           }
-        }
         eacc[j] = o;
       }
     }

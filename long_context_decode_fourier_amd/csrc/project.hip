@@ -619,14 +619,19 @@ __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a, EdgeArg
 }
 
 // fp32 inputs: one block per (sequence, matrix, KV head, kF32Coefs
-// coefficients; few per block, so that small problems still spread over many
-// CUs).
-// Thread (c, lane-of-8 positions) sums phi_n(tau) x[tau][c] over its residue
-// class of tau with Kahan compensation; the 8 partial sums are added in a
-// fixed tree.  The basis value is computed from the exact integer phase.
-constexpr int kF32Coefs = 2;
+// coefficients); few per block, so that small problems still spread over many
+// CUs.  The middle positions are walked in chunks of kF32Chunk: the chunk's
+// basis values are computed once into LDS (exact integer phase, sincospi) and
+// shared by the 32 column lanes; each thread (column lane, position lane of
+// 8) prefetches its 8 cache values of the next chunk while the current one is
+// summed, with Kahan compensation; the 8 position lanes are added in a fixed
+// tree.
+constexpr int kF32Coefs = 4;
+constexpr int kF32Chunk = 64;
+static_assert(kF32Coefs * kF32Chunk == 256, "one basis value per thread and chunk");
 
 __global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
+  __shared__ float phis[kF32Coefs][kF32Chunk];
   __shared__ float red[8][kF32Coefs][32];
   const int ntile = (a.k + kF32Coefs - 1) / kF32Coefs;
   int g = blockIdx.x;
@@ -640,30 +645,54 @@ __global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
   const float* X = static_cast<const float*>(a.x[mat]) +
                    (a.seq.row0[b] + static_cast<int64_t>(h) * L + a.sink) * a.dc;
   float* out = a.out[mat] + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc;
+  // this thread's basis value of each chunk: coefficient bn, position bt
+  const int bn = min(nt * kF32Coefs + static_cast<int>(threadIdx.x) / kF32Chunk, a.k - 1);
+  const int bt = static_cast<int>(threadIdx.x) % kF32Chunk;
+  const int bf = M > 0 ? basis_freq(bn) % M : 0;
+  const bool bcos = basis_is_cos(bn);
   for (int c0 = 0; c0 < a.dc; c0 += 32) {
     const int c = c0 + cl;
+    const bool col_ok = c < a.dc;
+    const float* xc = X + (col_ok ? c : 0);
     float sum[kF32Coefs], comp[kF32Coefs];
 #pragma unroll
     for (int i = 0; i < kF32Coefs; ++i) sum[i] = comp[i] = 0.0f;
-    if (c < a.dc) {
-      for (int tau = tl; tau < M; tau += 8) {
-        const float x = X[static_cast<int64_t>(tau) * a.dc + c];
+    // positions p0 + tl + 8 i of a chunk; reads past the middle are clamped
+    // to its last row (and weighted by a zero basis value)
+    float xv[8], xn[8];
+    auto load_x = [&](int p0, float* dst) {
 #pragma unroll
-        for (int i = 0; i < kF32Coefs; ++i) {
-          const int n = min(nt * kF32Coefs + i, a.k - 1);
-          float s, co;
-          sincos_phase(phase_mod(basis_freq(n), tau, M), M, &s, &co);
-          const float term = x * (basis_is_cos(n) ? co : s) - comp[i];
-          const float t = sum[i] + term;
-          comp[i] = (t - sum[i]) - term;
-          sum[i] = t;
+      for (int i = 0; i < 8; ++i) dst[i] = xc[static_cast<int64_t>(min(p0 + tl + 8 * i, M - 1)) * a.dc];
+    };
+    if (M > 0) load_x(0, xv);
+    for (int p0 = 0; p0 < M; p0 += kF32Chunk) {
+      {
+        const int tau = p0 + bt;
+        float sn = 0.0f, cs = 0.0f;
+        if (tau < M) sincos_phase(phase_mod(bf, tau, M), M, &sn, &cs);
+        phis[threadIdx.x / kF32Chunk][bt] = bcos ? cs : sn;
+      }
+      if (p0 + kF32Chunk < M) load_x(p0 + kF32Chunk, xn);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = col_ok ? xv[i] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kF32Coefs; ++j) {
+          const float term = x * phis[j][tl + 8 * i] - comp[j];
+          const float t = sum[j] + term;
+          comp[j] = (t - sum[j]) - term;
+          sum[j] = t;
         }
       }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] = xn[i];
     }
 #pragma unroll
     for (int i = 0; i < kF32Coefs; ++i) red[tl][i][cl] = sum[i];
     __syncthreads();
-    if (tl == 0 && c < a.dc) {
+    if (tl == 0 && col_ok) {
 #pragma unroll
       for (int i = 0; i < kF32Coefs; ++i) {
         const int n = nt * kF32Coefs + i;
