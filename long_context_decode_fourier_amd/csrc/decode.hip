@@ -948,6 +948,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // dims) applies C_V to the merged W of the head's query rows and writes those
 // dims of out.
 constexpr int kMergeRows = 4;
+constexpr int kMergeHeld = 2;    // split weights per lane kept in registers
+constexpr int kMergeBatch = 32;  // split loads in flight per thread
 
 __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   extern __shared__ float smem[];  // [ns] weights
@@ -961,13 +963,33 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   if (blockIdx.y * 256 >= nvec) return;  // uniform per block
   const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS;
   // every wave forms the split weights itself (wave reductions, no block
-  // barrier); wave 0 publishes them for the sums below
+  // barrier); wave 0 publishes them for the sums below.  The (m, l) pairs of
+  // a lane's first kMergeHeld splits are read once, in one round of loads
+  // (clamped index, no branch); splits beyond 64 kMergeHeld are read again.
   const int lane = threadIdx.x & 63;
+  float mh[kMergeHeld], lh[kMergeHeld];
+#pragma unroll
+  for (int j = 0; j < kMergeHeld; ++j) {
+    const int s = lane + 64 * j;
+    const int64_t o = static_cast<int64_t>(min(s, ns - 1)) * a.RS;
+    mh[j] = P[o];
+    lh[j] = P[o + 1];
+    if (s >= ns) mh[j] = -INFINITY;
+  }
   float mx = -INFINITY;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, P[static_cast<int64_t>(s) * a.RS]);
+#pragma unroll
+  for (int j = 0; j < kMergeHeld; ++j) mx = fmaxf(mx, mh[j]);
+  for (int s = lane + 64 * kMergeHeld; s < ns; s += 64) mx = fmaxf(mx, P[static_cast<int64_t>(s) * a.RS]);
   mx = wave_max(mx);
   float lsum = 0.0f;
-  for (int s = lane; s < ns; s += 64) {
+#pragma unroll
+  for (int j = 0; j < kMergeHeld; ++j) {
+    const int s = lane + 64 * j;
+    const float w = (mh[j] == -INFINITY) ? 0.0f : __expf(mh[j] - mx);
+    if (threadIdx.x < 64 && s < ns) smem[s] = w;
+    lsum += w * lh[j];
+  }
+  for (int s = lane + 64 * kMergeHeld; s < ns; s += 64) {
     const float m = P[static_cast<int64_t>(s) * a.RS];
     const float w = (m == -INFINITY) ? 0.0f : __expf(m - mx);
     if (threadIdx.x < 64) smem[s] = w;
@@ -986,12 +1008,22 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     if (idx < a.du + a.dc) s_lo = ns - 1;
     else s_hi = ns - 1;
   }
-  // fixed-order sum over the splits, 16 loads in flight
+  // fixed-order sum over the splits: whole batches of kMergeBatch loads in
+  // flight, then batches of 16 with a clamped index (no branch around a load,
+  // so the waits count instead of draining)
   float v = 0.0f;
-  for (int s0 = s_lo; s0 < s_hi; s0 += 16) {
+  int s0 = s_lo;
+  for (; s0 + kMergeBatch <= s_hi; s0 += kMergeBatch) {
+    float x[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) x[j] = Pi[static_cast<int64_t>(s0 + j) * a.RS];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) v = fmaf(smem[s0 + j], x[j], v);
+  }
+  for (; s0 < s_hi; s0 += 16) {
     float x[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = (s0 + j < s_hi) ? Pi[static_cast<int64_t>(s0 + j) * a.RS] : 0.0f;
+    for (int j = 0; j < 16; ++j) x[j] = Pi[static_cast<int64_t>(min(s0 + j, s_hi - 1)) * a.RS];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       if (s0 + j < s_hi) v = fmaf(smem[s0 + j], x[j], v);
@@ -1044,21 +1076,25 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
         float wv[kCvBatch][kMergeRows];
 #pragma unroll
         for (int j = 0; j < kCvBatch; ++j) {
+          // rows past k (and row slots past ng) read a valid entry (clamped
+          // index) and are weighted by 0: a multiply, not a select, so that the
+          // compiler keeps the load unconditional and its wait counted
           const int n = n0 + kCvLanes * j;
+          const int nc = min(n, a.k - 1);
 #pragma unroll
-          for (int g = 0; g < kMergeRows; ++g)
-            wv[j][g] = (n < a.k && g < ng) ? wrow[static_cast<int64_t>(g) * a.MS + n] : 0.0f;
+          for (int g = 0; g < kMergeRows; ++g) {
+            const float w = wrow[static_cast<int64_t>(min(g, ng - 1)) * a.MS + nc];
+            wv[j][g] = w * ((n < a.k && g < ng) ? 1.0f : 0.0f);
+          }
           float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (n < a.k) {
+          if (VEC) {
+            v = *reinterpret_cast<const float4*>(cvb + static_cast<int64_t>(nc) * a.dc + c);
+          } else if (n < a.k) {
             const float* src = cvb + static_cast<int64_t>(n) * a.dc + c;
-            if (VEC) {
-              v = *reinterpret_cast<const float4*>(src);
-            } else {
-              v.x = src[0];
-              if (c + 1 < a.dc) v.y = src[1];
-              if (c + 2 < a.dc) v.z = src[2];
-              if (c + 3 < a.dc) v.w = src[3];
-            }
+            v.x = src[0];
+            if (c + 1 < a.dc) v.y = src[1];
+            if (c + 2 < a.dc) v.z = src[2];
+            if (c + 3 < a.dc) v.w = src[3];
           }
           x[j] = v;
         }
