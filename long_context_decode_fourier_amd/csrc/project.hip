@@ -12,6 +12,10 @@
 // convert to fp16 exactly for |x| in [2^-14, 65504], and the unscaled cos/sin
 // values in [-1, 1] keep 11 significant bits (bf16 would keep 8, which costs
 // an order of magnitude in coefficient accuracy).  Accumulation is fp32.
+// Two tilings: square 256 x 256 tiles for large contractions
+// (project_f16_kernel) and tall 512 x 64 tiles for a small k
+// (project_tall_kernel); long sequences are split over positions and the
+// partial tiles summed in a fixed order by project_reduce_kernel.
 //
 // Basis values along a lane's run of 32 consecutive positions come from the
 // three-term recurrence y(t+1) = 2 cos(theta) y(t) - y(t-1), seeded with two
