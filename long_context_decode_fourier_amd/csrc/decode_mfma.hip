@@ -613,10 +613,13 @@ hipError_t launch_one(const DecodeArgs& a, int nitems, size_t smem, hipStream_t 
   return hipGetLastError();
 }
 
-// Compiled variants, chosen by row blocks and basis length (pair-order
-// positions kpp): each wave's slice of A and W stays in registers.
+// Compiled variants, chosen by row blocks, basis length (pair-order
+// positions kpp) and the item's KV heads: each wave's slice of A and W stays
+// in registers.  The first variant that fits is taken, so leaner variants
+// (fewer staging and exact-dim slots) come first.
 constexpr MfmaVariant kVariants[] = {
     // mb nw maxu pf xp xu kpp_min kpp_max
+    {1, 8, 2, 2, 1, 4, 0, 512},  // up to 8 KV heads of <= 64 exact dims
     {1, 8, 2, 4, 2, 8, 0, 512},
     {2, 8, 2, 2, 1, 4, 0, 512},
     {2, 8, 5, 1, 1, 2, 513, 1280},
@@ -655,9 +658,18 @@ __host__ __device__ MfmaLds mfma_lds(int mb, int nw, int kpp, int nheads, int du
   return o;
 }
 
-const MfmaVariant* decode_mfma_pick(int kpp, int mb) {
+// The item's exact dims fit the variant's per-wave slots: KV heads for the
+// exact scores, (KV head, 16-dim block) tiles for the exact values, 16-byte
+// vx chunks staged per thread.
+bool decode_mfma_fits(const MfmaVariant& v, int nheads, int du) {
+  const int du32 = (du + 31) / 32 * 32, nt = 64 * v.nw;
+  return nheads <= v.xp * v.nw && nheads * (du32 / 16) <= v.xu * v.nw &&
+         nheads * kMfmaTile * (du / 8) <= v.pf * nt;
+}
+
+const MfmaVariant* decode_mfma_pick(int kpp, int mb, int nheads, int du) {
   for (const MfmaVariant& v : kVariants)
-    if (v.mb == mb && kpp >= v.kpp_min && kpp <= v.kpp_max) return &v;
+    if (v.mb == mb && kpp >= v.kpp_min && kpp <= v.kpp_max && decode_mfma_fits(v, nheads, du)) return &v;
   return nullptr;
 }
 
@@ -667,16 +679,17 @@ size_t decode_mfma_smem(const DecodeArgs& a, const MfmaVariant& v, int nheads) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s) {
   if (nitems == 0) return hipSuccess;
-  const MfmaVariant* v = decode_mfma_pick(a.kpp, a.mb);
-  if (!v) return hipErrorInvalidValue;
   const int nheads = a.rows >= a.G ? a.rows / a.G : 1;
+  const MfmaVariant* v = decode_mfma_pick(a.kpp, a.mb, nheads, a.du);
+  if (!v) return hipErrorInvalidValue;
   const size_t smem = decode_mfma_smem(a, *v, nheads);
   switch (v - kVariants) {
-    case 0: return launch_one<1, 8, 2, 4, 2, 8>(a, nitems, smem, s);
-    case 1: return launch_one<2, 8, 2, 2, 1, 4>(a, nitems, smem, s);
-    case 2: return launch_one<2, 8, 5, 1, 1, 2>(a, nitems, smem, s);
-    case 3: return launch_one<1, 8, 5, 2, 2, 4>(a, nitems, smem, s);
-    case 4: return launch_one<1, 8, 9, 1, 1, 2>(a, nitems, smem, s);
+    case 0: return launch_one<1, 8, 2, 2, 1, 4>(a, nitems, smem, s);
+    case 1: return launch_one<1, 8, 2, 4, 2, 8>(a, nitems, smem, s);
+    case 2: return launch_one<2, 8, 2, 2, 1, 4>(a, nitems, smem, s);
+    case 3: return launch_one<2, 8, 5, 1, 1, 2>(a, nitems, smem, s);
+    case 4: return launch_one<1, 8, 5, 2, 2, 4>(a, nitems, smem, s);
+    case 5: return launch_one<1, 8, 9, 1, 1, 2>(a, nitems, smem, s);
   }
   return hipErrorInvalidValue;
 }

@@ -215,16 +215,12 @@ bool mfma_rows_ok(const Shape& sh, int rows, int kpp) {
   if (!(rows % G == 0 || G % rows == 0)) return false;
   if (rows > 16 && 16 % G) return false;  // each KV head's rows inside one 16-row block
   const int mb = rows > 16 ? 2 : 1;
-  const fa::MfmaVariant* v = fa::decode_mfma_pick(kpp, mb);
-  if (!v) return false;
-  const int T = fa::kMfmaTile;
   const int nheads = rows >= G ? rows / G : 1;
-  const int nt = 64 * v->nw;
   const int du32 = (sh.Du + 31) / 32 * 32;
   if (sh.Du % 8 || du32 > 64) return false;
-  if (nheads > v->xp * v->nw) return false;                   // exact-score heads per wave
-  if (nheads * (du32 / 16) > v->xu * v->nw) return false;     // exact-value tiles per wave
-  if (nheads * T * (sh.Du / 8) > v->pf * nt) return false;    // staged vx chunks per thread
+  // a compiled variant with enough exact-score, exact-value and staging slots
+  const fa::MfmaVariant* v = fa::decode_mfma_pick(kpp, mb, nheads, sh.Du);
+  if (!v) return false;
   return fa::mfma_lds(v->mb, v->nw, kpp, nheads, sh.Du, sh.Dc).total <= kMaxLds;
 }
 
