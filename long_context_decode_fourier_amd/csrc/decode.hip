@@ -91,7 +91,8 @@ __device__ inline int pair_pos_to_n(int pos, int k) {
 // Every block issues all of its global loads before it waits for any, and
 // the dims permutation of q is applied from LDS, so a block costs one memory
 // round trip plus its arithmetic.
-constexpr int kPrepPos = 64;  // coefficient positions per A block
+constexpr int kPrepPos = 64;       // coefficient positions per A block
+constexpr int kPrepThreads = 512;  // threads per prep block (edge blocks: one wave per 16-token or 16-dim block)
 
 // Stage the G query rows of (b, h) (scaled, as fp32) and the dims table in LDS.
 // Loads of a round are all issued before the first store.
@@ -135,25 +136,25 @@ __device__ __forceinline__ void prep_a_block(const DecodeArgs& a, int b, int h, 
   const int tid = threadIdx.x;
   if (VEC) {
     const int dc4 = dc / 4, n4 = nrows * dc4;
-    constexpr int kB = 16;  // float4 loads in flight per thread (dc <= 256)
+    constexpr int kB = kPrepPos * 64 / kPrepThreads;  // float4 loads in flight per thread (dc <= 256)
     float4 v[kB];
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int i = tid + u * 256;
+      const int i = tid + u * kPrepThreads;
       v[u] = (i < n4) ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     stage_q<T>(a, b, h, qraw, dl, a.scale);
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int i = tid + u * 256;
+      const int i = tid + u * kPrepThreads;
       if (i < n4) *reinterpret_cast<float4*>(ckl + (i / dc4) * CS + 4 * (i % dc4)) = v[u];
     }
   } else {
     stage_q<T>(a, b, h, qraw, dl, a.scale);
-    for (int i = tid; i < nrows * dc; i += 256) ckl[(i / dc) * CS + i % dc] = src[i];
+    for (int i = tid; i < nrows * dc; i += kPrepThreads) ckl[(i / dc) * CS + i % dc] = src[i];
   }
   __syncthreads();
-  for (int idx = tid; idx < G * dc; idx += 256) {
+  for (int idx = tid; idx < G * dc; idx += kPrepThreads) {
     const int g = idx / dc, c = idx % dc;
     const int d = dl[du + c];
     qc[idx] = (d >= 0 && d < D) ? qraw[g * D + d] : 0.0f;
@@ -165,7 +166,7 @@ __device__ __forceinline__ void prep_a_block(const DecodeArgs& a, int b, int h, 
   const bool live = n >= 0 && n < a.k && M > 0;
   const float alpha = live ? basis_alpha(n, M) : 0.0f;
   const float* crow = ckl + (live ? n - r0 : 0) * CS;
-  for (int g = tid >> 6; g < G; g += 4) {
+  for (int g = tid >> 6; g < G; g += kPrepThreads / 64) {
     const float* qg = qc + g * dc;
     float acc0 = 0.0f, acc1 = 0.0f;
     if (live) {
@@ -628,7 +629,7 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
 
 // Blocks [0, nedge) are edge blocks (MFMA path), the rest A blocks.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(256) void decode_prep_kernel(DecodeArgs a, int nedge, int chunks) {
+__global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a, int nedge, int chunks) {
   extern __shared__ float smem[];
   int blk = blockIdx.x;
   if (blk < nedge) {
@@ -1187,7 +1188,7 @@ hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
 #define FA_PREP(T, V)                                                                        \
   do {                                                                                       \
     if ((e = allow_lds(decode_prep_kernel<T, V>, sm)) != hipSuccess) return e;              \
-    hipLaunchKernelGGL((decode_prep_kernel<T, V>), dim3(blocks), dim3(256), sm, s, a, nedge, \
+    hipLaunchKernelGGL((decode_prep_kernel<T, V>), dim3(blocks), dim3(kPrepThreads), sm, s, a, nedge, \
                        max(chunks, 1));                                                      \
   } while (0)
   if (a.dtype == 1) {
