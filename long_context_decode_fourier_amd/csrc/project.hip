@@ -594,13 +594,22 @@ __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a, EdgeArg
     const int ns = a.seq.nsplit[b];
     const float* P = a.partial + (static_cast<int64_t>(a.seq.item0[b] + tile * ns) * a.tk + nl) * a.tn + 4 * q4;
     const int64_t stride = static_cast<int64_t>(a.tk) * a.tn;
+    // splits in ascending order, kReduceBatch loads in flight (clamped index,
+    // no branch around a load, so the waits count instead of draining)
+    constexpr int kReduceBatch = 8;
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < ns; ++sp) {
-      const float4 v = *reinterpret_cast<const float4*>(P + sp * stride);
-      sum.x += v.x;
-      sum.y += v.y;
-      sum.z += v.z;
-      sum.w += v.w;
+    for (int sp0 = 0; sp0 < ns; sp0 += kReduceBatch) {
+      float4 v[kReduceBatch];
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) v[j] = *reinterpret_cast<const float4*>(P + min(sp0 + j, ns - 1) * stride);
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j)
+        if (sp0 + j < ns) {
+          sum.x += v[j].x;
+          sum.y += v[j].y;
+          sum.z += v[j].z;
+          sum.w += v[j].w;
+        }
     }
     const int M = a.seq.mid[b];
     float alpha = 0.0f;
