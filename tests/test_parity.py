@@ -177,6 +177,11 @@ SMALL = {
                               n_comp=16, n_coef=17, sink=0, recent=24), [260, 24]),
     "bf16_long_window": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64,
                               n_comp=32, n_coef=101, sink=100, recent=200), [1000, 250]),
+    # a one-position middle next to a long one, four compressible dims (one
+    # column quad per KV head and matrix in the projection's 64-column tiles),
+    # exact dims that are not a multiple of 8
+    "bf16_m1_dc4": (dict(dtype="bf16", batch=2, n_q_heads=6, n_kv_heads=3, head_dim=16,
+                         n_comp=4, n_coef=1), [97, 2000]),
 }
 
 
