@@ -470,13 +470,24 @@ __host__ __device__ inline size_t edge_mfma_smem_bytes(int E, int G, int D) {
   return 2 * E16 * (D + 8) + 4 * static_cast<size_t>(G) * D + 2 * qb + 4 * static_cast<size_t>(G) * E16 + 4 * D;
 }
 
-__device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b, int h, float* sm) {
+//
+// The retained tokens of a (sequence, KV head) are cut into a.edge_split
+// parts of whole 16-token blocks; part `part` is split ns - edge_split + part
+// of each row (a part past the retained tokens writes an empty split).
+__device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b, int h, int part, float* sm) {
   const int L = a.seq.len[b], M = a.seq.mid[b];
   const int S = a.sink, E = a.sink + a.recent;
-  const int ne = (M > 0) ? E : L;
+  const int ne_all = (M > 0) ? E : L;
   const int D = a.D, du = a.du, dc = a.dc, G = a.G;
   const int ns = a.seq.nsplit[b];
   const int E16 = (E + 15) & ~15, RSE = D + 8, QS = D + 8;
+  // this part's tokens [e0, e0 + P16) of the retained ones (16-token blocks),
+  // ne of them real; local token el is retained token e0 + el
+  const int PT = ((E16 / 16 + a.edge_split - 1) / a.edge_split) * 16;
+  const int e0 = part * PT;
+  const int P16 = max(0, min(E16, e0 + PT) - e0);
+  const int ne = max(0, min(ne_all, e0 + P16) - e0);
+  const int esp = ns - a.edge_split + part;
   uint16_t* rows = reinterpret_cast<uint16_t*>(sm);
   float* qraw = sm + (E16 * RSE) / 2;
   uint16_t* qb = reinterpret_cast<uint16_t*>(qraw + G * D);
@@ -492,7 +503,7 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
   const int nu = du / 8, per_row = nu + dc / 8;  // 16-byte chunks: exact dims first
   const int nchunk = ne * per_row;
   auto chunk_src = [&](const uint16_t* xh, const uint16_t* eh, int i) {
-    const int e = i / per_row, w = i % per_row;
+    const int e = e0 + i / per_row, w = i % per_row;
     if (w < nu) {
       const int t = (M > 0 && e >= S) ? e + M : e;
       return xh + static_cast<int64_t>(t) * du + w * 8;
@@ -536,7 +547,7 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
     const int d = dl[j];
     qb[g * QS + j] = (d >= 0 && d < D) ? static_cast<uint16_t>(__float_as_uint(qraw[g * D + d]) >> 16) : 0;
   }
-  for (int idx = tid; idx < G * du32; idx += nt) {
+  for (int idx = tid; part == 0 && idx < G * du32; idx += nt) {
     const int g = idx / du32, j = idx % du32;
     const int64_t i = static_cast<int64_t>(b) * a.hq + h * G + g;
     uint16_t bits = 0;
@@ -548,7 +559,7 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
   }
   __syncthreads();
   // scores: wave -> token blocks of 16; lane (l16 = token, g4) -> rows 4 g4 + r
-  for (int eb = wave; eb < E16 / 16; eb += nwv) {
+  for (int eb = wave; eb < P16 / 16; eb += nwv) {
     efloat4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int kc = 0; kc < D / 32; ++kc) {
       uint4 qa = make_uint4(0u, 0u, 0u, 0u);
@@ -566,7 +577,7 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
   }
   __syncthreads();
   // V replaces K (the last round from registers, earlier rounds reloaded);
-  // padding rows [ne, E16) are zero
+  // padding rows [ne, P16) are zero
   for (int i0 = 0; i0 < last0; i0 += nt) {
     const int i = i0 + tid;
     *reinterpret_cast<uint4*>(chunk_dst(i)) = *reinterpret_cast<const uint4*>(chunk_src(vxh, veh, i));
@@ -576,7 +587,7 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
     const int i = last0 + tid + u * nt;
     if (i < nchunk) *reinterpret_cast<uint4*>(chunk_dst(i)) = vv[u];
   }
-  for (int i = tid; i < (E16 - ne) * (D / 8); i += nt)
+  for (int i = tid; i < (P16 - ne) * (D / 8); i += nt)
     *reinterpret_cast<uint4*>(rows + (ne + i / (D / 8)) * RSE + (i % (D / 8)) * 8) = make_uint4(0u, 0u, 0u, 0u);
   // softmax of each row (one wave per row); probabilities of padding tokens are 0
   for (int g = wave; g < G; g += nwv) {
@@ -584,14 +595,14 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
     for (int e = lane; e < ne; e += 64) m = fmaxf(m, ps[g * E16 + e]);
     m = wave_max(m);
     float l = 0.0f;
-    for (int e = lane; e < E16; e += 64) {
+    for (int e = lane; e < P16; e += 64) {
       const float pe = (e >= ne || m == -INFINITY) ? 0.0f : __expf(ps[g * E16 + e] - m);
       ps[g * E16 + e] = pe;
       l += pe;
     }
     l = wave_sum(l);
     if (lane == 0) {
-      float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G + g) * ns + ns - 1) * a.RS;
+      float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G + g) * ns + esp) * a.RS;
       P[0] = m;
       P[1] = l;
     }
@@ -599,11 +610,11 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
   __syncthreads();
   // values: wave -> 16-dim blocks; A = P (rows l16, tokens 4 g4 .. +3) as
   // bf16 hi + lo, B = V read transposed (tokens 4 g4 .. +3 of dim l16)
-  float* P0 = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G) * ns + ns - 1) * a.RS + 2;
+  float* P0 = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(h * G) * ns + esp) * a.RS + 2;
   const int64_t prs = static_cast<int64_t>(ns) * a.RS;
   for (int nb = wave; nb < D / 16; nb += nwv) {
     efloat4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kt = 0; kt < E16 / 16; ++kt) {
+    for (int kt = 0; kt < P16 / 16; ++kt) {
       float4 p4 = make_float4(0.f, 0.f, 0.f, 0.f);
       if (l16 < G) p4 = *reinterpret_cast<const float4*>(ps + l16 * E16 + kt * 16 + 4 * g4);
       const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
@@ -633,13 +644,16 @@ __global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a,
   extern __shared__ float smem[];
   int blk = blockIdx.x;
   if (blk < nedge) {
+    // edge blocks: (sequence, KV head, part); the VALU edge block takes the
+    // retained tokens whole (the planner gives it one part)
     if (a.edge_split) {
-      if (a.du % 8 == 0 && a.dc % 8 == 0 && a.D % 32 == 0 && a.G <= 16)
-        prep_edge_block_mfma(a, blk / a.hkv, blk % a.hkv, smem);
+      const int bh = blk / a.edge_split, part = blk % a.edge_split;
+      if (edge_mfma_ok(a))
+        prep_edge_block_mfma(a, bh / a.hkv, bh % a.hkv, part, smem);
       else if (a.G >= 4)
-        prep_edge_block<4>(a, blk / a.hkv, blk % a.hkv, smem);
+        prep_edge_block<4>(a, bh / a.hkv, bh % a.hkv, smem);
       else
-        prep_edge_block<1>(a, blk / a.hkv, blk % a.hkv, smem);
+        prep_edge_block<1>(a, bh / a.hkv, bh % a.hkv, smem);
     }
     return;
   }
@@ -1006,8 +1020,8 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   // from it alone and W from the other splits alone
   int s_lo = 0, s_hi = ns;
   if (a.edge_split && idx >= a.du) {
-    if (idx < a.du + a.dc) s_lo = ns - 1;
-    else s_hi = ns - 1;
+    if (idx < a.du + a.dc) s_lo = ns - a.edge_split;
+    else s_hi = ns - a.edge_split;
   }
   // fixed-order sum over the splits: whole batches of kMergeBatch loads in
   // flight, then batches of 16 with a clamped index (no branch around a load,
@@ -1177,7 +1191,7 @@ size_t decode_merge_cv_smem(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
-  const int nedge = a.mfma ? a.nseq * a.hkv : 0;
+  const int nedge = a.mfma ? a.nseq * a.hkv * a.edge_split : 0;
   const int len = a.mfma ? a.kpp : a.k;
   const int chunks = a.prep_a ? (len + kPrepPos - 1) / kPrepPos : 0;
   const int blocks = nedge + a.nseq * a.hkv * chunks;

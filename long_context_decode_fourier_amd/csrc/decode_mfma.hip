@@ -112,7 +112,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int b = seq_of_item(a.seq, a.nseq, blockIdx.x);
   const int local = blockIdx.x - a.seq.item0[b];
   const int ns = a.seq.nsplit[b];  // middle splits + the edge split
-  const int nsm = ns - 1;
+  const int nsm = ns - a.edge_split;  // middle splits (the edge splits come last)
   const int rg = local / nsm, sp = local % nsm;
   const int L = a.seq.len[b], M = a.seq.mid[b];
   const int S = a.sink;

@@ -286,7 +286,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   a.RS = 2 + a.du + a.dc + a.kpad;
   // MFMA path: the split kernel covers the middle tokens [S, S+M) and
   // decode_prep adds one split per row for the sink and recent tokens.
-  a.edge_split = a.mfma;
+  a.edge_split = a.mfma ? fa::edge_parts(a) : 0;
   auto span = [&](int b) { return a.edge_split ? sh.M[b] : sh.L[b]; };
   // Token chunk per item: the smallest multiple of the tile for which the
   // items fit one round of `target` co-resident blocks (ragged batches round

@@ -69,8 +69,9 @@ struct DecodeArgs {
   float* mrg;    // merged rows [B*Hq][MS]: o_E[dc], alpha*W[kpad], 1/l
   int nseq, hq, hkv, G, D, du, dc, k, kpad, kpp, sink, recent;
   int mfma;      // 1: decode_mfma kernel, 0: VALU kernel
-  int edge_split;  // 1: split nsplit-1 of every row holds the sink/recent tokens
-                   //    (decode_prep); the other splits cover middle tokens only
+  int edge_split;  // > 0: the last edge_split splits of every row hold the
+                   //    sink/recent tokens (decode_prep, one part each); the
+                   //    other splits cover middle tokens only
   int mb;        // MFMA path: 16-row blocks per item
   int rows;      // query rows per work item
   int ngroups;   // row groups per sequence (Hq / rows)
@@ -80,6 +81,21 @@ struct DecodeArgs {
   SeqTable seq;  // item0 / nsplit (splits per row, edge split included) / chunk
   int32_t prow0[kMaxBatch];  // first partial row of sequence b: sum Hq * nsplit
 };
+
+// The sink/recent split runs on MFMA for 16-byte rows, whole 32-dim chunks
+// and at most 16 query rows per KV head; there its retained tokens are cut
+// into up to kEdgeParts parts (prep blocks) of at least 32 tokens, else it is
+// one part.
+constexpr int kEdgeParts = 3;
+__host__ __device__ inline bool edge_mfma_ok(const DecodeArgs& a) {
+  return a.du % 8 == 0 && a.dc % 8 == 0 && a.D % 32 == 0 && a.G <= 16;
+}
+inline int edge_parts(const DecodeArgs& a) {
+  if (!edge_mfma_ok(a)) return 1;
+  const int blocks16 = (a.sink + a.recent + 15) / 16;
+  const int parts = blocks16 / 2 < kEdgeParts ? blocks16 / 2 : kEdgeParts;
+  return parts > 1 ? parts : 1;
+}
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s);
 size_t decode_edge_smem(const DecodeArgs& a);  // LDS of the edge split (decode_prep)
