@@ -84,16 +84,17 @@ struct DecodeArgs {
 
 // The sink/recent split runs on MFMA for 16-byte rows, whole 32-dim chunks
 // and at most 16 query rows per KV head; there its retained tokens are cut
-// into up to kEdgeParts parts (prep blocks) of at least 32 tokens, else it is
-// one part.
-constexpr int kEdgeParts = 3;
+// into up to kEdgeParts parts (prep blocks) of whole 16-token blocks, else it
+// is one part.  Short parts shorten the prep kernel's slowest blocks; each
+// part adds a split to the merge.
+constexpr int kEdgeParts = 6;
 __host__ __device__ inline bool edge_mfma_ok(const DecodeArgs& a) {
   return a.du % 8 == 0 && a.dc % 8 == 0 && a.D % 32 == 0 && a.G <= 16;
 }
 inline int edge_parts(const DecodeArgs& a) {
   if (!edge_mfma_ok(a)) return 1;
   const int blocks16 = (a.sink + a.recent + 15) / 16;
-  const int parts = blocks16 / 2 < kEdgeParts ? blocks16 / 2 : kEdgeParts;
+  const int parts = blocks16 < kEdgeParts ? blocks16 : kEdgeParts;
   return parts > 1 ? parts : 1;
 }
 
