@@ -964,8 +964,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // dims of out.
 constexpr int kMergeRows = 4;
 constexpr int kMergeHeld = 2;    // split weights per lane kept in registers
-constexpr int kMergeBatch = 32;  // split loads in flight per thread
+constexpr int kMergeBatch = 32;  // split loads in flight per thread after the first
+// FIRST: split loads issued before the weights exist.  64 holds a short
+// context's splits in one round but takes about 220 registers (two waves per
+// SIMD), so it is used only where the grid is one pass over the chip; larger
+// grids issue none early and keep the occupancy (about 80 registers).
+constexpr int kMergeFirstDeep = 64;
+constexpr int kMergeFirstLean = 0;
+constexpr int kMergeDeepBlocks = 512;  // two 256-thread blocks per CU
 
+template <int FIRST>
 __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   extern __shared__ float smem[];  // [ns] weights
   const int row = blockIdx.x;      // b * hq + i
@@ -977,10 +985,28 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   const int idx = blockIdx.y * 256 + threadIdx.x;
   if (blockIdx.y * 256 >= nvec) return;  // uniform per block
   const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS;
+  // The entry this thread sums (threads past nvec load the last one and
+  // store nothing) and the splits that hold it: with edge splits (the last
+  // ones), o_E comes from them alone and W from the other splits alone.
+  // Neither range is empty where its entry exists.
+  const int e = min(idx, nvec - 1);
+  int s_lo = 0, s_hi = ns;
+  if (a.edge_split && e >= a.du) {
+    if (e < a.du + a.dc) s_lo = ns - a.edge_split;
+    else s_hi = ns - a.edge_split;
+  }
+  const float* Pi = P + 2 + e;
+  // The entry's first FIRST splits and its output column are loaded in
+  // the same round as the (m, l) pairs (clamped indices, no branch around a
+  // load), so that the weights and the sum wait on one memory round trip.
+  float x0[FIRST > 0 ? FIRST : 1];
+#pragma unroll
+  for (int j = 0; j < FIRST; ++j) x0[j] = Pi[static_cast<int64_t>(min(s_lo + j, s_hi - 1)) * a.RS];
+  const int dd = a.dims[h * a.D + max(0, min(e, a.du - 1))];
   // every wave forms the split weights itself (wave reductions, no block
   // barrier); wave 0 publishes them for the sums below.  The (m, l) pairs of
-  // a lane's first kMergeHeld splits are read once, in one round of loads
-  // (clamped index, no branch); splits beyond 64 kMergeHeld are read again.
+  // a lane's first kMergeHeld splits are read once (clamped index, no
+  // branch); splits beyond 64 kMergeHeld are read again.
   const int lane = threadIdx.x & 63;
   float mh[kMergeHeld], lh[kMergeHeld];
 #pragma unroll
@@ -1015,19 +1041,17 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   float* mrow = a.mrg + static_cast<int64_t>(row) * a.MS;
   if (blockIdx.y == 0 && threadIdx.x == 0) mrow[a.dc + a.kpad] = linv;
   if (idx >= nvec) return;
-  const float* Pi = P + 2 + idx;
-  // splits that hold this entry: with an edge split (the last one), o_E comes
-  // from it alone and W from the other splits alone
-  int s_lo = 0, s_hi = ns;
-  if (a.edge_split && idx >= a.du) {
-    if (idx < a.du + a.dc) s_lo = ns - a.edge_split;
-    else s_hi = ns - a.edge_split;
-  }
-  // fixed-order sum over the splits: whole batches of kMergeBatch loads in
-  // flight, then batches of 16 with a clamped index (no branch around a load,
-  // so the waits count instead of draining)
+  // fixed-order sum over the splits s_lo, s_lo + 1, ...: the loads already
+  // held (a split past s_hi weighs 0: a multiply, not a branch, so that the
+  // compiler keeps the load where it is), then whole batches of kMergeBatch
+  // loads in flight, then batches of 16 with a clamped index
   float v = 0.0f;
-  int s0 = s_lo;
+#pragma unroll
+  for (int j = 0; j < FIRST; ++j) {
+    const float w = smem[min(s_lo + j, s_hi - 1)] * (s_lo + j < s_hi ? 1.0f : 0.0f);
+    v = fmaf(w, x0[j], v);
+  }
+  int s0 = s_lo + FIRST;
   for (; s0 + kMergeBatch <= s_hi; s0 += kMergeBatch) {
     float x[kMergeBatch];
 #pragma unroll
@@ -1040,11 +1064,12 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[j] = Pi[static_cast<int64_t>(min(s0 + j, s_hi - 1)) * a.RS];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (s0 + j < s_hi) v = fmaf(smem[s0 + j], x[j], v);
+    for (int j = 0; j < 16; ++j) {
+      const float w = smem[min(s0 + j, s_hi - 1)] * (s0 + j < s_hi ? 1.0f : 0.0f);
+      v = fmaf(w, x[j], v);
+    }
   }
   if (idx < a.du) {
-    const int dd = a.dims[h * a.D + idx];
     if (dd >= 0 && dd < a.D) a.out[static_cast<int64_t>(row) * a.D + dd] = v * linv;
   } else if (idx < a.du + a.dc) {
     mrow[idx - a.du] = v;
@@ -1081,6 +1106,14 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
   for (int g0 = 0; g0 < a.G; g0 += kMergeRows) {
     const int ng = min(kMergeRows, a.G - g0);
     const float* wrow = a.mrg + (static_cast<int64_t>(b) * a.hq + h * a.G + g0) * a.MS + a.dc;
+    // the epilogue's operands (merged o_E entry, 1/l, output column) are
+    // loaded with the pass's first round of loads (clamped, unconditional)
+    const int eg = min(tid / kCvCols, ng - 1);
+    const int ecc = min(blockIdx.y * kCvCols + tid % kCvCols, a.dc - 1);
+    const float* erow = a.mrg + (static_cast<int64_t>(b) * a.hq + h * a.G + g0 + eg) * a.MS;
+    const float e_oe = erow[ecc];
+    const float e_linv = erow[a.dc + a.kpad];
+    const int e_dd = a.dims[h * a.D + a.du + ecc];
     __syncthreads();
     float acc[kMergeRows][4];
 #pragma unroll
@@ -1092,15 +1125,12 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < kCvBatch; ++j) {
           // rows past k (and row slots past ng) read a valid entry (clamped
-          // index) and are weighted by 0: a multiply, not a select, so that the
-          // compiler keeps the load unconditional and its wait counted
+          // index) and are weighted by 0 below: a multiply, not a select, so
+          // that the compiler keeps the load unconditional and its wait counted
           const int n = n0 + kCvLanes * j;
           const int nc = min(n, a.k - 1);
 #pragma unroll
-          for (int g = 0; g < kMergeRows; ++g) {
-            const float w = wrow[static_cast<int64_t>(min(g, ng - 1)) * a.MS + nc];
-            wv[j][g] = w * ((n < a.k && g < ng) ? 1.0f : 0.0f);
-          }
+          for (int g = 0; g < kMergeRows; ++g) wv[j][g] = wrow[static_cast<int64_t>(min(g, ng - 1)) * a.MS + nc];
           float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
           if (VEC) {
             v = *reinterpret_cast<const float4*>(cvb + static_cast<int64_t>(nc) * a.dc + c);
@@ -1113,19 +1143,23 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
           }
           x[j] = v;
         }
+        // every product is taken (rows past k and row slots past ng weigh
+        // 0), so no load is left in flight at the loop's back edge and the
+        // loop head needs no drain of the loads issued before it; the
+        // scheduling barrier keeps all of the batch's loads ahead of its
+        // products (interleaved, each row would wait on its own round trip)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < kCvBatch; ++j) {
           const int n = n0 + kCvLanes * j;
-          if (n >= a.k) break;
 #pragma unroll
-          for (int g = 0; g < kMergeRows; ++g)
-            if (g < ng) {
-              const float w = wv[j][g];
-              acc[g][0] = fmaf(w, x[j].x, acc[g][0]);
-              acc[g][1] = fmaf(w, x[j].y, acc[g][1]);
-              acc[g][2] = fmaf(w, x[j].z, acc[g][2]);
-              acc[g][3] = fmaf(w, x[j].w, acc[g][3]);
-            }
+          for (int g = 0; g < kMergeRows; ++g) {
+            const float w = wv[j][g] * ((n < a.k && g < ng) ? 1.0f : 0.0f);
+            acc[g][0] = fmaf(w, x[j].x, acc[g][0]);
+            acc[g][1] = fmaf(w, x[j].y, acc[g][1]);
+            acc[g][2] = fmaf(w, x[j].z, acc[g][2]);
+            acc[g][3] = fmaf(w, x[j].w, acc[g][3]);
+          }
         }
       }
     }
@@ -1148,9 +1182,7 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
         float sum = 0.0f;
         for (int part = 0; part < 8; ++part) sum += red2[part * kCvQ + tid];
         const int64_t row = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
-        const float* mrow = a.mrg + row * a.MS;
-        const int dd = a.dims[h * a.D + a.du + cc];
-        if (dd >= 0 && dd < a.D) a.out[row * a.D + dd] = (sum + mrow[cc]) * mrow[a.dc + a.kpad];
+        if (e_dd >= 0 && e_dd < a.D) a.out[row * a.D + e_dd] = (sum + e_oe) * e_linv;
       }
     }
   }
@@ -1232,10 +1264,16 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
   int max_splits = 1;
   for (int b = 0; b < a.nseq; ++b) max_splits = max(max_splits, a.seq.nsplit[b]);
   const int nvec = a.du + a.dc + a.k;
-  hipError_t e = allow_lds(decode_merge_vec_kernel, sizeof(float) * max_splits);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_vec_kernel, dim3(a.nseq * a.hq, (nvec + 255) / 256), dim3(256),
-                     sizeof(float) * max_splits, s, a);
+  const dim3 vgrid(a.nseq * a.hq, (nvec + 255) / 256);
+  const size_t vsm = sizeof(float) * max_splits;
+  hipError_t e;
+  if (static_cast<int64_t>(vgrid.x) * vgrid.y <= kMergeDeepBlocks) {
+    if ((e = allow_lds(decode_merge_vec_kernel<kMergeFirstDeep>, vsm)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_vec_kernel<kMergeFirstDeep>, vgrid, dim3(256), vsm, s, a);
+  } else {
+    if ((e = allow_lds(decode_merge_vec_kernel<kMergeFirstLean>, vsm)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_vec_kernel<kMergeFirstLean>, vgrid, dim3(256), vsm, s, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dc == 0) return hipSuccess;
   const size_t sm = decode_merge_cv_smem(a);
