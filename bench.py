@@ -46,7 +46,7 @@ def algorithmic(w):
         if M > 0:
             dec += c.n_kv_heads * c.n_coef * c.n_comp * 2 * 4          # ck, cv
             flops += 2.0 * M * c.n_coef * c.n_kv_heads * c.n_comp * 2  # K and V
-    dec += c.batch * c.n_q_heads * c.head_dim * (esz + 4)              # q in, out
+    dec += c.batch * c.n_query * c.n_q_heads * c.head_dim * (esz + 4)  # q in, out
     pos = int(w.lens.sum()) * c.n_kv_heads
     return dec, flops, pos
 
@@ -114,7 +114,10 @@ def cpu_baseline(w, scale, seconds):
     while True:
         ck, cv = ob.project_all(w)
         if "decode" in steps:
-            ob.decode_all(w, ck, cv, scale)
+            if w.cfg.n_query > 1:
+                ob.attend_all(w, ck, cv, scale)
+            else:
+                ob.decode_all(w, ck, cv, scale)
         n += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -191,10 +194,12 @@ def main():
         s["ke"] = torch.empty((nblk, E, c.n_comp), dtype=base["kc"].dtype, device=dev)
         s["ve"] = torch.empty_like(s["ke"])
         if "decode" in steps:
-            s["out"] = torch.empty((c.batch, c.n_q_heads, c.head_dim), device=dev)
+            oshape = (c.batch, c.n_q_heads, c.head_dim) if c.n_query == 1 else \
+                (c.batch, c.n_query, c.n_q_heads, c.head_dim)
+            s["out"] = torch.empty(oshape, device=dev)
         sets.append(s)
     ws_p = fb.workspace(fb.project_workspace_size(desc))
-    ws_d = fb.workspace(fb.decode_workspace_size(desc)) if "decode" in steps else None
+    ws_d = fb.workspace(fb.attend_workspace_size(desc, c.n_query)) if "decode" in steps else None
     if "decode" in steps and "project" not in steps:
         for s in sets:  # decode-only workloads: coefficients and edges made once
             fb.project(desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], ws_p)
@@ -204,8 +209,12 @@ def main():
         fb.project(desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], ws_p, st)
 
     def call_decode(s, st):
-        fb.decode(desc, s["q"], s.get("kx"), s.get("vx"), s["ke"], s["ve"], s["ck"], s["cv"],
-                  scale, s["out"], ws_d, st)
+        if c.n_query > 1:  # several queries per sequence: fa_attend
+            fb.attend(desc, c.n_query, s["q"], s.get("kx"), s.get("vx"), s["ke"], s["ve"], s["ck"],
+                      s["cv"], scale, s["out"], None, ws_d, st)
+        else:
+            fb.decode(desc, s["q"], s.get("kx"), s.get("vx"), s["ke"], s["ve"], s["ck"], s["cv"],
+                      scale, s["out"], ws_d, st)
 
     graphs = None  # per input copy: (project graph, decode graph)
 
@@ -276,7 +285,8 @@ def main():
     # dominant call: the larger share of the step
     if "decode" in steps and (t_dec >= t_proj or "project" not in steps):
         ach = dec_bytes / t_dec / 1e9
-        roof = {"kernel": "fa_decode", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+        roof = {"kernel": "fa_decode" if c.n_query == 1 else "fa_attend", "bound": "hbm",
+                "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                 "traffic": measured_traffic(args.workload, "fa_decode")}
     else:
@@ -305,7 +315,8 @@ def main():
 
     line = {
         "metric": "KV-positions/s (fa_project K,V + fa_decode per step)" if len(steps) == 2
-                  else "KV-positions/s (%s)" % "+".join(steps),
+                  else ("KV-positions/s (%s)" % "+".join(steps) if c.n_query == 1
+                        else "KV-positions/s (fa_attend, %d queries per sequence)" % c.n_query),
         "value": positions / (ms_step * 1e-3),
         "unit": "KV-positions/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -317,7 +328,7 @@ def main():
                    "seq_len": [int(x) for x in w.lens] if c.len_range else int(w.lens[0]),
                    "n_q_heads": c.n_q_heads, "n_kv_heads": c.n_kv_heads, "head_dim": c.head_dim,
                    "n_comp_dims": c.n_comp, "n_coef": c.n_coef, "sink": c.sink,
-                   "recent": c.recent, "input_copies": copies},
+                   "recent": c.recent, "n_query": c.n_query, "input_copies": copies},
         "launch": "hip graph replay (one graph per call and input copy)" if args.graph else "eager",
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -134,6 +134,35 @@ fa_status_t fa_decode(const fa_desc_t *desc, const void *q, const void *kx,
                       const float *ck, const float *cv, float scale, float *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes fa_attend needs for `desc` and `n_query`. */
+fa_status_t fa_attend_workspace_size(const fa_desc_t *desc, int32_t n_query, size_t *bytes);
+
+/*
+ * fa_attend: n_query queries per sequence, each attending to the whole cache
+ * exactly as fa_decode's query does (no mask between the queries).  This is
+ * attention over the compressed cache during prefill as well as decode (skill
+ * page, Architecture overview and Practical guidance: the kernel serves the
+ * memory-bound attention of both phases): a chunk of new tokens attends to the
+ * cached past through this call, and to itself through ordinary causal
+ * attention; the two parts combine with their log-sum-exp values.
+ *   q    [B, n_query, Hq, D]   queries (desc.dtype), natural dim order;
+ *   out  [B, n_query, Hq, D]   float32;
+ *   lse  [B, n_query, Hq]      float32 log sum_t exp(s_t), the natural log of
+ *                              the softmax denominator in the units of s
+ *                              (scale included), or NULL.
+ * Query t of head i reads KV head i / (Hq/Hkv); the G * n_query query rows of
+ * a KV head share one pass over its cache.  n_query is 1 .. 1024, and the
+ * query rows of one KV head, G * n_query, must fit a workgroup's LDS
+ * (FA_ERR_SHAPE otherwise; 64 rows at D = 128 fit).  Everything else
+ * (required pointers, alignment, errors) is as for fa_decode, which is
+ * fa_attend with n_query = 1 and lse = NULL.
+ */
+fa_status_t fa_attend(const fa_desc_t *desc, int32_t n_query, const void *q,
+                      const void *kx, const void *vx, const void *ke,
+                      const void *ve, const float *ck, const float *cv,
+                      float scale, float *out, float *lse, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *fa_status_string(fa_status_t status);
 

@@ -53,6 +53,12 @@ _SIGS = [
      [ctypes.POINTER(fa_desc_t)] + [ctypes.c_void_p] * 7 + [ctypes.c_float, ctypes.c_void_p,
                                                            ctypes.c_void_p, ctypes.c_size_t,
                                                            ctypes.c_void_p]),
+    ("fa_attend_workspace_size", ctypes.c_int,
+     [ctypes.POINTER(fa_desc_t), ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+    ("fa_attend", ctypes.c_int,
+     [ctypes.POINTER(fa_desc_t), ctypes.c_int32] + [ctypes.c_void_p] * 7 +
+     [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+      ctypes.c_void_p]),
     ("fa_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("fa_last_error", ctypes.c_char_p, []),
     ("fa_version", ctypes.c_int32, []),
@@ -142,6 +148,23 @@ def decode(desc: Desc, q, kx, vx, ke, ve, ck, cv, scale, out, ws=None, stream=No
     _check(lib().fa_decode(ctypes.byref(desc.c), _ptr(q), _ptr(kx), _ptr(vx), _ptr(ke),
                            _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale), _ptr(out),
                            _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def attend_workspace_size(desc: Desc, n_query: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().fa_attend_workspace_size(ctypes.byref(desc.c), int(n_query), ctypes.byref(n)))
+    return n.value
+
+
+def attend(desc: Desc, n_query, q, kx, vx, ke, ve, ck, cv, scale, out, lse=None, ws=None,
+           stream=None):
+    """fa_attend: n_query queries per sequence (q, out [B, n_query, Hq, D]) over the
+    whole cache; lse [B, n_query, Hq] fp32 (optional) gets each row's log-sum-exp."""
+    if ws is None:
+        ws = workspace(attend_workspace_size(desc, n_query), q.device)
+    _check(lib().fa_attend(ctypes.byref(desc.c), int(n_query), _ptr(q), _ptr(kx), _ptr(vx),
+                           _ptr(ke), _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale),
+                           _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def to_device(a: np.ndarray, device="cuda"):

@@ -99,12 +99,14 @@ constexpr int kPrepThreads = 512;  // threads per prep block (edge blocks: one w
 template <typename T>
 __device__ inline void stage_q(const DecodeArgs& a, int b, int h, float* qraw, int* dl, float mul) {
   const int G = a.G, D = a.D, n = G * D, nt = blockDim.x;
-  const int64_t q0 = (static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(h) * G) * D;
   constexpr int kQ = 8;
   for (int i0 = threadIdx.x; i0 < n; i0 += kQ * nt) {
     float v[kQ];
 #pragma unroll
-    for (int u = 0; u < kQ; ++u) v[u] = (i0 + u * nt < n) ? ld<T>(a.q, q0 + i0 + u * nt) : 0.0f;
+    for (int u = 0; u < kQ; ++u) {
+      const int e = i0 + u * nt;
+      v[u] = (e < n) ? ld<T>(a.q, q_row(a, b, h * G + e / D) * D + e % D) : 0.0f;
+    }
     const int dj = (i0 < D) ? a.dims[h * D + i0] : 0;  // first round covers the dims (D <= 256)
 #pragma unroll
     for (int u = 0; u < kQ; ++u)
@@ -292,7 +294,7 @@ __device__ __forceinline__ void prep_edge_block(const DecodeArgs& a, int b, int 
     uint16_t bits = 0;
     if (j < du) {
       const int d = dl[j];
-      if (d >= 0 && d < D) bits = static_cast<const uint16_t*>(a.q)[i * D + d];
+      if (d >= 0 && d < D) bits = static_cast<const uint16_t*>(a.q)[q_row(a, b, h * G + g) * D + d];
     }
     static_cast<uint16_t*>(a.Q16)[i * du32 + j] = bits;
   }
@@ -553,7 +555,7 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
     uint16_t bits = 0;
     if (j < du) {
       const int d = dl[j];
-      if (d >= 0 && d < D) bits = static_cast<const uint16_t*>(a.q)[i * D + d];
+      if (d >= 0 && d < D) bits = static_cast<const uint16_t*>(a.q)[q_row(a, b, h * G + g) * D + d];
     }
     static_cast<uint16_t*>(a.Q16)[i * du32 + j] = bits;
   }
@@ -706,7 +708,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     if (r < a.rows) {
       const int d = a.dims[kh[r] * a.D + j];
       if (d >= 0 && d < a.D)
-        v = a.scale * ld<T>(a.q, (static_cast<int64_t>(b) * a.hq + qi[r]) * a.D + d);
+        v = a.scale * ld<T>(a.q, q_row(a, b, qi[r]) * a.D + d);
     }
     qs[idx] = v;
   }
@@ -1036,10 +1038,13 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     if (threadIdx.x < 64) smem[s] = w;
     lsum += w * P[static_cast<int64_t>(s) * a.RS + 1];
   }
-  const float linv = 1.0f / wave_sum(lsum);
+  const float ltot = wave_sum(lsum), linv = 1.0f / ltot;
   __syncthreads();
   float* mrow = a.mrg + static_cast<int64_t>(row) * a.MS;
-  if (blockIdx.y == 0 && threadIdx.x == 0) mrow[a.dc + a.kpad] = linv;
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
+    mrow[a.dc + a.kpad] = linv;
+    if (a.lse) a.lse[q_row(a, b, i)] = mx + logf(ltot);
+  }
   if (idx >= nvec) return;
   // fixed-order sum over the splits s_lo, s_lo + 1, ...: the loads already
   // held (a split past s_hi weighs 0: a multiply, not a branch, so that the
@@ -1070,7 +1075,7 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     }
   }
   if (idx < a.du) {
-    if (dd >= 0 && dd < a.D) a.out[static_cast<int64_t>(row) * a.D + dd] = v * linv;
+    if (dd >= 0 && dd < a.D) a.out[q_row(a, b, i) * a.D + dd] = v * linv;
   } else if (idx < a.du + a.dc) {
     mrow[idx - a.du] = v;
   } else {
@@ -1181,7 +1186,7 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
       if (cc < a.dc) {
         float sum = 0.0f;
         for (int part = 0; part < 8; ++part) sum += red2[part * kCvQ + tid];
-        const int64_t row = static_cast<int64_t>(b) * a.hq + h * a.G + g0 + g;
+        const int64_t row = q_row(a, b, h * a.G + g0 + g);
         if (e_dd >= 0 && e_dd < a.D) a.out[row * a.D + e_dd] = (sum + e_oe) * e_linv;
       }
     }

@@ -44,6 +44,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Shape {
   int dtype, B, Hq, Hkv, G, D, Dc, Du, S, R, k;
+  int nq;  // queries per sequence (fa_attend); Hq and G then count nq * heads
   int L[fa::kMaxBatch], M[fa::kMaxBatch];
   int64_t row0[fa::kMaxBatch];
   int64_t total_len;
@@ -79,6 +80,7 @@ fa_status_t validate(const fa_desc_t* d, Shape* sh) {
   sh->S = d->sink;
   sh->R = d->recent;
   sh->k = d->n_coef;
+  sh->nq = 1;
   sh->total_len = 0;
   sh->max_len = 0;
   sh->any_mid = false;
@@ -96,6 +98,18 @@ fa_status_t validate(const fa_desc_t* d, Shape* sh) {
     sh->max_len = std::max(sh->max_len, L);
     sh->any_mid = sh->any_mid || M > 0;
   }
+  return FA_OK;
+}
+
+// n_query queries per sequence run as n_query * Hq "virtual" query heads, the
+// G * n_query rows of a KV head sharing its cache reads.
+constexpr int kMaxQueries = 1024;
+fa_status_t apply_queries(int32_t n_query, Shape* sh) {
+  if (n_query < 1 || n_query > kMaxQueries)
+    return fail(FA_ERR_SHAPE, "n_query %d outside [1, %d]", n_query, kMaxQueries);
+  sh->nq = n_query;
+  sh->Hq *= n_query;
+  sh->G *= n_query;
   return FA_OK;
 }
 
@@ -240,6 +254,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   a.kpp = (2 * (sh.k / 2 + 1) + 31) / 32 * 32;
   a.sink = sh.S;
   a.recent = sh.R;
+  a.nq = sh.nq;
   // MFMA path for 16-bit caches: as many stacked rows as the basis length
   // pays for (long bases amortise their generation over more rows).
   int rows = 0;
@@ -343,6 +358,8 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   p->off_part = p->off_q16 + (a.mfma ? align_up(rows_total * du32 * 2) : 0);
   p->off_mrg = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
   p->ws_bytes = p->off_mrg + align_up(static_cast<size_t>(sh.B) * sh.Hq * a.MS * sizeof(float));
+  if (fa::decode_prep_smem(a) > kMaxLds)
+    return fail(FA_ERR_SHAPE, "%d query rows per KV head need more LDS than a workgroup has", sh.G);
   return FA_OK;
 }
 
@@ -454,10 +471,15 @@ fa_status_t fa_project(const fa_desc_t* desc, const void* kc, const void* vc, fl
 }
 
 fa_status_t fa_decode_workspace_size(const fa_desc_t* desc, size_t* bytes) {
+  return fa_attend_workspace_size(desc, 1, bytes);
+}
+
+fa_status_t fa_attend_workspace_size(const fa_desc_t* desc, int32_t n_query, size_t* bytes) {
   Shape sh;
   if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
   fa_status_t st = validate(desc, &sh);
   if (st != FA_OK) return st;
+  if ((st = apply_queries(n_query, &sh)) != FA_OK) return st;
   DecPlan p;
   st = plan_decode(sh, &p);
   if (st != FA_OK) return st;
@@ -468,9 +490,18 @@ fa_status_t fa_decode_workspace_size(const fa_desc_t* desc, size_t* bytes) {
 fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, const void* vx,
                       const void* ke, const void* ve, const float* ck, const float* cv, float scale,
                       float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_attend(desc, 1, q, kx, vx, ke, ve, ck, cv, scale, out, nullptr, workspace, workspace_bytes,
+                   stream);
+}
+
+fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, const void* kx,
+                      const void* vx, const void* ke, const void* ve, const float* ck, const float* cv,
+                      float scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   Shape sh;
   fa_status_t st = validate(desc, &sh);
   if (st != FA_OK) return st;
+  if ((st = apply_queries(n_query, &sh)) != FA_OK) return st;
   if (!q || !out) return fail(FA_ERR_NULL, "q and out are required");
   if (!desc->dims) return fail(FA_ERR_NULL, "desc.dims is NULL");
   if (sh.Du > 0 && (!kx || !vx)) return fail(FA_ERR_NULL, "kx and vx are required when Du > 0");
@@ -495,6 +526,7 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
     return fail(FA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
   const size_t esz = elem_bytes(sh.dtype);
   const size_t out_bytes = static_cast<size_t>(sh.B) * sh.Hq * sh.D * sizeof(float);
+  const size_t lse_bytes = lse ? static_cast<size_t>(sh.B) * sh.Hq * sizeof(float) : 0;
   const void* ins[8] = {q, kx, vx, ke, ve, ck, cv, desc->dims};
   const size_t isz[8] = {static_cast<size_t>(sh.B) * sh.Hq * sh.D * esz,
                          static_cast<size_t>(sh.Hkv) * sh.total_len * sh.Du * esz,
@@ -509,6 +541,12 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
     if (overlap(workspace, p.ws_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "workspace overlaps an input");
   }
   if (overlap(out, out_bytes, workspace, p.ws_bytes)) return fail(FA_ERR_ALIAS, "out overlaps the workspace");
+  if (lse) {
+    for (int i = 0; i < 8; ++i)
+      if (overlap(lse, lse_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "lse overlaps an input");
+    if (overlap(lse, lse_bytes, out, out_bytes) || overlap(lse, lse_bytes, workspace, p.ws_bytes))
+      return fail(FA_ERR_ALIAS, "lse overlaps out or the workspace");
+  }
 
   fa::DecodeArgs& a = p.args;
   a.q = q;
@@ -521,6 +559,7 @@ fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, cons
   a.dims = desc->dims;
   a.out = out;
   a.scale = scale;
+  a.lse = lse;
   a.A = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_A);
   a.A16 = static_cast<char*>(workspace) + p.off_A;
   a.Q16 = static_cast<char*>(workspace) + p.off_q16;

@@ -78,9 +78,22 @@ struct DecodeArgs {
   int RS;        // floats per partial row: 2 + du + dc + kpad
   int MS;        // floats per merged row: dc + kpad + 1
   float scale;
+  int nq;        // queries per sequence; hq and G count nq * (query heads)
+  float* lse;    // optional [B][nq][Hq]: log sum_t exp(s_t) of each query row
   SeqTable seq;  // item0 / nsplit (splits per row, edge split included) / chunk
   int32_t prow0[kMaxBatch];  // first partial row of sequence b: sum Hq * nsplit
 };
+
+// Rows of the kernels are "virtual" query heads: with nq queries per
+// sequence, KV head h owns rows h*G .. h*G + G-1 (G = nq * Hq/Hkv), row
+// h*G + t*(G/nq) + g being query t of query head h*(G/nq) + g.  q, out and
+// lse are laid out [B][nq][Hq]; this gives the (b, row) entry's index in them.
+__host__ __device__ inline int64_t q_row(const DecodeArgs& a, int b, int i) {
+  if (a.nq == 1) return static_cast<int64_t>(b) * a.hq + i;
+  const int gu = a.G / a.nq;  // query heads per KV head
+  const int h = i / a.G, r = i % a.G;
+  return (static_cast<int64_t>(b) * a.nq + r / gu) * (a.hq / a.nq) + h * gu + r % gu;
+}
 
 // The sink/recent split runs on MFMA for 16-byte rows, whole 32-dim chunks
 // and at most 16 query rows per KV head; there its retained tokens are cut
@@ -100,6 +113,7 @@ inline int edge_parts(const DecodeArgs& a) {
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s);
 size_t decode_edge_smem(const DecodeArgs& a);  // LDS of the edge split (decode_prep)
+size_t decode_prep_smem(const DecodeArgs& a);  // LDS of decode_prep
 hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);

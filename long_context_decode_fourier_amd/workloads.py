@@ -5,9 +5,10 @@ no Fourier basis, no projection, no attention.  Both the HIP path's tests and
 the CPU oracle consume the arrays it returns, so it is the one piece of code the
 two sides share.
 
-Workload shapes follow the five scenarios this library is measured on (single
-fp32 head, a LLaMA-2-7B-shaped layer, a LLaMA-3-8B-shaped GQA batch, a long
-prefill projection and a ragged long-context batch).  No dataset, checkpoint or
+Workload shapes follow the scenarios this library is measured on (single
+fp32 head, a LLaMA-2-7B-shaped layer, a LLaMA-3-8B-shaped GQA batch, the same
+batch with four queries per sequence, a long prefill projection and a ragged
+long-context batch).  No dataset, checkpoint or
 trained weight is used: the compressible head dims of K and V are smooth
 signals (a sum of four low-frequency sinusoids plus small noise), which is the
 kind of slowly varying time series the method's Fourier projection targets
@@ -26,7 +27,8 @@ Recipe (one ``numpy.random.Generator(PCG64(seed))``, draws in this order):
    draws), exact dims ``N(0,1)`` [L,Du] (float32 draws).  Compressible dim c
    at token t is ``sum_m A sin(2 pi f (t - S) / max(M,1) + phi) + noise``, so the
    sink and recent rows continue the same signal;
-4. queries ``q ~ N(0,1)`` [B,Hq,D] (float32 draws).
+4. queries ``q ~ N(0,1)`` [B,Hq,D] (float32 draws), or [B,nq,Hq,D] for a
+   workload with nq > 1 queries per sequence (the same draws, in that shape).
 
 bf16 workloads round every value to bfloat16 with round-to-nearest-even;
 fp32 workloads keep float32.
@@ -74,6 +76,7 @@ class Config:
     recent: int = RECENT
     seed: int = 0
     steps: Tuple[str, ...] = ("project", "decode")
+    n_query: int = 1           # queries per sequence (q is [B, n_query, Hq, D] when > 1)
     note: str = ""
 
     @property
@@ -85,7 +88,7 @@ class Config:
         return self.n_q_heads // self.n_kv_heads
 
 
-# The five workloads.  Names say what the workload is; the seed is fixed.
+# The workloads.  Names say what the workload is; the seed is fixed.
 CONFIGS = {
     "fp32_head": Config(
         name="fp32_head", dtype="f32", batch=1, n_q_heads=1, n_kv_heads=1,
@@ -108,6 +111,12 @@ CONFIGS = {
         seq_len=131040 + SINK + RECENT, seed=4, steps=("project",),
         note="projection only: 8 KV heads x 64 dims of K and V, M=131040, "
              "k=4097"),
+    "llama3_8b_gqa_4q": Config(
+        name="llama3_8b_gqa_4q", dtype="bf16", batch=4, n_q_heads=32,
+        n_kv_heads=8, head_dim=128, n_comp=96, n_coef=1025, seq_len=32768,
+        seed=3, steps=("decode",), n_query=4,
+        note="the LLaMA-3-8B-shaped GQA cache (same draws) with 4 queries per "
+             "sequence attending to it (e.g. 4 draft tokens verified at once)"),
     "ragged_batch": Config(
         name="ragged_batch", dtype="bf16", batch=16, n_q_heads=32,
         n_kv_heads=8, head_dim=128, n_comp=64, n_coef=2049,
@@ -142,7 +151,7 @@ class Workload:
     lens: np.ndarray        # int64 [B]
     offs: np.ndarray        # int64 [B], exclusive prefix sum of lens
     dims: np.ndarray        # int32 [Hkv, D]
-    q: Optional[np.ndarray]     # [B, Hq, D]
+    q: Optional[np.ndarray]     # [B, Hq, D], or [B, nq, Hq, D] when nq > 1
     kx: Optional[np.ndarray]    # [rows, Du]
     vx: Optional[np.ndarray]
     kc: np.ndarray              # [rows, Dc]
@@ -267,7 +276,7 @@ def make(cfg: Config, lens=None) -> Workload:
                     exact_out[r0:r0 + L] = _round(ex, cfg.dtype)
     q = None
     if need_exact:
-        q = _round(rng.standard_normal((B, cfg.n_q_heads, D), dtype=np.float32),
-                   cfg.dtype)
+        shape = (B, cfg.n_q_heads, D) if cfg.n_query == 1 else (B, cfg.n_query, cfg.n_q_heads, D)
+        q = _round(rng.standard_normal(shape, dtype=np.float32), cfg.dtype)
     return Workload(cfg=cfg, lens=lens, offs=offs, dims=dims, q=q,
                     kx=kx, vx=vx, kc=kc, vc=vc)

@@ -67,6 +67,27 @@ def decode_all(w, ck, cv, scale: float):
     return out
 
 
+def attend_all(w, ck, cv, scale: float):
+    """(out [B, nq, Hq, D], lse [B, nq, Hq]) for a workload with nq queries per
+    sequence (``w.q`` [B, nq, Hq, D], or [B, Hq, D] when nq = 1): the nq * G
+    query rows of KV head h are attended in one call of the per-head oracle."""
+    c = w.cfg
+    G = c.n_q_heads // c.n_kv_heads
+    q4 = w.q if w.q.ndim == 4 else w.q[:, None]
+    nq = q4.shape[1]
+    out = np.zeros((c.batch, nq, c.n_q_heads, c.head_dim))
+    lse = np.zeros((c.batch, nq, c.n_q_heads))
+    for b in range(c.batch):
+        for h in range(c.n_kv_heads):
+            i = b * c.n_kv_heads + h
+            K, V = w.natural_kv(b, h)
+            q = w.f64(q4[b, :, h * G:(h + 1) * G]).reshape(nq * G, c.head_dim)
+            o, l = fa.attend(q, K, V, w.comp_dims(h), ck[i], cv[i], c.sink, c.recent, scale)
+            out[b, :, h * G:(h + 1) * G] = o.reshape(nq, G, c.head_dim)
+            lse[b, :, h * G:(h + 1) * G] = l.reshape(nq, G)
+    return out, lse
+
+
 def exact_all(w, scale: float):
     """Uncompressed attention for every query row (context only)."""
     c = w.cfg

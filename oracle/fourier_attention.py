@@ -143,6 +143,35 @@ def decode(q_rows, K, V, comp_dims, ck, cv, sink: int, recent: int, scale: float
     return softmax_attention(q_rows, Kt, Vt, scale)
 
 
+# ------------------------------------------------------ several queries ----
+
+def softmax_attention_lse(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """(out, lse): softmax attention outputs of the query rows q and, per row,
+    lse_i = log sum_t exp(s_it) with s_it = scale * q[i] . K[t] (natural log,
+    in the units of s), taken through the row maximum so it cannot overflow."""
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    s = scale * (q @ np.asarray(K, dtype=np.float64).T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    out = (e / z) @ np.asarray(V, dtype=np.float64)
+    return out, (m + np.log(z))[:, 0]
+
+
+def attend(q_rows, K, V, comp_dims, ck, cv, sink: int, recent: int, scale: float):
+    """Several queries of one KV head over the compressed cache.
+
+    Every row of q_rows [n, D] attends to all L cached tokens, with no mask
+    between the rows: the attention the pages' kernel serves in prefill as well
+    as in decode [SKILL Architecture overview, Practical guidance].  Returns
+    (out [n, D], lse [n]); the lse lets a caller combine this attention with
+    attention over tokens that are not in the cache (a prefill chunk's own).
+    """
+    Kt = approximate_cache(K, comp_dims, ck, sink, recent)
+    Vt = approximate_cache(V, comp_dims, cv, sink, recent)
+    return softmax_attention_lse(q_rows, Kt, Vt, scale)
+
+
 def exact_attention(q_rows, K, V, scale: float):
     """Uncompressed attention (context only: the approximation error)."""
     return softmax_attention(q_rows, K, V, scale)

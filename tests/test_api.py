@@ -138,3 +138,38 @@ def test_project_host_errors_without_gpu():
     d10 = _desc(n_comp_dims=10)
     assert f(ctypes.byref(d10.c), P(base), P(0), P(base * 2), P(0), P(0), P(0), P(base * 3),
              1 << 30, None) == 2
+
+
+def _attend_size(d, nq):
+    n = ctypes.c_size_t(0)
+    st = fb.lib().fa_attend_workspace_size(ctypes.byref(d.c), nq, ctypes.byref(n))
+    return st, n.value
+
+
+def test_attend_workspace_and_limits():
+    d = _desc()
+    # one query per sequence is fa_decode
+    assert _attend_size(d, 1) == _size(fb.lib().fa_decode_workspace_size, d)
+    st4, n4 = _attend_size(d, 4)
+    assert st4 == 0 and n4 > _attend_size(d, 1)[1] and n4 % 256 == 0
+    assert _attend_size(d, 0)[0] == 2
+    assert _attend_size(d, 1025)[0] == 2
+    # the query rows of one KV head (G * n_query) must fit a workgroup's LDS
+    assert _attend_size(d, 64)[0] == 2 and "LDS" in fb.lib().fa_last_error().decode()
+
+
+def _call_attend(d, nq, q=1, out=8, lse=0, ws=9 * GB, nws=1 << 30):
+    P = lambda v: ctypes.c_void_p(v * GB if 0 < v < 64 else v)
+    return fb.lib().fa_attend(ctypes.byref(d.c), nq, P(q), P(2), P(3), P(4), P(5), P(6), P(7),
+                              ctypes.c_float(0.1), P(out), P(lse), P(ws), nws, None)
+
+
+def test_attend_host_errors_without_gpu():
+    dims_holder = type("T", (), {"data_ptr": lambda self: 10 * GB})()
+    d = _desc(dims=dims_holder)
+    assert _call_attend(d, 0) == 2
+    assert _call_attend(d, 2, q=0) == 1
+    assert _call_attend(d, 2, lse=8 * GB + 64) == 6      # lse inside out
+    assert _call_attend(d, 2, lse=1 * GB + 64) == 6      # lse inside q
+    assert _call_attend(d, 2, lse=9 * GB + 256) == 6     # lse inside the workspace
+    assert _call_attend(d, 2, nws=16) == 4

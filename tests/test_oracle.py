@@ -280,10 +280,97 @@ def pin_gqa_stacking(o):
             assert np.abs(out[b, i] - single[0]).max() < 1e-13
 
 
+def _brute_force_lse(K, V, q, comp, S, R, k, scale):
+    """Pure-Python log sum_t exp(s_t) per query row over the reconstructed keys
+    (the reconstruction of _brute_force, then math.log of a plain sum)."""
+    L, D = len(K), len(K[0])
+    M = max(0, L - S - R)
+    Kt = [list(map(float, row)) for row in K]
+    if M > 0:
+        def phi(n, t):
+            f = (n + 1) // 2
+            r = (f * t) % M
+            a = 1.0 / math.sqrt(M) if (f == 0 or 2 * f == M) else math.sqrt(2.0 / M)
+            trig = math.cos if (n == 0 or n % 2 == 1) else math.sin
+            return a * trig(2.0 * math.pi * r / M)
+        for d in comp:
+            coef = [sum(phi(n, t) * float(K[S + t][d]) for t in range(M)) for n in range(k)]
+            for t in range(M):
+                Kt[S + t][d] = sum(phi(n, t) * coef[n] for n in range(k))
+    return np.array([math.log(sum(math.exp(scale * sum(float(qi[d]) * Kt[t][d] for d in range(D)))
+                                  for t in range(L))) for qi in q])
+
+
+def _oracle_attend(o, K, V, q, comp, S, R, k, scale):
+    start, M = o.segment(len(K), S, R)
+    if M > 0:
+        ck = o.project(K[start:start + M][:, comp], k)
+        cv = o.project(V[start:start + M][:, comp], k)
+    else:
+        ck = cv = np.zeros((k, len(comp)))
+    return o.attend(q, K, V, comp, ck, cv, S, R, scale)
+
+
+def pin_attend_brute_force(o):
+    """Several queries of one KV head: outputs equal one decode per query row
+    and the pure-Python loops; lse equals a pure-Python log of the plain sum of
+    exp(s_t) over the reconstructed keys."""
+    cases = [dict(G=5), dict(L=7, k=5, G=3), dict(L=2, G=4), dict(L=8, S=2, R=2, k=4, G=6)]
+    for i, kw in enumerate(cases):
+        K, V, q, comp, S, R, k = _tiny_case(30 + i, **kw)
+        out, lse = _oracle_attend(o, K, V, q, comp, S, R, k, 0.6)
+        assert np.abs(out - _brute_force(K, V, q, comp, S, R, k, 0.6)).max() < 1e-12, (i, kw)
+        assert np.abs(lse - _brute_force_lse(K, V, q, comp, S, R, k, 0.6)).max() < 1e-12, (i, kw)
+        for r in range(len(q)):
+            one = _oracle_decode(o, K, V, q[r:r + 1], comp, S, R, k, 0.6)
+            assert np.abs(out[r] - one[0]).max() < 1e-13
+
+
+def pin_lse_closed_form(o):
+    """lse in closed form: zero keys give s = 0, so lse = log L; keys all equal
+    to kappa give s = scale q . kappa for every token, so lse = that + log L."""
+    rng = _rng(11)
+    L, D = 37, 6
+    V = rng.standard_normal((L, D))
+    q = rng.standard_normal((3, D))
+    _, lse0 = o.softmax_attention_lse(q, np.zeros((L, D)), V, 0.9)
+    assert np.abs(lse0 - math.log(L)).max() < 1e-13
+    kappa = rng.standard_normal(D)
+    _, lse1 = o.softmax_attention_lse(q, np.tile(kappa, (L, 1)), V, 0.9)
+    assert np.abs(lse1 - (0.9 * q @ kappa + math.log(L))).max() < 1e-12
+
+
+def pin_lse_merge(o):
+    """What the lse is for: attention over the cache and over further tokens
+    (a prefill chunk's own) combine into attention over their union, with
+    weights exp(lse_part - lse_union) and lse_union = logaddexp of the parts.
+    Checked against PyTorch's CPU attention over the concatenated keys."""
+    rng = _rng(12)
+    L, D, Dc, S, R, k = 120, 8, 5, 4, 6, 110
+    K = rng.standard_normal((L, D))
+    V = rng.standard_normal((L, D))
+    q = rng.standard_normal((4, D))
+    comp = np.sort(rng.permutation(D)[:Dc])
+    Kn = rng.standard_normal((9, D))
+    Vn = rng.standard_normal((9, D))
+    start, M = o.segment(L, S, R)
+    out1, lse1 = o.attend(q, K, V, comp, o.project(K[start:start + M][:, comp], k),
+                          o.project(V[start:start + M][:, comp], k), S, R, 0.5)
+    out2, lse2 = o.softmax_attention_lse(q, Kn, Vn, 0.5)
+    lse = np.logaddexp(lse1, lse2)
+    merged = np.exp(lse1 - lse)[:, None] * out1 + np.exp(lse2 - lse)[:, None] * out2
+    Kt = o.approximate_cache(K, comp, o.project(K[start:start + M][:, comp], k), S, R)
+    Vt = o.approximate_cache(V, comp, o.project(V[start:start + M][:, comp], k), S, R)
+    want = _sdpa(q, np.vstack([Kt, Kn]), np.vstack([Vt, Vn]), 0.5)
+    assert np.abs(merged - want).max() < 1e-12
+    s = 0.5 * q @ np.vstack([Kt, Kn]).T
+    assert np.abs(lse - np.log(np.exp(s).sum(1))).max() < 1e-12
+
+
 PINS = [pin_orthonormal, pin_rfft, pin_irfft_lowpass, pin_parseval_bessel,
         pin_closed_form, pin_golden_basis, pin_segment, pin_brute_force,
         pin_reduces_to_attention, pin_factored, pin_softmax_invariants,
-        pin_gqa_stacking]
+        pin_gqa_stacking, pin_attend_brute_force, pin_lse_closed_form, pin_lse_merge]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -353,6 +440,24 @@ def _softmax_transposed_v(q, K, V, scale, return_probs=False):
     return (out, p) if return_probs else out
 
 
+def _lse_log2(q, K, V, scale):
+    out, lse = _ORIG_LSE(q, K, V, scale)
+    return out, lse / math.log(2.0)
+
+
+def _lse_no_max(q, K, V, scale):
+    out, lse = _ORIG_LSE(q, K, V, scale)
+    s = scale * (np.atleast_2d(q) @ np.asarray(K).T)
+    return out, lse - s.max(1)
+
+
+def _attend_values_exact(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale):
+    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent)
+    return fa.softmax_attention_lse(q_rows, Kt, V, scale)
+
+
+_ORIG_LSE = fa.softmax_attention_lse
+
 MUTANTS = {
     "sin_cos_swapped": ("fourier_basis", _basis_variant(swap=True)),
     "sin_sign": ("fourier_basis", _basis_variant(neg_sin=True)),
@@ -366,6 +471,9 @@ MUTANTS = {
     "segment_drops_recent": ("segment", _segment_keeps_recent_short),
     "comp_dims_permuted": ("approximate_cache", _approx_wrong_dims),
     "value_rows_reversed": ("softmax_attention", _softmax_transposed_v),
+    "lse_log2": ("softmax_attention_lse", _lse_log2),
+    "lse_without_max": ("softmax_attention_lse", _lse_no_max),
+    "attend_values_not_reconstructed": ("attend", _attend_values_exact),
 }
 
 
