@@ -273,6 +273,11 @@ def main():
     t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
 
     extra = {}
+    full_b, comp_b = fb.cache_bytes(desc)
+    extra["cache_bytes_full"] = full_b
+    extra["cache_bytes_compressed"] = comp_b
+    extra["cache_compression"] = 1.0 - comp_b / full_b
+    extra["pages_budget_k"] = fb.coef_budget(w.mid_len(int(np.argmax(w.lens))), 0.3)
     if "decode" in steps:
         extra["decode_us"] = t_dec * 1e6
         extra["decode_kv_positions_per_s"] = positions / t_dec

@@ -163,6 +163,32 @@ fa_status_t fa_attend(const fa_desc_t *desc, int32_t n_query, const void *q,
                       float scale, float *out, float *lse, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/*
+ * fa_coef_budget: the number of real coefficients that spans the same space as
+ * the first floor(fraction * M) bins of the middle's real FFT, which is how the
+ * skill page (Step 3) sizes its coefficient budget (fraction 0.3 of the middle
+ * length, kept as frequency bins, Step 2).  The constant bin gives one real
+ * coefficient and every further bin a cosine and a sine, so
+ *   k = 2 * floor(fraction * M) - 1,   clamped to [1, M]
+ * (floor of the double product, as the pages' int() of a float).  Host only;
+ * M < 1 or a fraction outside [0, 1] (or NaN) returns 0.
+ */
+int32_t fa_coef_budget(int32_t M, double fraction);
+
+/*
+ * fa_cache_bytes: memory of the KV cache described by `desc`, before and after
+ * compression (the pages report the KV-cache reduction; skill page, Practical
+ * guidance and References):
+ *   *full:       K and V of every token, all D dims, at desc.dtype;
+ *   *compressed: kx and vx (exact dims of every token), the compressible dims
+ *                of the retained rows (min(L_b, sink+recent) per sequence and
+ *                KV head, as in ke / ve) and, for every sequence with middle
+ *                tokens, ck and cv (k float32 values per compressible dim).
+ * The compression ratio is 1 - compressed / full.  Host only; desc.dims is not
+ * used.  Either output pointer may be NULL.
+ */
+fa_status_t fa_cache_bytes(const fa_desc_t *desc, uint64_t *full, uint64_t *compressed);
+
 /* Static text for a status code. */
 const char *fa_status_string(fa_status_t status);
 

@@ -59,6 +59,9 @@ _SIGS = [
      [ctypes.POINTER(fa_desc_t), ctypes.c_int32] + [ctypes.c_void_p] * 7 +
      [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
       ctypes.c_void_p]),
+    ("fa_coef_budget", ctypes.c_int32, [ctypes.c_int32, ctypes.c_double]),
+    ("fa_cache_bytes", ctypes.c_int,
+     [ctypes.POINTER(fa_desc_t), ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]),
     ("fa_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("fa_last_error", ctypes.c_char_p, []),
     ("fa_version", ctypes.c_int32, []),
@@ -165,6 +168,18 @@ def attend(desc: Desc, n_query, q, kx, vx, ke, ve, ck, cv, scale, out, lse=None,
     _check(lib().fa_attend(ctypes.byref(desc.c), int(n_query), _ptr(q), _ptr(kx), _ptr(vx),
                            _ptr(ke), _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale),
                            _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def coef_budget(M: int, fraction: float = 0.3) -> int:
+    """fa_coef_budget: real coefficients for the first floor(fraction * M) FFT bins."""
+    return int(lib().fa_coef_budget(int(M), float(fraction)))
+
+
+def cache_bytes(desc: Desc):
+    """fa_cache_bytes: (uncompressed, compressed) bytes of the KV cache."""
+    f, c = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    _check(lib().fa_cache_bytes(ctypes.byref(desc.c), ctypes.byref(f), ctypes.byref(c)))
+    return f.value, c.value
 
 
 def to_device(a: np.ndarray, device="cuda"):

@@ -7,6 +7,7 @@
 #include "fa.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -573,6 +574,30 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
   if (e != hipSuccess) return hip_fail(e, "decode split kernel");
   e = fa::launch_decode_merge(a, s);
   if (e != hipSuccess) return hip_fail(e, "decode merge kernel");
+  return FA_OK;
+}
+
+int32_t fa_coef_budget(int32_t M, double fraction) {
+  if (M < 1 || !(fraction >= 0.0 && fraction <= 1.0)) return 0;
+  const int64_t bins = static_cast<int64_t>(std::floor(fraction * static_cast<double>(M)));
+  return static_cast<int32_t>(std::min<int64_t>(M, std::max<int64_t>(1, 2 * bins - 1)));
+}
+
+fa_status_t fa_cache_bytes(const fa_desc_t* desc, uint64_t* full, uint64_t* compressed) {
+  Shape sh;
+  fa_status_t st = validate(desc, &sh);
+  if (st != FA_OK) return st;
+  const uint64_t esz = elem_bytes(sh.dtype), hkv = static_cast<uint64_t>(sh.Hkv);
+  uint64_t f = 0, c = 0;
+  for (int b = 0; b < sh.B; ++b) {
+    const uint64_t L = static_cast<uint64_t>(sh.L[b]);
+    const uint64_t kept = std::min<uint64_t>(L, static_cast<uint64_t>(sh.S) + sh.R);
+    f += 2 * hkv * L * sh.D * esz;
+    c += 2 * hkv * L * sh.Du * esz + 2 * hkv * kept * sh.Dc * esz;
+    if (sh.M[b] > 0) c += 2 * hkv * static_cast<uint64_t>(sh.k) * sh.Dc * sizeof(float);
+  }
+  if (full) *full = f;
+  if (compressed) *compressed = c;
   return FA_OK;
 }
 

@@ -88,6 +88,27 @@ def attend_all(w, ck, cv, scale: float):
     return out, lse
 
 
+def cache_bytes(w):
+    """(uncompressed, compressed) bytes of the workload's KV cache: K and V in
+    full (the sizes of the natural [L, D] arrays), versus the exact dims of
+    every token, the compressible dims of the retained rows and the float32
+    coefficients of every (sequence, KV head) with a middle [SKILL Step 3]."""
+    c = w.cfg
+    esz = np.dtype(w.storage_dtype).itemsize
+    full = comp = 0
+    for b in range(c.batch):
+        for h in range(c.n_kv_heads):
+            K, V = w.natural_kv(b, h)
+            full += (K.size + V.size) * esz
+            comp += 2 * K.shape[0] * c.n_exact * esz  # kx, vx: exact dims of every token
+            start, M = fa.segment(K.shape[0], c.sink, c.recent)
+            kept = K.shape[0] - M
+            comp += 2 * kept * c.n_comp * esz
+            if M > 0 and c.n_comp > 0:
+                comp += 2 * c.n_coef * c.n_comp * 4
+    return full, comp
+
+
 def exact_all(w, scale: float):
     """Uncompressed attention for every query row (context only)."""
     c = w.cfg

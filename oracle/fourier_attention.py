@@ -95,6 +95,18 @@ def project(x_mid: np.ndarray, k: int) -> np.ndarray:
     return Phi.T @ x_mid
 
 
+def coef_budget(M: int, fraction: float = 0.3) -> int:
+    """Real coefficients for the pages' coefficient budget [SKILL Step 3]: the
+    first ``int(fraction * M)`` bins of the middle's rfft are kept (Step 2).
+    Bin 0 is the constant (one real coefficient); each further bin below the
+    Nyquist frequency has a cosine and a sine.  Clamped to [1, M]."""
+    bins = int(fraction * M)
+    real = 0
+    for j in range(bins):
+        real += 1 if (j == 0 or 2 * j == M) else 2
+    return max(1, min(M, real))
+
+
 # --------------------------------------------------------------- step 4 -----
 
 def reconstruct(coef: np.ndarray, M: int) -> np.ndarray:

@@ -173,3 +173,26 @@ def test_attend_host_errors_without_gpu():
     assert _call_attend(d, 2, lse=1 * GB + 64) == 6      # lse inside q
     assert _call_attend(d, 2, lse=9 * GB + 256) == 6     # lse inside the workspace
     assert _call_attend(d, 2, nws=16) == 4
+
+
+def test_coef_budget_matches_oracle():
+    from oracle import fourier_attention as fa
+    for M in list(range(1, 70)) + [416, 4000, 32672, 131040]:
+        for frac in (0.0, 0.1, 0.3, 0.5, 0.55, 0.7, 1.0):
+            assert fb.coef_budget(M, frac) == fa.coef_budget(M, frac), (M, frac)
+    assert fb.coef_budget(0, 0.3) == 0 and fb.coef_budget(10, 1.5) == 0
+    assert fb.coef_budget(10, float("nan")) == 0
+
+
+def test_cache_bytes_matches_oracle():
+    from long_context_decode_fourier_amd import workloads as wl
+    from oracle import batch as ob
+    cases = [(wl.custom(dtype="bf16", batch=3, n_q_heads=4, n_kv_heads=2, head_dim=16, n_comp=6,
+                        n_coef=9, seed=1), [300, 50, 105]),
+             (wl.custom(dtype="f32", batch=1, n_q_heads=2, n_kv_heads=2, head_dim=8, n_comp=0,
+                        n_coef=1, seed=2), [40]),
+             (wl.CONFIGS["llama2_7b_layer"], None)]
+    for cfg, lens in cases:
+        w = wl.make(cfg, lens=lens)
+        d = fb.Desc.from_workload(w)
+        assert fb.cache_bytes(d) == ob.cache_bytes(w), cfg.name

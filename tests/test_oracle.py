@@ -367,10 +367,47 @@ def pin_lse_merge(o):
     assert np.abs(lse - np.log(np.exp(s).sum(1))).max() < 1e-12
 
 
+def pin_coef_budget(o):
+    """The pages' budget keeps the first int(fraction * M) rfft bins [SKILL
+    Steps 2-3]; coef_budget must give the k whose projector Phi_k Phi_k^T is
+    exactly that low-pass (numpy's irfft of the zero-padded bins), for the
+    pages' fraction 0.3 (tests/golden/pages_facts.json) and for fractions that
+    reach the Nyquist bin and the whole spectrum."""
+    with open(os.path.join(GOLDEN, "pages_facts.json")) as f:
+        frac0 = json.load(f)["example_coefficient_fraction"]
+    rng = _rng(13)
+    for M in (4, 7, 8, 10, 33, 416, 1000):
+        x = rng.standard_normal(M)
+        for frac in (frac0, 0.55, 0.7, 1.0):
+            bins = int(frac * M)
+            if bins < 1:
+                continue
+            X = np.fft.rfft(x)
+            X[bins:] = 0
+            low = np.fft.irfft(X, n=M)
+            k = o.coef_budget(M, frac)
+            P = o.fourier_basis(M, k)
+            assert np.abs(P @ (P.T @ x) - low).max() < 1e-12, (M, frac, k)
+    assert o.coef_budget(3, 0.3) == 1  # no bin kept: the constant at least
+
+
+def pin_cache_bytes(o):
+    """Cache sizes on a worked example: one f32 head, L = 100, D = 4 (2
+    compressible), sink = recent = 1, k = 3: full 2*100*4*4 = 3200 bytes;
+    compressed = exact dims 2*100*2*4 + retained rows 2*2*2*4 + coefficients
+    2*3*2*4 = 1680 bytes; a second sequence of 2 tokens has no middle and
+    keeps both rows (2*2*4*4 = 64 bytes either way)."""
+    cfg = wl.custom(dtype="f32", batch=2, n_q_heads=1, n_kv_heads=1, head_dim=4, n_comp=2,
+                    n_coef=3, sink=1, recent=1, mask="low", seed=14)
+    w = wl.make(cfg, lens=[100, 2])
+    assert ob.cache_bytes(w) == (3200 + 64, 1680 + 64)
+
+
 PINS = [pin_orthonormal, pin_rfft, pin_irfft_lowpass, pin_parseval_bessel,
         pin_closed_form, pin_golden_basis, pin_segment, pin_brute_force,
         pin_reduces_to_attention, pin_factored, pin_softmax_invariants,
-        pin_gqa_stacking, pin_attend_brute_force, pin_lse_closed_form, pin_lse_merge]
+        pin_gqa_stacking, pin_attend_brute_force, pin_lse_closed_form, pin_lse_merge,
+        pin_coef_budget, pin_cache_bytes]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -458,6 +495,10 @@ def _attend_values_exact(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale):
 
 _ORIG_LSE = fa.softmax_attention_lse
 
+
+def _budget_plus_one_pair(M, fraction=0.3):
+    return min(M, 2 * int(fraction * M) + 1)
+
 MUTANTS = {
     "sin_cos_swapped": ("fourier_basis", _basis_variant(swap=True)),
     "sin_sign": ("fourier_basis", _basis_variant(neg_sin=True)),
@@ -474,6 +515,7 @@ MUTANTS = {
     "lse_log2": ("softmax_attention_lse", _lse_log2),
     "lse_without_max": ("softmax_attention_lse", _lse_no_max),
     "attend_values_not_reconstructed": ("attend", _attend_values_exact),
+    "budget_one_pair_too_many": ("coef_budget", _budget_plus_one_pair),
 }
 
 
