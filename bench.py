@@ -100,6 +100,52 @@ def box_peaks(torch):
             "gemm": "torch.matmul fp16 %dx%dx%d" % (m, m, m), "copy": "torch copy_ of 2 GiB fp32"}
 
 
+def approximation_context(w, out, ck, cv, scale):
+    """How far the compressed cache's result is from the uncompressed one, as
+    context (not a gate).  Decode: the GPU's outputs against plain softmax
+    attention over the full K and V (float64 numpy, written here), on sampled
+    (sequence, KV head) blocks.  Projection only: the share of each sampled
+    middle column's energy that the k coefficients miss, which for an
+    orthonormal basis is sqrt(|x|^2 - |c|^2) / |x| (no reconstruction needed)."""
+    c = w.cfg
+    G = c.n_q_heads // c.n_kv_heads
+    longest = int(np.argmax(w.lens))
+    if c.batch * c.n_kv_heads <= 32:
+        blocks = [(b, h) for b in range(c.batch) for h in range(c.n_kv_heads)]
+    else:
+        blocks = [(longest, 0), (longest, c.n_kv_heads - 1)]
+    if out is None:
+        M = w.mid_len(longest)
+        worst, miss, energy = 0.0, 0.0, 0.0
+        for h in (0, c.n_kv_heads - 1):
+            for X, C in ((w.kc, ck), (w.vc, cv)):
+                x = w.f64(w.block(X, longest, h))[c.sink:c.sink + M]
+                coef = C[longest * c.n_kv_heads + h].astype(np.float64)
+                nx, ncf = (x * x).sum(0), (coef * coef).sum(0)
+                worst = max(worst, float(np.sqrt(np.maximum(nx - ncf, 0.0) / nx).max()))
+                miss += float(np.maximum(nx - ncf, 0.0).sum())
+                energy += float(nx.sum())
+        return {"kind": "middle-row energy the coefficients miss (K and V, sampled KV heads)",
+                "rel_l2": float(np.sqrt(miss / energy)), "worst_column_rel_l2": worst,
+                "blocks": [[longest, 0], [longest, c.n_kv_heads - 1]]}
+    q4 = w.q if w.q.ndim == 4 else w.q[:, None]
+    o4 = out if out.ndim == 4 else out[:, None]
+    num = den = 0.0
+    mab = 0.0
+    for b, h in blocks:
+        K, V = w.natural_kv(b, h)
+        q = w.f64(q4[b, :, h * G:(h + 1) * G]).reshape(-1, c.head_dim)
+        sc = scale * (q @ K.T)
+        p = np.exp(sc - sc.max(1, keepdims=True))
+        exact = (p / p.sum(1, keepdims=True)) @ V
+        got = o4[b, :, h * G:(h + 1) * G].reshape(-1, c.head_dim).astype(np.float64)
+        mab = max(mab, float(np.abs(got - exact).max()))
+        num += float(((got - exact) ** 2).sum())
+        den += float((exact ** 2).sum())
+    return {"kind": "GPU output vs uncompressed attention", "max_abs": mab,
+            "rel_l2": float(np.sqrt(num / den)), "blocks": [list(x) for x in blocks]}
+
+
 def cpu_baseline(w, scale, seconds):
     """The oracle (fp64 numpy) on the same workload, repeated ~`seconds`."""
     from oracle import batch as ob
@@ -311,6 +357,17 @@ def main():
     except (OSError, ValueError, KeyError):
         pass
 
+    # context: the result against attention over the uncompressed cache
+    s0 = sets[0]
+    if "project" in steps:
+        call_project(s0, stream)
+    if "decode" in steps:
+        call_decode(s0, stream)
+    torch.cuda.synchronize()
+    approx = approximation_context(
+        w, s0["out"].cpu().numpy() if "decode" in steps else None,
+        s0["ck"].cpu().numpy(), s0["cv"].cpu().numpy(), scale)
+
     cpu = None
     if not args.no_cpu_baseline:
         dt, threads, n = cpu_baseline(w, scale, args.cpu_seconds)
@@ -337,6 +394,7 @@ def main():
         "launch": "hip graph replay (one graph per call and input copy)" if args.graph else "eager",
         "roofline": roof,
         "cpu_baseline": cpu,
+        "approx_error_vs_exact": approx,
         "calls": extra,
     }
     print(json.dumps(line))
