@@ -127,7 +127,7 @@ def approximation_context(w, out, ck, cv, scale):
                 energy += float(nx.sum())
         return {"kind": "middle-row energy the coefficients miss (K and V, sampled KV heads)",
                 "rel_l2": float(np.sqrt(miss / energy)), "worst_column_rel_l2": worst,
-                "blocks": [[longest, 0], [longest, c.n_kv_heads - 1]]}
+                "blocks": "(sequence, KV head) blocks %s" % [[longest, 0], [longest, c.n_kv_heads - 1]]}
     q4 = w.q if w.q.ndim == 4 else w.q[:, None]
     o4 = out if out.ndim == 4 else out[:, None]
     num = den = 0.0
@@ -142,8 +142,10 @@ def approximation_context(w, out, ck, cv, scale):
         mab = max(mab, float(np.abs(got - exact).max()))
         num += float(((got - exact) ** 2).sum())
         den += float((exact ** 2).sum())
+    where = ("all %d (sequence, KV head) blocks" % len(blocks) if len(blocks) > 2
+             else "(sequence, KV head) blocks %s" % [list(x) for x in blocks])
     return {"kind": "GPU output vs uncompressed attention", "max_abs": mab,
-            "rel_l2": float(np.sqrt(num / den)), "blocks": [list(x) for x in blocks]}
+            "rel_l2": float(np.sqrt(num / den)), "blocks": where}
 
 
 def cpu_baseline(w, scale, seconds):
