@@ -151,8 +151,9 @@ fa_status_t fa_attend_workspace_size(const fa_desc_t *desc, int32_t n_query, siz
  *                              the softmax denominator in the units of s
  *                              (scale included), or NULL.
  * Query t of head i reads KV head i / (Hq/Hkv); the G * n_query query rows of
- * a KV head share one pass over its cache.  n_query is 1 .. 1024, and the
- * query rows of one KV head, G * n_query, must fit a workgroup's LDS
+ * a KV head share one pass over its cache.  n_query is 1 .. 1024, a sequence
+ * has at most 65536 query rows (n_query * Hq; this bounds fa_decode's Hq too),
+ * and the query rows of one KV head, G * n_query, must fit a workgroup's LDS
  * (FA_ERR_SHAPE otherwise; 64 rows at D = 128 fit).  Everything else
  * (required pointers, alignment, errors) is as for fa_decode, which is
  * fa_attend with n_query = 1 and lse = NULL.

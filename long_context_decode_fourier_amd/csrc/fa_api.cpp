@@ -105,9 +105,13 @@ fa_status_t validate(const fa_desc_t* d, Shape* sh) {
 // n_query queries per sequence run as n_query * Hq "virtual" query heads, the
 // G * n_query rows of a KV head sharing its cache reads.
 constexpr int kMaxQueries = 1024;
+constexpr int64_t kMaxRows = 1 << 16;  // query rows per sequence (n_query * Hq)
 fa_status_t apply_queries(int32_t n_query, Shape* sh) {
   if (n_query < 1 || n_query > kMaxQueries)
     return fail(FA_ERR_SHAPE, "n_query %d outside [1, %d]", n_query, kMaxQueries);
+  if (static_cast<int64_t>(sh->Hq) * n_query > kMaxRows)
+    return fail(FA_ERR_SHAPE, "n_query * n_q_heads = %lld exceeds %lld query rows per sequence",
+                static_cast<long long>(sh->Hq) * n_query, static_cast<long long>(kMaxRows));
   sh->nq = n_query;
   sh->Hq *= n_query;
   sh->G *= n_query;

@@ -154,6 +154,8 @@ def test_attend_workspace_and_limits():
     assert st4 == 0 and n4 > _attend_size(d, 1)[1] and n4 % 256 == 0
     assert _attend_size(d, 0)[0] == 2
     assert _attend_size(d, 1025)[0] == 2
+    big = _desc(n_q_heads=1 << 15, n_kv_heads=1 << 14)  # 2^15 heads x 4 queries: too many rows
+    assert _attend_size(big, 4)[0] == 2 and "query rows" in fb.lib().fa_last_error().decode()
     # the query rows of one KV head (G * n_query) must fit a workgroup's LDS
     assert _attend_size(d, 64)[0] == 2 and "LDS" in fb.lib().fa_last_error().decode()
 
