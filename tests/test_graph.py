@@ -1,4 +1,4 @@
-"""HIP graph capture of fa_project + fa_decode.
+"""HIP graph capture of fa_project + fa_decode, and of fa_attend.
 
 A serving loop (and bench.py) launches the step as HIP graphs.  The library
 makes no allocation, host synchronisation or memset, so both calls can be
@@ -77,3 +77,52 @@ def test_graph_replays_match_eager(fb, name):
         fb.decode(desc, q, kx, vx, ke, ve, ck, cv, scale, other, ws_d, torch.cuda.current_stream())
         torch.cuda.synchronize()
         assert torch.equal(other, want[4])
+
+
+def test_graph_attend_with_lse(fb):
+    """fa_attend (four queries per sequence, with lse) captured and replayed."""
+    print("graph replay attend", flush=True)
+    sys.stdout.flush()
+    cfg = wl.custom(name="graph_attend", dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2,
+                    head_dim=128, n_comp=64, n_coef=129, n_query=4, seed=77)
+    w = wl.make(cfg, lens=[1800, 700])
+    c = w.cfg
+    dims = torch.from_numpy(w.dims).cuda()
+    desc = fb.Desc.from_workload(w, dims)
+    kc, vc = fb.to_device(w.kc), fb.to_device(w.vc)
+    q, kx, vx = fb.to_device(w.q), fb.to_device(w.kx), fb.to_device(w.vx)
+    nblk, E = c.batch * c.n_kv_heads, c.sink + c.recent
+    ck = torch.empty((nblk, c.n_coef, c.n_comp), device="cuda")
+    cv = torch.empty_like(ck)
+    ke = torch.empty((nblk, E, c.n_comp), dtype=kc.dtype, device="cuda")
+    ve = torch.empty_like(ke)
+    fb.project(desc, kc, vc, ck, cv, ke, ve)
+    out = torch.empty((c.batch, 4, c.n_q_heads, c.head_dim), device="cuda")
+    lse = torch.empty((c.batch, 4, c.n_q_heads), device="cuda")
+    ws = fb.workspace(fb.attend_workspace_size(desc, 4))
+    scale = 1.0 / np.sqrt(c.head_dim)
+
+    def step(st):
+        fb.attend(desc, 4, q, kx, vx, ke, ve, ck, cv, scale, out, lse, ws, st)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = (out.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want[0]) and torch.equal(lse, want[1]), "replay %d differs" % r
+        # eager work on the same workspace between replays (one query needs less)
+        one = torch.empty((c.batch, c.n_q_heads, c.head_dim), device="cuda")
+        fb.decode(desc, q[:, 0].contiguous(), kx, vx, ke, ve, ck, cv, scale, one, ws,
+                  torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.isfinite(one).all()
