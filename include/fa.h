@@ -150,11 +150,14 @@ fa_status_t fa_attend_workspace_size(const fa_desc_t *desc, int32_t n_query, siz
  *   lse  [B, n_query, Hq]      float32 log sum_t exp(s_t), the natural log of
  *                              the softmax denominator in the units of s
  *                              (scale included), or NULL.
- * Query t of head i reads KV head i / (Hq/Hkv); the G * n_query query rows of
- * a KV head share one pass over its cache.  n_query is 1 .. 1024, a sequence
- * has at most 65536 query rows (n_query * Hq; this bounds fa_decode's Hq too),
- * and the query rows of one KV head, G * n_query, must fit a workgroup's LDS
- * (FA_ERR_SHAPE otherwise; 64 rows at D = 128 fit).  Everything else
+ * Query t of head i reads KV head i / (Hq/Hkv).  The queries run in passes
+ * over the cache: one pass takes as many queries as the prep kernel's LDS
+ * holds for a KV head's rows on the single query's kernel path (96 query rows
+ * per KV head at D = 128, Dc = 64, i.e. 24 queries of a 4-head group), and the
+ * G * (queries of the pass) rows of a KV head share that pass; more queries
+ * take more passes, in order, on `stream`.  n_query is 1 .. 1024 and a
+ * sequence has at most 65536 query rows (n_query * Hq; this bounds
+ * fa_decode's Hq too); FA_ERR_SHAPE otherwise.  Everything else
  * (required pointers, alignment, errors) is as for fa_decode, which is
  * fa_attend with n_query = 1 and lse = NULL.
  */

@@ -260,6 +260,8 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   a.sink = sh.S;
   a.recent = sh.R;
   a.nq = sh.nq;
+  a.nq_total = sh.nq;
+  a.q0 = 0;
   // MFMA path for 16-bit caches: as many stacked rows as the basis length
   // pays for (long bases amortise their generation over more rows).
   int rows = 0;
@@ -369,6 +371,53 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
 }
 
 size_t elem_bytes(int dtype) { return dtype == FA_BF16 ? 2 : 4; }
+
+// Several queries: the n_query queries of a sequence run in passes of `chunk`
+// queries (the last pass may hold fewer).  One pass holds as many queries as
+// fit the prep kernel's LDS on the same kernel path as a single query, so a
+// prefill chunk larger than that reads the cache once per pass.
+struct AttendPlan {
+  int n_query, chunk;
+  DecPlan full, last;  // plans of a full pass and of the last pass
+  size_t ws_bytes;
+};
+
+fa_status_t plan_queries(const Shape& base, int nq, DecPlan* p) {
+  Shape sh = base;
+  const fa_status_t st = apply_queries(nq, &sh);
+  return st != FA_OK ? st : plan_decode(sh, p);
+}
+
+fa_status_t plan_attend(const Shape& base, int32_t n_query, AttendPlan* ap) {
+  Shape probe = base;
+  fa_status_t st = apply_queries(n_query, &probe);  // range checks of the whole call
+  if (st != FA_OK) return st;
+  DecPlan one;
+  if ((st = plan_queries(base, 1, &one)) != FA_OK) return st;
+  // largest pass that plans on the single query's kernel path (both
+  // conditions only get harder as the pass grows)
+  auto fits = [&](int c, DecPlan* p) {
+    return plan_queries(base, c, p) == FA_OK && p->args.mfma == one.args.mfma;
+  };
+  int lo = 1, hi = n_query;
+  DecPlan tmp;
+  if (!fits(hi, &tmp)) {
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (fits(mid, &tmp)) lo = mid; else hi = mid;
+    }
+    hi = lo;
+  }
+  ap->n_query = n_query;
+  ap->chunk = hi;
+  if (hi == 1) ap->full = one;
+  else if ((st = plan_queries(base, hi, &ap->full)) != FA_OK) return st;
+  const int rest = n_query % hi;
+  ap->last = ap->full;
+  if (rest && (st = plan_queries(base, rest, &ap->last)) != FA_OK) return st;
+  ap->ws_bytes = std::max(ap->full.ws_bytes, ap->last.ws_bytes);
+  return FA_OK;
+}
 
 }  // namespace
 
@@ -484,11 +533,9 @@ fa_status_t fa_attend_workspace_size(const fa_desc_t* desc, int32_t n_query, siz
   if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
   fa_status_t st = validate(desc, &sh);
   if (st != FA_OK) return st;
-  if ((st = apply_queries(n_query, &sh)) != FA_OK) return st;
-  DecPlan p;
-  st = plan_decode(sh, &p);
-  if (st != FA_OK) return st;
-  *bytes = p.ws_bytes;
+  AttendPlan ap;
+  if ((st = plan_attend(sh, n_query, &ap)) != FA_OK) return st;
+  *bytes = ap.ws_bytes;
   return FA_OK;
 }
 
@@ -515,17 +562,19 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
   if (sh.Dc > 0 && sh.any_mid && (!ck || !cv))
     return fail(FA_ERR_NULL, "ck and cv are required when a sequence has middle tokens");
   if (!(scale == scale)) return fail(FA_ERR_SHAPE, "scale is NaN");
-  DecPlan p;
-  st = plan_decode(sh, &p);
-  if (st != FA_OK) return st;
+  Shape base;
+  validate(desc, &base);
+  AttendPlan ap;
+  if ((st = plan_attend(base, n_query, &ap)) != FA_OK) return st;
+  const DecPlan& p = ap.full;
   if (p.args.mfma) {
     const void* rows16[4] = {kx, vx, ke, ve};
     for (const void* ptr : rows16)
       if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 15))
         return fail(FA_ERR_SHAPE, "bf16 kx, vx, ke, ve must be 16-byte aligned");
   }
-  if (!workspace || workspace_bytes < p.ws_bytes)
-    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+  if (!workspace || workspace_bytes < ap.ws_bytes)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ap.ws_bytes,
                 workspace ? workspace_bytes : 0);
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return fail(FA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
@@ -543,41 +592,46 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
                          static_cast<size_t>(sh.Hkv) * sh.D * sizeof(int32_t)};
   for (int i = 0; i < 8; ++i) {
     if (overlap(out, out_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "out overlaps an input");
-    if (overlap(workspace, p.ws_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "workspace overlaps an input");
+    if (overlap(workspace, ap.ws_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "workspace overlaps an input");
   }
-  if (overlap(out, out_bytes, workspace, p.ws_bytes)) return fail(FA_ERR_ALIAS, "out overlaps the workspace");
+  if (overlap(out, out_bytes, workspace, ap.ws_bytes)) return fail(FA_ERR_ALIAS, "out overlaps the workspace");
   if (lse) {
     for (int i = 0; i < 8; ++i)
       if (overlap(lse, lse_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "lse overlaps an input");
-    if (overlap(lse, lse_bytes, out, out_bytes) || overlap(lse, lse_bytes, workspace, p.ws_bytes))
+    if (overlap(lse, lse_bytes, out, out_bytes) || overlap(lse, lse_bytes, workspace, ap.ws_bytes))
       return fail(FA_ERR_ALIAS, "lse overlaps out or the workspace");
   }
 
-  fa::DecodeArgs& a = p.args;
-  a.q = q;
-  a.kx = kx;
-  a.vx = vx;
-  a.ke = ke;
-  a.ve = ve;
-  a.ck = ck;
-  a.cv = cv;
-  a.dims = desc->dims;
-  a.out = out;
-  a.scale = scale;
-  a.lse = lse;
-  a.A = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_A);
-  a.A16 = static_cast<char*>(workspace) + p.off_A;
-  a.Q16 = static_cast<char*>(workspace) + p.off_q16;
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_part);
-  a.mrg = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_mrg);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  e = fa::launch_decode_prep(a, s);
-  if (e != hipSuccess) return hip_fail(e, "decode prep kernel");
-  e = a.mfma ? fa::launch_decode_mfma(a, p.nitems, s) : fa::launch_decode_split(a, p.nitems, s);
-  if (e != hipSuccess) return hip_fail(e, "decode split kernel");
-  e = fa::launch_decode_merge(a, s);
-  if (e != hipSuccess) return hip_fail(e, "decode merge kernel");
+  for (int t0 = 0; t0 < n_query; t0 += ap.chunk) {
+    const DecPlan& pp = (n_query - t0 >= ap.chunk) ? ap.full : ap.last;
+    fa::DecodeArgs a = pp.args;
+    a.nq_total = n_query;
+    a.q0 = t0;
+    a.q = q;
+    a.kx = kx;
+    a.vx = vx;
+    a.ke = ke;
+    a.ve = ve;
+    a.ck = ck;
+    a.cv = cv;
+    a.dims = desc->dims;
+    a.out = out;
+    a.scale = scale;
+    a.lse = lse;
+    a.A = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_A);
+    a.A16 = static_cast<char*>(workspace) + pp.off_A;
+    a.Q16 = static_cast<char*>(workspace) + pp.off_q16;
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_part);
+    a.mrg = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_mrg);
+    hipError_t e;
+    e = fa::launch_decode_prep(a, s);
+    if (e != hipSuccess) return hip_fail(e, "decode prep kernel");
+    e = a.mfma ? fa::launch_decode_mfma(a, pp.nitems, s) : fa::launch_decode_split(a, pp.nitems, s);
+    if (e != hipSuccess) return hip_fail(e, "decode split kernel");
+    e = fa::launch_decode_merge(a, s);
+    if (e != hipSuccess) return hip_fail(e, "decode merge kernel");
+  }
   return FA_OK;
 }
 

@@ -78,21 +78,24 @@ struct DecodeArgs {
   int RS;        // floats per partial row: 2 + du + dc + kpad
   int MS;        // floats per merged row: dc + kpad + 1
   float scale;
-  int nq;        // queries per sequence; hq and G count nq * (query heads)
+  int nq;        // queries per sequence in this pass; hq and G count nq * (query heads)
+  int nq_total;  // queries per sequence in q / out / lse (passes of nq cover q0 ..)
+  int q0;        // first query of this pass
   float* lse;    // optional [B][nq][Hq]: log sum_t exp(s_t) of each query row
   SeqTable seq;  // item0 / nsplit (splits per row, edge split included) / chunk
   int32_t prow0[kMaxBatch];  // first partial row of sequence b: sum Hq * nsplit
 };
 
 // Rows of the kernels are "virtual" query heads: with nq queries per
-// sequence, KV head h owns rows h*G .. h*G + G-1 (G = nq * Hq/Hkv), row
-// h*G + t*(G/nq) + g being query t of query head h*(G/nq) + g.  q, out and
-// lse are laid out [B][nq][Hq]; this gives the (b, row) entry's index in them.
+// sequence in a pass, KV head h owns rows h*G .. h*G + G-1 (G = nq * Hq/Hkv),
+// row h*G + t*(G/nq) + g being query q0 + t of query head h*(G/nq) + g.  q,
+// out and lse are laid out [B][nq_total][Hq]; this gives the (b, row) entry's
+// index in them.
 __host__ __device__ inline int64_t q_row(const DecodeArgs& a, int b, int i) {
-  if (a.nq == 1) return static_cast<int64_t>(b) * a.hq + i;
+  if (a.nq_total == 1) return static_cast<int64_t>(b) * a.hq + i;
   const int gu = a.G / a.nq;  // query heads per KV head
   const int h = i / a.G, r = i % a.G;
-  return (static_cast<int64_t>(b) * a.nq + r / gu) * (a.hq / a.nq) + h * gu + r % gu;
+  return (static_cast<int64_t>(b) * a.nq_total + a.q0 + r / gu) * (a.hq / a.nq) + h * gu + r % gu;
 }
 
 // The sink/recent split runs on MFMA for 16-byte rows, whole 32-dim chunks

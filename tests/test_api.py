@@ -156,8 +156,11 @@ def test_attend_workspace_and_limits():
     assert _attend_size(d, 1025)[0] == 2
     big = _desc(n_q_heads=1 << 15, n_kv_heads=1 << 14)  # 2^15 heads x 4 queries: too many rows
     assert _attend_size(big, 4)[0] == 2 and "query rows" in fb.lib().fa_last_error().decode()
-    # the query rows of one KV head (G * n_query) must fit a workgroup's LDS
-    assert _attend_size(d, 64)[0] == 2 and "LDS" in fb.lib().fa_last_error().decode()
+    # more query rows than one pass over the cache holds run as several passes
+    # that share one workspace: 64 and 1024 queries need no more than one pass
+    st64, n64 = _attend_size(d, 64)
+    st1k, n1k = _attend_size(d, 1024)
+    assert st64 == 0 and st1k == 0 and n1k == n64
 
 
 def _call_attend(d, nq, q=1, out=8, lse=0, ws=9 * GB, nws=1 << 30):

@@ -6,10 +6,11 @@ max-abs <= 3e-3); the log-sum-exp of each row to the same bars (it is a
 weighted mean of the scores' errors, so it shares the outputs' error budget).
 Each case runs end to end (GPU coefficients against oracle coefficients) and in
 isolation (both sides fed the oracle's coefficients rounded to fp32).  The
-cases cover 1, 3, 4, 8 and 16 queries, GQA groups of 1 and 4 (so 3 to 64 query
-rows per KV head, on both the MFMA and the VALU edge blocks), a sequence
-without middle tokens, fp32 inputs, and sampled blocks of the LLaMA-3-8B-shaped
-batch with four queries per sequence.
+cases cover 1, 3, 4, 8, 16, 40 and 300 queries, GQA groups of 1, 2 and 4 (3 to
+600 query rows per KV head: the MFMA and the VALU edge blocks, and queries run
+as several passes over the cache), a sequence without middle tokens, fp32
+inputs, and sampled blocks of the LLaMA-3-8B-shaped batch with four queries
+per sequence.
 """
 import sys
 
@@ -92,6 +93,13 @@ CASES = {
                                n_comp=64, n_coef=33, n_query=16), [90, 260]),
     "f32_q4": (dict(dtype="f32", batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64, n_comp=32,
                     n_coef=33, n_query=4), [512, 200]),
+    # more queries than one pass over the cache holds: 40 queries of a 4-head
+    # group (160 rows per KV head) run as passes of 24 and 16 queries; 300 fp32
+    # queries of a 2-head group as passes of up to 195
+    "bf16_g4_q40_passes": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                n_comp=64, n_coef=97, n_query=40), [1300, 600]),
+    "f32_g2_q300_passes": (dict(dtype="f32", batch=1, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                                n_comp=32, n_coef=17, n_query=300), [230]),
 }
 
 
