@@ -317,8 +317,14 @@ def main():
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    t_proj = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-    t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    d_proj = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    d_dec = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_proj = float(d_proj.mean())
+    t_dec = float(d_dec.mean())
+
+    def spread(d):  # per-call durations, microseconds
+        p10, p50, p90 = np.percentile(d, [10, 50, 90]) * 1e6
+        return {"p10": float(p10), "median": float(p50), "p90": float(p90)}
 
     extra = {}
     full_b, comp_b = fb.cache_bytes(desc)
@@ -328,11 +334,13 @@ def main():
     extra["pages_budget_k"] = fb.coef_budget(w.mid_len(int(np.argmax(w.lens))), 0.3)
     if "decode" in steps:
         extra["decode_us"] = t_dec * 1e6
+        extra["decode_us_spread"] = spread(d_dec)
         extra["decode_kv_positions_per_s"] = positions / t_dec
         extra["decode_hbm_GBps"] = dec_bytes / t_dec / 1e9
         extra["decode_algorithmic_bytes"] = dec_bytes
     if "project" in steps:
         extra["project_us"] = t_proj * 1e6
+        extra["project_us_spread"] = spread(d_proj)
         extra["project_tflops"] = proj_flops / t_proj / 1e12
         extra["project_algorithmic_flops"] = proj_flops
     # dominant call: the larger share of the step
