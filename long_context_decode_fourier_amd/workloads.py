@@ -7,8 +7,8 @@ two sides share.
 
 Workload shapes follow the scenarios this library is measured on (single
 fp32 head, a LLaMA-2-7B-shaped layer, a LLaMA-3-8B-shaped GQA batch, the same
-batch with four queries per sequence, a long prefill projection and a ragged
-long-context batch).  No dataset, checkpoint or
+batch with four queries or a 64-token prefill chunk per sequence, a long
+prefill projection and a ragged long-context batch).  No dataset, checkpoint or
 trained weight is used: the compressible head dims of K and V are smooth
 signals (a sum of four low-frequency sinusoids plus small noise), which is the
 kind of slowly varying time series the method's Fourier projection targets
@@ -117,6 +117,13 @@ CONFIGS = {
         seed=3, steps=("decode",), n_query=4,
         note="the LLaMA-3-8B-shaped GQA cache (same draws) with 4 queries per "
              "sequence attending to it (e.g. 4 draft tokens verified at once)"),
+    "llama3_8b_gqa_chunk64": Config(
+        name="llama3_8b_gqa_chunk64", dtype="bf16", batch=4, n_q_heads=32,
+        n_kv_heads=8, head_dim=128, n_comp=96, n_coef=1025, seq_len=32768,
+        seed=3, steps=("decode",), n_query=64,
+        note="the LLaMA-3-8B-shaped GQA cache (same draws) with a 64-token "
+             "prefill chunk per sequence attending to it (256 query rows per KV "
+             "head, run as passes over the cache)"),
     "ragged_batch": Config(
         name="ragged_batch", dtype="bf16", batch=16, n_q_heads=32,
         n_kv_heads=8, head_dim=128, n_comp=64, n_coef=2049,
