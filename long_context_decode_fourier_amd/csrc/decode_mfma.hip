@@ -124,6 +124,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int h0 = qi0 / a.G;
   const int nheads = rows >= a.G ? rows / a.G : 1;
   const int rph = min(rows, a.G);  // query rows per KV head inside the item
+  // 16-row blocks per KV head: 1 when a head's rows sit inside one block, 2
+  // when one head's rows fill an item of more than 16 rows.  The exact-dim
+  // work is cut into (KV head, row block) units u: head u / bph, block u % bph.
+  const int bph = MB > 1 ? (rph + 15) >> 4 : 1;  // compile-time 1 for one-block items
+  const int bsh = bph - 1;  // log2(bph): unit u is head u >> bsh, block u & bsh
+  const int nunit = nheads * bph;
   const bool has_mid = a.dc > 0;  // items exist only for sequences with middle tokens
   const int du = a.du, dc = a.dc;
   const int du32 = (du + 31) & ~31;
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   uint4 kreg[XP][KCM];
 #pragma unroll
   for (int x = 0; x < XP; ++x)
-    kx_src[x] = (row0 + static_cast<int64_t>(h0 + wave + NW * x) * L + t_begin + l16) * du + 8 * g4;
+    kx_src[x] = (row0 + static_cast<int64_t>(h0 + ((wave + NW * x) >> bsh)) * L + t_begin + l16) * du + 8 * g4;
   auto prefetch_k = [&](int tile) {
     const int64_t shift = static_cast<int64_t>(tile - t_begin) * du;
     const bool tok_ok = tile + l16 < t_end;
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kc = 0; kc < KCM; ++kc) {
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (tok_ok && wave + NW * x < nheads && kc < KC && 32 * kc + 8 * g4 < du)
+        if (tok_ok && wave + NW * x < nunit && kc < KC && 32 * kc + 8 * g4 < du)
           v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kx) + kx_src[x] + shift + 32 * kc);
         kreg[x][kc] = v;
       }
@@ -392,10 +398,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     if (du8 > 0) {
 #pragma unroll
       for (int x = 0; x < XP; ++x) {
-        const int hh = wave + NW * x;
-        if (hh < nheads) {
-          const int rb = (rows >= a.G) ? hh * a.G : 0;
-          const int mb = rb >> 4;
+        const int un = wave + NW * x;
+        if (un < nunit) {
+          const int rb = (rows >= a.G) ? (un >> bsh) * a.G : 0;
+          const int mb = (rb >> 4) + (un & bsh);
           floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kc = 0; kc < KCM; ++kc)
@@ -491,8 +497,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int x = 0; x < XU; ++x) {
           const int q = wave + NW * x;
-          const int rb = (rows >= a.G) ? (q / max(ndb, 1)) * a.G : 0;
-          if ((rb >> 4) == mb)
+          const int qu = q / max(ndb, 1);  // (KV head, row block) unit
+          const int rb = (rows >= a.G) ? (qu >> bsh) * a.G : 0;
+          if ((rb >> 4) + (qu & bsh) == mb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) Uacc[x][r] *= cr[mb][r];
         }
@@ -505,10 +512,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int x = 0; x < XU; ++x) {
       const int q = wave + NW * x;
-      if (ndb == 0 || q >= nheads * ndb) continue;
-      const int hh = q / ndb, db = q % ndb;
+      if (ndb == 0 || q >= nunit * ndb) continue;
+      const int hh = (q / ndb) >> bsh, db = q % ndb;
       const int rb = (rows >= a.G) ? hh * a.G : 0;
-      const int mb = rb >> 4;
+      const int mb = (rb >> 4) + ((q / ndb) & bsh);
       const uint16_t* vbase = vbuf + hh * T * DUS + db * 16 + 4 * (l16 & 3);
       const short4v bv = lds_read_tr4(vbase + (4 * g4 + (l16 >> 2)) * DUS);
       const short4v ph4 = *reinterpret_cast<const short4v*>(pbh + (mb * 16 + l16) * TP + 4 * g4);
@@ -564,10 +571,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int x = 0; x < XU; ++x) {
     const int q = wave + NW * x;
-    if (ndb == 0 || q >= nheads * ndb) continue;
-    const int hh = q / ndb, db = q % ndb;
+    if (ndb == 0 || q >= nunit * ndb) continue;
+    const int hh = (q / ndb) >> bsh, db = q % ndb;
     const int rb = (rows >= a.G) ? hh * a.G : 0;
-    const int mb = rb >> 4;
+    const int mb = (rb >> 4) + ((q / ndb) & bsh);
     const int d = db * 16 + l16;
     if (d >= du) continue;
 #pragma unroll
@@ -661,15 +668,16 @@ __host__ __device__ MfmaLds mfma_lds(int mb, int nw, int kpp, int nheads, int du
 // The item's exact dims fit the variant's per-wave slots: KV heads for the
 // exact scores, (KV head, 16-dim block) tiles for the exact values, 16-byte
 // vx chunks staged per thread.
-bool decode_mfma_fits(const MfmaVariant& v, int nheads, int du) {
+bool decode_mfma_fits(const MfmaVariant& v, int nheads, int nunit, int du) {
   const int du32 = (du + 31) / 32 * 32, nt = 64 * v.nw;
-  return nheads <= v.xp * v.nw && nheads * (du32 / 16) <= v.xu * v.nw &&
+  return nunit <= v.xp * v.nw && nunit * (du32 / 16) <= v.xu * v.nw &&
          nheads * kMfmaTile * (du / 8) <= v.pf * nt;
 }
 
-const MfmaVariant* decode_mfma_pick(int kpp, int mb, int nheads, int du) {
+const MfmaVariant* decode_mfma_pick(int kpp, int mb, int nheads, int nunit, int du) {
   for (const MfmaVariant& v : kVariants)
-    if (v.mb == mb && kpp >= v.kpp_min && kpp <= v.kpp_max && decode_mfma_fits(v, nheads, du)) return &v;
+    if (v.mb == mb && kpp >= v.kpp_min && kpp <= v.kpp_max && decode_mfma_fits(v, nheads, nunit, du))
+      return &v;
   return nullptr;
 }
 
@@ -680,7 +688,8 @@ size_t decode_mfma_smem(const DecodeArgs& a, const MfmaVariant& v, int nheads) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s) {
   if (nitems == 0) return hipSuccess;
   const int nheads = a.rows >= a.G ? a.rows / a.G : 1;
-  const MfmaVariant* v = decode_mfma_pick(a.kpp, a.mb, nheads, a.du);
+  const int nunit = nheads * ((std::min(a.rows, a.G) + 15) / 16);
+  const MfmaVariant* v = decode_mfma_pick(a.kpp, a.mb, nheads, nunit, a.du);
   if (!v) return hipErrorInvalidValue;
   const size_t smem = decode_mfma_smem(a, *v, nheads);
   switch (v - kVariants) {

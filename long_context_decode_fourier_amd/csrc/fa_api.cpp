@@ -232,13 +232,15 @@ bool mfma_rows_ok(const Shape& sh, int rows, int kpp) {
   const int G = sh.G;
   if (rows > 32 || sh.Hq % rows) return false;
   if (!(rows % G == 0 || G % rows == 0)) return false;
-  if (rows > 16 && 16 % G) return false;  // each KV head's rows inside one 16-row block
+  // several KV heads per item: each head's rows inside one 16-row block
+  if (rows > 16 && rows > G && 16 % G) return false;
   const int mb = rows > 16 ? 2 : 1;
   const int nheads = rows >= G ? rows / G : 1;
+  const int nunit = nheads * ((std::min(rows, G) + 15) / 16);  // (KV head, 16-row block) units
   const int du32 = (sh.Du + 31) / 32 * 32;
   if (sh.Du % 8 || du32 > 64) return false;
   // a compiled variant with enough exact-score, exact-value and staging slots
-  const fa::MfmaVariant* v = fa::decode_mfma_pick(kpp, mb, nheads, sh.Du);
+  const fa::MfmaVariant* v = fa::decode_mfma_pick(kpp, mb, nheads, nunit, sh.Du);
   if (!v) return false;
   return fa::mfma_lds(v->mb, v->nw, kpp, nheads, sh.Du, sh.Dc).total <= kMaxLds;
 }

@@ -136,8 +136,9 @@ struct MfmaLds {
   int phi, vxs, spart, sx, ph, pbh, pbl, corr, total;  // byte offsets
 };
 __host__ __device__ MfmaLds mfma_lds(int mb, int nw, int kpp, int nheads, int du, int dc);
-const MfmaVariant* decode_mfma_pick(int kpp, int mb, int nheads, int du);
-bool decode_mfma_fits(const MfmaVariant& v, int nheads, int du);
+// nheads: KV heads of an item; nunit: its (KV head, 16-row block) units
+const MfmaVariant* decode_mfma_pick(int kpp, int mb, int nheads, int nunit, int du);
+bool decode_mfma_fits(const MfmaVariant& v, int nheads, int nunit, int du);
 size_t decode_mfma_smem(const DecodeArgs& a, const MfmaVariant& v, int nheads);
 
 }  // namespace fa

@@ -182,6 +182,10 @@ SMALL = {
     # exact dims that are not a multiple of 8
     "bf16_m1_dc4": (dict(dtype="bf16", batch=2, n_q_heads=6, n_kv_heads=3, head_dim=16,
                          n_comp=4, n_coef=1), [97, 2000]),
+    # 32 query heads on one KV head: an item's 32 rows are one head's, across
+    # both 16-row blocks
+    "bf16_g32_one_kv_head": (dict(dtype="bf16", batch=2, n_q_heads=32, n_kv_heads=1, head_dim=128,
+                                  n_comp=64, n_coef=129), [900, 2000]),
 }
 
 
