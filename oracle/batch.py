@@ -107,16 +107,3 @@ def cache_bytes(w):
             if M > 0 and c.n_comp > 0:
                 comp += 2 * c.n_coef * c.n_comp * 4
     return full, comp
-
-
-def exact_all(w, scale: float):
-    """Uncompressed attention for every query row (context only)."""
-    c = w.cfg
-    G = c.n_q_heads // c.n_kv_heads
-    out = np.zeros((c.batch, c.n_q_heads, c.head_dim))
-    for b in range(c.batch):
-        for h in range(c.n_kv_heads):
-            K, V = w.natural_kv(b, h)
-            q = w.f64(w.q[b, h * G:(h + 1) * G])
-            out[b, h * G:(h + 1) * G] = fa.exact_attention(q, K, V, scale)
-    return out

@@ -85,13 +85,28 @@ def fourier_basis(M: int, k: int) -> np.ndarray:
     return phi * scale[None, :]
 
 
+# The last basis built, reused while (M, k) repeat (the K and V blocks and the
+# KV heads of one sequence share it).  A memo only: it changes no value.  The
+# key holds the basis function itself, so a replaced fourier_basis (the tests'
+# planted mistakes) is never answered from an earlier function's result.
+_BASIS_MEMO = {}
+
+
+def _basis(M: int, k: int) -> np.ndarray:
+    key = (fourier_basis, M, k)
+    if key not in _BASIS_MEMO:
+        _BASIS_MEMO.clear()
+        _BASIS_MEMO[key] = fourier_basis(M, k)
+    return _BASIS_MEMO[key]
+
+
 def project(x_mid: np.ndarray, k: int) -> np.ndarray:
     """Fourier coefficients C [k, c] = Phi^T x_mid of middle rows x_mid [M, c].
 
     [SKILL Step 2: project the middle tokens onto k << M basis functions.]
     """
     x_mid = np.asarray(x_mid, dtype=np.float64)
-    Phi = fourier_basis(x_mid.shape[0], k)
+    Phi = _basis(x_mid.shape[0], k)
     return Phi.T @ x_mid
 
 
@@ -112,7 +127,7 @@ def coef_budget(M: int, fraction: float = 0.3) -> int:
 def reconstruct(coef: np.ndarray, M: int) -> np.ndarray:
     """Approximate middle rows [M, c] = Phi @ coef  [SKILL Step 4]."""
     coef = np.asarray(coef, dtype=np.float64)
-    return fourier_basis(M, coef.shape[0]) @ coef
+    return _basis(M, coef.shape[0]) @ coef
 
 
 def approximate_cache(X: np.ndarray, comp_dims, coef, sink: int, recent: int):
