@@ -202,6 +202,20 @@ const char *fa_last_error(void);
 /* Library version, major*10000 + minor*100 + patch. */
 int32_t fa_version(void);
 
+/*
+ * fa_time_main_kernel: measurement hook.  With two events given (hipEvent_t
+ * handles, created by the caller), every later fa_project / fa_decode /
+ * fa_attend call made by the calling thread records `before` on its stream
+ * right before its dominant kernel and `after` right after it, so that the
+ * caller can time that kernel alone with hipEventElapsedTime: the projection
+ * kernel of fa_project (not its reduce or gather), the main split kernel of
+ * fa_decode, and of fa_attend's first pass.  NULL, NULL turns it off (the
+ * default).  Only one of the two NULL is FA_ERR_NULL.  The library keeps the
+ * handles (thread-local), not the events: the caller keeps them alive while
+ * the hook is on.
+ */
+fa_status_t fa_time_main_kernel(void *before, void *after);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,7 @@ _SIGS = [
     ("fa_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("fa_last_error", ctypes.c_char_p, []),
     ("fa_version", ctypes.c_int32, []),
+    ("fa_time_main_kernel", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
 ]
 
 
@@ -136,10 +137,19 @@ def workspace(nbytes: int, device="cuda"):
     return torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
 
 
+def _own_workspace(nbytes, device, stream):
+    """A workspace for one call on `stream`: allocated there, so that torch's
+    caching allocator does not hand it out again while the call still runs."""
+    if stream is None:
+        return workspace(nbytes, device)
+    with torch.cuda.stream(stream):
+        return workspace(nbytes, device)
+
+
 def project(desc: Desc, kc, vc, ck, cv, ke=None, ve=None, ws=None, stream=None):
     """fa_project: coefficients of the middle rows (and optional edge rows)."""
     if ws is None:
-        ws = workspace(project_workspace_size(desc), (kc if kc is not None else vc).device)
+        ws = _own_workspace(project_workspace_size(desc), (kc if kc is not None else vc).device, stream)
     _check(lib().fa_project(ctypes.byref(desc.c), _ptr(kc), _ptr(vc), _ptr(ck), _ptr(cv),
                             _ptr(ke), _ptr(ve), _ptr(ws), ws.numel(), _stream(stream)))
 
@@ -147,7 +157,7 @@ def project(desc: Desc, kc, vc, ck, cv, ke=None, ve=None, ws=None, stream=None):
 def decode(desc: Desc, q, kx, vx, ke, ve, ck, cv, scale, out, ws=None, stream=None):
     """fa_decode: one decode step for every query row into out [B, Hq, D] fp32."""
     if ws is None:
-        ws = workspace(decode_workspace_size(desc), q.device)
+        ws = _own_workspace(decode_workspace_size(desc), q.device, stream)
     _check(lib().fa_decode(ctypes.byref(desc.c), _ptr(q), _ptr(kx), _ptr(vx), _ptr(ke),
                            _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale), _ptr(out),
                            _ptr(ws), ws.numel(), _stream(stream)))
@@ -164,7 +174,7 @@ def attend(desc: Desc, n_query, q, kx, vx, ke, ve, ck, cv, scale, out, lse=None,
     """fa_attend: n_query queries per sequence (q, out [B, n_query, Hq, D]) over the
     whole cache; lse [B, n_query, Hq] fp32 (optional) gets each row's log-sum-exp."""
     if ws is None:
-        ws = workspace(attend_workspace_size(desc, n_query), q.device)
+        ws = _own_workspace(attend_workspace_size(desc, n_query), q.device, stream)
     _check(lib().fa_attend(ctypes.byref(desc.c), int(n_query), _ptr(q), _ptr(kx), _ptr(vx),
                            _ptr(ke), _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale),
                            _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
@@ -180,6 +190,20 @@ def cache_bytes(desc: Desc):
     f, c = ctypes.c_uint64(0), ctypes.c_uint64(0)
     _check(lib().fa_cache_bytes(ctypes.byref(desc.c), ctypes.byref(f), ctypes.byref(c)))
     return f.value, c.value
+
+
+def time_main_kernel(before=None, after=None):
+    """fa_time_main_kernel: record two torch.cuda.Event around the dominant
+    kernel of this thread's later calls (None, None: off).  The events are
+    recorded once here first, so that their HIP handles exist."""
+    if before is None or after is None:
+        _check(lib().fa_time_main_kernel(None, None))
+        return
+    for e in (before, after):
+        if not e.cuda_event:
+            e.record()
+    _check(lib().fa_time_main_kernel(ctypes.c_void_p(before.cuda_event),
+                                     ctypes.c_void_p(after.cuda_event)))
 
 
 def to_device(a: np.ndarray, device="cuda"):

@@ -26,6 +26,9 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kMinTiles = 3;            // preferred tiles per decode item (MFMA path)
 
 thread_local std::string g_err;
+// fa_time_main_kernel: events recorded around the dominant kernel of the
+// calling thread's next calls (nullptr: off)
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
 fa_status_t fail(fa_status_t s, const char* fmt, ...) {
   char buf[512];
@@ -507,16 +510,20 @@ fa_status_t fa_project(const fa_desc_t* desc, const void* kc, const void* vc, fl
   bool edges_done = false;
   if (sh.Dc > 0) {
     if (p.f16) {
+      if (g_ev_before && (e = hipEventRecord(g_ev_before, s)) != hipSuccess) return hip_fail(e, "event record");
       e = fa::launch_project_f16(a, p.nitems, s);
       if (e != hipSuccess) return hip_fail(e, "project kernel");
+      if (g_ev_after && (e = hipEventRecord(g_ev_after, s)) != hipSuccess) return hip_fail(e, "event record");
       if (!a.direct) {
         e = fa::launch_project_reduce(a, ea, s);
         if (e != hipSuccess) return hip_fail(e, "project reduce kernel");
         edges_done = true;
       }
     } else {
+      if (g_ev_before && (e = hipEventRecord(g_ev_before, s)) != hipSuccess) return hip_fail(e, "event record");
       e = fa::launch_project_f32(a, s);
       if (e != hipSuccess) return hip_fail(e, "project f32 kernel");
+      if (g_ev_after && (e = hipEventRecord(g_ev_after, s)) != hipSuccess) return hip_fail(e, "event record");
     }
   }
   if (ea.nmat > 0 && !edges_done) {
@@ -629,8 +636,13 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
     hipError_t e;
     e = fa::launch_decode_prep(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode prep kernel");
+    const bool timed = t0 == 0;  // the first pass's main kernel
+    if (timed && g_ev_before && (e = hipEventRecord(g_ev_before, s)) != hipSuccess)
+      return hip_fail(e, "event record");
     e = a.mfma ? fa::launch_decode_mfma(a, pp.nitems, s) : fa::launch_decode_split(a, pp.nitems, s);
     if (e != hipSuccess) return hip_fail(e, "decode split kernel");
+    if (timed && g_ev_after && (e = hipEventRecord(g_ev_after, s)) != hipSuccess)
+      return hip_fail(e, "event record");
     e = fa::launch_decode_merge(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode merge kernel");
   }
@@ -677,5 +689,13 @@ const char* fa_status_string(fa_status_t s) {
 const char* fa_last_error(void) { return g_err.c_str(); }
 
 int32_t fa_version(void) { return 100; }
+
+fa_status_t fa_time_main_kernel(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(FA_ERR_NULL, "give both events or neither");
+  g_ev_before = static_cast<hipEvent_t>(before);
+  g_ev_after = static_cast<hipEvent_t>(after);
+  return FA_OK;
+}
 
 }  // extern "C"

@@ -91,6 +91,9 @@ int main(void) {
   for (int s = 0; s <= 7; ++s) EXPECT(fa_status_string((fa_status_t)s) != NULL, 1);
   EXPECT(fa_last_error() != NULL, 1);
   EXPECT(fa_version() >= 100, 1);
+  EXPECT(fa_time_main_kernel(P(1), NULL), FA_ERR_NULL);
+  EXPECT(fa_time_main_kernel(NULL, P(2)), FA_ERR_NULL);
+  EXPECT(fa_time_main_kernel(NULL, NULL), FA_OK);
 
   if (failures) fprintf(stderr, "%d check(s) failed\n", failures);
   else printf("api_driver: all checks passed\n");

@@ -133,16 +133,14 @@ def test_attend_one_query_is_decode(fb):
     _check(w, (got_o, got_l), ob.attend_all(w, ck_o, cv_o, run.scale), "end-to-end")
 
 
-def test_llama3_8b_gqa_4q(fb):
-    """Full-size batch with four queries per sequence; oracle on sampled blocks."""
-    _say("case llama3_8b_gqa_4q (sampled blocks)")
-    w = wl.make(wl.CONFIGS["llama3_8b_gqa_4q"])
+def _check_blocks(fb, w, blocks):
+    """GPU fa_attend of the whole workload; oracle attend on the given blocks."""
     run = AttendRun(fb, w)
     got_o, got_l = run.attend()
     c = w.cfg
     G = c.group
     from oracle import fourier_attention as fa
-    for b, h in [(0, 0), (3, 7)]:
+    for b, h in blocks:
         ck_o, cv_o = ob.project_block(w, b, h)
         K, V = w.natural_kv(b, h)
         q = w.f64(w.q[b, :, h * G:(h + 1) * G]).reshape(c.n_query * G, c.head_dim)
@@ -150,3 +148,18 @@ def test_llama3_8b_gqa_4q(fb):
         _check(w, (got_o[b, :, h * G:(h + 1) * G], got_l[b, :, h * G:(h + 1) * G]),
                (o.reshape(c.n_query, G, c.head_dim), l.reshape(c.n_query, G)),
                "end-to-end b=%d h=%d" % (b, h))
+
+
+def test_llama3_8b_gqa_4q(fb):
+    """Full-size batch with four queries per sequence; every sequence at two KV heads."""
+    _say("case llama3_8b_gqa_4q (every sequence at two KV heads)")
+    w = wl.make(wl.CONFIGS["llama3_8b_gqa_4q"])
+    _check_blocks(fb, w, [(b, h) for b in range(4) for h in ((2 * b) % 8, (2 * b + 5) % 8)])
+
+
+def test_llama3_8b_gqa_chunk64(fb):
+    """A 64-token prefill chunk per sequence (three passes over the cache), all
+    64 queries of sampled blocks: every pass is compared."""
+    _say("case llama3_8b_gqa_chunk64 (every sequence at one KV head, all 64 queries)")
+    w = wl.make(wl.CONFIGS["llama3_8b_gqa_chunk64"])
+    _check_blocks(fb, w, [(0, 0), (1, 3), (2, 6), (3, 7)])
