@@ -203,6 +203,28 @@ const char *fa_last_error(void);
 int32_t fa_version(void);
 
 /*
+ * fa_decode_noalloc: fa_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a static device
+ * array inside the library, FA_NOALLOC_SCRATCH_MIB MiB per GPU, held by every
+ * GPU the library runs on until the process ends; its device address is
+ * looked up once per device (hipGetSymbolAddress) on the first call made with
+ * that device current.  The call allocates nothing and runs the same kernels
+ * as fa_decode on that array, so its results are fa_decode's.  A shape whose
+ * fa_decode_workspace_size exceeds the array returns FA_ERR_WORKSPACE (with a
+ * text in fa_last_error) and enqueues nothing.  Every call on one GPU shares
+ * the one array: calls that may overlap on a GPU (several host threads, or
+ * several streams without ordering between them) race and must not be made;
+ * calls ordered on one stream are fine.  Arguments, outputs and errors are
+ * otherwise those of fa_decode.
+ */
+#define FA_NOALLOC_SCRATCH_MIB 256
+fa_status_t fa_decode_noalloc(const fa_desc_t *desc, const void *q, const void *kx,
+                              const void *vx, const void *ke, const void *ve,
+                              const float *ck, const float *cv, float scale, float *out,
+                              void *stream);
+
+/*
  * fa_time_main_kernel: measurement hook.  With two events given (hipEvent_t
  * handles, created by the caller), every later fa_project / fa_decode /
  * fa_attend call made by the calling thread records `before` on its stream

@@ -66,6 +66,9 @@ _SIGS = [
     ("fa_last_error", ctypes.c_char_p, []),
     ("fa_version", ctypes.c_int32, []),
     ("fa_time_main_kernel", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    ("fa_decode_noalloc", ctypes.c_int,
+     [ctypes.POINTER(fa_desc_t)] + [ctypes.c_void_p] * 7 + [ctypes.c_float, ctypes.c_void_p,
+                                                           ctypes.c_void_p]),
 ]
 
 
@@ -161,6 +164,17 @@ def decode(desc: Desc, q, kx, vx, ke, ve, ck, cv, scale, out, ws=None, stream=No
     _check(lib().fa_decode(ctypes.byref(desc.c), _ptr(q), _ptr(kx), _ptr(vx), _ptr(ke),
                            _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale), _ptr(out),
                            _ptr(ws), ws.numel(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20  # FA_NOALLOC_SCRATCH_MIB of include/fa.h
+
+
+def decode_noalloc(desc: Desc, q, kx, vx, ke, ve, ck, cv, scale, out, stream=None):
+    """fa_decode_noalloc: fa_decode on the library's static scratch buffer (no
+    workspace argument, no allocation)."""
+    _check(lib().fa_decode_noalloc(ctypes.byref(desc.c), _ptr(q), _ptr(kx), _ptr(vx), _ptr(ke),
+                                   _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale), _ptr(out),
+                                   _stream(stream)))
 
 
 def attend_workspace_size(desc: Desc, n_query: int) -> int:

@@ -426,6 +426,11 @@ fa_status_t plan_attend(const Shape& base, int32_t n_query, AttendPlan* ap) {
 
 }  // namespace
 
+// The error text of fa_last_error, for the library's other source files.
+extern "C" __attribute__((visibility("hidden"))) void fa_set_last_error(const char* text) {
+  g_err = text ? text : "";
+}
+
 extern "C" {
 
 fa_status_t fa_project_workspace_size(const fa_desc_t* desc, size_t* bytes) {

@@ -201,3 +201,28 @@ def test_cache_bytes_matches_oracle():
         w = wl.make(cfg, lens=lens)
         d = fb.Desc.from_workload(w)
         assert fb.cache_bytes(d) == ob.cache_bytes(w), cfg.name
+
+
+def test_decode_noalloc_rejects_oversized_without_gpu():
+    """fa_decode_noalloc refuses a shape whose workspace exceeds its static
+    scratch array, before any HIP call."""
+    dims_holder = type("T", (), {"data_ptr": lambda self: 10 * GB})()
+    d = _desc(batch=64, n_q_heads=256, n_kv_heads=8, n_coef=4097, seq_len=[1 << 20] * 64,
+              dims=dims_holder)
+    st, need = _size(fb.lib().fa_decode_workspace_size, d)
+    assert st == 0 and need > fb.NOALLOC_SCRATCH_BYTES
+    P = lambda v: ctypes.c_void_p(v * GB)
+    st = fb.lib().fa_decode_noalloc(ctypes.byref(d.c), P(1), P(2), P(3), P(4), P(5), P(6), P(7),
+                                    ctypes.c_float(0.1), P(8), None)
+    assert st == 4
+    assert "static scratch" in fb.lib().fa_last_error().decode()
+    # invalid shapes report their own code first
+    assert fb.lib().fa_decode_noalloc(ctypes.byref(_desc(n_coef=0).c), P(1), P(2), P(3), P(4), P(5),
+                                      P(6), P(7), ctypes.c_float(0.1), P(8), None) == 2
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    import re as _re
+    mib = int(_re.search(r"#define FA_NOALLOC_SCRATCH_MIB (\d+)", text).group(1))
+    assert fb.NOALLOC_SCRATCH_BYTES == mib << 20
