@@ -168,6 +168,24 @@ fa_status_t fa_attend(const fa_desc_t *desc, int32_t n_query, const void *q,
                       size_t workspace_bytes, void *stream);
 
 /*
+ * fa_attend_plan: how fa_attend (fa_decode for n_query = 1) would run `desc`,
+ * host only (nothing is enqueued, device arrays are not read):
+ *   path     0: VALU kernels (fp32 caches and shapes the MFMA kernels do not
+ *               take), 1: one MFMA pass over the middle tokens, 2: two MFMA
+ *               passes (scores and exact values, then the value moments W);
+ *   rows     query rows stacked per work item;
+ *   items    work items of the main kernel (per pass over the cache);
+ *   items2   work items of the second MFMA pass (path 2), else 0;
+ *   passes   passes over the cache (queries per pass bounded by LDS);
+ *   queries_per_pass  queries of a full pass.
+ * Errors as for fa_attend_workspace_size.
+ */
+typedef struct {
+  int32_t path, rows, items, items2, passes, queries_per_pass;
+} fa_plan_t;
+fa_status_t fa_attend_plan(const fa_desc_t *desc, int32_t n_query, fa_plan_t *plan);
+
+/*
  * fa_coef_budget: the number of real coefficients that spans the same space as
  * the first floor(fraction * M) bins of the middle's real FFT, which is how the
  * skill page (Step 3) sizes its coefficient budget (fraction 0.3 of the middle

@@ -66,6 +66,8 @@ _SIGS = [
     ("fa_last_error", ctypes.c_char_p, []),
     ("fa_version", ctypes.c_int32, []),
     ("fa_time_main_kernel", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    ("fa_attend_plan", ctypes.c_int,
+     [ctypes.POINTER(fa_desc_t), ctypes.c_int32, ctypes.c_void_p]),
     ("fa_decode_noalloc", ctypes.c_int,
      [ctypes.POINTER(fa_desc_t)] + [ctypes.c_void_p] * 7 + [ctypes.c_float, ctypes.c_void_p,
                                                            ctypes.c_void_p]),
@@ -164,6 +166,24 @@ def decode(desc: Desc, q, kx, vx, ke, ve, ck, cv, scale, out, ws=None, stream=No
     _check(lib().fa_decode(ctypes.byref(desc.c), _ptr(q), _ptr(kx), _ptr(vx), _ptr(ke),
                            _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale), _ptr(out),
                            _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class fa_plan_t(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("rows", ctypes.c_int32), ("items", ctypes.c_int32),
+                ("items2", ctypes.c_int32), ("passes", ctypes.c_int32),
+                ("queries_per_pass", ctypes.c_int32)]
+
+
+PATHS = {0: "valu", 1: "mfma", 2: "two_pass"}
+
+
+def attend_plan(desc: Desc, n_query: int = 1) -> dict:
+    """fa_attend_plan: the kernel path and work split fa_attend would use (host only)."""
+    p = fa_plan_t()
+    _check(lib().fa_attend_plan(ctypes.byref(desc.c), int(n_query), ctypes.byref(p)))
+    d = {f: getattr(p, f) for f, _ in fa_plan_t._fields_}
+    d["path"] = PATHS[d["path"]]
+    return d
 
 
 NOALLOC_SCRATCH_BYTES = 256 << 20  # FA_NOALLOC_SCRATCH_MIB of include/fa.h

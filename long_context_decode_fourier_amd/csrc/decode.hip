@@ -997,7 +997,9 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     if (e < a.du + a.dc) s_lo = ns - a.edge_split;
     else s_hi = ns - a.edge_split;
   }
-  const float* Pi = P + 2 + e;
+  // two-pass path: W comes from Wp, and the partial rows end after o_E
+  const bool wpass = a.two_pass && e >= a.du + a.dc;
+  const float* Pi = P + 2 + (wpass ? 0 : e);
   // The entry's first FIRST splits and its output column are loaded in
   // the same round as the (m, l) pairs (clamped indices, no branch around a
   // load), so that the weights and the sum wait on one memory round trip.
@@ -1046,6 +1048,18 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     if (a.lse) a.lse[q_row(a, b, i)] = mx + logf(ltot);
   }
   if (idx >= nvec) return;
+  if (wpass) {
+    // W relative to the row's maximum over its splits, summed over the split
+    // groups in order
+    const int n = idx - a.du - a.dc;
+    const int nsg = (ns - a.edge_split + kMomentWaves - 1) / kMomentWaves;
+    const float* wp = a.Wp + (static_cast<int64_t>(a.sgcum[b]) * a.hq + i) * a.kpad + n;
+    const int64_t sgs = static_cast<int64_t>(a.hq) * a.kpad;
+    float v = 0.0f;
+    for (int sg = 0; sg < nsg; ++sg) v += wp[sg * sgs];
+    mrow[a.dc + n] = v * basis_alpha(n, M);
+    return;
+  }
   // fixed-order sum over the splits s_lo, s_lo + 1, ...: the loads already
   // held (a split past s_hi weighs 0: a multiply, not a branch, so that the
   // compiler keeps the load where it is), then whole batches of kMergeBatch

@@ -226,7 +226,7 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
 struct DecPlan {
   fa::DecodeArgs args;
   int nitems;
-  size_t off_A, off_q16, off_part, off_mrg, ws_bytes;
+  size_t off_A, off_q16, off_part, off_mrg, off_P16, off_msub, off_Wp, ws_bytes;
 };
 
 // Row grouping of the MFMA path: `rows` consecutive query heads per item,
@@ -247,6 +247,28 @@ bool mfma_rows_ok(const Shape& sh, int rows, int kpp) {
   if (!v) return false;
   return fa::mfma_lds(v->mb, v->nw, kpp, nheads, sh.Du, sh.Dc).total <= kMaxLds;
 }
+
+// Row grouping of the two-pass path: `rows` consecutive query heads per item
+// (32 or 16), checked against the compiled pass-1 and pass-2 variants.
+bool two_pass_rows_ok(const Shape& sh, int rows, int kpp) {
+  const int G = sh.G;
+  if (rows > sh.Hq || sh.Hq % rows) return false;
+  if (!(rows % G == 0 || G % rows == 0)) return false;
+  if (rows > 16 && rows > G && 16 % G) return false;
+  const int mb = rows > 16 ? 2 : 1;
+  const int nheads = rows >= G ? rows / G : 1;
+  const int nunit = nheads * ((std::min(rows, G) + 15) / 16);
+  if (!fa::decode_score_pick(kpp, mb, nheads, nunit, sh.Du)) return false;
+  return fa::decode_score_smem(mb, nheads, sh.Du) <= kMaxLds &&
+         fa::decode_moment_smem(mb, fa::decode_moment_max_groups(mb)) <= kMaxLds;
+}
+
+// The two-pass path pays for its extra launch, its P16 traffic and the fixed
+// cost of its second-pass items on long middles: at least this many middle
+// tokens per pass-1 item on average (measured: a 16-sequence batch of
+// 33k-65k tokens, about 3000 per item, runs faster in two passes; 4 x 32k
+// tokens, about 500 per item, in one).
+constexpr int64_t kTwoPassMinTokensPerCU = 1024;
 
 fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   fa::DecodeArgs& a = p->args;
@@ -281,8 +303,28 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
     // that 7 picks; longer contexts are not affected.
     int64_t mid_tokens = 0;
     for (int b = 0; b < sh.B; ++b) mid_tokens += sh.M[b];
+    // two passes for long middles, and for shapes the one-pass kernel does
+    // not take (exact dims past 64, k past 2303)
+    int two_rows = 0;
+    if (sh.Dc > 0 && sh.any_mid && sh.Du % 8 == 0)
+      for (int r : {32, 16, 8})
+        if (two_pass_rows_ok(sh, r, a.kpp)) {
+          two_rows = r;
+          break;
+        }
+    bool one_pass_ok = false;
+    for (int r = 32; r >= 1 && !one_pass_ok; --r) one_pass_ok = mfma_rows_ok(sh, r, a.kpp);
+    // P16 is written and read once (2 + 2 bytes per query row and token);
+    // past an eighth of the cache bytes per token (prefill chunks, several
+    // queries per step) the extra traffic outweighs the saving
+    const bool p_cheap = static_cast<int64_t>(sh.Hq) * 8 <= static_cast<int64_t>(sh.Hkv) * sh.Du;
+    const bool long_items = mid_tokens * (sh.Hq / std::max(two_rows, 1)) >= kTwoPassMinTokensPerCU * kNumCU;
+    if (two_rows && (!one_pass_ok || (p_cheap && long_items))) {
+      rows = two_rows;
+      a.two_pass = 1;
+    }
     int fallback = 0;
-    for (int r = 32; r >= 1; --r) {
+    for (int r = 32; r >= 1 && !a.two_pass; --r) {
       if (!mfma_rows_ok(sh, r, a.kpp)) continue;
       if (!fallback) fallback = r;
       const int64_t per_item = mid_tokens * (sh.Hq / r) / kNumCU;
@@ -297,7 +339,8 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   if (rows > 0) {
     a.mfma = 1;
     a.mb = rows > 16 ? 2 : 1;
-    tile = fa::kMfmaTile;
+    // two-pass: pass-1 splits are whole pass-2 steps
+    tile = a.two_pass ? fa::kMomentTile : fa::kMfmaTile;
   } else {
     a.mfma = 0;
     tile = fa::kDecTile;
@@ -310,7 +353,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   }
   a.rows = rows;
   a.ngroups = sh.Hq / rows;
-  a.RS = 2 + a.du + a.dc + a.kpad;
+  a.RS = 2 + a.du + a.dc + (a.two_pass ? 0 : a.kpad);  // two-pass: W lives in Wp
   // MFMA path: the split kernel covers the middle tokens [S, S+M) and
   // decode_prep adds one split per row for the sink and recent tokens.
   a.edge_split = a.mfma ? fa::edge_parts(a) : 0;
@@ -370,6 +413,46 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   p->off_part = p->off_q16 + (a.mfma ? align_up(rows_total * du32 * 2) : 0);
   p->off_mrg = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
   p->ws_bytes = p->off_mrg + align_up(static_cast<size_t>(sh.B) * sh.Hq * a.MS * sizeof(float));
+  p->off_P16 = p->off_msub = p->off_Wp = 0;
+  if (a.two_pass) {
+    // pass-2 plan: split groups of kMomentWaves pass-1 splits per sequence,
+    // frequency slices chosen to fill the CUs (two blocks each) in whole rounds
+    int64_t pc = 0;
+    int sgc = 0;
+    for (int b = 0; b < sh.B; ++b) {
+      a.pcum[b] = pc;
+      a.sgcum[b] = sgc;
+      pc += (static_cast<int64_t>(sh.M[b]) + fa::kMomentTile - 1) / fa::kMomentTile * fa::kMomentTile;
+      const int nsm = a.seq.nsplit[b] - a.edge_split;
+      sgc += sh.M[b] > 0 ? (nsm + fa::kMomentWaves - 1) / fa::kMomentWaves : 0;
+    }
+    a.ngr = (sh.k / 2 + 1 + 15) / 16;
+    const int maxg = fa::decode_moment_max_groups(a.mb);
+    const int64_t per_slice = static_cast<int64_t>(sgc) * a.ngroups;  // items of one slice
+    double best = 1e300;
+    a.nslices = 0;
+    for (int sl = (a.ngr + maxg - 1) / maxg; sl <= a.ngr; ++sl) {
+      const int64_t items = per_slice * sl;
+      const double rounds = static_cast<double>((items + 2 * kNumCU - 1) / (2 * kNumCU));
+      const double cost = rounds * ((a.ngr + sl - 1) / sl + 0.5);
+      if (cost < best - 1e-9) {
+        best = cost;
+        a.nslices = sl;
+      }
+    }
+    int it = 0;
+    for (int b = 0; b < sh.B; ++b) {
+      a.item2_0[b] = it;
+      const int nsm = a.seq.nsplit[b] - a.edge_split;
+      if (sh.M[b] > 0) it += a.ngroups * ((nsm + fa::kMomentWaves - 1) / fa::kMomentWaves) * a.nslices;
+    }
+    a.nitems2 = it;
+    const size_t rows_all = static_cast<size_t>(sh.Hq);
+    p->off_P16 = p->ws_bytes;
+    p->off_msub = p->off_P16 + align_up(rows_all * static_cast<size_t>(pc) * 2);
+    p->off_Wp = p->off_msub + align_up(rows_all * static_cast<size_t>(pc / 16) * sizeof(float));
+    p->ws_bytes = p->off_Wp + align_up(static_cast<size_t>(sgc) * rows_all * a.kpad * sizeof(float));
+  }
   if (fa::decode_prep_smem(a) > kMaxLds)
     return fail(FA_ERR_SHAPE, "%d query rows per KV head need more LDS than a workgroup has", sh.G);
   return FA_OK;
@@ -553,6 +636,23 @@ fa_status_t fa_attend_workspace_size(const fa_desc_t* desc, int32_t n_query, siz
   return FA_OK;
 }
 
+fa_status_t fa_attend_plan(const fa_desc_t* desc, int32_t n_query, fa_plan_t* plan) {
+  Shape sh;
+  if (!plan) return fail(FA_ERR_NULL, "plan is NULL");
+  fa_status_t st = validate(desc, &sh);
+  if (st != FA_OK) return st;
+  AttendPlan ap;
+  if ((st = plan_attend(sh, n_query, &ap)) != FA_OK) return st;
+  const fa::DecodeArgs& a = ap.full.args;
+  plan->path = a.two_pass ? 2 : (a.mfma ? 1 : 0);
+  plan->rows = a.rows;
+  plan->items = ap.full.nitems;
+  plan->items2 = a.two_pass ? a.nitems2 : 0;
+  plan->passes = (n_query + ap.chunk - 1) / ap.chunk;
+  plan->queries_per_pass = ap.chunk;
+  return FA_OK;
+}
+
 fa_status_t fa_decode(const fa_desc_t* desc, const void* q, const void* kx, const void* vx,
                       const void* ke, const void* ve, const float* ck, const float* cv, float scale,
                       float* out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -638,16 +738,26 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
     a.Q16 = static_cast<char*>(workspace) + pp.off_q16;
     a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_part);
     a.mrg = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_mrg);
+    if (a.two_pass) {
+      a.P16 = static_cast<char*>(workspace) + pp.off_P16;
+      a.msub = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_msub);
+      a.Wp = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_Wp);
+    }
     hipError_t e;
     e = fa::launch_decode_prep(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode prep kernel");
     const bool timed = t0 == 0;  // the first pass's main kernel
     if (timed && g_ev_before && (e = hipEventRecord(g_ev_before, s)) != hipSuccess)
       return hip_fail(e, "event record");
-    e = a.mfma ? fa::launch_decode_mfma(a, pp.nitems, s) : fa::launch_decode_split(a, pp.nitems, s);
+    if (a.two_pass)
+      e = fa::launch_decode_score(a, pp.nitems, s);
+    else
+      e = a.mfma ? fa::launch_decode_mfma(a, pp.nitems, s) : fa::launch_decode_split(a, pp.nitems, s);
     if (e != hipSuccess) return hip_fail(e, "decode split kernel");
     if (timed && g_ev_after && (e = hipEventRecord(g_ev_after, s)) != hipSuccess)
       return hip_fail(e, "event record");
+    if (a.two_pass && (e = fa::launch_decode_moment(a, s)) != hipSuccess)
+      return hip_fail(e, "decode moment kernel");
     e = fa::launch_decode_merge(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode merge kernel");
   }

@@ -84,6 +84,24 @@ struct DecodeArgs {
   float* lse;    // optional [B][nq][Hq]: log sum_t exp(s_t) of each query row
   SeqTable seq;  // item0 / nsplit (splits per row, edge split included) / chunk
   int32_t prow0[kMaxBatch];  // first partial row of sequence b: sum Hq * nsplit
+  // Two-pass path (two_pass = 1; MFMA only): decode_score writes each middle
+  // split's probabilities and references, decode_moment forms W from them.
+  //   P16  fp16 [b][row i < hq][tau < mpad_b]: p of middle token tau relative
+  //        to the reference of its 16-token tile (mpad_b = M_b rounded up to 128);
+  //   msub fp32 [b][row][mpad_b / 16]: that reference, per 16-token tile;
+  //   Wp   fp32 [b][sg][row][kpad]: W of sequence b over its middle splits
+  //        4 sg .. 4 sg + 3, relative to the row's maximum over all its splits,
+  //        in basis order (without the basis scale).
+  int two_pass;
+  void* P16;
+  float* msub;
+  float* Wp;
+  int nitems2;    // decode_moment items: (sequence, row group, split group, frequency slice)
+  int nslices;    // frequency slices per (sequence, row group, split group)
+  int ngr;        // frequency groups of 16 (frequencies 0 .. k/2)
+  int64_t pcum[kMaxBatch];   // sum of mpad over sequences before b
+  int32_t sgcum[kMaxBatch];  // sum of split groups over sequences before b
+  int32_t item2_0[kMaxBatch];  // first decode_moment item of sequence b
 };
 
 // Rows of the kernels are "virtual" query heads: with nq queries per
@@ -120,6 +138,19 @@ size_t decode_prep_smem(const DecodeArgs& a);  // LDS of decode_prep
 hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nitems, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
+// Two-pass path: pass 1 (scores, softmax, exact values; writes P16 / msub and
+// the (m, l, o_U) partials) and pass 2 (W = P phi into Wp).
+constexpr int kMomentTile = 128;   // tokens per pass-2 step of one wave
+constexpr int kMomentWaves = 4;    // pass-1 splits per split group (one wave each)
+struct ScoreVariant {
+  int mb, maxu, pf, xp, xu, kcm, kpp_max;
+};
+const ScoreVariant* decode_score_pick(int kpp, int mb, int nheads, int nunit, int du);
+size_t decode_score_smem(int mb, int nheads, int du);
+hipError_t launch_decode_score(const DecodeArgs& a, int nitems, hipStream_t s);
+int decode_moment_max_groups(int mb);  // frequency groups per item of the compiled variants
+size_t decode_moment_smem(int mb, int ngw);
+hipError_t launch_decode_moment(const DecodeArgs& a, hipStream_t s);
 // MFMA decode kernel: tokens per tile, compiled variants and LDS carve-up.
 constexpr int kMfmaTile = 16;
 struct MfmaVariant {

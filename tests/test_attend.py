@@ -58,7 +58,9 @@ class AttendRun:
         self.ke = torch.zeros((nblk, E, c.n_comp), dtype=self.kc.dtype, device="cuda")
         self.ve = torch.zeros_like(self.ke)
         self.scale = 1.0 / np.sqrt(c.head_dim)
-        self.fb.project(self.desc, self.kc, self.vc, self.ck, self.cv, self.ke, self.ve)
+        ws = self.fb.workspace(self.fb.project_workspace_size(self.desc))
+        ws.fill_(0xFF)  # NaN everywhere: reads of unwritten workspace show up
+        self.fb.project(self.desc, self.kc, self.vc, self.ck, self.cv, self.ke, self.ve, ws)
         torch.cuda.synchronize()
 
     def attend(self, ck=None, cv=None, nq=None):
@@ -68,8 +70,10 @@ class AttendRun:
         cv = self.cv if cv is None else torch.from_numpy(np.asarray(cv, np.float32)).cuda()
         out = torch.full((c.batch, nq, c.n_q_heads, c.head_dim), float("nan"), device="cuda")
         lse = torch.full((c.batch, nq, c.n_q_heads), float("nan"), device="cuda")
+        ws = self.fb.workspace(self.fb.attend_workspace_size(self.desc, nq))
+        ws.fill_(0xFF)  # NaN everywhere: reads of unwritten workspace show up
         self.fb.attend(self.desc, nq, self.q, self.kx, self.vx, self.ke, self.ve, ck, cv,
-                       self.scale, out, lse)
+                       self.scale, out, lse, ws)
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 

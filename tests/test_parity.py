@@ -44,6 +44,14 @@ def fb():
     return binding
 
 
+def poisoned_workspace(fb, nbytes):
+    """A workspace whose every byte is 0xFF (NaN as fp16 and fp32): a kernel that
+    reads workspace memory no kernel of the call wrote turns the result NaN."""
+    ws = fb.workspace(nbytes)
+    ws.fill_(0xFF)
+    return ws
+
+
 class Run:
     """Uploads a workload and runs fa_project / fa_decode on it."""
 
@@ -67,7 +75,8 @@ class Run:
         self.scale = 1.0 / np.sqrt(c.head_dim)
 
     def project(self):
-        self.fb.project(self.desc, self.kc, self.vc, self.ck, self.cv, self.ke, self.ve)
+        ws = poisoned_workspace(self.fb, self.fb.project_workspace_size(self.desc))
+        self.fb.project(self.desc, self.kc, self.vc, self.ck, self.cv, self.ke, self.ve, ws)
         torch.cuda.synchronize()
         return self.ck.cpu().numpy().astype(np.float64), self.cv.cpu().numpy().astype(np.float64)
 
@@ -76,8 +85,9 @@ class Run:
         ck = self.ck if ck is None else torch.from_numpy(np.asarray(ck, np.float32)).cuda()
         cv = self.cv if cv is None else torch.from_numpy(np.asarray(cv, np.float32)).cuda()
         out = torch.full((c.batch, c.n_q_heads, c.head_dim), float("nan"), device="cuda")
+        ws = poisoned_workspace(self.fb, self.fb.decode_workspace_size(self.desc))
         self.fb.decode(self.desc, self.q, self.kx, self.vx, self.ke, self.ve, ck, cv,
-                       self.scale, out)
+                       self.scale, out, ws)
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64)
 
@@ -189,12 +199,80 @@ SMALL = {
 }
 
 
+# the row grouping some small cases exist to cover
+SMALL_PLAN = {"bf16_g32_one_kv_head": (32, "mfma")}
+
+
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_small_shapes(fb, name):
     kw, lens = SMALL[name]
     cfg = wl.custom(name=name, seed=100 + sorted(SMALL).index(name), **kw)
     _say("case %s lens=%s" % (name, lens))
     w = wl.make(cfg, lens=lens)
+    if name in SMALL_PLAN:
+        plan = fb.attend_plan(fb.Desc.from_workload(w))
+        _say("  plan %s" % plan)
+        assert (plan["rows"], plan["path"]) == SMALL_PLAN[name]
+    _full_check(fb, w)
+
+
+# Long middles that the planner runs in two passes (scores and exact values,
+# then the value moments): 32 and 16 stacked rows, exact dims up to 128, k up
+# to 4097 (the largest the API takes), a sequence without middle tokens, one
+# KV head whose 32 query rows span two items, and "needle" tokens
+# whose exact-dim keys are scaled by 16 (exact in bf16), so that some rows'
+# softmax reference moves inside splits (the second pass then rescales the
+# probabilities of the earlier tiles).  The third field is that needle stride
+# in middle tokens (0: none).
+TWO_PASS = {
+    "tp_g4_rows32": (dict(dtype="bf16", batch=4, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                          n_comp=64, n_coef=257), [70000, 66001, 64999, 63500], 0, (32, "two_pass")),
+    "tp_g2_rows16_du128": (dict(dtype="bf16", batch=2, n_q_heads=16, n_kv_heads=8, head_dim=160,
+                                n_comp=32, n_coef=129), [50000, 21000], 0, (16, "two_pass")),
+    "tp_k4097_rows16": (dict(dtype="bf16", batch=1, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                             n_comp=64, n_coef=4097), [70000], 0, (16, "two_pass")),
+    "tp_k2049_ragged_empty": (dict(dtype="bf16", batch=5, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                   n_comp=64, n_coef=2049), [90000, 50, 9100, 81000, 85000], 0,
+                              (32, "two_pass")),
+    "tp_g32_one_kv_head_k2399": (dict(dtype="bf16", batch=4, n_q_heads=32, n_kv_heads=1,
+                                      head_dim=128, n_comp=96, n_coef=2399),
+                                 [70000, 68000, 66500, 65600], 0, (16, "two_pass")),
+    # the LLaMA-2-7B layer at the pages' coefficient budget for its middle
+    # (30% of M = 4000 bins: k = 2399), past the one-pass kernel's k
+    "tp_llama2_7b_budget": (dict(dtype="bf16", batch=1, n_q_heads=32, n_kv_heads=32, head_dim=128,
+                                 n_comp=64, n_coef=2399), [4096], 0, (8, "two_pass")),
+    "tp_moving_reference": (dict(dtype="bf16", batch=4, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                                 n_comp=64, n_coef=129), [70000, 68000, 66000, 64000], 600,
+                            (32, "two_pass")),
+}
+
+
+def _plant_needles(w, stride):
+    """Scale the exact-dim keys of every stride-th middle token (from middle
+    token 100 on) by 16, in every KV head: a power of two, exact in bf16."""
+    c = w.cfg
+    kx = w.kx.copy()
+    for b in range(c.batch):
+        M = w.mid_len(b)
+        for h in range(c.n_kv_heads):
+            r0 = w.row0(b, h)
+            for tau in range(100, M, stride):
+                r = r0 + c.sink + tau
+                kx[r] = wl.bf16_bits(wl.bf16_to_f32(kx[r]) * np.float32(16.0))
+    w.kx = kx
+
+
+@pytest.mark.parametrize("name", sorted(TWO_PASS))
+def test_two_pass_shapes(fb, name):
+    kw, lens, needle, (rows, path) = TWO_PASS[name]
+    cfg = wl.custom(name=name, seed=200 + sorted(TWO_PASS).index(name), **kw)
+    _say("case %s lens=%s needle stride %d" % (name, lens, needle))
+    w = wl.make(cfg, lens=lens)
+    if needle:
+        _plant_needles(w, needle)
+    plan = fb.attend_plan(fb.Desc.from_workload(w))
+    _say("  plan %s" % plan)
+    assert (plan["rows"], plan["path"]) == (rows, path)
     _full_check(fb, w)
 
 
@@ -269,7 +347,7 @@ def test_prefill_projection(fb):
     kc, vc = fb.to_device(w.kc), fb.to_device(w.vc)
     ck = torch.full((c.n_kv_heads, c.n_coef, c.n_comp), float("nan"), device="cuda")
     cv = torch.full_like(ck, float("nan"))
-    fb.project(desc, kc, vc, ck, cv)
+    fb.project(desc, kc, vc, ck, cv, ws=poisoned_workspace(fb, fb.project_workspace_size(desc)))
     torch.cuda.synchronize()
     ck_g, cv_g = ck.cpu().numpy().astype(np.float64), cv.cpu().numpy().astype(np.float64)
     del kc, vc, ck, cv

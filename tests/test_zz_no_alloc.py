@@ -40,7 +40,9 @@ def _run(fb, cfg, lens):
     scale = 1.0 / np.sqrt(c.head_dim)
     want = torch.full((c.batch, c.n_q_heads, c.head_dim), float("nan"), device="cuda")
     got = torch.full_like(want, float("nan"))
-    fb.decode(desc, q, kx, vx, ke, ve, ck, cv, scale, want)
+    ws = fb.workspace(fb.decode_workspace_size(desc))
+    ws.fill_(0xFF)  # NaN everywhere: the reference reads no unwritten workspace either
+    fb.decode(desc, q, kx, vx, ke, ve, ck, cv, scale, want, ws)
     fb.decode_noalloc(desc, q, kx, vx, ke, ve, ck, cv, scale, got)
     torch.cuda.synchronize()
     return want.cpu().numpy(), got.cpu().numpy()
