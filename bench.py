@@ -39,16 +39,17 @@ DEFAULT_WORKLOAD = "ragged_batch"
 DEFAULT_PROJECTION = "prefill_projection"
 
 
-def algorithmic(w):
-    """Per step: decode must-read+write bytes, the main decode kernel's share
-    of them (exact dims of the middle rows), projection flops, KV positions."""
-    c = w.cfg
+def algorithmic(c, lens):
+    """Per step of workload config ``c`` with sequence lengths ``lens``:
+    decode must-read+write bytes, the main decode kernel's share of them
+    (exact dims of the middle rows), projection flops, KV positions."""
     esz = 2 if c.dtype == "bf16" else 4
     E = c.sink + c.recent
     dec = main = 0
     flops = 0.0
     for b in range(c.batch):
-        L, M = int(w.lens[b]), w.mid_len(b)
+        L = int(lens[b])
+        M = max(0, L - E)
         dec += c.n_kv_heads * L * c.n_exact * 2 * esz                 # kx, vx
         main += c.n_kv_heads * M * c.n_exact * 2 * esz                # kx, vx middle rows
         dec += c.n_kv_heads * min(L, E) * c.n_comp * 2 * esz          # ke, ve
@@ -56,28 +57,41 @@ def algorithmic(w):
             dec += c.n_kv_heads * c.n_coef * c.n_comp * 2 * 4          # ck, cv
             flops += 2.0 * M * c.n_coef * c.n_kv_heads * c.n_comp * 2  # K and V
     dec += c.batch * c.n_query * c.n_q_heads * c.head_dim * (esz + 4)  # q in, out
-    pos = int(w.lens.sum()) * c.n_kv_heads
+    pos = int(np.sum(lens)) * c.n_kv_heads
     return dec, main, flops, pos
 
 
-def kernel_sources_hash():
+# the source files behind each main kernel (its own file and the headers it
+# includes): a change to any of them voids that kernel's committed counters
+MAIN_KERNEL_FILES = {
+    "decode_score_kernel": ["decode_two_pass.hip", "mfma_util.hpp", "kernels.hpp", "common.hpp"],
+    "decode_mfma_kernel": ["decode_mfma.hip", "mfma_util.hpp", "kernels.hpp", "common.hpp"],
+    "decode_split_kernel": ["decode.hip", "kernels.hpp", "common.hpp"],
+    "project_f16_kernel": ["project.hip", "kernels.hpp", "common.hpp"],
+    "project_tall_kernel": ["project.hip", "kernels.hpp", "common.hpp"],
+    "project_f32_kernel": ["project.hip", "kernels.hpp", "common.hpp"],
+}
+
+
+def sources_hash(files):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_decode_fourier_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch from committed rocprofv3 counters, if still valid."""
+    """HBM bytes per launch of a main kernel ("decode_main" / "project_main")
+    from committed rocprofv3 counters, if its sources have not changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     e = t.get(workload, {}).get(kernel)
-    if not e or e.get("sources") != kernel_sources_hash():
+    if not e or e.get("sources") != sources_hash(e.get("files", [])):
         return None
     return e.get("bytes_per_launch")
 
@@ -322,7 +336,7 @@ def projection_figures(torch, fb, wl, name, steps, warmup):
     """fa_project on its own workload: TFLOP/s of the call and of its main kernel."""
     w = wl.make(wl.CONFIGS[name])
     bn = Bench(torch, fb, w)
-    _, _, flops, _ = algorithmic(w)
+    _, _, flops, _ = algorithmic(w.cfg, w.lens)
     ms, d_proj, _, kern = bn.run(steps, warmup)
     t_call, t_kern = float(d_proj.mean()), float(kern["project"].mean())
     out = {"workload": name, "note": w.cfg.note, "n_coef": w.cfg.n_coef,
@@ -334,7 +348,7 @@ def projection_figures(torch, fb, wl, name, steps, warmup):
            "main_kernel_us": t_kern * 1e6, "main_kernel_tflops": flops / t_kern / 1e12,
            "main_kernel_mfma_frac": flops / t_kern / 1e12 / MFMA_F16_PEAK_TFLOPS,
            "input_copies": bn.copies,
-           "traffic_bytes_per_launch": measured_traffic(name, "fa_project")}
+           "traffic_bytes_per_launch": measured_traffic(name, "project_main")}
     del bn
     torch.cuda.synchronize()
     return out
@@ -389,7 +403,7 @@ def main():
     w = wl.make(wl.CONFIGS[args.workload])
     c = w.cfg
     steps = c.steps
-    dec_bytes, main_bytes, proj_flops, positions = algorithmic(w)
+    dec_bytes, main_bytes, proj_flops, positions = algorithmic(w.cfg, w.lens)
     bn = Bench(torch, fb, w, args.copies)
     ms_step, d_proj, d_dec, kern = bn.run(args.steps, args.warmup)
     t_proj = float(d_proj.mean())

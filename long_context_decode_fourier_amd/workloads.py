@@ -226,6 +226,15 @@ def _round(x: np.ndarray, dtype: str) -> np.ndarray:
     return bf16_bits(x) if dtype == "bf16" else x
 
 
+def lengths(cfg: Config) -> np.ndarray:
+    """The sequence lengths make(cfg) draws (its generator's first draw)."""
+    if cfg.len_range is None:
+        return np.full(cfg.batch, cfg.seq_len, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    lo, hi = cfg.len_range
+    return rng.integers(lo, hi + 1, size=cfg.batch).astype(np.int64)
+
+
 def make(cfg: Config, lens=None) -> Workload:
     """Draw the workload for ``cfg`` (deterministic in ``cfg.seed``).
 
@@ -243,6 +252,7 @@ def make(cfg: Config, lens=None) -> Workload:
         lens = rng.integers(lo, hi + 1, size=B).astype(np.int64)
     else:
         lens = np.full(B, cfg.seq_len, dtype=np.int64)
+    # (lengths(cfg) repeats this first draw without the rest of the workload)
     offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
 
     dims = np.empty((Hkv, D), dtype=np.int32)

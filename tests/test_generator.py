@@ -66,3 +66,14 @@ def test_signal_is_smooth_and_bounded():
     d = np.diff(x, axis=0)
     assert np.abs(d).mean() < 0.2 * np.abs(x).mean()
     assert np.abs(x).max() < 20
+
+
+def test_lengths_without_drawing_the_workload():
+    for cfg in (wl.custom(name="ragged_small", dtype="bf16", batch=5, n_q_heads=4, n_kv_heads=2, head_dim=32,
+                          n_comp=8, n_coef=9, seq_len=None, len_range=(100, 900), seed=7),
+                wl.CONFIGS["fp32_head"]):
+        assert np.array_equal(wl.lengths(cfg), wl.make(cfg).lens)
+    # the large ragged workload's lengths stay inside its range
+    c = wl.CONFIGS["ragged_batch"]
+    lens = wl.lengths(c)
+    assert lens.shape == (c.batch,) and lens.min() >= c.len_range[0] and lens.max() <= c.len_range[1]
