@@ -640,6 +640,104 @@ __device__ __forceinline__ void prep_edge_block_mfma(const DecodeArgs& a, int b,
   }
 }
 
+// A rows on the MFMA path (dc % 4 == 0, ck 16-byte aligned), as an fp32
+// MFMA product per (sequence, KV head): D[g][n] = sum_c qC[g][c] ck[n][c].
+// Each wave takes TILES 16-row tiles of ck and runs over the columns in
+// groups of 16 NI: lane (r, q) = (lane % 16, lane / 16) holds columns 16 i +
+// 4 q .. 16 i + 4 q + 3 of the group for row r as float4 i, so that step (i,
+// j) of v_mfma_f32_16x16x4f32 (k index q) sums column 16 i + 4 q + j; q_C
+// uses the same column map, read from the block's q rows and dims staged in
+// LDS.  NI covers dc in one group up to 128 columns (TILES * NI <= 12 float4
+// per lane), so the ck loads and the q / dims loads go out together: one
+// memory round trip and one barrier per block.  Coefficient n sits at pair
+// position 0 (n = 0) or n + 1; position 1 (the sine of frequency 0) is 0.
+constexpr int kPrepF4 = 12;  // float4 of ck in flight per lane
+__host__ __device__ constexpr int prep_a_ni(int dc) {
+  return dc <= 32 ? 2 : dc <= 64 ? 4 : dc <= 96 ? 6 : 8;
+}
+__host__ __device__ constexpr int prep_a_tiles(int ni) { return ni >= 8 ? 1 : kPrepF4 / ni / (ni == 2 ? 2 : 1); }
+// ck rows per A block
+__host__ __device__ inline int prep_a_rows(int dc) { return 16 * prep_a_tiles(prep_a_ni(dc)) * (kPrepThreads / 64); }
+
+__host__ __device__ inline bool prep_a_mfma_ok(const DecodeArgs& a, bool vec) {
+  return a.mfma && vec && a.dc % 4 == 0;
+}
+
+template <typename T, int NI>
+__device__ __forceinline__ void prep_a_mfma(const DecodeArgs& a, int b, int h, int chunk, float* sm) {
+  constexpr int TILES = prep_a_tiles(NI);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int G = a.G, D = a.D, dc = a.dc, k = a.k, kpp = a.kpp;
+  const int M = a.seq.mid[b];
+  const int n0 = chunk * (16 * TILES * (kPrepThreads / 64)) + wave * (16 * TILES);
+  const float* ckh = a.ck + (static_cast<int64_t>(b) * a.hkv + h) * k * dc;
+  float* qraw = sm;                                    // [G][D] scaled q rows
+  int* dl = reinterpret_cast<int*>(qraw + G * D);      // [D] dims of KV head h
+  auto load_ck = [&](float4 (&ckv)[TILES][NI], int c0) {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int n = n0 + 16 * t + r16;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = c0 + 16 * i + 4 * q4;
+        ckv[t][i] = (n < k && c < dc) ? *reinterpret_cast<const float4*>(ckh + static_cast<int64_t>(n) * dc + c)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  float4 ckv[TILES][NI];  // the current column group's tiles
+  load_ck(ckv, 0);
+  stage_q<T>(a, b, h, qraw, dl, a.scale);
+  __syncthreads();
+  if (n0 >= kpp) return;  // no barrier follows
+  _Float16* A16 = static_cast<_Float16*>(a.A16);
+  const int64_t arow0 = static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(h) * G;
+  for (int g0 = 0; g0 < G; g0 += 16) {
+    const int g = g0 + r16;
+    efloat4 acc[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) acc[t] = efloat4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < dc; c0 += 16 * NI) {
+      if (c0 > 0 || (g0 > 0 && dc > 16 * NI)) load_ck(ckv, c0);  // else still loaded
+      float qc[NI][4];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = c0 + 16 * i + 4 * q4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = (c + j < dc) ? dl[a.du + c + j] : -1;
+          qc[i][j] = (g < G && d >= 0 && d < D) ? qraw[g * D + d] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const float cv4[4] = {ckv[t][i].x, ckv[t][i].y, ckv[t][i].z, ckv[t][i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(qc[i][j], cv4[j], acc[t], 0, 0, 0);
+        }
+    }
+    // lane holds D[g0 + 4 q + r][n0 + 16 t + r16]
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int n = n0 + 16 * t + r16;
+      const int pos = (n == 0) ? 0 : n + 1;
+      const float alpha = (M > 0 && n < k) ? basis_alpha(n, M) : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gr = g0 + 4 * q4 + r;
+        if (gr >= G) continue;
+        _Float16* row = A16 + (arow0 + gr) * kpp;
+        if (pos < kpp) row[pos] = static_cast<_Float16>(alpha * acc[t][r]);
+        if (n == 0) row[1] = static_cast<_Float16>(0.0f);
+      }
+    }
+  }
+}
+
 // Blocks [0, nedge) are edge blocks (MFMA path), the rest A blocks.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a, int nedge, int chunks) {
@@ -661,7 +759,16 @@ __global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a,
   }
   blk -= nedge;
   const int bh = blk / chunks, chunk = blk % chunks;
-  prep_a_block<T, VEC>(a, bh / a.hkv, bh % a.hkv, chunk, smem);
+  if (prep_a_mfma_ok(a, VEC)) {
+    switch (prep_a_ni(a.dc)) {
+      case 2: prep_a_mfma<T, 2>(a, bh / a.hkv, bh % a.hkv, chunk, smem); break;
+      case 4: prep_a_mfma<T, 4>(a, bh / a.hkv, bh % a.hkv, chunk, smem); break;
+      case 6: prep_a_mfma<T, 6>(a, bh / a.hkv, bh % a.hkv, chunk, smem); break;
+      default: prep_a_mfma<T, 8>(a, bh / a.hkv, bh % a.hkv, chunk, smem); break;
+    }
+  }
+  else
+    prep_a_block<T, VEC>(a, bh / a.hkv, bh % a.hkv, chunk, smem);
 }
 
 // -------------------------------------------------------------- split ----
@@ -1243,12 +1350,13 @@ size_t decode_merge_cv_smem(const DecodeArgs& a) {
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
   const int nedge = a.mfma ? a.nseq * a.hkv * a.edge_split : 0;
+  const bool vec = a.dc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.ck) & 15) == 0;
   const int len = a.mfma ? a.kpp : a.k;
-  const int chunks = a.prep_a ? (len + kPrepPos - 1) / kPrepPos : 0;
+  const int per = prep_a_mfma_ok(a, vec) ? prep_a_rows(a.dc) : kPrepPos;
+  const int chunks = a.prep_a ? (len + per - 1) / per : 0;
   const int blocks = nedge + a.nseq * a.hkv * chunks;
   if (blocks == 0) return hipSuccess;
   const size_t sm = decode_prep_smem(a);
-  const bool vec = a.dc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.ck) & 15) == 0;
   hipError_t e;
 #define FA_PREP(T, V)                                                                        \
   do {                                                                                       \

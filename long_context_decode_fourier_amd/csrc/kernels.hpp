@@ -125,10 +125,16 @@ constexpr int kEdgeParts = 6;
 __host__ __device__ inline bool edge_mfma_ok(const DecodeArgs& a) {
   return a.du % 8 == 0 && a.dc % 8 == 0 && a.D % 32 == 0 && a.G <= 16;
 }
+// The parts are also capped so that the edge blocks of all (sequence, KV
+// head) pairs fit one block per CU: past that, more parts only queue behind
+// each other.
+constexpr int kEdgeBlocksMax = 256;
 inline int edge_parts(const DecodeArgs& a) {
   if (!edge_mfma_ok(a)) return 1;
   const int blocks16 = (a.sink + a.recent + 15) / 16;
-  const int parts = blocks16 < kEdgeParts ? blocks16 : kEdgeParts;
+  int parts = blocks16 < kEdgeParts ? blocks16 : kEdgeParts;
+  const int heads = a.nseq * a.hkv;
+  if (heads > 0 && parts > kEdgeBlocksMax / heads) parts = kEdgeBlocksMax / heads;
   return parts > 1 ? parts : 1;
 }
 
