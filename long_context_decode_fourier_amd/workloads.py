@@ -77,6 +77,7 @@ class Config:
     seed: int = 0
     steps: Tuple[str, ...] = ("project", "decode")
     n_query: int = 1           # queries per sequence (q is [B, n_query, Hq, D] when > 1)
+    period: int = 0            # basis period: 0 = each sequence's middle length, > 0 fixed
     note: str = ""
 
     @property
@@ -202,6 +203,28 @@ class Workload:
         K[:, cp] = self.f64(self.block(self.kc, b, h))
         V[:, cp] = self.f64(self.block(self.vc, b, h))
         return K, V
+
+    def truncated(self, lens) -> "Workload":
+        """The same cache with sequence b cut to its first lens[b] tokens
+        (the rows re-laid out for the shorter lengths; q and dims shared):
+        the state before tokens were appended."""
+        c = self.cfg
+        lens = np.asarray(lens, dtype=np.int64)
+        if lens.shape != self.lens.shape or (lens > self.lens).any() or (lens < 1).any():
+            raise ValueError("truncated lengths must lie in [1, L_b]")
+        offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+
+        def cut(a):
+            if a is None:
+                return None
+            out = np.empty((int(c.n_kv_heads * lens.sum()), a.shape[1]), dtype=a.dtype)
+            for b in range(c.batch):
+                for h in range(c.n_kv_heads):
+                    r0 = int(c.n_kv_heads * offs[b] + h * lens[b])
+                    out[r0:r0 + int(lens[b])] = self.block(a, b, h)[:int(lens[b])]
+            return out
+        return Workload(cfg=c, lens=lens, offs=offs, dims=self.dims, q=self.q, kx=cut(self.kx),
+                        vx=cut(self.vx), kc=cut(self.kc), vc=cut(self.vc))
 
     def edges(self, a: np.ndarray) -> np.ndarray:
         """Gather the sink+recent rows of kc or vc into [B*Hkv, S+R, Dc]."""

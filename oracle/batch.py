@@ -16,6 +16,16 @@ import numpy as np
 from . import fourier_attention as fa
 
 
+def _period(c):
+    """The workload's basis period: 0 (each sequence's own M) or a fixed P."""
+    return getattr(c, "period", 0)
+
+
+def _pkw(c):
+    p = _period(c)
+    return {"period": p} if p else {}
+
+
 def project_block(w, b: int, h: int):
     """(C_K, C_V) [k, Dc] of sequence b, KV head h; zeros when M = 0."""
     c = w.cfg
@@ -25,8 +35,8 @@ def project_block(w, b: int, h: int):
     if M == 0:
         z = np.zeros((c.n_coef, c.n_comp))
         return z, z.copy()
-    return (fa.project(K[start:start + M][:, cd], c.n_coef),
-            fa.project(V[start:start + M][:, cd], c.n_coef))
+    return (fa.project(K[start:start + M][:, cd], c.n_coef, **_pkw(c)),
+            fa.project(V[start:start + M][:, cd], c.n_coef, **_pkw(c)))
 
 
 def project_all(w):
@@ -52,7 +62,7 @@ def decode_block(w, ck_blk, cv_blk, scale: float, b: int, h: int, heads=None):
     K, V = w.natural_kv(b, h)
     q = w.f64(w.q[b, heads])
     return fa.decode(q, K, V, w.comp_dims(h), ck_blk, cv_blk,
-                     c.sink, c.recent, scale)
+                     c.sink, c.recent, scale, **_pkw(c))
 
 
 def decode_all(w, ck, cv, scale: float):
@@ -82,10 +92,34 @@ def attend_all(w, ck, cv, scale: float):
             i = b * c.n_kv_heads + h
             K, V = w.natural_kv(b, h)
             q = w.f64(q4[b, :, h * G:(h + 1) * G]).reshape(nq * G, c.head_dim)
-            o, l = fa.attend(q, K, V, w.comp_dims(h), ck[i], cv[i], c.sink, c.recent, scale)
+            o, l = fa.attend(q, K, V, w.comp_dims(h), ck[i], cv[i], c.sink, c.recent, scale,
+                             **_pkw(c))
             out[b, :, h * G:(h + 1) * G] = o.reshape(nq, G, c.head_dim)
             lse[b, :, h * G:(h + 1) * G] = l.reshape(nq, G)
     return out, lse
+
+
+def append_all(w, ck, cv, ke, ve, k_new, v_new):
+    """One appended token per sequence (``fa.append`` on every (sequence, KV
+    head) block, K and V), for a workload with a fixed basis period.
+
+    ck, cv [B*Hkv, k, Dc] and ke, ve [B*Hkv, S+R, Dc] (retained rows in token
+    order, rows past min(L_b, S+R) unused) describe the cache at lengths
+    ``w.lens``; k_new, v_new [B, Hkv, Dc] are the new token's compressible
+    rows.  Returns the four arrays for lengths ``w.lens + 1``."""
+    c = w.cfg
+    ck, cv = np.array(ck, dtype=np.float64), np.array(cv, dtype=np.float64)
+    ke, ve = np.array(ke, dtype=np.float64), np.array(ve, dtype=np.float64)
+    for b in range(c.batch):
+        L = int(w.lens[b])
+        n = min(L, c.sink + c.recent)
+        for h in range(c.n_kv_heads):
+            i = b * c.n_kv_heads + h
+            for C, E, x in ((ck, ke, k_new), (cv, ve, v_new)):
+                C[i], kept = fa.append(C[i], E[i][:n], np.asarray(x[b, h], dtype=np.float64), L,
+                                       c.sink, c.recent, _period(c))
+                E[i][:kept.shape[0]] = kept
+    return ck, cv, ke, ve
 
 
 def cache_bytes(w):

@@ -35,6 +35,11 @@ What the method computes, restated:
    ``Phi @ C`` (the real-basis form of zero-padding the kept bins and inverting).
 5. Decode: standard softmax attention of the query over the cache in which the
    middle compressible entries are the reconstruction.
+6. Streaming append (a reading; the pages name a translation-invariant
+   transform in the Architecture overview but give no update rule): with a
+   fixed basis period P (``fourier_basis(..., period=P)``) the coefficients of
+   a middle are a sum of one term per token, so the token that leaves the
+   recent window when a new token arrives adds its term (``append``).
 
 Readings where the pages are silent (each is listed in the design notes too):
 basis order is the constant term, then (cos, sin) pairs of ascending frequency;
@@ -63,50 +68,58 @@ def segment(L: int, sink: int, recent: int):
 
 # --------------------------------------------------------------- step 3 -----
 
-def fourier_basis(M: int, k: int) -> np.ndarray:
+def fourier_basis(M: int, k: int, period: int = 0) -> np.ndarray:
     """Orthonormal real Fourier basis Phi [M, k]: Phi[tau, n] = phi_n(tau).
 
     phi_0 is the constant; basis index n >= 1 has frequency f = ceil(n/2); odd n
-    is the cosine and even n the sine of 2 pi f tau / M.  Scale sqrt(2/M), or
-    1/sqrt(M) for the constant and for the Nyquist cosine (2f = M).  The phase
-    f*tau is reduced mod M in integer arithmetic before the trig call.
+    is the cosine and even n the sine of 2 pi f tau / P.  Scale sqrt(2/P), or
+    1/sqrt(P) for the constant and for the Nyquist cosine (2f = P).  The phase
+    f*tau is reduced mod P in integer arithmetic before the trig call.
     [ABSTRACT: orthogonal Fourier bases; SKILL Step 2.]
+
+    P is the period: the middle length M itself (``period`` 0, the pages'
+    transform of the middle), or a fixed P >= M, the basis of a window of P
+    positions of which the first M are filled (a reading for streaming
+    appends, under which appending a token adds one term; the pages give no
+    update rule).  The columns are orthonormal over [0, P).
     """
-    if not (1 <= k <= M):
-        raise ValueError("need 1 <= k <= M (k=%d, M=%d)" % (k, M))
+    P = M if period == 0 else period
+    if not (1 <= k <= P) or not (0 <= M <= P):
+        raise ValueError("need 1 <= k <= P and M <= P (k=%d, M=%d, P=%d)" % (k, M, P))
     tau = np.arange(M, dtype=np.int64)
     n = np.arange(k, dtype=np.int64)
     f = (n + 1) // 2
-    r = np.outer(tau, f) % M
-    angle = 2.0 * np.pi * r / M
+    r = np.outer(tau, f) % P
+    angle = 2.0 * np.pi * r / P
     use_cos = (n == 0) | (n % 2 == 1)
     phi = np.where(use_cos[None, :], np.cos(angle), np.sin(angle))
-    scale = np.where((f == 0) | (2 * f == M), 1.0 / np.sqrt(M), np.sqrt(2.0 / M))
+    scale = np.where((f == 0) | (2 * f == P), 1.0 / np.sqrt(P), np.sqrt(2.0 / P))
     return phi * scale[None, :]
 
 
-# The last basis built, reused while (M, k) repeat (the K and V blocks and the
-# KV heads of one sequence share it).  A memo only: it changes no value.  The
-# key holds the basis function itself, so a replaced fourier_basis (the tests'
-# planted mistakes) is never answered from an earlier function's result.
+# The last basis built, reused while (M, k, period) repeat (the K and V blocks
+# and the KV heads of one sequence share it).  A memo only: it changes no
+# value.  The key holds the basis function itself, so a replaced
+# fourier_basis (the tests' planted mistakes) is never answered from an
+# earlier function's result.
 _BASIS_MEMO = {}
 
 
-def _basis(M: int, k: int) -> np.ndarray:
-    key = (fourier_basis, M, k)
+def _basis(M: int, k: int, period: int = 0) -> np.ndarray:
+    key = (fourier_basis, M, k, period)
     if key not in _BASIS_MEMO:
         _BASIS_MEMO.clear()
-        _BASIS_MEMO[key] = fourier_basis(M, k)
+        _BASIS_MEMO[key] = fourier_basis(M, k, period)
     return _BASIS_MEMO[key]
 
 
-def project(x_mid: np.ndarray, k: int) -> np.ndarray:
+def project(x_mid: np.ndarray, k: int, period: int = 0) -> np.ndarray:
     """Fourier coefficients C [k, c] = Phi^T x_mid of middle rows x_mid [M, c].
 
     [SKILL Step 2: project the middle tokens onto k << M basis functions.]
     """
     x_mid = np.asarray(x_mid, dtype=np.float64)
-    Phi = _basis(x_mid.shape[0], k)
+    Phi = _basis(x_mid.shape[0], k, period)
     return Phi.T @ x_mid
 
 
@@ -124,13 +137,13 @@ def coef_budget(M: int, fraction: float = 0.3) -> int:
 
 # --------------------------------------------------------------- step 4 -----
 
-def reconstruct(coef: np.ndarray, M: int) -> np.ndarray:
+def reconstruct(coef: np.ndarray, M: int, period: int = 0) -> np.ndarray:
     """Approximate middle rows [M, c] = Phi @ coef  [SKILL Step 4]."""
     coef = np.asarray(coef, dtype=np.float64)
-    return _basis(M, coef.shape[0]) @ coef
+    return _basis(M, coef.shape[0], period) @ coef
 
 
-def approximate_cache(X: np.ndarray, comp_dims, coef, sink: int, recent: int):
+def approximate_cache(X: np.ndarray, comp_dims, coef, sink: int, recent: int, period: int = 0):
     """The cache as decode sees it: X [L, D] with the middle rows' compressible
     dims replaced by their reconstruction from ``coef`` [k, len(comp_dims)].
 
@@ -140,7 +153,7 @@ def approximate_cache(X: np.ndarray, comp_dims, coef, sink: int, recent: int):
     start, M = segment(X.shape[0], sink, recent)
     comp_dims = np.asarray(comp_dims, dtype=np.int64)
     if M > 0 and comp_dims.size > 0:
-        X[start:start + M][:, comp_dims] = reconstruct(coef, M)
+        X[start:start + M][:, comp_dims] = reconstruct(coef, M, period)
     return X
 
 
@@ -158,15 +171,15 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
     return (out, p) if return_probs else out
 
 
-def decode(q_rows, K, V, comp_dims, ck, cv, sink: int, recent: int, scale: float):
+def decode(q_rows, K, V, comp_dims, ck, cv, sink: int, recent: int, scale: float, period: int = 0):
     """One decode step of the query rows q_rows [G, D] that share one KV head.
 
     K, V: [L, D] in natural dim order (their middle compressible entries are not
     used: those come from the coefficients ck, cv [k, Dc]).  Reconstruct, then
     attend [SKILL Step 4, then standard attention].
     """
-    Kt = approximate_cache(K, comp_dims, ck, sink, recent)
-    Vt = approximate_cache(V, comp_dims, cv, sink, recent)
+    Kt = approximate_cache(K, comp_dims, ck, sink, recent, period)
+    Vt = approximate_cache(V, comp_dims, cv, sink, recent, period)
     return softmax_attention(q_rows, Kt, Vt, scale)
 
 
@@ -185,7 +198,7 @@ def softmax_attention_lse(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: fl
     return out, (m + np.log(z))[:, 0]
 
 
-def attend(q_rows, K, V, comp_dims, ck, cv, sink: int, recent: int, scale: float):
+def attend(q_rows, K, V, comp_dims, ck, cv, sink: int, recent: int, scale: float, period: int = 0):
     """Several queries of one KV head over the compressed cache.
 
     Every row of q_rows [n, D] attends to all L cached tokens, with no mask
@@ -194,9 +207,52 @@ def attend(q_rows, K, V, comp_dims, ck, cv, sink: int, recent: int, scale: float
     (out [n, D], lse [n]); the lse lets a caller combine this attention with
     attention over tokens that are not in the cache (a prefill chunk's own).
     """
-    Kt = approximate_cache(K, comp_dims, ck, sink, recent)
-    Vt = approximate_cache(V, comp_dims, cv, sink, recent)
+    Kt = approximate_cache(K, comp_dims, ck, sink, recent, period)
+    Vt = approximate_cache(V, comp_dims, cv, sink, recent, period)
     return softmax_attention_lse(q_rows, Kt, Vt, scale)
+
+
+# ------------------------------------------------------ streaming append --
+
+def retained(X: np.ndarray, sink: int, recent: int) -> np.ndarray:
+    """The rows a sequence keeps exactly, in token order [SKILL Step 3]: all L
+    rows when there is no middle, else the first ``sink`` and the last
+    ``recent`` rows."""
+    X = np.asarray(X)
+    start, M = segment(X.shape[0], sink, recent)
+    if M == 0:
+        return X.copy()
+    return np.concatenate([X[:start], X[start + M:]], axis=0)
+
+
+def append(coef: np.ndarray, kept: np.ndarray, x_new: np.ndarray, L: int, sink: int,
+           recent: int, period: int):
+    """One token appended to a compressed sequence of length L, under the
+    fixed-period reading (``fourier_basis`` with ``period`` P > 0; the pages
+    give no update rule for a growing middle).
+
+    ``coef`` [k, c] are the middle's coefficients, ``kept`` [min(L, sink +
+    recent), c] the retained rows in token order, ``x_new`` [c] the new token's
+    row.  The new token is the last recent token; the token that leaves the
+    recent window (the first recent one, or the new token itself when
+    ``recent`` is 0) becomes middle position tau = M and adds its term
+    phi_n(M) x to every coefficient.  Returns (coef, kept) of length L + 1.
+    """
+    coef = np.array(coef, dtype=np.float64, copy=True)
+    kept = np.asarray(kept, dtype=np.float64)
+    x_new = np.asarray(x_new, dtype=np.float64)
+    _, M = segment(L, sink, recent)
+    _, M1 = segment(L + 1, sink, recent)
+    if M1 == M:  # still no middle: the new token is kept
+        return coef, np.concatenate([kept, x_new[None, :]], axis=0)
+    # the middle grows by one position, tau = M
+    if recent > 0:
+        leaving = kept[sink]
+        kept = np.concatenate([kept[:sink], kept[sink + 1:], x_new[None, :]], axis=0)
+    else:
+        leaving = x_new
+    phi_M = fourier_basis(M + 1, coef.shape[0], period)[M]
+    return coef + np.outer(phi_M, leaving), kept
 
 
 def exact_attention(q_rows, K, V, scale: float):

@@ -77,3 +77,17 @@ def test_lengths_without_drawing_the_workload():
     c = wl.CONFIGS["ragged_batch"]
     lens = wl.lengths(c)
     assert lens.shape == (c.batch,) and lens.min() >= c.len_range[0] and lens.max() <= c.len_range[1]
+
+
+def test_truncated_keeps_each_sequence_prefix():
+    cfg = wl.custom(name="trunc", dtype="bf16", batch=3, n_q_heads=4, n_kv_heads=2, head_dim=16,
+                    n_comp=8, n_coef=5, seed=3)
+    w = wl.make(cfg, lens=[50, 9, 31])
+    t = w.truncated([49, 1, 20])
+    assert list(t.lens) == [49, 1, 20] and list(t.offs) == [0, 49, 50]
+    for b in range(3):
+        for h in range(2):
+            K, V = w.natural_kv(b, h)
+            Kt, Vt = t.natural_kv(b, h)
+            L = int(t.lens[b])
+            assert np.array_equal(Kt, K[:L]) and np.array_equal(Vt, V[:L])

@@ -403,11 +403,77 @@ def pin_cache_bytes(o):
     assert ob.cache_bytes(w) == (3200 + 64, 1680 + 64)
 
 
+def pin_fixed_period_basis(o):
+    """A fixed period P reduces to the pinned basis: the first M rows of the
+    period-P basis (M <= P), for odd and even P (the Nyquist cosine); P = M is
+    the plain basis."""
+    for M, k, P in [(5, 3, 12), (7, 7, 8), (1, 4, 4), (9, 9, 9), (10, 6, 15)]:
+        np.testing.assert_allclose(o.fourier_basis(M, k, P), o.fourier_basis(P, k)[:M], atol=1e-14)
+    np.testing.assert_allclose(o.fourier_basis(6, 4, 6), o.fourier_basis(6, 4), atol=1e-14)
+
+
+def pin_fixed_period_complete(o):
+    """With k = P the period-P basis is complete over its window: the middle
+    rows come back exactly from their coefficients (the window's unfilled
+    positions act as zeros)."""
+    x = _rng(31).standard_normal((9, 3))
+    for P in (9, 12, 13):
+        c = o.project(x, P, period=P)
+        np.testing.assert_allclose(o.reconstruct(c, 9, period=P), x, atol=1e-12)
+        # and the energy is kept (Parseval over the window)
+        np.testing.assert_allclose((c * c).sum(0), (x * x).sum(0), rtol=1e-12)
+
+
+def _stream(o, X, L0, S, R, k, P):
+    """Compress X[:L0], then append X[L0], X[L0+1], ... one at a time."""
+    start, M = o.segment(L0, S, R)
+    coef = o.project(X[start:start + M], k, period=P)
+    kept = o.retained(X[:L0], S, R)
+    for L in range(L0, X.shape[0]):
+        coef, kept = o.append(coef, kept, X[L], L, S, R, P)
+    return coef, kept
+
+
+def pin_append_equals_project(o):
+    """Appending token by token gives what compressing the longer sequence at
+    once gives: the same retained rows and (to rounding) the same coefficients,
+    across the step where the sequence first gets a middle, with and without
+    sink and recent tokens."""
+    X = _rng(32).standard_normal((40, 3))
+    for S, R, L0, k, P in [(2, 3, 1, 5, 48), (2, 3, 6, 7, 40), (0, 4, 2, 3, 37),
+                           (3, 0, 3, 6, 50), (0, 0, 1, 4, 41), (2, 3, 20, 9, 64)]:
+        coef, kept = _stream(o, X, L0, S, R, k, P)
+        start, M = o.segment(40, S, R)
+        np.testing.assert_allclose(coef, o.project(X[start:start + M], k, period=P), atol=1e-12)
+        np.testing.assert_array_equal(kept, o.retained(X, S, R))
+
+
+def pin_append_brute_force(o):
+    """Pure-Python loops: the coefficients of a streamed sequence are
+    sum_tau phi_n(tau) x[S + tau] with the period-P cos/sin written out."""
+    X = _rng(33).standard_normal((14, 2))
+    S, R, k, P = 2, 3, 5, 16
+    coef, kept = _stream(o, X, 1, S, R, k, P)
+    M = 14 - S - R
+    for n in range(k):
+        f = (n + 1) // 2
+        a = 1 / math.sqrt(P) if (f == 0 or 2 * f == P) else math.sqrt(2 / P)
+        for c in range(2):
+            want = 0.0
+            for tau in range(M):
+                ang = 2 * math.pi * f * tau / P
+                want += a * (math.cos(ang) if (n == 0 or n % 2 == 1) else math.sin(ang)) * X[S + tau, c]
+            assert abs(coef[n, c] - want) < 1e-12, (n, c)
+    assert kept.shape == (S + R, 2)
+    assert np.array_equal(kept[:S], X[:S]) and np.array_equal(kept[S:], X[14 - R:])
+
+
 PINS = [pin_orthonormal, pin_rfft, pin_irfft_lowpass, pin_parseval_bessel,
         pin_closed_form, pin_golden_basis, pin_segment, pin_brute_force,
         pin_reduces_to_attention, pin_factored, pin_softmax_invariants,
         pin_gqa_stacking, pin_attend_brute_force, pin_lse_closed_form, pin_lse_merge,
-        pin_coef_budget, pin_cache_bytes]
+        pin_coef_budget, pin_cache_bytes, pin_fixed_period_basis, pin_fixed_period_complete,
+        pin_append_equals_project, pin_append_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -419,35 +485,60 @@ def test_pin(pin):
 # Plausible mistakes planted in the oracle (CPU only).  Each must fail a pin.
 
 def _basis_variant(**mut):
-    def basis(M, k):
-        if not (1 <= k <= M):
+    def basis(M, k, period=0):
+        P = M if (period == 0 or mut.get("period_ignored")) else period
+        if not (1 <= k <= P) or M > P:
             raise ValueError
         tau = np.arange(M, dtype=np.int64) + mut.get("tau_shift", 0)
         n = np.arange(k)
         f = n // 2 if mut.get("freq_off") else (n + 1) // 2
-        ang = 2 * np.pi * (np.outer(tau, f) % M) / M
+        ang = 2 * np.pi * (np.outer(tau, f) % P) / P
         use_cos = (n == 0) | (n % 2 == 1)
         if mut.get("swap"):
             use_cos = (n == 0) | ((n % 2 == 0) & (n > 0))
         sin = -np.sin(ang) if mut.get("neg_sin") else np.sin(ang)
         phi = np.where(use_cos[None], np.cos(ang), sin)
-        a = np.where((f == 0) | (2 * f == M), 1 / np.sqrt(M), np.sqrt(2 / M))
+        a = np.where((f == 0) | (2 * f == P), 1 / np.sqrt(P), np.sqrt(2 / P))
         if mut.get("nyquist"):
-            a = np.where(f == 0, 1 / np.sqrt(M), np.sqrt(2 / M))
+            a = np.where(f == 0, 1 / np.sqrt(P), np.sqrt(2 / P))
         if mut.get("no_scale"):
             a = np.ones_like(a)
+        if mut.get("period_scale_m"):  # angle over P but the scale of M
+            a = np.where((f == 0) | (2 * f == M), 1 / np.sqrt(max(M, 1)), np.sqrt(2 / max(M, 1)))
         return phi * a[None]
     return basis
 
 
-def _decode_no_scale(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale):
-    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent)
-    Vt = fa.approximate_cache(V, comp_dims, cv, sink, recent)
+def _append_variant(**mut):
+    def append(coef, kept, x_new, L, sink, recent, period):
+        coef = np.array(coef, dtype=np.float64, copy=True)
+        kept = np.asarray(kept, dtype=np.float64)
+        _, M = fa.segment(L, sink, recent)
+        _, M1 = fa.segment(L + 1, sink, recent)
+        if M1 == M:
+            return coef, np.concatenate([kept, x_new[None, :]], axis=0)
+        if recent > 0:
+            leaving = kept[-1] if mut.get("last_recent") else kept[sink]
+            if mut.get("wrong_end"):  # drops the newest recent row instead of the oldest
+                kept = np.concatenate([kept[:-1], x_new[None, :]], axis=0)
+            else:
+                kept = np.concatenate([kept[:sink], kept[sink + 1:], x_new[None, :]], axis=0)
+        else:
+            leaving = np.zeros_like(x_new) if mut.get("r0_dropped") else x_new
+        tau = M + 1 if mut.get("next_phase") else M
+        phi = fa.fourier_basis(tau + 1, coef.shape[0], period)[tau]
+        return coef + np.outer(phi, leaving), kept
+    return append
+
+
+def _decode_no_scale(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale, period=0):
+    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent, period)
+    Vt = fa.approximate_cache(V, comp_dims, cv, sink, recent, period)
     return fa.softmax_attention(q_rows, Kt, Vt, 1.0)
 
 
-def _decode_values_exact(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale):
-    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent)
+def _decode_values_exact(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale, period=0):
+    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent, period)
     return fa.softmax_attention(q_rows, Kt, V, scale)
 
 
@@ -459,12 +550,12 @@ def _segment_keeps_recent_short(L, sink, recent):
     return sink, max(0, L - sink)
 
 
-def _approx_wrong_dims(X, comp_dims, coef, sink, recent):
+def _approx_wrong_dims(X, comp_dims, coef, sink, recent, period=0):
     X = np.array(X, dtype=np.float64, copy=True)
     start, M = fa.segment(X.shape[0], sink, recent)
     cd = np.sort(np.asarray(comp_dims))[::-1]  # dims permuted vs the coefficients
     if M > 0 and cd.size > 0:
-        X[start:start + M][:, cd] = fa.reconstruct(coef, M)
+        X[start:start + M][:, cd] = fa.reconstruct(coef, M, period)
     return X
 
 
@@ -488,8 +579,8 @@ def _lse_no_max(q, K, V, scale):
     return out, lse - s.max(1)
 
 
-def _attend_values_exact(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale):
-    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent)
+def _attend_values_exact(q_rows, K, V, comp_dims, ck, cv, sink, recent, scale, period=0):
+    Kt = fa.approximate_cache(K, comp_dims, ck, sink, recent, period)
     return fa.softmax_attention_lse(q_rows, Kt, V, scale)
 
 
@@ -516,6 +607,12 @@ MUTANTS = {
     "lse_without_max": ("softmax_attention_lse", _lse_no_max),
     "attend_values_not_reconstructed": ("attend", _attend_values_exact),
     "budget_one_pair_too_many": ("coef_budget", _budget_plus_one_pair),
+    "period_ignored": ("fourier_basis", _basis_variant(period_ignored=True)),
+    "period_scale_of_middle": ("fourier_basis", _basis_variant(period_scale_m=True)),
+    "append_last_recent_leaves": ("append", _append_variant(last_recent=True)),
+    "append_window_shifted_at_wrong_end": ("append", _append_variant(wrong_end=True)),
+    "append_no_recent_drops_token": ("append", _append_variant(r0_dropped=True)),
+    "append_phase_one_ahead": ("append", _append_variant(next_phase=True)),
 }
 
 
@@ -527,8 +624,10 @@ def test_mutants_are_caught(name, monkeypatch):
     for pin in PINS:
         try:
             pin(fa)
-        except Exception:  # noqa: BLE001 - any failure counts as caught
+        except AssertionError:  # a wrong value; other exceptions do not count
             failed.append(pin.__name__)
+        except Exception:  # noqa: BLE001
+            pass
     assert failed, "mutant %s passed every pin" % name
 
 

@@ -144,7 +144,75 @@ def pin_attend_rows(o):
             assert np.abs(out[:, 0] - o.decode_all(w, ck, cv, SCALE)).max() < 1e-12
 
 
-PINS = [pin_project_blocks, pin_decode_rows, pin_attend_rows]
+def _period_workload():
+    # fixed basis period 48 (every middle of the lengths + 1 fits); sequence 1
+    # gets its first middle token on the append (L = 7 = sink + recent), and
+    # sequence 3 stays without one (L = 5)
+    cfg = wl.custom(name="batch_append", dtype="f32", batch=4, n_q_heads=6, n_kv_heads=2,
+                    head_dim=8, n_comp=3, n_coef=5, sink=3, recent=4, mask="seeded", seed=29,
+                    period=48)
+    return wl.make(cfg, lens=[41, 8, 23, 6])
+
+
+def _kept_rows(w, X, b, h):
+    """Retained rows of block (b, h) in token order, padded to sink + recent."""
+    c = w.cfg
+    rows = _rows(w, X, b, h).astype(np.float64)
+    L = rows.shape[0]
+    out = np.zeros((c.sink + c.recent, rows.shape[1]))
+    kept = rows if L <= c.sink + c.recent else np.concatenate([rows[:c.sink], rows[L - c.recent:]])
+    out[:kept.shape[0]] = kept
+    return out
+
+
+def pin_append_blocks(o):
+    """append_all: each (sequence, KV head) block, K and V, takes its own new
+    row; the result equals the coefficients (fixed period) and retained rows
+    of the longer cache, built here block by block.  project_all passes the
+    workload's period to the per-block projection."""
+    w1 = _period_workload()
+    c = w1.cfg
+    w0 = w1.truncated(w1.lens - 1)
+    P = c.period
+    nb = c.batch * c.n_kv_heads
+
+    def state(w):
+        ck = np.zeros((nb, c.n_coef, c.n_comp))
+        cv = np.zeros_like(ck)
+        ke = np.zeros((nb, c.sink + c.recent, c.n_comp))
+        ve = np.zeros_like(ke)
+        for b in range(c.batch):
+            M = max(0, int(w.lens[b]) - c.sink - c.recent)
+            for h in range(c.n_kv_heads):
+                i = b * c.n_kv_heads + h
+                for X, C, E in ((w.kc, ck, ke), (w.vc, cv, ve)):
+                    if M > 0:
+                        C[i] = fa.project(_rows(w, X, b, h)[c.sink:c.sink + M].astype(np.float64),
+                                          c.n_coef, period=P)
+                    E[i] = _kept_rows(w, X, b, h)
+        return ck, cv, ke, ve
+
+    ck0, cv0, ke0, ve0 = state(w0)
+    k_new = np.zeros((c.batch, c.n_kv_heads, c.n_comp))
+    v_new = np.zeros_like(k_new)
+    for b in range(c.batch):
+        for h in range(c.n_kv_heads):
+            k_new[b, h] = _rows(w1, w1.kc, b, h)[-1]
+            v_new[b, h] = _rows(w1, w1.vc, b, h)[-1]
+    got = o.append_all(w0, ck0, cv0, ke0, ve0, k_new, v_new)
+    want = state(w1)
+    for g, x in zip(got, want):
+        assert g.shape == x.shape and np.abs(g - x).max() < 1e-12
+    for b in (0, 2):  # middles longer than k
+        for h in range(c.n_kv_heads):
+            bk, bv = o.project_block(w1, b, h)
+            i = b * c.n_kv_heads + h
+            assert np.abs(bk - want[0][i]).max() < 1e-12 and np.abs(bv - want[1][i]).max() < 1e-12
+    pk, pv = o.project_all(w1)
+    assert np.abs(pk - want[0]).max() < 1e-12 and np.abs(pv - want[1]).max() < 1e-12
+
+
+PINS = [pin_project_blocks, pin_decode_rows, pin_attend_rows, pin_append_blocks]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -232,7 +300,33 @@ def _attend_all_lse_shifted(w, ck, cv, scale):
     return out, np.roll(lse, 1, axis=2)
 
 
+_ORIG_APPEND_ALL = ob.append_all
+
+
+def _append_all_kv_rows_swapped(w, ck, cv, ke, ve, k_new, v_new):
+    return _ORIG_APPEND_ALL(w, ck, cv, ke, ve, v_new, k_new)
+
+
+def _append_all_head_rows_rolled(w, ck, cv, ke, ve, k_new, v_new):
+    return _ORIG_APPEND_ALL(w, ck, cv, ke, ve, np.roll(k_new, 1, axis=1), np.roll(v_new, 1, axis=1))
+
+
+def _project_block_period_dropped(w, b, h):
+    c = w.cfg
+    K, V = w.natural_kv(b, h)
+    start, M = fa.segment(K.shape[0], c.sink, c.recent)
+    cd = w.comp_dims(h)
+    if M == 0:
+        z = np.zeros((c.n_coef, c.n_comp))
+        return z, z.copy()
+    return (fa.project(K[start:start + M][:, cd], c.n_coef),
+            fa.project(V[start:start + M][:, cd], c.n_coef))
+
+
 BATCH_MUTANTS = {
+    "append_all_k_v_rows_swapped": ("append_all", _append_all_kv_rows_swapped),
+    "append_all_new_rows_of_other_head": ("append_all", _append_all_head_rows_rolled),
+    "project_block_period_dropped": ("project_block", _project_block_period_dropped),
     "project_all_block_index_swapped": ("project_all", _project_all_index_swapped),
     "project_block_k_v_swapped": ("project_block", _project_block_kv_swapped),
     "project_block_no_middle_not_zero": ("project_block", _project_block_empty_ones),
@@ -251,6 +345,8 @@ def test_batch_mutants_are_caught(name, monkeypatch):
     for pin in PINS:
         try:
             pin(ob)
-        except Exception:  # noqa: BLE001 - any failure counts as caught
+        except AssertionError:  # a wrong value; other exceptions do not count
             failed.append(pin.__name__)
+        except Exception:  # noqa: BLE001
+            pass
     assert failed, "mutant %s passed every pin" % name
