@@ -88,7 +88,8 @@ typedef struct {
   int32_t sink;        /* tokens kept exactly at the start, >= 0              */
   int32_t recent;      /* tokens kept exactly at the end, >= 0                */
   int32_t n_coef;      /* k >= 1; k <= M_b for every b with M_b > 0           */
-  int32_t reserved;    /* must be 0                                           */
+  int32_t period;      /* basis period P: 0 = each sequence's M_b (default);  */
+                       /* > 0: a fixed P with M_b <= P and k <= P (fa_append) */
   const int32_t *seq_len; /* HOST array [B], L_b >= 1                         */
   const int32_t *dims;    /* DEVICE array [Hkv][D] (fa_decode only)           */
 } fa_desc_t;
@@ -184,6 +185,36 @@ typedef struct {
   int32_t path, rows, items, items2, passes, queries_per_pass;
 } fa_plan_t;
 fa_status_t fa_attend_plan(const fa_desc_t *desc, int32_t n_query, fa_plan_t *plan);
+
+/*
+ * fa_append: one token appended to every sequence (streaming decode).  The
+ * pages name a translation-invariant transform (skill page, Architecture
+ * overview; Step 2) but give no rule for a middle that grows; the reading
+ * taken here is a fixed basis period P = desc.period > 0 (fa_project and
+ * fa_decode use the same P), under which the coefficients of a middle are a
+ * sum of one term per token.  desc describes the cache BEFORE the append
+ * (seq_len = L_b); afterwards the caller describes it with L_b + 1.  For each
+ * sequence b and KV head h, K and V alike:
+ *   - L_b + 1 <= sink + recent: the new token is retained: its compressible
+ *     row becomes retained row L_b of ke / ve;
+ *   - otherwise the token that leaves the recent window (retained row `sink`,
+ *     or the new token itself when recent = 0) enters the middle at tau =
+ *     M_b = L_b - sink - recent:  ck[n][c] += phi_n(M_b) * x[c]  for n < k
+ *     (the ck of fa_project for L_b tokens becomes the ck of fa_project for
+ *     L_b + 1 tokens, to rounding); the recent rows of ke / ve move down by
+ *     one and the new token's row becomes the last.
+ * k_new, v_new: [B][Hkv][Dc] compressible dims of the new token (dims order
+ * of the cache, desc.dtype).  ck, cv, ke, ve are updated in place.  kx / vx
+ * are the caller's: with the packed row layout the new token's exact dims go
+ * into the caller's own layout for L_b + 1.  Required: k_new and v_new; ke
+ * and ve when sink + recent > 0; ck and cv when some sequence has middle
+ * tokens after the append (others may be NULL).  With n_comp_dims = 0 the
+ * call does nothing.  Errors: desc.period = 0 or a middle that would exceed
+ * the period is FA_ERR_SHAPE; overlapping buffers FA_ERR_ALIAS.  No workspace;
+ * two small kernels on `stream`, so calls on one stream are ordered.
+ */
+fa_status_t fa_append(const fa_desc_t *desc, const void *k_new, const void *v_new,
+                      float *ck, float *cv, void *ke, void *ve, void *stream);
 
 /*
  * fa_coef_budget: the number of real coefficients that spans the same space as

@@ -33,7 +33,7 @@ class fa_desc_t(ctypes.Structure):
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("n_comp_dims", ctypes.c_int32),
                 ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
-                ("n_coef", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_coef", ctypes.c_int32), ("period", ctypes.c_int32),
                 ("seq_len", ctypes.POINTER(ctypes.c_int32)),
                 ("dims", ctypes.c_void_p)]
 
@@ -71,6 +71,7 @@ _SIGS = [
     ("fa_decode_noalloc", ctypes.c_int,
      [ctypes.POINTER(fa_desc_t)] + [ctypes.c_void_p] * 7 + [ctypes.c_float, ctypes.c_void_p,
                                                            ctypes.c_void_p]),
+    ("fa_append", ctypes.c_int, [ctypes.POINTER(fa_desc_t)] + [ctypes.c_void_p] * 7),
 ]
 
 
@@ -99,12 +100,12 @@ class Desc:
     """Python view of fa_desc_t; keeps the host length array alive."""
 
     def __init__(self, dtype, batch, n_q_heads, n_kv_heads, head_dim, n_comp_dims,
-                 n_coef, seq_len, sink=32, recent=64, dims=None):
+                 n_coef, seq_len, sink=32, recent=64, dims=None, period=0):
         self._lens = (ctypes.c_int32 * max(1, len(seq_len)))(*[int(x) for x in seq_len])
         self.dims = dims  # device int32 tensor [Hkv, D] (decode only)
         self.c = fa_desc_t(int(dtype), int(batch), int(n_q_heads), int(n_kv_heads),
                            int(head_dim), int(n_comp_dims), int(sink), int(recent),
-                           int(n_coef), 0, self._lens,
+                           int(n_coef), int(period), self._lens,
                            ctypes.c_void_p(dims.data_ptr() if dims is not None else 0))
 
     @classmethod
@@ -112,7 +113,7 @@ class Desc:
         c = w.cfg
         return cls(BF16 if c.dtype == "bf16" else F32, c.batch, c.n_q_heads, c.n_kv_heads,
                    c.head_dim, c.n_comp, c.n_coef, [int(x) for x in w.lens],
-                   sink=c.sink, recent=c.recent, dims=dims)
+                   sink=c.sink, recent=c.recent, dims=dims, period=c.period)
 
 
 def _ptr(t):
@@ -166,6 +167,13 @@ def decode(desc: Desc, q, kx, vx, ke, ve, ck, cv, scale, out, ws=None, stream=No
     _check(lib().fa_decode(ctypes.byref(desc.c), _ptr(q), _ptr(kx), _ptr(vx), _ptr(ke),
                            _ptr(ve), _ptr(ck), _ptr(cv), ctypes.c_float(scale), _ptr(out),
                            _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def append(desc: Desc, k_new, v_new, ck, cv, ke, ve, stream=None):
+    """fa_append: one token per sequence appended to a fixed-period cache
+    (desc describes the lengths before the append); ck, cv, ke, ve in place."""
+    _check(lib().fa_append(ctypes.byref(desc.c), _ptr(k_new), _ptr(v_new), _ptr(ck), _ptr(cv),
+                           _ptr(ke), _ptr(ve), _stream(stream)))
 
 
 class fa_plan_t(ctypes.Structure):

@@ -11,10 +11,12 @@ namespace fa {
 
 constexpr int kMaxBatch = 64;
 
-// Basis convention (orthonormal real Fourier basis over M middle positions):
+// Basis convention (orthonormal real Fourier basis of period P over the M
+// middle positions; P = M unless the descriptor fixes a period P >= M):
 // index n has frequency f = (n+1)/2; n = 0 and odd n are cosines, even n >= 2
-// sines; scale sqrt(2/M), or 1/sqrt(M) for f = 0 and for 2f = M.  Kernels work
-// with the unscaled trig values and apply the scale on the coefficient side.
+// sines, of 2 pi f tau / P; scale sqrt(2/P), or 1/sqrt(P) for f = 0 and for
+// 2f = P.  Kernels work with the unscaled trig values and apply the scale on
+// the coefficient side.
 __host__ __device__ inline int basis_freq(int n) { return (n + 1) >> 1; }
 __host__ __device__ inline bool basis_is_cos(int n) { return n == 0 || (n & 1); }
 
@@ -22,6 +24,7 @@ __host__ __device__ inline bool basis_is_cos(int n) { return n == 0 || (n & 1); 
 struct SeqTable {
   int32_t len[kMaxBatch];    // L_b
   int32_t mid[kMaxBatch];    // M_b = max(0, L_b - sink - recent)
+  int32_t per[kMaxBatch];    // basis period P_b: M_b, or the descriptor's fixed period
   int64_t row0[kMaxBatch];   // Hkv * (L_0 + ... + L_{b-1}): first cache row of b
   int32_t item0[kMaxBatch];  // first work item of sequence b
   int32_t nsplit[kMaxBatch]; // token splits of sequence b

@@ -54,18 +54,19 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-__device__ inline float basis_alpha(int n, int M) {
+// Scale of basis function n for the basis period per.
+__device__ inline float basis_alpha(int n, int per) {
   const int f = basis_freq(n);
-  return (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
-                                 : sqrtf(2.0f / static_cast<float>(M));
+  return (f == 0 || 2 * f == per) ? 1.0f / sqrtf(static_cast<float>(per))
+                                 : sqrtf(2.0f / static_cast<float>(per));
 }
 
-// e^{i 2 pi (j * tau mod M) / M} for any integer tau (negative allowed).
-__device__ inline float2 unit_phase(int j, int tau, int M) {
-  int64_t r = (static_cast<int64_t>(j) * tau) % M;
-  if (r < 0) r += M;
+// e^{i 2 pi (j * tau mod per) / per} for any integer tau (negative allowed).
+__device__ inline float2 unit_phase(int j, int tau, int per) {
+  int64_t r = (static_cast<int64_t>(j) * tau) % per;
+  if (r < 0) r += per;
   float s, c;
-  sincos_phase(static_cast<int>(r), M, &s, &c);
+  sincos_phase(static_cast<int>(r), per, &s, &c);
   return make_float2(c, s);
 }
 
@@ -123,7 +124,7 @@ __device__ inline void stage_q(const DecodeArgs& a, int b, int h, float* qraw, i
 template <typename T, bool VEC>
 __device__ __forceinline__ void prep_a_block(const DecodeArgs& a, int b, int h, int chunk, float* sm) {
   const int G = a.G, D = a.D, dc = a.dc, du = a.du;
-  const int M = a.seq.mid[b];
+  const int M = a.seq.mid[b], per = a.seq.per[b];
   const int len = a.mfma ? a.kpp : a.k;
   const int p0 = chunk * kPrepPos;
   // pair order: position p >= 2 uses row p - 1, position 0 row 0
@@ -166,7 +167,7 @@ __device__ __forceinline__ void prep_a_block(const DecodeArgs& a, int b, int h, 
   if (pos >= len) return;
   const int n = a.mfma ? pair_pos_to_n(pos, a.k) : pos;
   const bool live = n >= 0 && n < a.k && M > 0;
-  const float alpha = live ? basis_alpha(n, M) : 0.0f;
+  const float alpha = live ? basis_alpha(n, per) : 0.0f;
   const float* crow = ckl + (live ? n - r0 : 0) * CS;
   for (int g = tid >> 6; g < G; g += kPrepThreads / 64) {
     const float* qg = qc + g * dc;
@@ -669,7 +670,7 @@ __device__ __forceinline__ void prep_a_mfma(const DecodeArgs& a, int b, int h, i
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int G = a.G, D = a.D, dc = a.dc, k = a.k, kpp = a.kpp;
-  const int M = a.seq.mid[b];
+  const int M = a.seq.mid[b], per = a.seq.per[b];
   const int n0 = chunk * (16 * TILES * (kPrepThreads / 64)) + wave * (16 * TILES);
   const float* ckh = a.ck + (static_cast<int64_t>(b) * a.hkv + h) * k * dc;
   float* qraw = sm;                                    // [G][D] scaled q rows
@@ -725,7 +726,7 @@ __device__ __forceinline__ void prep_a_mfma(const DecodeArgs& a, int b, int h, i
     for (int t = 0; t < TILES; ++t) {
       const int n = n0 + 16 * t + r16;
       const int pos = (n == 0) ? 0 : n + 1;
-      const float alpha = (M > 0 && n < k) ? basis_alpha(n, M) : 0.0f;
+      const float alpha = (M > 0 && n < k) ? basis_alpha(n, per) : 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int gr = g0 + 4 * q4 + r;
@@ -793,7 +794,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int local = item - a.seq.item0[b];
   const int ns = a.seq.nsplit[b];
   const int rg = local / ns, sp = local % ns;
-  const int L = a.seq.len[b], M = a.seq.mid[b];
+  const int L = a.seq.len[b], M = a.seq.mid[b], per = a.seq.per[b];
   const int S = a.sink, E = a.sink + a.recent;
   const int t_begin = sp * a.seq.chunk[b];
   const int t_end = min(L, t_begin + a.seq.chunk[b]);
@@ -841,7 +842,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   float wacc[kMaxSlots][2][R];
 #pragma unroll
   for (int i = 0; i < kMaxSlots; ++i) {
-    wstep[i] = (has_mid && i < nown) ? unit_phase(tid + 256 * i, 1, M) : make_float2(1.0f, 0.0f);
+    wstep[i] = (has_mid && i < nown) ? unit_phase(tid + 256 * i, 1, per) : make_float2(1.0f, 0.0f);
 #pragma unroll
     for (int r = 0; r < R; ++r) wacc[i][0][r] = wacc[i][1][r] = 0.0f;
   }
@@ -891,10 +892,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
           } else {
             const int tau = t - S;
             const int j0 = part * sl4, j1 = min(nslots, j0 + sl4);
-            const float2 w = unit_phase(1, tau, M);
+            const float2 w = unit_phase(1, tau, per);
             float2 z = make_float2(1.0f, 0.0f);
             for (int j = j0; j < j1; ++j) {
-              if (((j - j0) & 31) == 0) z = unit_phase(j, tau, M);
+              if (((j - j0) & 31) == 0) z = unit_phase(j, tau, per);
               if (j == 0) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[r] = fmaf(As[r * a.kpad], z.x, acc[r]);
@@ -993,7 +994,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < kMaxSlots; ++i) {
         // anchor at the tile's first middle token (tau >= 0)
-        z[i] = (i < nown && mid_lo < mid_hi) ? unit_phase(tid + 256 * i, tile0 + mid_lo - S, M)
+        z[i] = (i < nown && mid_lo < mid_hi) ? unit_phase(tid + 256 * i, tile0 + mid_lo - S, per)
                                              : make_float2(0.0f, 0.0f);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -1088,7 +1089,7 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   const int row = blockIdx.x;      // b * hq + i
   const int b = row / a.hq, i = row % a.hq, h = i / a.G;
   const int ns = a.seq.nsplit[b];
-  const int M = a.seq.mid[b];
+  const int M = a.seq.mid[b], per = a.seq.per[b];
   const bool has_mid = a.dc > 0 && M > 0;
   const int nvec = a.du + a.dc + (has_mid ? a.k : 0);
   const int idx = blockIdx.y * 256 + threadIdx.x;
@@ -1164,7 +1165,7 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     const int64_t sgs = static_cast<int64_t>(a.hq) * a.kpad;
     float v = 0.0f;
     for (int sg = 0; sg < nsg; ++sg) v += wp[sg * sgs];
-    mrow[a.dc + n] = v * basis_alpha(n, M);
+    mrow[a.dc + n] = v * basis_alpha(n, per);
     return;
   }
   // fixed-order sum over the splits s_lo, s_lo + 1, ...: the loads already
@@ -1201,7 +1202,7 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     mrow[idx - a.du] = v;
   } else {
     const int n = idx - a.du - a.dc;
-    mrow[a.dc + n] = v * basis_alpha(n, M);
+    mrow[a.dc + n] = v * basis_alpha(n, per);
   }
 }
 

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int ns = a.seq.nsplit[b];  // middle splits + the edge split
   const int nsm = ns - a.edge_split;  // middle splits (the edge splits come last)
   const int rg = local / nsm, sp = local % nsm;
-  const int L = a.seq.len[b], M = a.seq.mid[b];
+  const int L = a.seq.len[b], M = a.seq.mid[b], per = a.seq.per[b];
   const int S = a.sink;
   const int t_begin = S + sp * a.seq.chunk[b];
   const int t_end = min(S + M, t_begin + a.seq.chunk[b]);
@@ -217,21 +217,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
 
   // ---- basis generator: lane -> token l16 of the tile and frequencies
-  //      16 u + 4 g4 + j (j < 4) of its wave's units.  Integer phases (mod M)
+  //      16 u + 4 g4 + j (j < 4) of its wave's units.  Integer phases (mod per)
   //      of tau, 16 tau and f0 tau (f0 = 16 u0 + 4 g4) for this lane's token,
   //      advanced by 16 tokens per tile.
-  const float invM = has_mid ? 1.0f / static_cast<float>(M) : 0.0f;
+  const float inv_per = has_mid ? 1.0f / static_cast<float>(per) : 0.0f;
   const int f0 = 16 * u0 + 4 * g4;
   int ph_tau = 0, ph_16 = 0, ph_f0 = 0, inc_tau = 0, inc_16 = 0, inc_f0 = 0;
   if (has_mid) {
-    int tau0 = (t_begin + l16 - S) % M;
-    if (tau0 < 0) tau0 += M;
+    int tau0 = (t_begin + l16 - S) % per;
+    if (tau0 < 0) tau0 += per;
     ph_tau = tau0;
-    ph_16 = phase_mod(16, tau0, M);
-    ph_f0 = phase_mod(f0, tau0, M);
-    inc_tau = T % M;
-    inc_16 = phase_mod(16, T, M);
-    inc_f0 = phase_mod(f0, T, M);
+    ph_16 = phase_mod(16, tau0, per);
+    ph_f0 = phase_mod(f0, tau0, per);
+    inc_tau = T % per;
+    inc_16 = phase_mod(16, T, per);
+    inc_f0 = phase_mod(f0, T, per);
   }
 
   // ============================================ [C] value moments + [A] basis
@@ -253,10 +253,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         for (int mb = 0; mb < MB; ++mb) pv4[mb] = *reinterpret_cast<const half4*>(ph + (mb * 16 + l16) * TP + 4 * g4);
       }
       const bool mid = do_a && tile0 + l16 < t_end;
-      // seeds of this lane's token: e^{i f0 x}, e^{i x}, e^{i 16 x}, x = 2 pi tau / M
-      const float x0 = static_cast<float>(ph_f0) * invM;
-      const float x1 = static_cast<float>(ph_tau) * invM;
-      const float x16 = static_cast<float>(ph_16) * invM;
+      // seeds of this lane's token: e^{i f0 x}, e^{i x}, e^{i 16 x}, x = 2 pi tau / per
+      const float x0 = static_cast<float>(ph_f0) * inv_per;
+      const float x1 = static_cast<float>(ph_tau) * inv_per;
+      const float x16 = static_cast<float>(ph_16) * inv_per;
       // a lane whose token is not a middle token seeds zeros: all its values are 0
       const float c0 = mid ? cos_rev(x0) : 0.0f, s0 = mid ? sin_rev(x0) : 0.0f;
       const float c1 = cos_rev(x1), s1 = sin_rev(x1);
@@ -340,9 +340,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) spart[(wave * MR + mb * 16 + 4 * g4 + r) * TP + l16] = sacc[mb][r];
-        ph_tau = add_mod(ph_tau, inc_tau, M);
-        ph_16 = add_mod(ph_16, inc_16, M);
-        ph_f0 = add_mod(ph_f0, inc_f0, M);
+        ph_tau = add_mod(ph_tau, inc_tau, per);
+        ph_16 = add_mod(ph_16, inc_16, per);
+        ph_f0 = add_mod(ph_f0, inc_f0, per);
       }
     }
   };

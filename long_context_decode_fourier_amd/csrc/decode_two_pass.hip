@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64 * NW) void decode_score_kernel(DecodeArgs a) {
   const int ns = a.seq.nsplit[b];
   const int nsm = ns - a.edge_split;  // middle splits (the edge splits come last)
   const int rg = local / nsm, sp = local % nsm;
-  const int L = a.seq.len[b], M = a.seq.mid[b];
+  const int L = a.seq.len[b], M = a.seq.mid[b], per = a.seq.per[b];
   const int S = a.sink;
   const int t_begin = S + sp * a.seq.chunk[b];
   const int t_end = min(S + M, t_begin + a.seq.chunk[b]);
@@ -252,27 +252,27 @@ __global__ __launch_bounds__(64 * NW) void decode_score_kernel(DecodeArgs a) {
   float* m_out = a.msub + a.hq * (a.pcum[b] / 16) + static_cast<int64_t>(orow) * (mpad / 16) + (t_begin - S) / 16;
 
   // ---- basis generator: lane -> token l16 of the tile and frequencies
-  //      16 u + 4 g4 + j (j < 4) of its wave's units; integer phases (mod M)
+  //      16 u + 4 g4 + j (j < 4) of its wave's units; integer phases (mod per)
   //      of tau, 16 tau and f0 tau for the lane's token, advanced per tile
-  const float invM = 1.0f / static_cast<float>(M);
+  const float inv_per = 1.0f / static_cast<float>(per);
   const int f0 = 16 * u0 + 4 * g4;
   int ph_tau, ph_16, ph_f0;
   {
     const int tau0 = t_begin + l16 - S;  // < M + 16 <= 2^30 + 16
-    ph_tau = tau0 % M;
-    ph_16 = phase_mod(16, tau0, M);
-    ph_f0 = phase_mod(f0, tau0, M);
+    ph_tau = tau0 % per;
+    ph_16 = phase_mod(16, tau0, per);
+    ph_f0 = phase_mod(f0, tau0, per);
   }
-  const int inc_tau = T % M;
-  const int inc_16 = phase_mod(16, T, M);
-  const int inc_f0 = phase_mod(f0, T, M);
+  const int inc_tau = T % per;
+  const int inc_16 = phase_mod(16, T, per);
+  const int inc_f0 = phase_mod(f0, T, per);
 
   // [A] compressed score partials of tile tile0 -> spart
   auto scores_a = [&](int tile0) {
     const bool mid = tile0 + l16 < t_end;
-    const float x0 = static_cast<float>(ph_f0) * invM;
-    const float x1 = static_cast<float>(ph_tau) * invM;
-    const float x16 = static_cast<float>(ph_16) * invM;
+    const float x0 = static_cast<float>(ph_f0) * inv_per;
+    const float x1 = static_cast<float>(ph_tau) * inv_per;
+    const float x16 = static_cast<float>(ph_16) * inv_per;
     // a lane whose token is past the range seeds zeros: all its values are 0
     const float c0 = mid ? cos_rev(x0) : 0.0f, s0 = mid ? sin_rev(x0) : 0.0f;
     const float c1 = cos_rev(x1), s1 = sin_rev(x1);
@@ -327,9 +327,9 @@ __global__ __launch_bounds__(64 * NW) void decode_score_kernel(DecodeArgs a) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) spart[(wave * MR + mb * 16 + 4 * g4 + r) * TP + l16] = sacc[mb][r];
-    ph_tau = add_mod(ph_tau, inc_tau, M);
-    ph_16 = add_mod(ph_16, inc_16, M);
-    ph_f0 = add_mod(ph_f0, inc_f0, M);
+    ph_tau = add_mod(ph_tau, inc_tau, per);
+    ph_16 = add_mod(ph_16, inc_16, per);
+    ph_f0 = add_mod(ph_f0, inc_f0, per);
   };
 
   // exact-dim scores of tile tile0 from the kx operands kr
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
   const int sigma = local % a.nslices;
   const int rem = local / a.nslices;
   const int sg = rem % nsg, rg = rem / nsg;
-  const int M = a.seq.mid[b], chunk = a.seq.chunk[b];
+  const int M = a.seq.mid[b], period = a.seq.per[b], chunk = a.seq.chunk[b];
   const int mpad = (M + TT - 1) & ~(TT - 1);
   const int m16 = (M + 15) & ~15;
   const int rows = a.rows, qi0 = rg * rows;
@@ -591,10 +591,10 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
   const int64_t prow = static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(qi0) * ns;
 
   // maximum of every row over all its splits (the merge uses the same):
-  // 64 * NW / MR threads per row, each with its splits' loads all in flight
+  // 64 * NW / MR threads period row, each with its splits' loads all in flight
   // before the first use, then a reduction over the row's lanes
   {
-    constexpr int TPR = 64 * NW / MR;  // threads per row (a power of two <= 64)
+    constexpr int TPR = 64 * NW / MR;  // threads period row (a power of two <= 64)
     constexpr int kLoads = 8;
     const int row = tid / TPR, part = tid % TPR;
     float m = -INFINITY;
@@ -640,32 +640,32 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
     // Fixed basis table of the lane's frequencies f = 16 (gbeg + j) + l16 at
     // the block offsets t = 32 kp + 8 g4 + e (the B operand layout), fp16, and
     // the frame rotation e^{-i theta_f TB} between consecutive blocks
-    const float invM = 1.0f / static_cast<float>(M);
+    const float inv_period = 1.0f / static_cast<float>(period);
     half8 Ec[NGW][2], Es[NGW][2];
     float rc[NGW], rs[NGW];
 #pragma unroll
     for (int j = 0; j < NGW; ++j) {
-      // integer phases f t mod M: f < 2^13 and t < 64 keep every product in
-      // 32 bits; consecutive offsets add f mod M
+      // integer phases f t mod period: f < 2^13 and t < 64 keep every product in
+      // 32 bits; consecutive offsets add f mod period
       const int f = 16 * (gbeg + min(j, max(ng - 1, 0))) + l16;
-      const int fm = f % M;
+      const int fm = f % period;
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        int ph = (f * (32 * kp + 8 * g4)) % M;
+        int ph = (f * (32 * kp + 8 * g4)) % period;
         uint32_t pc[4], ps[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float x0 = static_cast<float>(ph) * invM;
-          ph = add_mod(ph, fm, M);
-          const float x1 = static_cast<float>(ph) * invM;
-          ph = add_mod(ph, fm, M);
+          const float x0 = static_cast<float>(ph) * inv_period;
+          ph = add_mod(ph, fm, period);
+          const float x1 = static_cast<float>(ph) * inv_period;
+          ph = add_mod(ph, fm, period);
           pc[e2] = pack_f16(cos_rev(x0), cos_rev(x1));
           ps[e2] = pack_f16(sin_rev(x0), sin_rev(x1));
         }
         Ec[j][kp] = __builtin_bit_cast(half8, make_uint4(pc[0], pc[1], pc[2], pc[3]));
         Es[j][kp] = __builtin_bit_cast(half8, make_uint4(ps[0], ps[1], ps[2], ps[3]));
       }
-      const float xr = static_cast<float>((f * TB) % M) * invM;
+      const float xr = static_cast<float>((f * TB) % period) * inv_period;
       rc[j] = cos_rev(xr);
       rs[j] = sin_rev(xr);
     }
@@ -686,7 +686,7 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
     // References only grow inside a pass-1 split, so a row whose first tile
     // already has the split's final reference kept it throughout: when that
     // holds for every row of the wave, no tile needs rescaling and the
-    // per-tile references are not read at all
+    // period-tile references are not read at all
     bool moved_any;
     {
       bool mv = false;
@@ -795,7 +795,7 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
 #pragma unroll
     for (int j = 0; j < NGW; ++j) {
       const int f = 16 * (gbeg + min(j, max(ng - 1, 0))) + l16;
-      const float x = static_cast<float>(phase_mod(f, tau_last, M)) * invM;
+      const float x = static_cast<float>(phase_mod(f, tau_last, period)) * inv_period;
       const float cb = cos_rev(x), sb = sin_rev(x);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)

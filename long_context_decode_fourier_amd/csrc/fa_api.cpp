@@ -50,6 +50,8 @@ struct Shape {
   int dtype, B, Hq, Hkv, G, D, Dc, Du, S, R, k;
   int nq;  // queries per sequence (fa_attend); Hq and G then count nq * heads
   int L[fa::kMaxBatch], M[fa::kMaxBatch];
+  int P;                  // fixed basis period (0: each sequence's own M)
+  int per[fa::kMaxBatch]; // basis period of sequence b
   int64_t row0[fa::kMaxBatch];
   int64_t total_len;
   int max_len;
@@ -59,7 +61,8 @@ struct Shape {
 fa_status_t validate(const fa_desc_t* d, Shape* sh) {
   if (!d) return fail(FA_ERR_NULL, "desc is NULL");
   if (d->dtype != FA_F32 && d->dtype != FA_BF16) return fail(FA_ERR_DTYPE, "unknown dtype %d", d->dtype);
-  if (d->reserved != 0) return fail(FA_ERR_SHAPE, "desc.reserved must be 0");
+  if (d->period < 0 || d->period > (1 << 30))
+    return fail(FA_ERR_SHAPE, "desc.period %d outside [0, 2^30]", d->period);
   if (d->batch < 1 || d->batch > FA_MAX_BATCH)
     return fail(FA_ERR_SHAPE, "batch %d outside [1, %d]", d->batch, FA_MAX_BATCH);
   if (!d->seq_len) return fail(FA_ERR_NULL, "desc.seq_len is NULL");
@@ -84,6 +87,9 @@ fa_status_t validate(const fa_desc_t* d, Shape* sh) {
   sh->S = d->sink;
   sh->R = d->recent;
   sh->k = d->n_coef;
+  sh->P = d->period;
+  if (sh->P > 0 && sh->k > sh->P)
+    return fail(FA_ERR_SHAPE, "n_coef %d exceeds the basis period %d", sh->k, sh->P);
   sh->nq = 1;
   sh->total_len = 0;
   sh->max_len = 0;
@@ -92,11 +98,15 @@ fa_status_t validate(const fa_desc_t* d, Shape* sh) {
     const int L = d->seq_len[b];
     if (L < 1 || L > (1 << 30)) return fail(FA_ERR_SHAPE, "seq_len[%d] = %d outside [1, 2^30]", b, L);
     const int64_t M = std::max<int64_t>(0, static_cast<int64_t>(L) - sh->S - sh->R);
-    if (M > 0 && sh->Dc > 0 && sh->k > M)
+    if (sh->P == 0 && M > 0 && sh->Dc > 0 && sh->k > M)
       return fail(FA_ERR_SHAPE, "n_coef %d exceeds the %lld middle tokens of sequence %d", sh->k,
                   static_cast<long long>(M), b);
+    if (sh->P > 0 && M > sh->P)
+      return fail(FA_ERR_SHAPE, "the %lld middle tokens of sequence %d exceed the basis period %d",
+                  static_cast<long long>(M), b, sh->P);
     sh->L[b] = L;
     sh->M[b] = static_cast<int>(M);
+    sh->per[b] = sh->P > 0 ? sh->P : static_cast<int>(M);
     sh->row0[b] = static_cast<int64_t>(sh->Hkv) * sh->total_len;
     sh->total_len += L;
     sh->max_len = std::max(sh->max_len, L);
@@ -170,6 +180,7 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
   for (int b = 0; b < sh.B; ++b) {
     a.seq.len[b] = sh.L[b];
     a.seq.mid[b] = sh.M[b];
+    a.seq.per[b] = sh.per[b];
     a.seq.row0[b] = sh.row0[b];
   }
   if (!p->f16 || a.ncols == 0) return FA_OK;
@@ -393,6 +404,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
     const int ns = nsm + a.edge_split;
     a.seq.len[b] = sh.L[b];
     a.seq.mid[b] = sh.M[b];
+    a.seq.per[b] = sh.per[b];
     a.seq.row0[b] = sh.row0[b];
     a.seq.item0[b] = item;
     a.seq.nsplit[b] = ns;
@@ -761,6 +773,74 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
     e = fa::launch_decode_merge(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode merge kernel");
   }
+  return FA_OK;
+}
+
+fa_status_t fa_append(const fa_desc_t* desc, const void* k_new, const void* v_new, float* ck, float* cv,
+                      void* ke, void* ve, void* stream) {
+  Shape sh;
+  fa_status_t st = validate(desc, &sh);
+  if (st != FA_OK) return st;
+  if (sh.P == 0)
+    return fail(FA_ERR_SHAPE, "fa_append needs a fixed basis period (desc.period > 0): with the "
+                              "period set by the middle length every coefficient would change");
+  bool any_mid = false;  // some sequence has a middle after the append
+  for (int b = 0; b < sh.B; ++b) {
+    if (sh.L[b] >= (1 << 30)) return fail(FA_ERR_SHAPE, "seq_len[%d] = %d cannot grow", b, sh.L[b]);
+    const int64_t M1 = std::max<int64_t>(0, static_cast<int64_t>(sh.L[b]) + 1 - sh.S - sh.R);
+    if (M1 > sh.P)
+      return fail(FA_ERR_SHAPE, "sequence %d would have %lld middle tokens, more than the basis period %d", b,
+                  static_cast<long long>(M1), sh.P);
+    any_mid = any_mid || M1 > 0;
+  }
+  if (sh.Dc == 0) return FA_OK;
+  const bool keep = sh.S + sh.R > 0;
+  if (!k_new || !v_new) return fail(FA_ERR_NULL, "k_new and v_new are required");
+  if (keep && (!ke || !ve)) return fail(FA_ERR_NULL, "ke and ve are required when sink + recent > 0");
+  if (any_mid && (!ck || !cv)) return fail(FA_ERR_NULL, "ck and cv are required once a sequence has a middle");
+  const size_t esz = elem_bytes(sh.dtype);
+  const size_t nb = static_cast<size_t>(sh.B) * sh.Hkv;
+  const size_t x_bytes = nb * sh.Dc * esz, e_bytes = nb * (sh.S + sh.R) * sh.Dc * esz;
+  const size_t c_bytes = nb * static_cast<size_t>(sh.k) * sh.Dc * sizeof(float);
+  if (esz == 2 && ((reinterpret_cast<uintptr_t>(ke) | reinterpret_cast<uintptr_t>(ve) |
+                    reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 1))
+    return fail(FA_ERR_SHAPE, "bf16 rows must be 2-byte aligned");
+  const void* outs[4] = {ck, cv, ke, ve};
+  const size_t osz[4] = {c_bytes, c_bytes, e_bytes, e_bytes};
+  const void* ins[2] = {k_new, v_new};
+  for (int i = 0; i < 4; ++i) {
+    if (!osz[i] || !outs[i]) continue;
+    for (int j = 0; j < 2; ++j)
+      if (overlap(outs[i], osz[i], ins[j], x_bytes))
+        return fail(FA_ERR_ALIAS, "an updated cache buffer overlaps k_new or v_new");
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[j] && overlap(outs[i], osz[i], outs[j], osz[j]))
+        return fail(FA_ERR_ALIAS, "ck, cv, ke and ve must not overlap");
+  }
+  fa::AppendArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.xnew[0] = k_new;
+  a.xnew[1] = v_new;
+  if (any_mid) {
+    a.c[0] = ck;
+    a.c[1] = cv;
+  }
+  if (keep) {
+    a.e[0] = ke;
+    a.e[1] = ve;
+  }
+  a.nmat = 2;
+  a.hkv = sh.Hkv;
+  a.dc = sh.Dc;
+  a.k = sh.k;
+  a.sink = sh.S;
+  a.recent = sh.R;
+  a.esz = static_cast<int>(esz);
+  a.nseq = sh.B;
+  a.period = sh.P;
+  for (int b = 0; b < sh.B; ++b) a.len[b] = sh.L[b];
+  const hipError_t e = fa::launch_append(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append kernels");
   return FA_OK;
 }
 

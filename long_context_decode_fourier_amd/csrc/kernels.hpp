@@ -44,6 +44,18 @@ hipError_t launch_edge_gather(const EdgeArgs& a, hipStream_t s);
 // the retained rows (then no separate gather is launched).
 hipError_t launch_project_reduce(const ProjArgs& a, const EdgeArgs& ea, hipStream_t s);
 
+// ---------------------------------------------------------------- append --
+// One token appended to each sequence of a fixed-period cache (fa_append).
+constexpr int kMaxAppendDc = 256;
+struct AppendArgs {
+  const void* xnew[2];     // new token's compressible rows [B*Hkv][Dc] (K, V)
+  float* c[2];             // ck, cv [B*Hkv][k][Dc] (nullptr: no sequence gets a middle)
+  void* e[2];              // ke, ve [B*Hkv][sink+recent][Dc] (nullptr: nothing retained)
+  int nmat, hkv, dc, k, sink, recent, esz, nseq, period;
+  int32_t len[kMaxBatch];  // lengths before the append
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- decode --
 constexpr int kDecRows = 4;    // query rows per work item (VALU path)
 constexpr int kDecTile = 64;   // tokens per tile (VALU path)

@@ -40,7 +40,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kLdsStride = kProjTT + 8;  // halves per LDS column (padding spreads banks)
 
 struct ProjItem {
-  int b, ktile, ctile, t_begin, t_end, M;
+  int b, ktile, ctile, t_begin, t_end, M, per;  // M middle positions, per the basis period
   int slot;  // partial-tile slot: item0[b] + (ktile * nctiles + ctile) * nsplit + split
 };
 
@@ -64,6 +64,7 @@ __device__ inline bool proj_item(const ProjArgs& a, int nitems, int block, ProjI
   it.ctile = group / ns;
   const int sp = group % ns;
   it.M = a.seq.mid[it.b];
+  it.per = a.seq.per[it.b];
   it.t_begin = sp * a.seq.chunk[it.b];
   it.t_end = min(it.M, it.t_begin + a.seq.chunk[it.b]);
   it.slot = a.seq.item0[it.b] + (it.ktile * a.nctiles + it.ctile) * ns + sp;
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
   // a wave whose coefficient rows all lie past k (the padding of the last
   // k-tile) only loads and converts the cache tile
   const bool active = it.ktile * TK + wr * (RB * 32) < a.k;
-  const int M = it.M;
+  const int M = it.M, per = it.per;
   const int L = a.seq.len[it.b];
   const int64_t row0 = a.seq.row0[it.b];
 
@@ -124,21 +125,21 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
   uint2 raw[NPG][8];
 
   // ---- basis generator state, one coefficient row per lane and row block
-  const float invM = 1.0f / static_cast<float>(M);
+  const float inv_per = 1.0f / static_cast<float>(per);
   float c2[RB], off[RB];
   int fr[RB], ph[RB], d64[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int n = it.ktile * TK + wr * (RB * 32) + rb * 32 + (lane & 31);
     const int ne = min(n, a.k - 1);
-    const int f = basis_freq(ne) % M;
+    const int f = basis_freq(ne) % per;
     float s, c;
-    sincos_phase(f, M, &s, &c);
+    sincos_phase(f, per, &s, &c);
     c2[rb] = 2.0f * c;
     off[rb] = basis_is_cos(ne) ? 0.25f : 0.0f;  // cos(2 pi x) = sin(2 pi (x + 1/4))
     fr[rb] = f;
-    ph[rb] = phase_mod(f, it.t_begin + 32 * (lane >> 5), M);
-    d64[rb] = phase_mod(f, kProjTT, M);
+    ph[rb] = phase_mod(f, it.t_begin + 32 * (lane >> 5), per);
+    d64[rb] = phase_mod(f, kProjTT, per);
   }
 
   floatx16 acc[RB][CB];
@@ -216,9 +217,9 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
         if (s == 0) {
           const int r0 = ph[rb];
           int r1 = r0 + fr[rb];
-          if (r1 >= M) r1 -= M;
-          v[0] = sin_rev(fmaf(static_cast<float>(r0), invM, off[rb]));
-          v[1] = sin_rev(fmaf(static_cast<float>(r1), invM, off[rb]));
+          if (r1 >= per) r1 -= per;
+          v[0] = sin_rev(fmaf(static_cast<float>(r0), inv_per, off[rb]));
+          v[1] = sin_rev(fmaf(static_cast<float>(r1), inv_per, off[rb]));
 #pragma unroll
           for (int e = 2; e < 8; ++e) v[e] = fmaf(c2[rb], v[e - 1], -v[e - 2]);
         } else {
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       ph[rb] += d64[rb];
-      if (ph[rb] >= M) ph[rb] -= M;
+      if (ph[rb] >= per) ph[rb] -= per;
     }
     __syncthreads();
     buf ^= 1;
@@ -292,8 +293,8 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void project_f16_kernel(ProjArgs a
           const int col = it.ctile * TN + wc * (CB * 32) + cb * 32 + (lane & 31);
           if (n < a.k && col < a.ncols) {
             const int f = basis_freq(n);
-            const float alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
-                                                       : sqrtf(2.0f / static_cast<float>(M));
+            const float alpha = (f == 0 || 2 * f == per) ? 1.0f / sqrtf(static_cast<float>(per))
+                                                       : sqrtf(2.0f / static_cast<float>(per));
             const int blk = col / a.dc, c = col % a.dc, mat = blk / a.hkv, h = blk % a.hkv;
             (mat ? a.out[1] : a.out[0])[((static_cast<int64_t>(it.b) * a.hkv + h) * a.k + n) * a.dc + c] = alpha * acc[rb][cb][r];
           }
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(64 * kTallWaves, 2) void project_tall_kernel(ProjAr
   if (!proj_item(a, a.nitems, blockIdx.x, &it)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool active = it.ktile * TK + wave * (RB * 32) < a.k;
-  const int M = it.M;
+  const int M = it.M, per = it.per;
   const int L = a.seq.len[it.b];
   const int64_t row0 = a.seq.row0[it.b];
 
@@ -380,21 +381,21 @@ __global__ __launch_bounds__(64 * kTallWaves, 2) void project_tall_kernel(ProjAr
   };
 
   // ---- basis generator state, one coefficient row per lane and row block
-  const float invM = 1.0f / static_cast<float>(M);
+  const float inv_per = 1.0f / static_cast<float>(per);
   float c2[RB], off[RB];
   int fr[RB], ph[RB], d64[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int n = it.ktile * TK + wave * (RB * 32) + rb * 32 + (lane & 31);
     const int ne = min(n, a.k - 1);
-    const int f = basis_freq(ne) % M;
+    const int f = basis_freq(ne) % per;
     float sn, cs;
-    sincos_phase(f, M, &sn, &cs);
+    sincos_phase(f, per, &sn, &cs);
     c2[rb] = 2.0f * cs;
     off[rb] = basis_is_cos(ne) ? 0.25f : 0.0f;
     fr[rb] = f;
-    ph[rb] = phase_mod(f, it.t_begin + 32 * (lane >> 5), M);
-    d64[rb] = phase_mod(f, kProjTT, M);
+    ph[rb] = phase_mod(f, it.t_begin + 32 * (lane >> 5), per);
+    d64[rb] = phase_mod(f, kProjTT, per);
   }
   floatx16 acc[RB][CB];
 #pragma unroll
@@ -414,9 +415,9 @@ __global__ __launch_bounds__(64 * kTallWaves, 2) void project_tall_kernel(ProjAr
       if (s == 0) {
         const int r0 = ph[rb];
         int r1 = r0 + fr[rb];
-        if (r1 >= M) r1 -= M;
-        v[0] = sin_rev(fmaf(static_cast<float>(r0), invM, off[rb]));
-        v[1] = sin_rev(fmaf(static_cast<float>(r1), invM, off[rb]));
+        if (r1 >= per) r1 -= per;
+        v[0] = sin_rev(fmaf(static_cast<float>(r0), inv_per, off[rb]));
+        v[1] = sin_rev(fmaf(static_cast<float>(r1), inv_per, off[rb]));
 #pragma unroll
         for (int e = 2; e < 8; ++e) v[e] = fmaf(c2[rb], v[e - 1], -v[e - 2]);
       } else {
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(64 * kTallWaves, 2) void project_tall_kernel(ProjAr
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       ph[rb] += d64[rb];
-      if (ph[rb] >= M) ph[rb] -= M;
+      if (ph[rb] >= per) ph[rb] -= per;
     }
   };
 
@@ -516,8 +517,8 @@ __global__ __launch_bounds__(64 * kTallWaves, 2) void project_tall_kernel(ProjAr
           const int col = it.ctile * kTallTN + cb * 32 + (lane & 31);
           if (n < a.k && col < a.ncols) {
             const int f = basis_freq(n);
-            const float alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
-                                                       : sqrtf(2.0f / static_cast<float>(M));
+            const float alpha = (f == 0 || 2 * f == per) ? 1.0f / sqrtf(static_cast<float>(per))
+                                                       : sqrtf(2.0f / static_cast<float>(per));
             const int cblk = col / a.dc, c = col % a.dc, cmat = cblk / a.hkv, ch = cblk % a.hkv;
             (cmat ? a.out[1] : a.out[0])[((static_cast<int64_t>(it.b) * a.hkv + ch) * a.k + n) * a.dc + c] =
                 alpha * acc[rb][cb][r];
@@ -611,12 +612,12 @@ __global__ __launch_bounds__(256) void project_reduce_kernel(ProjArgs a, EdgeArg
           sum.w += v[j].w;
         }
     }
-    const int M = a.seq.mid[b];
+    const int M = a.seq.mid[b], per = a.seq.per[b];
     float alpha = 0.0f;
     if (M > 0) {
       const int f = basis_freq(n);
-      alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
-                                     : sqrtf(2.0f / static_cast<float>(M));
+      alpha = (f == 0 || 2 * f == per) ? 1.0f / sqrtf(static_cast<float>(per))
+                                     : sqrtf(2.0f / static_cast<float>(per));
     }
     // Dc % 4 == 0: the 4 columns share (matrix, KV head) and are 16-byte aligned
     const int blk = col0 / a.dc, c = col0 % a.dc, mat = blk / a.hkv, h = blk % a.hkv;
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
   const int h = g % a.hkv;
   g /= a.hkv;
   const int mat = g % a.nmat, b = g / a.nmat;
-  const int M = a.seq.mid[b], L = a.seq.len[b];
+  const int M = a.seq.mid[b], per = a.seq.per[b], L = a.seq.len[b];
   const int cl = threadIdx.x & 31, tl = threadIdx.x >> 5;
   const float* X = static_cast<const float*>(a.x[mat]) +
                    (a.seq.row0[b] + static_cast<int64_t>(h) * L + a.sink) * a.dc;
@@ -661,7 +662,7 @@ __global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
   // this thread's basis value of each chunk: coefficient bn, position bt
   const int bn = min(nt * kF32Coefs + static_cast<int>(threadIdx.x) / kF32Chunk, a.k - 1);
   const int bt = static_cast<int>(threadIdx.x) % kF32Chunk;
-  const int bf = M > 0 ? basis_freq(bn) % M : 0;
+  const int bf = M > 0 ? basis_freq(bn) % per : 0;
   const bool bcos = basis_is_cos(bn);
   for (int c0 = 0; c0 < a.dc; c0 += 32) {
     const int c = c0 + cl;
@@ -682,7 +683,7 @@ __global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
       {
         const int tau = p0 + bt;
         float sn = 0.0f, cs = 0.0f;
-        if (tau < M) sincos_phase(phase_mod(bf, tau, M), M, &sn, &cs);
+        if (tau < M) sincos_phase(phase_mod(bf, tau, per), per, &sn, &cs);
         phis[threadIdx.x / kF32Chunk][bt] = bcos ? cs : sn;
       }
       if (p0 + kF32Chunk < M) load_x(p0 + kF32Chunk, xn);
@@ -716,8 +717,8 @@ __global__ __launch_bounds__(256) void project_f32_kernel(ProjArgs a) {
           float alpha = 0.0f;
           if (M > 0) {
             const int f = basis_freq(n);
-            alpha = (f == 0 || 2 * f == M) ? 1.0f / sqrtf(static_cast<float>(M))
-                                           : sqrtf(2.0f / static_cast<float>(M));
+            alpha = (f == 0 || 2 * f == per) ? 1.0f / sqrtf(static_cast<float>(per))
+                                           : sqrtf(2.0f / static_cast<float>(per));
           }
           out[static_cast<int64_t>(n) * a.dc + c] = alpha * total;
         }

@@ -82,6 +82,23 @@ int main(void) {
                     NULL), FA_ERR_ALIAS);
 
   /* host-only helpers */
+  /* fixed basis period: validation and fa_append's host checks (no launch) */
+  bad = d;
+  bad.period = 3000; /* sequence 0's middle (4000) past the period */
+  EXPECT(fa_decode_workspace_size(&bad, &n), FA_ERR_SHAPE);
+  bad = d;
+  bad.period = -5;
+  EXPECT(fa_project_workspace_size(&bad, &n), FA_ERR_SHAPE);
+  bad = d;
+  bad.period = 5000;
+  EXPECT(fa_decode_workspace_size(&bad, &n), FA_OK);
+  EXPECT(fa_append(&d, P(1), P(2), (float*)P(3), (float*)P(4), P(5), P(6), NULL), FA_ERR_SHAPE);
+  EXPECT(fa_append(&bad, NULL, P(2), (float*)P(3), (float*)P(4), P(5), P(6), NULL), FA_ERR_NULL);
+  EXPECT(fa_append(&bad, P(1), P(2), (float*)P(3), (float*)P(4), P(5), NULL, NULL), FA_ERR_NULL);
+  EXPECT(fa_append(&bad, P(1), P(2), (float*)P(1), (float*)P(4), P(5), P(6), NULL), FA_ERR_ALIAS);
+  bad.period = 4000; /* one more middle token would not fit */
+  EXPECT(fa_append(&bad, P(1), P(2), (float*)P(3), (float*)P(4), P(5), P(6), NULL), FA_ERR_SHAPE);
+
   EXPECT(fa_coef_budget(4000, 0.3), 2399);
   EXPECT(fa_coef_budget(3, 0.3), 1);
   EXPECT(fa_coef_budget(0, 0.3), 0);

@@ -66,6 +66,9 @@ def _size(fn, d):
     (dict(seq_len=[4096, 0]), 2),
     (dict(seq_len=[4096, 120]), 2),   # 24 middle tokens < 33 coefficients
     (dict(sink=-1), 2),
+    (dict(period=-1), 2),
+    (dict(period=3000), 2),          # sequence 0's middle (4000) exceeds the period
+    (dict(period=4000, n_coef=4001), 2),  # k past the period
 ])
 def test_invalid_desc(kw, code):
     d = _desc(**kw)
@@ -87,6 +90,14 @@ def test_workspace_sizes_and_short_sequences():
     # no compressible dims: k is not checked against the middle length
     st, _ = _size(fb.lib().fa_decode_workspace_size, _desc(n_comp_dims=0, seq_len=[100, 100]))
     assert st == 0
+
+
+def test_fixed_period_accepts_k_past_the_middle():
+    # with a fixed period, k is bounded by the period, not by each middle
+    st, _ = _size(fb.lib().fa_decode_workspace_size, _desc(period=5000, n_coef=2049, seq_len=[4096, 200]))
+    assert st == 0, fb.lib().fa_last_error()
+    st, _ = _size(fb.lib().fa_project_workspace_size, _desc(period=5000, n_coef=2049, seq_len=[4096, 200]))
+    assert st == 0, fb.lib().fa_last_error()
 
 
 GB = 1 << 30  # fake device addresses, 1 GiB apart; every call below fails validation
@@ -226,3 +237,24 @@ def test_noalloc_scratch_size_matches_header():
     import re as _re
     mib = int(_re.search(r"#define FA_NOALLOC_SCRATCH_MIB (\d+)", text).group(1))
     assert fb.NOALLOC_SCRATCH_BYTES == mib << 20
+
+
+def _call_append(d, kn=1, vn=2, ck=3, cv=4, ke=5, ve=6):
+    P = lambda v: ctypes.c_void_p(v * GB if 0 < v < 64 else v)
+    return fb.lib().fa_append(ctypes.byref(d.c), P(kn), P(vn), P(ck), P(cv), P(ke), P(ve), None)
+
+
+def test_append_host_errors_without_gpu():
+    # the basis must have a fixed period
+    assert _call_append(_desc()) == 2
+    assert "period" in fb.lib().fa_last_error().decode()
+    d = _desc(period=4500)
+    # a middle that would pass the period: 4500 - 4000 = 500 more tokens fit, then no more
+    assert _call_append(_desc(period=4000, seq_len=[4096, 1000])) == 2
+    assert _call_append(d, kn=0) == 1
+    assert _call_append(d, ve=0) == 1
+    assert _call_append(d, cv=0) == 1
+    assert _call_append(d, ck=1) == 6                     # ck overlaps k_new
+    assert _call_append(d, ke=3) == 6                     # ke overlaps ck
+    # no compressible dims: nothing to do, every pointer may be NULL
+    assert _call_append(_desc(period=4500, n_comp_dims=0), 0, 0, 0, 0, 0, 0) == 0

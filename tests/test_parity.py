@@ -276,6 +276,38 @@ def test_two_pass_shapes(fb, name):
     _full_check(fb, w)
 
 
+# A fixed basis period P (the descriptor's period field, the basis of
+# streaming appends): P past every middle, for the fp32 kernels, the bf16
+# one-pass MFMA path (several tiles, ragged tails), the bf16 VALU path (exact
+# dims not a multiple of 8) and the two-pass path (long middles); the
+# projection's tall and square tiles.
+PERIOD = {
+    "per_f32_gqa": (dict(dtype="f32", batch=3, n_q_heads=4, n_kv_heads=2, head_dim=16, n_comp=8,
+                         n_coef=9, period=500), [200, 106, 333], None),
+    "per_bf16_mfma": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                           n_comp=64, n_coef=301, period=1201), [1000, 777], "mfma"),
+    "per_bf16_valu": (dict(dtype="bf16", batch=2, n_q_heads=6, n_kv_heads=3, head_dim=16,
+                           n_comp=4, n_coef=7, period=4096), [97, 2000], "valu"),
+    "per_bf16_two_pass": (dict(dtype="bf16", batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                               n_comp=64, n_coef=2401, period=10007), [9000, 6001], "two_pass"),
+    "per_bf16_square_tiles": (dict(dtype="bf16", batch=1, n_q_heads=8, n_kv_heads=8, head_dim=128,
+                                   n_comp=64, n_coef=1025, period=20000), [16100], None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PERIOD))
+def test_fixed_period(fb, name):
+    kw, lens, path = PERIOD[name]
+    cfg = wl.custom(name=name, seed=300 + sorted(PERIOD).index(name), **kw)
+    _say("case %s lens=%s period %d" % (name, lens, cfg.period))
+    w = wl.make(cfg, lens=lens)
+    if path:
+        plan = fb.attend_plan(fb.Desc.from_workload(w))
+        _say("  plan %s" % plan)
+        assert plan["path"] == path
+    _full_check(fb, w)
+
+
 def test_fp32_head(fb):
     _say("case fp32_head")
     _full_check(fb, wl.make(wl.CONFIGS["fp32_head"]))
