@@ -204,6 +204,37 @@ class Workload:
         V[:, cp] = self.f64(self.block(self.vc, b, h))
         return K, V
 
+    def value_noise(self, std: float = 0.1) -> np.ndarray:
+        """Noise for the dimension analysis, laid out like K and V in natural
+        dim order: [rows, D] in the storage dtype, N(0, std^2) draws from a
+        generator of its own (seed + 7919), so the rest of the workload is
+        unchanged.  Column d is the noise added to dim d of the values when
+        that dim is perturbed."""
+        c = self.cfg
+        rng = np.random.Generator(np.random.PCG64(c.seed + 7919))
+        rows = int(c.n_kv_heads * self.lens.sum())
+        return _round(rng.standard_normal((rows, c.head_dim)) * std, c.dtype)
+
+    def natural_rows(self, X: np.ndarray, b: int, h: int) -> np.ndarray:
+        """Block (b, h) of a [rows, D] natural-order array as float64 [L, D]."""
+        return self.f64(self.block(X, b, h))
+
+    def natural_k_rows(self) -> np.ndarray:
+        """K of every (sequence, KV head) block as one [rows, D] array in
+        natural dim order and the storage dtype (the uncompressed keys the
+        dimension analysis runs over), packed like kx / kc."""
+        c = self.cfg
+        rows = int(c.n_kv_heads * self.lens.sum())
+        out = np.zeros((rows, c.head_dim), dtype=self.kc.dtype)
+        for h in range(c.n_kv_heads):
+            ex, cp = self.dims[h, :c.n_exact], self.dims[h, c.n_exact:]
+            for b in range(c.batch):
+                r0, L = self.row0(b, h), int(self.lens[b])
+                if self.kx is not None:
+                    out[r0:r0 + L][:, ex] = self.block(self.kx, b, h)
+                out[r0:r0 + L][:, cp] = self.block(self.kc, b, h)
+        return out
+
     def truncated(self, lens) -> "Workload":
         """The same cache with sequence b cut to its first lens[b] tokens
         (the rows re-laid out for the shorter lengths; q and dims shared):

@@ -122,6 +122,26 @@ def append_all(w, ck, cv, ke, ve, k_new, v_new):
     return ck, cv, ke, ve
 
 
+def dim_sensitivity_all(w, noise, scale: float):
+    """Squared per-dim sensitivities [Hq, D] of a workload [SKILL Step 1]:
+    entry (i, d) sums, over the sequences and the n_query queries, the squared
+    change of query head i's outputs when ``noise[:, d]`` (``noise`` [rows, D],
+    natural dim order, packed like the cache rows) is added to dim d of its
+    KV head's values.  The pages' score of dim d is sqrt(sum_i entry (i, d))."""
+    c = w.cfg
+    G = c.n_q_heads // c.n_kv_heads
+    q4 = w.q if w.q.ndim == 4 else w.q[:, None]
+    out = np.zeros((c.n_q_heads, c.head_dim))
+    for b in range(c.batch):
+        for h in range(c.n_kv_heads):
+            K, V = w.natural_kv(b, h)
+            eps = w.natural_rows(noise, b, h)
+            for i in range(h * G, (h + 1) * G):
+                q = w.f64(q4[b, :, i])
+                out[i] += fa.dim_sensitivity(q, K, V, eps, scale)
+    return out
+
+
 def cache_bytes(w):
     """(uncompressed, compressed) bytes of the workload's KV cache: K and V in
     full (the sizes of the natural [L, D] arrays), versus the exact dims of

@@ -40,6 +40,9 @@ What the method computes, restated:
    fixed basis period P (``fourier_basis(..., period=P)``) the coefficients of
    a middle are a sum of one term per token, so the token that leaves the
    recent window when a new token arrives adds its term (``append``).
+7. Dimension analysis [SKILL Step 1]: noise added to one dim of the values at a
+   time, and the norm of the change of the attention output, per dim
+   (``dim_sensitivity``); low scores mark dims that can be compressed.
 
 Readings where the pages are silent (each is listed in the design notes too):
 basis order is the constant term, then (cos, sin) pairs of ascending frequency;
@@ -253,6 +256,33 @@ def append(coef: np.ndarray, kept: np.ndarray, x_new: np.ndarray, L: int, sink: 
         leaving = x_new
     phi_M = fourier_basis(M + 1, coef.shape[0], period)[M]
     return coef + np.outer(phi_M, leaving), kept
+
+
+# ------------------------------------------------------ dimension analysis --
+
+def dim_sensitivity(q_rows, K, V, noise, scale: float) -> np.ndarray:
+    """Per-dim sensitivity of one head's attention output to noise on the
+    values [SKILL Step 1, Architecture overview (dimension analysis stage)]:
+    for each dim d, the values get ``noise[:, d]`` added to their dim d only,
+    attention runs again, and the score is the Frobenius norm of the change of
+    the outputs of the query rows ``q_rows`` [n, D] over the cache K, V
+    [L, D].  ``noise`` [L, D] holds the pages' N(0, 0.1^2) draws, one column
+    per perturbed dim, passed in.  Every query row attends to every token (the
+    module's mask is not given; decode and ``attend`` use none).  Returns the
+    squared norms [D] (the pages' score is their square root, summed over the
+    heads and rows a caller aggregates before the root)."""
+    q_rows = np.atleast_2d(np.asarray(q_rows, dtype=np.float64))
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    noise = np.asarray(noise, dtype=np.float64)
+    base = softmax_attention(q_rows, K, V, scale)
+    out = np.zeros(V.shape[1])
+    for d in range(V.shape[1]):
+        Vn = V.copy()
+        Vn[:, d] += noise[:, d]
+        diff = softmax_attention(q_rows, K, Vn, scale) - base
+        out[d] = float((diff * diff).sum())
+    return out
 
 
 def exact_attention(q_rows, K, V, scale: float):

@@ -468,12 +468,74 @@ def pin_append_brute_force(o):
     assert np.array_equal(kept[:S], X[:S]) and np.array_equal(kept[S:], X[14 - R:])
 
 
+def pin_sensitivity_linear(o):
+    """Noise on one dim of the values changes only that dim of the outputs, by
+    the attention probabilities applied to the noise (linearity of attention
+    in V): the score of dim d is |P noise[:, d]|^2 with P the softmax of the
+    unperturbed scores, whatever V holds."""
+    rng = _rng(41)
+    L, D, n = 30, 6, 4
+    K, V, q = rng.standard_normal((L, D)), rng.standard_normal((L, D)), rng.standard_normal((n, D))
+    eps = 0.1 * rng.standard_normal((L, D))
+    got = o.dim_sensitivity(q, K, V, eps, 0.4)
+    s = 0.4 * q @ K.T
+    P = np.exp(s - s.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    np.testing.assert_allclose(got, ((P @ eps) ** 2).sum(0), rtol=1e-9, atol=1e-15)
+    # V does not enter; a dim without noise scores 0
+    eps2 = eps.copy()
+    eps2[:, 2] = 0.0
+    got2 = o.dim_sensitivity(q, K, 5.0 * V + 1.0, eps2, 0.4)
+    np.testing.assert_allclose(np.delete(got2, 2), np.delete(got, 2), rtol=1e-9, atol=1e-15)
+    assert abs(got2[2]) < 1e-24
+
+
+def pin_sensitivity_uniform(o):
+    """Zero queries attend uniformly: each row's change in dim d is the mean
+    noise of dim d over the L tokens, so the score is n * mean^2."""
+    rng = _rng(42)
+    L, D, n = 17, 5, 3
+    eps = 0.1 * rng.standard_normal((L, D))
+    got = o.dim_sensitivity(np.zeros((n, D)), rng.standard_normal((L, D)), rng.standard_normal((L, D)), eps, 1.0)
+    np.testing.assert_allclose(got, n * eps.mean(0) ** 2, rtol=1e-9, atol=1e-18)
+
+
+def pin_sensitivity_brute_force(o):
+    """Pure-Python loops: perturb dim d of V, rerun attention, sum the squared
+    changes of every output entry."""
+    rng = _rng(43)
+    L, D, n, scale = 5, 3, 2, 0.7
+    K, V, q = rng.standard_normal((L, D)), rng.standard_normal((L, D)), rng.standard_normal((n, D))
+    eps = 0.1 * rng.standard_normal((L, D))
+
+    def attn(Vm):
+        out = []
+        for i in range(n):
+            sc = [scale * sum(q[i][j] * K[t][j] for j in range(D)) for t in range(L)]
+            m = max(sc)
+            e = [math.exp(x - m) for x in sc]
+            z = sum(e)
+            out.append([sum(e[t] / z * Vm[t][j] for t in range(L)) for j in range(D)])
+        return out
+
+    base = attn(V.tolist())
+    got = o.dim_sensitivity(q, K, V, eps, scale)
+    for d in range(D):
+        Vn = V.tolist()
+        for t in range(L):
+            Vn[t][d] += eps[t][d]
+        pert = attn(Vn)
+        want = sum((pert[i][j] - base[i][j]) ** 2 for i in range(n) for j in range(D))
+        assert abs(got[d] - want) < 1e-12 * max(1.0, want), (d, got[d], want)
+
+
 PINS = [pin_orthonormal, pin_rfft, pin_irfft_lowpass, pin_parseval_bessel,
         pin_closed_form, pin_golden_basis, pin_segment, pin_brute_force,
         pin_reduces_to_attention, pin_factored, pin_softmax_invariants,
         pin_gqa_stacking, pin_attend_brute_force, pin_lse_closed_form, pin_lse_merge,
         pin_coef_budget, pin_cache_bytes, pin_fixed_period_basis, pin_fixed_period_complete,
-        pin_append_equals_project, pin_append_brute_force]
+        pin_append_equals_project, pin_append_brute_force, pin_sensitivity_linear,
+        pin_sensitivity_uniform, pin_sensitivity_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -590,6 +652,30 @@ _ORIG_LSE = fa.softmax_attention_lse
 def _budget_plus_one_pair(M, fraction=0.3):
     return min(M, 2 * int(fraction * M) + 1)
 
+def _sens_variant(**mut):
+    def dim_sensitivity(q_rows, K, V, noise, scale):
+        q_rows = np.atleast_2d(np.asarray(q_rows, dtype=np.float64))
+        K, V, noise = (np.asarray(x, dtype=np.float64) for x in (K, V, noise))
+        base = fa.softmax_attention(q_rows, K, V, scale)
+        out = np.zeros(V.shape[1])
+        for d in range(V.shape[1]):
+            Vn, Kn = V.copy(), K.copy()
+            if mut.get("all_dims"):
+                Vn += noise
+            elif mut.get("keys"):
+                Kn[:, d] += noise[:, d]
+            else:
+                Vn[:, d] += noise[:, d]
+            col = (d + 1) % V.shape[1] if mut.get("wrong_column") else d
+            if mut.get("wrong_column"):
+                Vn = V.copy()
+                Vn[:, d] += noise[:, col]
+            diff = fa.softmax_attention(q_rows, Kn, Vn, scale) - base
+            out[d] = float(np.sqrt((diff * diff).sum())) if mut.get("root") else float((diff * diff).sum())
+        return out
+    return dim_sensitivity
+
+
 MUTANTS = {
     "sin_cos_swapped": ("fourier_basis", _basis_variant(swap=True)),
     "sin_sign": ("fourier_basis", _basis_variant(neg_sin=True)),
@@ -613,6 +699,10 @@ MUTANTS = {
     "append_window_shifted_at_wrong_end": ("append", _append_variant(wrong_end=True)),
     "append_no_recent_drops_token": ("append", _append_variant(r0_dropped=True)),
     "append_phase_one_ahead": ("append", _append_variant(next_phase=True)),
+    "sensitivity_noise_on_every_dim": ("dim_sensitivity", _sens_variant(all_dims=True)),
+    "sensitivity_noise_on_keys": ("dim_sensitivity", _sens_variant(keys=True)),
+    "sensitivity_noise_column_shifted": ("dim_sensitivity", _sens_variant(wrong_column=True)),
+    "sensitivity_norm_not_squared": ("dim_sensitivity", _sens_variant(root=True)),
 }
 
 

@@ -212,7 +212,30 @@ def pin_append_blocks(o):
     assert np.abs(pk - want[0]).max() < 1e-12 and np.abs(pv - want[1]).max() < 1e-12
 
 
-PINS = [pin_project_blocks, pin_decode_rows, pin_attend_rows, pin_append_blocks]
+def pin_sensitivity_rows(o):
+    """dim_sensitivity_all: entry (i, d) sums fa.dim_sensitivity of query head
+    i's rows (every query of every sequence) over KV head i // G's cache and
+    its noise rows, rebuilt here by the row formula."""
+    for nq in (1, 3):
+        w = _workload(nq)
+        c = w.cfg
+        G = c.n_q_heads // c.n_kv_heads
+        rng = np.random.Generator(np.random.PCG64(5))
+        noise = 0.1 * rng.standard_normal((int(c.n_kv_heads * w.lens.sum()), c.head_dim))
+        got = o.dim_sensitivity_all(w, noise, SCALE)
+        assert got.shape == (c.n_q_heads, c.head_dim)
+        q4 = w.q if w.q.ndim == 4 else w.q[:, None]
+        want = np.zeros_like(got)
+        for b in range(c.batch):
+            for i in range(c.n_q_heads):
+                h = i // G
+                K, V = _natural(w, b, h)
+                eps = _rows(w, noise, b, h)
+                want[i] += fa.dim_sensitivity(q4[b, :, i].astype(np.float64), K, V, eps, SCALE)
+        assert np.abs(got - want).max() <= 1e-12 * max(1.0, np.abs(want).max())
+
+
+PINS = [pin_project_blocks, pin_decode_rows, pin_attend_rows, pin_append_blocks, pin_sensitivity_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -323,7 +346,20 @@ def _project_block_period_dropped(w, b, h):
             fa.project(V[start:start + M][:, cd], c.n_coef))
 
 
+_ORIG_SENS_ALL = ob.dim_sensitivity_all
+
+
+def _sens_all_noise_of_other_block(w, noise, scale):
+    return _ORIG_SENS_ALL(w, np.roll(noise, 7, axis=0), scale)
+
+
+def _sens_all_heads_reversed(w, noise, scale):
+    return _ORIG_SENS_ALL(w, noise, scale)[::-1]
+
+
 BATCH_MUTANTS = {
+    "sensitivity_noise_rows_shifted": ("dim_sensitivity_all", _sens_all_noise_of_other_block),
+    "sensitivity_query_heads_reversed": ("dim_sensitivity_all", _sens_all_heads_reversed),
     "append_all_k_v_rows_swapped": ("append_all", _append_all_kv_rows_swapped),
     "append_all_new_rows_of_other_head": ("append_all", _append_all_head_rows_rolled),
     "project_block_period_dropped": ("project_block", _project_block_period_dropped),
