@@ -47,6 +47,12 @@ def algorithmic(c, lens):
     E = c.sink + c.recent
     dec = main = 0
     flops = 0.0
+    if "sensitivity" in c.steps:
+        # dimension analysis: keys and noise of every token, all dims (the
+        # main kernel's stream), queries in and the [Hq, D] result out
+        main = c.n_kv_heads * int(np.sum(lens)) * c.head_dim * 2 * esz
+        dec = main + c.batch * c.n_query * c.n_q_heads * c.head_dim * esz + c.n_q_heads * c.head_dim * 4
+        return dec, main, flops, int(np.sum(lens)) * c.n_kv_heads
     for b in range(c.batch):
         L = int(lens[b])
         M = max(0, L - E)
@@ -190,6 +196,29 @@ def cpu_baseline(w, scale, seconds):
     c = w.cfg
     b = int(np.argmin(w.lens))
     n = positions = 0
+    if "sensitivity" in c.steps:
+        # the dimension analysis of whole (sequence, KV head) blocks: every
+        # query head of the block perturbed dim by dim (fa.dim_sensitivity)
+        from oracle import fourier_attention as fa
+        G = c.n_q_heads // c.n_kv_heads
+        noise = w.value_noise()
+        q4 = w.q if w.q.ndim == 4 else w.q[:, None]
+        t0 = time.perf_counter()
+        while True:
+            h = n % c.n_kv_heads
+            K, V = w.natural_kv(b, h)
+            eps = w.natural_rows(noise, b, h)
+            for i in range(h * G, (h + 1) * G):
+                fa.dim_sensitivity(w.f64(q4[b, :, i]), K, V, eps, scale)
+            n += 1
+            positions += int(w.lens[b])
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": positions / dt, "unit": "KV-positions/s", "cores": threads, "kind": "oracle",
+                "sample": "%d (sequence, KV head) block(s) of sequence %d (L = %d): the oracle's "
+                          "perturb-and-rerun analysis of its %d query heads x %d queries, %.1f s in all"
+                          % (n, b, int(w.lens[b]), G, c.n_query, dt)}
     t0 = time.perf_counter()
     while True:
         h = n % c.n_kv_heads
@@ -228,6 +257,21 @@ class Bench:
         self.scale = 1.0 / np.sqrt(c.head_dim)
         self.dims = torch.from_numpy(w.dims).to(dev)
         self.desc = fb.Desc.from_workload(w, self.dims)
+        self.stream = torch.cuda.current_stream()
+        self.sens = "sensitivity" in self.steps
+        if self.sens:  # dimension analysis: keys and noise in natural dim order
+            base = dict(q=fb.to_device(w.q), k=fb.to_device(w.natural_k_rows()),
+                        noise=fb.to_device(w.value_noise()))
+            per_copy = sum(t.numel() * t.element_size() for t in base.values())
+            self.copies = copies or max(2, int(np.ceil(2 * LLC_BYTES / per_copy)) + 1)
+            self.sets = []
+            for i in range(self.copies):
+                s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
+                s["sq"] = torch.empty((c.n_q_heads, c.head_dim), device=dev)
+                self.sets.append(s)
+            self.ws_p = None
+            self.ws_d = fb.workspace(fb.dim_sensitivity_workspace_size(self.desc, c.n_query))
+            return
         nblk = c.batch * c.n_kv_heads
         E = c.sink + c.recent
         base = dict(kc=fb.to_device(w.kc), vc=fb.to_device(w.vc))
@@ -259,7 +303,6 @@ class Bench:
         if "decode" in self.steps and "project" not in self.steps:
             for s in self.sets:  # decode-only steps: coefficients and edges made once
                 fb.project(self.desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], self.ws_p)
-        self.stream = torch.cuda.current_stream()
 
     def call_project(self, s):
         self.fb.project(self.desc, s["kc"], s["vc"], s["ck"], s["cv"], s["ke"], s["ve"], self.ws_p,
@@ -267,7 +310,10 @@ class Bench:
 
     def call_decode(self, s):
         c, fb = self.c, self.fb
-        if c.n_query > 1:  # several queries per sequence: fa_attend
+        if self.sens:
+            fb.dim_sensitivity(self.desc, c.n_query, s["q"], s["k"], s["noise"], self.scale, s["sq"],
+                               self.ws_d, self.stream)
+        elif c.n_query > 1:  # several queries per sequence: fa_attend
             fb.attend(self.desc, c.n_query, s["q"], s.get("kx"), s.get("vx"), s["ke"], s["ve"],
                       s["ck"], s["cv"], self.scale, s["out"], None, self.ws_d, self.stream)
         else:
@@ -282,7 +328,7 @@ class Bench:
             self.call_project(s)
         if ev is not None:
             ev[1].record(self.stream)
-        if "decode" in self.steps:
+        if "decode" in self.steps or self.sens:
             self.call_decode(s)
         if ev is not None:
             ev[2].record(self.stream)
@@ -311,7 +357,7 @@ class Bench:
         # around it on the same stream (fa_time_main_kernel)
         kern = {}
         for name, fn in (("project", self.call_project), ("decode", self.call_decode)):
-            if name not in self.steps:
+            if name not in self.steps and not (name == "decode" and self.sens):
                 continue
             pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                      for _ in range(steps)]
@@ -403,6 +449,10 @@ def main():
     w = wl.make(wl.CONFIGS[args.workload])
     c = w.cfg
     steps = c.steps
+    sens = "sensitivity" in steps
+    if sens:  # the analysis is the step's one call, in the decode slot
+        steps = ("decode",)
+        args.no_context = True
     dec_bytes, main_bytes, proj_flops, positions = algorithmic(w.cfg, w.lens)
     bn = Bench(torch, fb, w, args.copies)
     ms_step, d_proj, d_dec, kern = bn.run(args.steps, args.warmup)
@@ -435,11 +485,14 @@ def main():
     if "decode" in steps and (t_dec >= t_proj or "project" not in steps):
         tk = float(kern["decode"].mean())
         ach = main_bytes / tk / 1e9
-        roof = {"kernel": "main split kernel of %s" % ("fa_decode" if c.n_query == 1 else "fa_attend"),
+        roof = {"kernel": "main split kernel of %s" % (
+                    "fa_dim_sensitivity (fa_attend with the noise as the values)" if sens
+                    else "fa_decode" if c.n_query == 1 else "fa_attend"),
                 "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS, "launch_us": tk * 1e6,
                 "algorithmic_bytes_per_launch": main_bytes,
-                "algorithmic": "exact dims of the middle rows, K and V: sum_b Hkv * M_b * Du * 2 * 2 B",
+                "algorithmic": ("keys and noise of every token, all dims: Hkv * sum_b L_b * D * 2 * 2 B" if sens
+                                else "exact dims of the middle rows, K and V: sum_b Hkv * M_b * Du * 2 * 2 B"),
                 "traffic": measured_traffic(args.workload, "decode_main"),
                 "call_achieved": dec_bytes / t_dec / 1e9,
                 "call_frac": dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS}
@@ -488,7 +541,9 @@ def main():
         print("bench: CPU baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, 1.0 / np.sqrt(c.head_dim), args.cpu_seconds)
 
-    if len(steps) == 2:
+    if sens:
+        metric = "KV-positions/s (dimension analysis, %d queries per sequence)" % c.n_query
+    elif len(steps) == 2:
         metric = "KV-positions/s (fa_project K,V + fa_decode per step)"
     elif c.n_query == 1:
         metric = "decode KV-positions/s (%s)" % "+".join(steps)

@@ -216,6 +216,37 @@ fa_status_t fa_attend_plan(const fa_desc_t *desc, int32_t n_query, fa_plan_t *pl
 fa_status_t fa_append(const fa_desc_t *desc, const void *k_new, const void *v_new,
                       float *ck, float *cv, void *ke, void *ve, void *stream);
 
+/* Workspace bytes fa_dim_sensitivity needs for `desc` and `n_query`. */
+fa_status_t fa_dim_sensitivity_workspace_size(const fa_desc_t *desc, int32_t n_query, size_t *bytes);
+
+/*
+ * fa_dim_sensitivity: the dimension analysis of the skill page (Step 1;
+ * Architecture overview, dimension analysis stage), over the uncompressed
+ * cache.  Dim d is perturbed by adding noise[row][d] to dim d of the values of
+ * every token; the score of dim d is the change of the attention outputs.
+ * Adding noise to one dim of V changes only that dim of the outputs, by
+ * sum_t p_t noise[t][d] (p the unperturbed probabilities), so
+ *   sq[i][d] = sum over sequences b and queries t of
+ *              ( sum_tau p_{b,t,i}(tau) noise[row(b, i/G, tau)][d] )^2,
+ * the squared change for query head i; the pages' score of dim d is
+ * sqrt(sum_i sq[i][d]) (small: dim d can be compressed).
+ * q     [B, n_query, Hq, D]  queries (natural dim order; [B, Hq, D] for 1);
+ * k     [rows, D]            keys of every token, natural dim order, rows
+ *                            packed as kx (row(b, h, t) = Hkv*off_b + h*L_b + t);
+ * noise [rows, D]            the perturbations (the pages draw N(0, 0.1^2)),
+ *                            same layout and dtype as k;
+ * sq    [Hq, D] float32.
+ * Every query attends to all L_b tokens.  desc.n_comp_dims, n_coef, period,
+ * sink, recent and dims are not used (the analysis precedes the dim split).
+ * The values themselves do not enter.  Runs the decode kernels on all-exact
+ * dims (noise as the values, an identity dims table in the workspace), then a
+ * fixed-order sum of squares.  Errors as fa_attend; sq must not overlap an
+ * input or the workspace (FA_ERR_ALIAS).
+ */
+fa_status_t fa_dim_sensitivity(const fa_desc_t *desc, int32_t n_query, const void *q,
+                               const void *k, const void *noise, float scale, float *sq,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * fa_coef_budget: the number of real coefficients that spans the same space as
  * the first floor(fraction * M) bins of the middle's real FFT, which is how the

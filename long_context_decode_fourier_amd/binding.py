@@ -72,6 +72,11 @@ _SIGS = [
      [ctypes.POINTER(fa_desc_t)] + [ctypes.c_void_p] * 7 + [ctypes.c_float, ctypes.c_void_p,
                                                            ctypes.c_void_p]),
     ("fa_append", ctypes.c_int, [ctypes.POINTER(fa_desc_t)] + [ctypes.c_void_p] * 7),
+    ("fa_dim_sensitivity_workspace_size", ctypes.c_int,
+     [ctypes.POINTER(fa_desc_t), ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+    ("fa_dim_sensitivity", ctypes.c_int,
+     [ctypes.POINTER(fa_desc_t), ctypes.c_int32] + [ctypes.c_void_p] * 3 +
+     [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 ]
 
 
@@ -174,6 +179,22 @@ def append(desc: Desc, k_new, v_new, ck, cv, ke, ve, stream=None):
     (desc describes the lengths before the append); ck, cv, ke, ve in place."""
     _check(lib().fa_append(ctypes.byref(desc.c), _ptr(k_new), _ptr(v_new), _ptr(ck), _ptr(cv),
                            _ptr(ke), _ptr(ve), _stream(stream)))
+
+
+def dim_sensitivity_workspace_size(desc: Desc, n_query: int = 1) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().fa_dim_sensitivity_workspace_size(ctypes.byref(desc.c), int(n_query), ctypes.byref(n)))
+    return n.value
+
+
+def dim_sensitivity(desc: Desc, n_query, q, k, noise, scale, sq, ws=None, stream=None):
+    """fa_dim_sensitivity: squared per-dim output changes sq [Hq, D] fp32 when
+    noise is added to one dim of the values at a time."""
+    if ws is None:
+        ws = _own_workspace(dim_sensitivity_workspace_size(desc, n_query), q.device, stream)
+    _check(lib().fa_dim_sensitivity(ctypes.byref(desc.c), int(n_query), _ptr(q), _ptr(k), _ptr(noise),
+                                    ctypes.c_float(scale), _ptr(sq), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
 
 
 class fa_plan_t(ctypes.Structure):

@@ -220,8 +220,9 @@ __global__ __launch_bounds__(64 * NW) void decode_score_kernel(DecodeArgs a) {
                                                32 * kc + 8 * g4);
       Qreg[kc][mb] = __builtin_bit_cast(bf16x8, bits);
     }
-  // ---- this wave's coefficient units and its slice of A (fp16 A operand)
-  const int U = a.kpp / 32;
+  // ---- this wave's coefficient units and its slice of A (fp16 A operand);
+  //      none without compressible dims (the compressed partials are then 0)
+  const int U = a.dc > 0 ? a.kpp / 32 : 0;
   const int u0 = (U * wave) / NW, nu = (U * (wave + 1)) / NW - u0;
   half8 Areg[MAXU][MB];
 #pragma unroll
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(64 * NW) void decode_score_kernel(DecodeArgs a) {
       pbh[o] = hb;
       pbl[o] = bf16_rne(p - __uint_as_float(static_cast<uint32_t>(hb) << 16));
       if (s_tt == 0) corr[s_row] = c;
-      if (s_row < rows) {
+      if (s_row < rows && a.dc > 0) {  // pass 2's input (no pass 2 without compressible dims)
         const int off = tile0 - t_begin;
         p_out[off] = static_cast<_Float16>(p);
         if (s_tt == 0) m_out[off / T] = m_run;
@@ -885,7 +886,7 @@ hipError_t launch_decode_score(const DecodeArgs& a, int nitems, hipStream_t s) {
   if (nitems == 0) return hipSuccess;
   const int nheads = a.rows >= a.G ? a.rows / a.G : 1;
   const int nunit = nheads * ((std::min(a.rows, a.G) + 15) / 16);
-  const ScoreVariant* v = decode_score_pick(a.kpp, a.mb, nheads, nunit, a.du);
+  const ScoreVariant* v = decode_score_pick(a.dc > 0 ? a.kpp : 0, a.mb, nheads, nunit, a.du);
   if (!v) return hipErrorInvalidValue;
   const size_t smem = decode_score_smem(a.mb, nheads, a.du);
   switch (v - kScoreVariants) {

@@ -260,7 +260,7 @@ bool mfma_rows_ok(const Shape& sh, int rows, int kpp) {
 }
 
 // Row grouping of the two-pass path: `rows` consecutive query heads per item
-// (32 or 16), checked against the compiled pass-1 and pass-2 variants.
+// (32, 16, 8 or 4), checked against the compiled pass-1 and pass-2 variants.
 bool two_pass_rows_ok(const Shape& sh, int rows, int kpp) {
   const int G = sh.G;
   if (rows > sh.Hq || sh.Hq % rows) return false;
@@ -316,15 +316,17 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
     for (int b = 0; b < sh.B; ++b) mid_tokens += sh.M[b];
     // two passes for long middles, and for shapes the one-pass kernel does
     // not take (exact dims past 64, k past 2303)
+    bool one_pass_ok = false;
+    for (int r = 32; r >= 1 && !one_pass_ok; --r) one_pass_ok = mfma_rows_ok(sh, r, a.kpp);
+    // without compressible dims pass 1 alone is the whole attention (no P16,
+    // no pass 2): it serves the exact dims the one-pass kernel does not take
     int two_rows = 0;
-    if (sh.Dc > 0 && sh.any_mid && sh.Du % 8 == 0)
-      for (int r : {32, 16, 8})
-        if (two_pass_rows_ok(sh, r, a.kpp)) {
+    if (sh.any_mid && sh.Du % 8 == 0 && (sh.Dc > 0 || !one_pass_ok))
+      for (int r : {32, 16, 8, 4})
+        if (two_pass_rows_ok(sh, r, sh.Dc > 0 ? a.kpp : 0)) {
           two_rows = r;
           break;
         }
-    bool one_pass_ok = false;
-    for (int r = 32; r >= 1 && !one_pass_ok; --r) one_pass_ok = mfma_rows_ok(sh, r, a.kpp);
     // P16 is written and read once (2 + 2 bytes per query row and token);
     // past an eighth of the cache bytes per token (prefill chunks, several
     // queries per step) the extra traffic outweighs the saving
@@ -426,7 +428,7 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
   p->off_mrg = p->off_part + align_up(static_cast<size_t>(prow) * a.RS * sizeof(float));
   p->ws_bytes = p->off_mrg + align_up(static_cast<size_t>(sh.B) * sh.Hq * a.MS * sizeof(float));
   p->off_P16 = p->off_msub = p->off_Wp = 0;
-  if (a.two_pass) {
+  if (a.two_pass && a.dc > 0) {
     // pass-2 plan: split groups of kMomentWaves pass-1 splits per sequence,
     // frequency slices chosen to fill the CUs (two blocks each) in whole rounds
     int64_t pc = 0;
@@ -750,7 +752,7 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
     a.Q16 = static_cast<char*>(workspace) + pp.off_q16;
     a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_part);
     a.mrg = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_mrg);
-    if (a.two_pass) {
+    if (a.two_pass && a.dc > 0) {
       a.P16 = static_cast<char*>(workspace) + pp.off_P16;
       a.msub = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_msub);
       a.Wp = reinterpret_cast<float*>(static_cast<char*>(workspace) + pp.off_Wp);
@@ -768,7 +770,7 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
     if (e != hipSuccess) return hip_fail(e, "decode split kernel");
     if (timed && g_ev_after && (e = hipEventRecord(g_ev_after, s)) != hipSuccess)
       return hip_fail(e, "event record");
-    if (a.two_pass && (e = fa::launch_decode_moment(a, s)) != hipSuccess)
+    if (a.two_pass && a.dc > 0 && (e = fa::launch_decode_moment(a, s)) != hipSuccess)
       return hip_fail(e, "decode moment kernel");
     e = fa::launch_decode_merge(a, s);
     if (e != hipSuccess) return hip_fail(e, "decode merge kernel");
@@ -841,6 +843,78 @@ fa_status_t fa_append(const fa_desc_t* desc, const void* k_new, const void* v_ne
   for (int b = 0; b < sh.B; ++b) a.len[b] = sh.L[b];
   const hipError_t e = fa::launch_append(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append kernels");
+  return FA_OK;
+}
+
+// Dimension analysis: the uncompressed cache as an all-exact descriptor, and
+// the workspace layout [dims int32 Hkv*D | responses fp32 B*nq*Hq*D | attend].
+struct SensLayout {
+  fa_desc_t inner;
+  size_t off_resp, off_att, att_bytes, total;
+};
+
+fa_status_t sens_layout(const fa_desc_t* desc, int32_t n_query, SensLayout* l) {
+  if (!desc) return fail(FA_ERR_NULL, "desc is NULL");
+  l->inner = *desc;
+  l->inner.n_comp_dims = 0;  // every dim exact: the analysis precedes the dim split
+  l->inner.n_coef = 1;
+  l->inner.period = 0;
+  l->inner.dims = nullptr;
+  Shape sh;
+  fa_status_t st = validate(&l->inner, &sh);
+  if (st != FA_OK) return st;
+  if ((st = apply_queries(n_query, &sh)) != FA_OK) return st;
+  if ((st = fa_attend_workspace_size(&l->inner, n_query, &l->att_bytes)) != FA_OK) return st;
+  l->off_resp = align_up(static_cast<size_t>(sh.Hkv) * sh.D * sizeof(int32_t));
+  l->off_att = l->off_resp + align_up(static_cast<size_t>(sh.B) * sh.Hq * sh.D * sizeof(float));
+  l->total = l->off_att + l->att_bytes;
+  return FA_OK;
+}
+
+fa_status_t fa_dim_sensitivity_workspace_size(const fa_desc_t* desc, int32_t n_query, size_t* bytes) {
+  if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
+  SensLayout l;
+  const fa_status_t st = sens_layout(desc, n_query, &l);
+  if (st != FA_OK) return st;
+  *bytes = l.total;
+  return FA_OK;
+}
+
+fa_status_t fa_dim_sensitivity(const fa_desc_t* desc, int32_t n_query, const void* q, const void* k,
+                               const void* noise, float scale, float* sq, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  SensLayout l;
+  fa_status_t st = sens_layout(desc, n_query, &l);
+  if (st != FA_OK) return st;
+  if (!q || !k || !noise || !sq) return fail(FA_ERR_NULL, "q, k, noise and sq are required");
+  if (!(scale == scale)) return fail(FA_ERR_SHAPE, "scale is NaN");
+  if (!workspace || workspace_bytes < l.total)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", l.total,
+                workspace ? workspace_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(FA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  Shape sh;
+  validate(&l.inner, &sh);
+  apply_queries(n_query, &sh);
+  const size_t esz = elem_bytes(sh.dtype);
+  const size_t sq_bytes = static_cast<size_t>(sh.Hq / sh.nq) * sh.D * sizeof(float);
+  const void* ins[4] = {q, k, noise, workspace};
+  const size_t isz[4] = {static_cast<size_t>(sh.B) * sh.Hq * sh.D * esz,
+                         static_cast<size_t>(sh.Hkv) * sh.total_len * sh.D * esz,
+                         static_cast<size_t>(sh.Hkv) * sh.total_len * sh.D * esz, l.total};
+  for (int i = 0; i < 4; ++i)
+    if (overlap(sq, sq_bytes, ins[i], isz[i])) return fail(FA_ERR_ALIAS, "sq overlaps an input or the workspace");
+  char* ws = static_cast<char*>(workspace);
+  l.inner.dims = reinterpret_cast<const int32_t*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fa::launch_iota_dims(reinterpret_cast<int32_t*>(ws), sh.Hkv, sh.D, s);
+  if (e != hipSuccess) return hip_fail(e, "dims table kernel");
+  float* resp = reinterpret_cast<float*>(ws + l.off_resp);
+  st = fa_attend(&l.inner, n_query, q, k, noise, nullptr, nullptr, nullptr, nullptr, scale, resp, nullptr,
+                 ws + l.off_att, l.att_bytes, stream);
+  if (st != FA_OK) return st;
+  e = fa::launch_sens_norm(resp, sq, sh.B, sh.nq, sh.Hq / sh.nq, sh.D, s);
+  if (e != hipSuccess) return hip_fail(e, "sensitivity norm kernel");
   return FA_OK;
 }
 

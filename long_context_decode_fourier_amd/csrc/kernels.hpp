@@ -56,6 +56,11 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
+// ---------------------------------------------------- dimension analysis --
+// Identity dims table [hkv][D], and sq[i][d] = sum_{b,t} resp[b][t][i][d]^2.
+hipError_t launch_iota_dims(int32_t* dims, int hkv, int D, hipStream_t s);
+hipError_t launch_sens_norm(const float* resp, float* sq, int B, int nq, int hq, int D, hipStream_t s);
+
 // ---------------------------------------------------------------- decode --
 constexpr int kDecRows = 4;    // query rows per work item (VALU path)
 constexpr int kDecTile = 64;   // tokens per tile (VALU path)

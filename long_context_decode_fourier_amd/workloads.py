@@ -125,6 +125,12 @@ CONFIGS = {
         note="the LLaMA-3-8B-shaped GQA cache (same draws) with a 64-token "
              "prefill chunk per sequence attending to it (256 query rows per KV "
              "head, run as passes over the cache)"),
+    "llama2_7b_dim_analysis": Config(
+        name="llama2_7b_dim_analysis", dtype="bf16", batch=1, n_q_heads=32,
+        n_kv_heads=32, head_dim=128, n_comp=64, n_coef=401, seq_len=4096, seed=2,
+        steps=("sensitivity",), n_query=16,
+        note="dimension analysis of the LLaMA-2-7B-shaped layer's cache: 16 queries, "
+             "noise N(0, 0.1^2) on one value dim at a time, L=4096"),
     "ragged_batch": Config(
         name="ragged_batch", dtype="bf16", batch=16, n_q_heads=32,
         n_kv_heads=8, head_dim=128, n_comp=64, n_coef=2049,
@@ -318,7 +324,7 @@ def make(cfg: Config, lens=None) -> Workload:
         exact = np.setdiff1d(np.arange(D), comp)
         dims[h] = np.concatenate([exact, comp])
 
-    need_exact = "decode" in cfg.steps
+    need_exact = "decode" in cfg.steps or "sensitivity" in cfg.steps
     rows = int(Hkv * lens.sum())
     sd = np.uint16 if cfg.dtype == "bf16" else np.float32
     kc = np.empty((rows, Dc), dtype=sd)

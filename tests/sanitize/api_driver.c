@@ -99,6 +99,15 @@ int main(void) {
   bad.period = 4000; /* one more middle token would not fit */
   EXPECT(fa_append(&bad, P(1), P(2), (float*)P(3), (float*)P(4), P(5), P(6), NULL), FA_ERR_SHAPE);
 
+  /* dimension analysis: workspace query and host errors (no launch) */
+  EXPECT(fa_dim_sensitivity_workspace_size(&d, 4, &n), FA_OK);
+  EXPECT(fa_dim_sensitivity_workspace_size(&d, 0, &n), FA_ERR_SHAPE);
+  EXPECT(fa_dim_sensitivity(&d, 4, NULL, P(2), P(3), 0.1f, (float*)P(4), P(5), (size_t)1 << 40, NULL),
+         FA_ERR_NULL);
+  EXPECT(fa_dim_sensitivity(&d, 4, P(1), P(2), P(3), 0.1f, (float*)P(4), P(5), 64, NULL), FA_ERR_WORKSPACE);
+  EXPECT(fa_dim_sensitivity(&d, 4, P(1), P(2), P(3), 0.1f, (float*)P(2), P(5), (size_t)1 << 40, NULL),
+         FA_ERR_ALIAS);
+
   EXPECT(fa_coef_budget(4000, 0.3), 2399);
   EXPECT(fa_coef_budget(3, 0.3), 1);
   EXPECT(fa_coef_budget(0, 0.3), 0);

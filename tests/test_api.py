@@ -258,3 +258,23 @@ def test_append_host_errors_without_gpu():
     assert _call_append(d, ke=3) == 6                     # ke overlaps ck
     # no compressible dims: nothing to do, every pointer may be NULL
     assert _call_append(_desc(period=4500, n_comp_dims=0), 0, 0, 0, 0, 0, 0) == 0
+
+
+def test_dim_sensitivity_host_errors_without_gpu():
+    d = _desc(n_coef=5000, period=0)  # k and the dim split are ignored by the analysis
+    n = ctypes.c_size_t(0)
+    assert fb.lib().fa_dim_sensitivity_workspace_size(ctypes.byref(d.c), 4, ctypes.byref(n)) == 0, \
+        fb.lib().fa_last_error()
+    assert n.value > 0 and n.value % 256 == 0
+    assert fb.lib().fa_dim_sensitivity_workspace_size(ctypes.byref(d.c), 0, ctypes.byref(n)) == 2
+    P = lambda v: ctypes.c_void_p(v * GB if 0 < v < 64 else v)
+    f = fb.lib().fa_dim_sensitivity
+    args = lambda q=1, k=2, nz=3, sq=4, ws=5, nws=1 << 40: (ctypes.byref(d.c), 4, P(q), P(k), P(nz),
+                                                            ctypes.c_float(0.1), P(sq), P(ws), nws, None)
+    assert f(*args(q=0)) == 1
+    assert f(*args(nz=0)) == 1
+    assert f(*args(sq=0)) == 1
+    assert f(*args(ws=0)) == 4
+    assert f(*args(nws=64)) == 4
+    assert f(*args(sq=2)) == 6  # sq inside k
+    assert f(*args(sq=5)) == 6  # sq inside the workspace

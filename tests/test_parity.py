@@ -241,6 +241,13 @@ TWO_PASS = {
     # (30% of M = 4000 bins: k = 2399), past the one-pass kernel's k
     "tp_llama2_7b_budget": (dict(dtype="bf16", batch=1, n_q_heads=32, n_kv_heads=32, head_dim=128,
                                  n_comp=64, n_coef=2399), [4096], 0, (8, "two_pass")),
+    # 4 stacked rows (a 4-head layer) with k past the one-pass limit
+    "tp_rows4_k2401": (dict(dtype="bf16", batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                            n_comp=64, n_coef=2401), [9000], 0, (4, "two_pass")),
+    # no compressible dims and 128 exact dims: pass 1 alone is the whole
+    # attention (no probabilities stored, no pass 2)
+    "tp_dc0_d128": (dict(dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                         n_comp=0, n_coef=1), [3000, 200], 0, (8, "two_pass")),
     "tp_moving_reference": (dict(dtype="bf16", batch=4, n_q_heads=32, n_kv_heads=8, head_dim=128,
                                  n_comp=64, n_coef=129), [70000, 68000, 66000, 64000], 600,
                             (32, "two_pass")),
