@@ -50,6 +50,14 @@
  * FA_ERR_HIP.  fa_last_error() gives a text for the last failure on the calling
  * thread.  Device arrays are not read by the host: entries of `dims` outside
  * [0, D) are skipped by the kernels (no fault) and give unspecified results.
+ *
+ * Check mode.  With the environment variable FA_CHECK=1 (read at every call),
+ * fa_project (bf16) first scans kc / vc for values its fp16 operands cannot
+ * hold (magnitude >= 65536, inf, NaN) and fa_decode / fa_attend scan
+ * desc.dims for entries outside [0, D); the call then synchronises its stream,
+ * reads the result and returns FA_ERR_SHAPE (with a text) before any other
+ * kernel runs.  The workspace queries add one 256-byte slot for the flag in
+ * this mode.  It is the one mode in which a call copies to the host and waits.
  */
 #ifndef FA_H
 #define FA_H
@@ -107,7 +115,8 @@ fa_status_t fa_project_workspace_size(const fa_desc_t *desc, size_t *bytes);
  * Step 3).  Either matrix may be skipped: pass kc = ck = ke = NULL (or the V
  * trio).  With n_comp_dims = 0 the call does nothing and every pointer may be
  * NULL.  The 16-bit path needs n_comp_dims % 4 == 0 and 8-byte aligned kc/vc;
- * it computes in fp16 operands, so |kc|, |vc| must stay below 65504.
+ * it computes in fp16 operands, so |kc|, |vc| must stay below 65504 (FA_CHECK=1
+ * rejects larger values, see Check mode above).
  * desc.dims is not used.
  */
 fa_status_t fa_project(const fa_desc_t *desc, const void *kc, const void *vc,

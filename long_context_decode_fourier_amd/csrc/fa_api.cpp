@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -45,6 +46,28 @@ fa_status_t hip_fail(hipError_t e, const char* what) {
 }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// FA_CHECK=1 (environment, read per call): validating scans run before a
+// call's kernels and the call waits for their flag, the one case in which the
+// library synchronises and copies to the host.  The flag takes one aligned
+// slot at the end of the workspace.
+constexpr size_t kCheckBytes = kAlign;
+bool check_mode() {
+  const char* v = std::getenv("FA_CHECK");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+fa_status_t check_read(int32_t* flag, hipStream_t s, const char* what) {
+  int32_t h = 0;
+  hipError_t e = hipMemcpyAsync(&h, flag, sizeof h, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "FA_CHECK read-back");
+  if (h & 1)
+    return fail(FA_ERR_SHAPE, "FA_CHECK: %s holds a value of magnitude >= 65536, inf or NaN (the bf16 "
+                              "projection's fp16 operands end at 65504)", what);
+  if (h & 2) return fail(FA_ERR_SHAPE, "FA_CHECK: desc.dims has an entry outside [0, head_dim)");
+  return FA_OK;
+}
 
 struct Shape {
   int dtype, B, Hq, Hkv, G, D, Dc, Du, S, R, k;
@@ -479,6 +502,7 @@ size_t elem_bytes(int dtype) { return dtype == FA_BF16 ? 2 : 4; }
 // fit the prep kernel's LDS on the same kernel path as a single query, so a
 // prefill chunk larger than that reads the cache once per pass.
 struct AttendPlan {
+  size_t flag_off;  // FA_CHECK flag slot (check mode only)
   int n_query, chunk;
   DecPlan full, last;  // plans of a full pass and of the last pass
   size_t ws_bytes;
@@ -518,6 +542,11 @@ fa_status_t plan_attend(const Shape& base, int32_t n_query, AttendPlan* ap) {
   ap->last = ap->full;
   if (rest && (st = plan_queries(base, rest, &ap->last)) != FA_OK) return st;
   ap->ws_bytes = std::max(ap->full.ws_bytes, ap->last.ws_bytes);
+  ap->flag_off = 0;
+  if (check_mode()) {
+    ap->flag_off = align_up(ap->ws_bytes);
+    ap->ws_bytes = ap->flag_off + kCheckBytes;
+  }
   return FA_OK;
 }
 
@@ -543,6 +572,7 @@ fa_status_t fa_project_workspace_size(const fa_desc_t* desc, size_t* bytes) {
     if (st != FA_OK) return st;
     need = std::max(need, p.ws_bytes);
   }
+  if (check_mode() && sh.dtype == FA_BF16 && sh.Dc > 0) need = align_up(need) + kCheckBytes;
   *bytes = need;
   return FA_OK;
 }
@@ -574,6 +604,12 @@ fa_status_t fa_project(const fa_desc_t* desc, const void* kc, const void* vc, fl
   ProjPlan p;
   st = plan_project(sh, nmat, &p);
   if (st != FA_OK) return st;
+  const bool chk = check_mode() && sh.dtype == FA_BF16;
+  size_t flag_off = 0;
+  if (chk) {
+    flag_off = align_up(p.ws_bytes);
+    p.ws_bytes = flag_off + kCheckBytes;
+  }
   fa::ProjArgs& a = p.args;
   int m = 0;
   if (kc) { a.x[m] = kc; a.out[m] = ck; ++m; }
@@ -609,6 +645,14 @@ fa_status_t fa_project(const fa_desc_t* desc, const void* kc, const void* vc, fl
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (chk) {
+    int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + flag_off);
+    const int64_t n = static_cast<int64_t>(sh.Hkv) * sh.total_len * sh.Dc;
+    if ((e = fa::launch_check_clear(flag, s)) != hipSuccess) return hip_fail(e, "FA_CHECK kernel");
+    for (int i = 0; i < nmat; ++i)
+      if ((e = fa::launch_check_bf16_range(a.x[i], n, flag, s)) != hipSuccess) return hip_fail(e, "FA_CHECK kernel");
+    if ((st = check_read(flag, s, "kc or vc")) != FA_OK) return st;
+  }
   bool edges_done = false;
   if (sh.Dc > 0) {
     if (p.f16) {
@@ -731,6 +775,13 @@ fa_status_t fa_attend(const fa_desc_t* desc, int32_t n_query, const void* q, con
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (check_mode()) {
+    int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + ap.flag_off);
+    hipError_t e = fa::launch_check_clear(flag, s);
+    if (e == hipSuccess) e = fa::launch_check_dims(desc->dims, sh.Hkv * sh.D, sh.D, flag, s);
+    if (e != hipSuccess) return hip_fail(e, "FA_CHECK kernel");
+    if ((st = check_read(flag, s, "")) != FA_OK) return st;
+  }
   for (int t0 = 0; t0 < n_query; t0 += ap.chunk) {
     const DecPlan& pp = (n_query - t0 >= ap.chunk) ? ap.full : ap.last;
     fa::DecodeArgs a = pp.args;

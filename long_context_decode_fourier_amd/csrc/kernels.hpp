@@ -56,6 +56,13 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
+// ------------------------------------------------------- FA_CHECK mode --
+// A flag word in device memory: cleared, then or-ed by the scans (1: a bf16
+// cache value of magnitude >= 65536, inf or NaN; 2: a dims entry outside [0, D)).
+hipError_t launch_check_clear(int32_t* flag, hipStream_t s);
+hipError_t launch_check_bf16_range(const void* x, int64_t n, int32_t* flag, hipStream_t s);
+hipError_t launch_check_dims(const int32_t* dims, int n, int D, int32_t* flag, hipStream_t s);
+
 // ---------------------------------------------------- dimension analysis --
 // Identity dims table [hkv][D], and sq[i][d] = sum_{b,t} resp[b][t][i][d]^2.
 hipError_t launch_iota_dims(int32_t* dims, int hkv, int D, hipStream_t s);

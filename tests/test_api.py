@@ -278,3 +278,17 @@ def test_dim_sensitivity_host_errors_without_gpu():
     assert f(*args(nws=64)) == 4
     assert f(*args(sq=2)) == 6  # sq inside k
     assert f(*args(sq=5)) == 6  # sq inside the workspace
+
+
+def test_check_mode_adds_a_flag_slot(monkeypatch):
+    d = _desc()
+    st, n0 = _size(fb.lib().fa_decode_workspace_size, d)
+    st2, p0 = _size(fb.lib().fa_project_workspace_size, d)
+    assert st == 0 and st2 == 0
+    monkeypatch.setenv("FA_CHECK", "1")
+    st, n1 = _size(fb.lib().fa_decode_workspace_size, d)
+    st2, p1 = _size(fb.lib().fa_project_workspace_size, d)
+    assert st == 0 and st2 == 0
+    assert n1 == (n0 + 255) // 256 * 256 + 256 and p1 == (p0 + 255) // 256 * 256 + 256
+    monkeypatch.setenv("FA_CHECK", "0")
+    assert _size(fb.lib().fa_decode_workspace_size, d)[1] == n0
