@@ -1206,37 +1206,43 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   }
 }
 
-// Pass 2 body: one block per (sequence, KV head, 8-column slice of the
-// compressible dims) computes O_C[g][c] = sum_n (alpha W)[g][n] cv[n][c] for
-// the head's query rows, kMergeRows rows at a time.  Thread (column quad cq,
-// n-lane nl) reads 4 consecutive columns of the cv rows n = nl + 128 j and
-// the matching (alpha W)[g][n], up to kCvBatch rows of both in flight; the
-// 128 n-lanes are summed in a fixed order (16-lane partial sums, then the 8
-// partials).
-constexpr int kCvCols = 8;
-constexpr int kCvLanes = 128;
+// Pass 2 body: one block per (sequence, KV head, slice of 4 QPB compressible
+// dims) computes O_C[g][c] = sum_n (alpha W)[g][n] cv[n][c] for the head's
+// query rows, kMergeRows rows at a time.  Thread (column quad cq, n-lane nl)
+// reads 4 consecutive columns of the cv rows n = nl + NL j (NL = 256 / QPB
+// n-lanes) and the matching (alpha W)[g][n], up to kCvBatch rows of both in
+// flight; the NL n-lanes are summed in a fixed order (partial sums over
+// groups of lanes, then the partials).  Wide slices (QPB 8: 32 columns, a
+// 128-byte run of every cv row per block) read each head's alpha W twice
+// instead of eight times; narrow ones (QPB 2) make more blocks for batches of
+// few heads.
 constexpr int kCvBatch = 16;
-constexpr int kCvQ = kMergeRows * kCvCols;  // (row, column) pairs of a pass
+constexpr int kCvWideHeads = 128;  // (sequence, KV head) pairs from which slices are 32 columns wide
 
-template <bool VEC>
+template <bool VEC, int QPB>
 __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
+  constexpr int kCols = 4 * QPB;              // columns of a block
+  constexpr int kLanes = 256 / QPB;           // n-lanes
+  constexpr int kQ = kMergeRows * kCols;      // (row, column) pairs of a pass
+  constexpr int kParts = 256 / kQ;            // partial sums of the lane reduction
+  static_assert(kParts >= 1 && kLanes % kParts == 0, "lane groups tile the n-lanes");
   extern __shared__ float smem[];
   const int b = blockIdx.x / a.hkv, h = blockIdx.x % a.hkv;
   const int M = a.seq.mid[b];
   const bool has_mid = a.dc > 0 && M > 0;
-  float* red = smem;                         // [kCvLanes][kCvQ]
-  float* red2 = red + kCvLanes * kCvQ;       // [8][kCvQ]
+  float* red = smem;                         // [kLanes][kQ]
+  float* red2 = red + kLanes * kQ;           // [kParts][kQ]
   const int tid = threadIdx.x;
-  const int cq = tid & 1, nl = tid >> 1;
-  const int c = blockIdx.y * kCvCols + 4 * cq;
+  const int cq = tid % QPB, nl = tid / QPB;
+  const int c = blockIdx.y * kCols + 4 * cq;
   const float* cvb = a.cv + (static_cast<int64_t>(b) * a.hkv + h) * a.k * a.dc;
   for (int g0 = 0; g0 < a.G; g0 += kMergeRows) {
     const int ng = min(kMergeRows, a.G - g0);
     const float* wrow = a.mrg + (static_cast<int64_t>(b) * a.hq + h * a.G + g0) * a.MS + a.dc;
     // the epilogue's operands (merged o_E entry, 1/l, output column) are
     // loaded with the pass's first round of loads (clamped, unconditional)
-    const int eg = min(tid / kCvCols, ng - 1);
-    const int ecc = min(blockIdx.y * kCvCols + tid % kCvCols, a.dc - 1);
+    const int eg = min(tid / kCols, ng - 1);
+    const int ecc = min(blockIdx.y * kCols + tid % kCols, a.dc - 1);
     const float* erow = a.mrg + (static_cast<int64_t>(b) * a.hq + h * a.G + g0 + eg) * a.MS;
     const float e_oe = erow[ecc];
     const float e_linv = erow[a.dc + a.kpad];
@@ -1246,7 +1252,7 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < kMergeRows; ++g) acc[g][0] = acc[g][1] = acc[g][2] = acc[g][3] = 0.0f;
     if (has_mid && c < a.dc) {
-      for (int n0 = nl; n0 < a.k; n0 += kCvLanes * kCvBatch) {
+      for (int n0 = nl; n0 < a.k; n0 += kLanes * kCvBatch) {
         float4 x[kCvBatch];
         float wv[kCvBatch][kMergeRows];
 #pragma unroll
@@ -1254,7 +1260,7 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
           // rows past k (and row slots past ng) read a valid entry (clamped
           // index) and are weighted by 0 below: a multiply, not a select, so
           // that the compiler keeps the load unconditional and its wait counted
-          const int n = n0 + kCvLanes * j;
+          const int n = n0 + kLanes * j;
           const int nc = min(n, a.k - 1);
 #pragma unroll
           for (int g = 0; g < kMergeRows; ++g) wv[j][g] = wrow[static_cast<int64_t>(min(g, ng - 1)) * a.MS + nc];
@@ -1278,7 +1284,7 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < kCvBatch; ++j) {
-          const int n = n0 + kCvLanes * j;
+          const int n = n0 + kLanes * j;
 #pragma unroll
           for (int g = 0; g < kMergeRows; ++g) {
             const float w = wv[j][g] * ((n < a.k && g < ng) ? 1.0f : 0.0f);
@@ -1293,21 +1299,21 @@ __global__ __launch_bounds__(256) void decode_merge_cv_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < kMergeRows; ++g)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[nl * kCvQ + g * kCvCols + 4 * cq + e] = acc[g][e];
+      for (int e = 0; e < 4; ++e) red[nl * kQ + g * kCols + 4 * cq + e] = acc[g][e];
     __syncthreads();
-    {  // 8 partial sums of 16 n-lanes each: thread (part, pair)
-      const int q = tid % kCvQ, part = tid / kCvQ;
+    {  // kParts partial sums of kLanes / kParts n-lanes each: thread (part, pair)
+      const int q = tid % kQ, part = tid / kQ;
       float sum = 0.0f;
-      for (int l = 0; l < kCvLanes / 8; ++l) sum += red[(part * (kCvLanes / 8) + l) * kCvQ + q];
-      red2[part * kCvQ + q] = sum;
+      for (int l = 0; l < kLanes / kParts; ++l) sum += red[(part * (kLanes / kParts) + l) * kQ + q];
+      red2[part * kQ + q] = sum;
     }
     __syncthreads();
-    if (tid < ng * kCvCols) {
-      const int g = tid / kCvCols, col = tid % kCvCols;
-      const int cc = blockIdx.y * kCvCols + col;
+    if (tid < ng * kCols) {
+      const int g = tid / kCols, col = tid % kCols;
+      const int cc = blockIdx.y * kCols + col;
       if (cc < a.dc) {
         float sum = 0.0f;
-        for (int part = 0; part < 8; ++part) sum += red2[part * kCvQ + tid];
+        for (int part = 0; part < kParts; ++part) sum += red2[part * kQ + tid];
         const int64_t row = q_row(a, b, h * a.G + g0 + g);
         if (e_dd >= 0 && e_dd < a.D) a.out[row * a.D + e_dd] = (sum + e_oe) * e_linv;
       }
@@ -1346,7 +1352,10 @@ size_t decode_split_smem(const DecodeArgs& a) {
 }
 size_t decode_merge_cv_smem(const DecodeArgs& a) {
   (void)a;
-  return sizeof(float) * (kCvLanes * kCvQ + 8 * kCvQ);
+  // the larger of the two slice widths: [lanes][pairs] + [parts][pairs]
+  constexpr size_t narrow = 128 * (kMergeRows * 8) + 8 * (kMergeRows * 8);
+  constexpr size_t wide = 32 * (kMergeRows * 32) + 2 * (kMergeRows * 32);
+  return sizeof(float) * (narrow > wide ? narrow : wide);
 }
 
 hipError_t launch_decode_prep(const DecodeArgs& a, hipStream_t s) {
@@ -1405,15 +1414,22 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dc == 0) return hipSuccess;
   const size_t sm = decode_merge_cv_smem(a);
-  const dim3 grid(a.nseq * a.hkv, (a.dc + kCvCols - 1) / kCvCols);
   const bool vec = a.dc % 4 == 0 && (reinterpret_cast<uintptr_t>(a.cv) & 15) == 0;
+  // 32-column slices once the (sequence, KV head) pairs alone fill half the
+  // chip; 8-column slices below that
+  const bool wide = a.nseq * a.hkv >= kCvWideHeads;
+  const dim3 grid(a.nseq * a.hkv, (a.dc + (wide ? 31 : 7)) / (wide ? 32 : 8));
+#define FA_MERGE_CV(V, Q)                                                                 \
+  do {                                                                                    \
+    if ((e = allow_lds(decode_merge_cv_kernel<V, Q>, sm)) != hipSuccess) return e;       \
+    hipLaunchKernelGGL((decode_merge_cv_kernel<V, Q>), grid, dim3(256), sm, s, a);       \
+  } while (0)
   if (vec) {
-    if ((e = allow_lds(decode_merge_cv_kernel<true>, sm)) != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_cv_kernel<true>, grid, dim3(256), sm, s, a);
+    if (wide) FA_MERGE_CV(true, 8); else FA_MERGE_CV(true, 2);
   } else {
-    if ((e = allow_lds(decode_merge_cv_kernel<false>, sm)) != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_cv_kernel<false>, grid, dim3(256), sm, s, a);
+    if (wide) FA_MERGE_CV(false, 8); else FA_MERGE_CV(false, 2);
   }
+#undef FA_MERGE_CV
   return hipGetLastError();
 }
 

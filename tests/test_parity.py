@@ -192,6 +192,10 @@ SMALL = {
     # exact dims that are not a multiple of 8
     "bf16_m1_dc4": (dict(dtype="bf16", batch=2, n_q_heads=6, n_kv_heads=3, head_dim=16,
                          n_comp=4, n_coef=1), [97, 2000]),
+    # 128 (sequence, KV head) pairs: the merge's 32-column slices, with a
+    # compressible width (40) that leaves the second slice mostly empty
+    "bf16_many_heads_merge": (dict(dtype="bf16", batch=4, n_q_heads=64, n_kv_heads=32, head_dim=64,
+                                   n_comp=40, n_coef=37), [300, 200, 96, 250]),
     # 32 query heads on one KV head: an item's 32 rows are one head's, across
     # both 16-row blocks (long enough that the planner picks 32-row items)
     "bf16_g32_one_kv_head": (dict(dtype="bf16", batch=2, n_q_heads=32, n_kv_heads=1, head_dim=128,
