@@ -1094,6 +1094,27 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   const int nvec = a.du + a.dc + (has_mid ? a.k : 0);
   const int idx = blockIdx.y * 256 + threadIdx.x;
   if (blockIdx.y * 256 >= nvec) return;  // uniform per block
+  if (a.two_pass && blockIdx.y * 256 >= a.du + a.dc) {
+    // a block of W entries only: pass 2 has already scaled each split group's
+    // W to the row's maximum, so it needs no split weights: the groups'
+    // entries are summed in order, eight loads in flight (clamped indices,
+    // groups past the last add 0)
+    if (idx >= nvec) return;
+    const int n = idx - a.du - a.dc;
+    const int nsg = (ns - a.edge_split + kMomentWaves - 1) / kMomentWaves;
+    const float* wp = a.Wp + (static_cast<int64_t>(a.sgcum[b]) * a.hq + i) * a.kpad + n;
+    const int64_t sgs = static_cast<int64_t>(a.hq) * a.kpad;
+    float v = 0.0f;
+    for (int sg0 = 0; sg0 < nsg; sg0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = wp[static_cast<int64_t>(min(sg0 + j, nsg - 1)) * sgs];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += (sg0 + j < nsg) ? x[j] : 0.0f;
+    }
+    a.mrg[static_cast<int64_t>(row) * a.MS + a.dc + n] = v * basis_alpha(n, per);
+    return;
+  }
   const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS;
   // The entry this thread sums (threads past nvec load the last one and
   // store nothing) and the splits that hold it: with edge splits (the last
@@ -1164,7 +1185,13 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
     const float* wp = a.Wp + (static_cast<int64_t>(a.sgcum[b]) * a.hq + i) * a.kpad + n;
     const int64_t sgs = static_cast<int64_t>(a.hq) * a.kpad;
     float v = 0.0f;
-    for (int sg = 0; sg < nsg; ++sg) v += wp[sg * sgs];
+    for (int sg0 = 0; sg0 < nsg; sg0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = wp[static_cast<int64_t>(min(sg0 + j, nsg - 1)) * sgs];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += (sg0 + j < nsg) ? x[j] : 0.0f;
+    }
     mrow[a.dc + n] = v * basis_alpha(n, per);
     return;
   }
