@@ -28,11 +28,24 @@ def fb():
     return binding
 
 
-@pytest.mark.parametrize("name", ["llama2_7b_layer", "llama3_8b_gqa", "fp32_head"])
+# a two-pass shape (k past the one-pass limit): pass 1, pass 2 and the merges
+# under one graph
+GRAPH_CUSTOM = {
+    "two_pass_k2401": (dict(dtype="bf16", batch=2, n_q_heads=16, n_kv_heads=4, head_dim=128, n_comp=64,
+                            n_coef=2401, seed=61), [9000, 5000]),
+}
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_layer", "llama3_8b_gqa", "fp32_head", "two_pass_k2401"])
 def test_graph_replays_match_eager(fb, name):
     print("graph replay", name, flush=True)
     sys.stdout.flush()
-    w = wl.make(wl.CONFIGS[name])
+    if name in GRAPH_CUSTOM:
+        kw, lens = GRAPH_CUSTOM[name]
+        w = wl.make(wl.custom(name=name, **kw), lens=lens)
+        assert fb.attend_plan(fb.Desc.from_workload(w))["path"] == "two_pass"
+    else:
+        w = wl.make(wl.CONFIGS[name])
     c = w.cfg
     dims = torch.from_numpy(w.dims).cuda()
     desc = fb.Desc.from_workload(w, dims)
