@@ -624,11 +624,13 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
     }
   __syncthreads();
 
-  floatx4 Wc[NGW][MB], Ws[NGW][MB];
+  // the moments in the rotating frame, then (in place) the split's W; zero
+  // for a wave without a split
+  floatx4 Vc[NGW][MB], Vs[NGW][MB];
 #pragma unroll
   for (int j = 0; j < NGW; ++j)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) Wc[j][mb] = Ws[j][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb) Vc[j][mb] = Vs[j][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if (active) {
     // the split's final reference of the lane's P rows (A layout)
@@ -713,11 +715,6 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
           }
         }
     };
-    floatx4 Vc[NGW][MB], Vs[NGW][MB];
-#pragma unroll
-    for (int j = 0; j < NGW; ++j)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) Vc[j][mb] = Vs[j][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
     load_p(0);
     for (int t = 0; t < nblk; ++t) {
       const int tau0 = tau_beg + t * TB;
@@ -790,8 +787,8 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
         }
       }
     }
-    // back to absolute phases: W = e^{i theta_f tau_last} V, tau_last the
-    // start of the last block (exact integer phase)
+    // back to absolute phases: W = e^{i theta_f tau_last} V (in place),
+    // tau_last the start of the last block (exact integer phase)
     const int tau_last = tau_beg + (nblk - 1) * TB;
 #pragma unroll
     for (int j = 0; j < NGW; ++j) {
@@ -803,8 +800,8 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float vc = Vc[j][mb][r], vs = Vs[j][mb][r];
-          Wc[j][mb][r] = fmaf(vc, cb, -vs * sb);
-          Ws[j][mb][r] = fmaf(vc, sb, vs * cb);
+          Vc[j][mb][r] = fmaf(vc, cb, -vs * sb);
+          Vs[j][mb][r] = fmaf(vc, sb, vs * cb);
         }
     }
     // relative to the row's maximum: W *= exp(m_split - m_row)
@@ -816,8 +813,8 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
         const float f = row < rows ? __expf(mfC[mb][r] - mg[row]) : 0.0f;
 #pragma unroll
         for (int j = 0; j < NGW; ++j) {
-          Wc[j][mb][r] *= f;
-          Ws[j][mb][r] *= f;
+          Vc[j][mb][r] *= f;
+          Vs[j][mb][r] *= f;
         }
       }
   }
@@ -829,8 +826,8 @@ __global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(Decode
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = mb * 16 + 4 * g4 + r;
-        red[(((wave * NGW + j) * 2 + 0) * MR + row) * 16 + l16] = Wc[j][mb][r];
-        red[(((wave * NGW + j) * 2 + 1) * MR + row) * 16 + l16] = Ws[j][mb][r];
+        red[(((wave * NGW + j) * 2 + 0) * MR + row) * 16 + l16] = Vc[j][mb][r];
+        red[(((wave * NGW + j) * 2 + 1) * MR + row) * 16 + l16] = Vs[j][mb][r];
       }
   __syncthreads();
   const int nent = ng * 2 * rows * 16;

@@ -209,19 +209,21 @@ fa_status_t plan_project(const Shape& sh, int nmat, ProjPlan* p) {
   if (!p->f16 || a.ncols == 0) return FA_OK;
   if (sh.Dc % 4) return fail(FA_ERR_SHAPE, "bf16 projection needs n_comp_dims %% 4 == 0 (got %d)", sh.Dc);
 
-  // Large square tiles (256 x 256) for large contractions; else tall tiles
-  // (512 coefficient rows x 64 columns), which load and convert each cache
-  // value once for all the coefficients of a small k.  Both are 8-wave
-  // blocks, one per CU.
+  // Large contractions: 256 x 128 tiles of 4-wave blocks, two per CU (each
+  // wave 64 coefficient rows of all 128 columns: no basis row is generated
+  // twice in a block; measured 5% faster than 256 x 256 tiles of 8 waves,
+  // whose column wave pairs generated the same rows).  Else tall tiles (512
+  // coefficient rows x 64 columns, 8 waves, one block per CU), which load and
+  // convert each cache value once for all the coefficients of a small k.
   double flops = 0.0;
   for (int b = 0; b < sh.B; ++b) flops += 2.0 * sh.M[b] * sh.k * a.ncols;
   const bool big = flops > 1.0e11;
   a.tk = big ? 256 : 512;
-  a.tn = big ? 256 : 64;
+  a.tn = big ? 128 : 64;
   a.nktiles = (sh.k + a.tk - 1) / a.tk;
   a.nctiles = (a.ncols + a.tn - 1) / a.tn;
   const int tiles = a.nktiles * a.nctiles;
-  const int slots = kNumCU;
+  const int slots = big ? 2 * kNumCU : kNumCU;
   int64_t total_steps = 0;
   for (int b = 0; b < sh.B; ++b) total_steps += (sh.M[b] + fa::kProjTT - 1) / fa::kProjTT;
   bool any_split = false;

@@ -12,10 +12,12 @@
 // convert to fp16 exactly for |x| in [2^-14, 65504], and the unscaled cos/sin
 // values in [-1, 1] keep 11 significant bits (bf16 would keep 8, which costs
 // an order of magnitude in coefficient accuracy).  Accumulation is fp32.
-// Two tilings: square 256 x 256 tiles for large contractions
-// (project_f16_kernel) and tall 512 x 64 tiles for a small k
-// (project_tall_kernel); long sequences are split over positions and the
-// partial tiles summed in a fixed order by project_reduce_kernel.
+// Two tilings: 256 x 128 tiles of 4-wave blocks, two per CU, for large
+// contractions (project_f16_kernel: each wave owns 64 coefficient rows of all
+// 128 columns, so every basis row is generated once per block) and tall
+// 512 x 64 tiles for a small k (project_tall_kernel); long sequences are split
+// over positions and the partial tiles summed in a fixed order by
+// project_reduce_kernel.
 //
 // Basis values along a lane's run of 32 consecutive positions come from the
 // three-term recurrence y(t+1) = 2 cos(theta) y(t) - y(t-1), seeded with two
@@ -741,13 +743,13 @@ int64_t edge_words(const EdgeArgs& a) {
 
 }  // namespace
 
-// Tile configurations of the 16-bit path: 256 x 256 square tiles for large
-// contractions, 512 x 64 tall tiles otherwise (both 8-wave blocks).
+// Tile configurations of the 16-bit path: 256 x 128 tiles of 4-wave blocks for
+// large contractions, 512 x 64 tall tiles of 8-wave blocks otherwise.
 hipError_t launch_project_f16(const ProjArgs& a, int nitems, hipStream_t s) {
   if (nitems == 0) return hipSuccess;
   const int blocks = (nitems + kXcds - 1) / kXcds * kXcds;
-  if (a.tk == 256 && a.tn == 256)
-    hipLaunchKernelGGL((project_f16_kernel<4, 2, 2, 4>), dim3(blocks), dim3(512), 0, s, a);
+  if (a.tk == 256 && a.tn == 128)
+    hipLaunchKernelGGL((project_f16_kernel<4, 1, 2, 4>), dim3(blocks), dim3(256), 0, s, a);
   else if (a.tk == kTallWaves * 64 && a.tn == kTallTN)
     hipLaunchKernelGGL((project_tall_kernel<2, 4>), dim3(blocks), dim3(64 * kTallWaves), 0, s, a);
   else

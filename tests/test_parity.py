@@ -291,7 +291,7 @@ def test_two_pass_shapes(fb, name):
 # streaming appends): P past every middle, for the fp32 kernels, the bf16
 # one-pass MFMA path (several tiles, ragged tails), the bf16 VALU path (exact
 # dims not a multiple of 8) and the two-pass path (long middles); the
-# projection's tall and square tiles.
+# projection's tall and large tiles.
 PERIOD = {
     "per_f32_gqa": (dict(dtype="f32", batch=3, n_q_heads=4, n_kv_heads=2, head_dim=16, n_comp=8,
                          n_coef=9, period=500), [200, 106, 333], None),
