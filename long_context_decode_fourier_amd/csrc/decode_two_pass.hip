@@ -556,9 +556,11 @@ constexpr ScoreVariant kScoreVariants[] = {
 };
 
 // ============================================================== pass 2 ====
-// MB: 16-row blocks; NGW: max frequency groups (of 16) per item.
+// MB: 16-row blocks; NGW: max frequency groups (of 16) per item.  Two
+// blocks per CU, as the planner's rounds assume: the bound keeps the kernel
+// within 256 registers (two waves per SIMD; unbounded it took 284, one wave).
 template <int MB, int NGW>
-__global__ __launch_bounds__(64 * kMomentWaves) void decode_moment_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(DecodeArgs a) {
   constexpr int NW = kMomentWaves, MR = 16 * MB, TT = kMomentTile;
   constexpr int TB = 64;  // tokens per block of the rotating frame
   extern __shared__ __attribute__((aligned(16))) float red[];  // [NW][NGW][2][MR][16], then mg[MR]
