@@ -650,9 +650,10 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     float rc[NGW], rs[NGW];
 #pragma unroll
     for (int j = 0; j < NGW; ++j) {
+      if (j >= ng) break;  // uniform: groups past the item's are never used
       // integer phases f t mod period: f < 2^13 and t < 64 keep every product in
       // 32 bits; consecutive offsets add f mod period
-      const int f = 16 * (gbeg + min(j, max(ng - 1, 0))) + l16;
+      const int f = 16 * (gbeg + j) + l16;
       const int fm = f % period;
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
@@ -699,12 +700,13 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
       for (int mb = 0; mb < MB; ++mb) mv = mv || mbase[moff[mb] + tau_beg / 16] != mfA[mb];
       moved_any = __any(mv);
     }
-    uint4 pn[MB][2];
-    float mn[MB][2];
-    // loads of block t, one block ahead: P (and, in a split whose reference
-    // moved, the references of the lane's 16-token tiles) together, so that
-    // the wait for them never covers the next block's loads
-    auto load_p = [&](int t) {
+    // loads of block t, one block ahead into the other of two register sets
+    // (blocks alternate between them, so no set is copied): P (and, in a split
+    // whose reference moved, the references of the lane's 16-token tiles)
+    // together, so that the wait for them never covers the next block's loads
+    uint4 pa[MB][2], pb[MB][2];
+    float ma[MB][2], mbr[MB][2];
+    auto load_p = [&](uint4 (&pn)[MB][2], float (&mn)[MB][2], int t) {
       const int tt = min(t, nblk - 1) * TB;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -717,8 +719,7 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
           }
         }
     };
-    load_p(0);
-    for (int t = 0; t < nblk; ++t) {
+    auto block = [&](int t, const uint4 (&pc)[MB][2], const float (&mc)[MB][2]) {
       const int tau0 = tau_beg + t * TB;
       half8 P[MB][2];
       float ms[MB][2];
@@ -726,10 +727,9 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          P[mb][kp] = __builtin_bit_cast(half8, pn[mb][kp]);
-          ms[mb][kp] = mn[mb][kp];
+          P[mb][kp] = __builtin_bit_cast(half8, pc[mb][kp]);
+          ms[mb][kp] = mc[mb][kp];
         }
-      load_p(t + 1);
       // tokens past the last written 16-token tile hold no probabilities
       if (tau0 + TB > m16) {
 #pragma unroll
@@ -788,13 +788,22 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
             }
         }
       }
+    };
+    load_p(pa, ma, 0);
+    for (int t = 0; t < nblk; t += 2) {
+      load_p(pb, mbr, t + 1);
+      block(t, pa, ma);
+      if (t + 1 >= nblk) break;  // uniform
+      load_p(pa, ma, t + 2);
+      block(t + 1, pb, mbr);
     }
     // back to absolute phases: W = e^{i theta_f tau_last} V (in place),
     // tau_last the start of the last block (exact integer phase)
     const int tau_last = tau_beg + (nblk - 1) * TB;
 #pragma unroll
     for (int j = 0; j < NGW; ++j) {
-      const int f = 16 * (gbeg + min(j, max(ng - 1, 0))) + l16;
+      if (j >= ng) break;  // uniform: the other groups stay zero
+      const int f = 16 * (gbeg + j) + l16;
       const float x = static_cast<float>(phase_mod(f, tau_last, period)) * inv_period;
       const float cb = cos_rev(x), sb = sin_rev(x);
 #pragma unroll
@@ -832,17 +841,21 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
         red[(((wave * NGW + j) * 2 + 1) * MR + row) * 16 + l16] = Vs[j][mb][r];
       }
   __syncthreads();
-  const int nent = ng * 2 * rows * 16;
+  // thread -> (row tid / 16 + 16 i, frequency lane tid % 16), over the groups
+  // and cosines / sines (no index division)
   float* wout = a.Wp + (static_cast<int64_t>(a.sgcum[b] + sg) * a.hq + qi0) * a.kpad;
-  for (int e = tid; e < nent; e += 64 * NW) {
-    const int fl = e % 16, row = (e / 16) % rows, cs = (e / (16 * rows)) % 2, j = e / (32 * rows);
-    float v = 0.0f;
+  const int fl = tid % 16;
+  for (int row = tid / 16; row < rows; row += 64 * NW / 16)
+    for (int j = 0; j < ng; ++j)
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[(((w * NGW + j) * 2 + cs) * MR + row) * 16 + fl];
-    const int f = 16 * (gbeg + j) + fl;
-    const int n = cs ? 2 * f : (f == 0 ? 0 : 2 * f - 1);
-    if (n < a.k && !(cs && f == 0)) wout[static_cast<int64_t>(row) * a.kpad + n] = v;
-  }
+      for (int cs = 0; cs < 2; ++cs) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += red[(((w * NGW + j) * 2 + cs) * MR + row) * 16 + fl];
+        const int f = 16 * (gbeg + j) + fl;
+        const int n = cs ? 2 * f : (f == 0 ? 0 : 2 * f - 1);
+        if (n < a.k && !(cs && f == 0)) wout[static_cast<int64_t>(row) * a.kpad + n] = v;
+      }
 }
 
 template <int MB, int NGW>
