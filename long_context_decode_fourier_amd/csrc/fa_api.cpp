@@ -22,6 +22,7 @@ namespace {
 constexpr int kNumCU = 256;         // MI355X compute units
 constexpr int kMaxCoef = 4097;      // decode keeps per-thread coefficient slots
 constexpr int kMaxHeadDim = 256;
+static_assert(kMaxHeadDim <= fa::kMaxAppendDc, "fa_append stages one compressible row of any head in LDS");
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 constexpr int kMinTiles = 3;            // preferred tiles per decode item (MFMA path)
