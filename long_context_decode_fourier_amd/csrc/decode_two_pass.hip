@@ -52,6 +52,16 @@
 namespace fa {
 namespace {
 
+// P16 layout (per sequence, a.ngroups * MB 16-row blocks of mpad tokens): block
+// g * MB + mb holds query rows g * rows + 16 mb + s (s < 16) of row group g, in
+// 32-token chunks of 1 KB, each in the A-operand order of
+// v_mfma_f32_16x16x32_f16 (lane s + 16 q holds tokens 8 q .. 8 q + 7 of row s),
+// so that pass 2 loads a chunk with one contiguous 16-byte load per lane.
+__device__ inline int64_t p16_index(int blk16, int slot, int tau, int mpad) {
+  return (static_cast<int64_t>(blk16) * (mpad / 32) + (tau >> 5)) * 512 + 8 * (slot + 16 * ((tau & 31) >> 3)) +
+         (tau & 7);
+}
+
 using namespace mfma;
 
 // LDS of pass 1: vx staging (double buffer), partial scores of each wave,
@@ -248,8 +258,9 @@ __global__ __launch_bounds__(64 * NW) void decode_score_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
   // probability and reference outputs of this slot's row
   const int orow = qi0 + min(s_row, rows - 1);
-  _Float16* p_out = static_cast<_Float16*>(a.P16) + a.hq * a.pcum[b] +
-                    static_cast<int64_t>(orow) * mpad + (t_begin - S) + s_tt;
+  // the slot's row in the P16 layout (token offsets added per tile)
+  _Float16* p_out = static_cast<_Float16*>(a.P16) + static_cast<int64_t>(a.ngroups) * MB * 16 * a.pcum[b] +
+                    p16_index(rg * MB + min(s_row, MR - 1) / 16, s_row % 16, 0, mpad);
   float* m_out = a.msub + a.hq * (a.pcum[b] / 16) + static_cast<int64_t>(orow) * (mpad / 16) + (t_begin - S) / 16;
 
   // ---- basis generator: lane -> token l16 of the tile and frequencies
@@ -400,7 +411,8 @@ __global__ __launch_bounds__(64 * NW) void decode_score_kernel(DecodeArgs a) {
       if (s_tt == 0) corr[s_row] = c;
       if (s_row < rows && a.dc > 0) {  // pass 2's input (no pass 2 without compressible dims)
         const int off = tile0 - t_begin;
-        p_out[off] = static_cast<_Float16>(p);
+        const int tau = tile0 - S + s_tt;
+        p_out[((tau >> 5) << 9) + (((tau >> 3) & 3) << 7) + (tau & 7)] = static_cast<_Float16>(p);
         if (s_tt == 0) m_out[off / T] = m_run;
       }
     }
@@ -677,17 +689,21 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     }
     const int tau_beg = sidx * chunk, tau_end = min(M, tau_beg + chunk);
     const int nblk = (tau_end - tau_beg + TB - 1) / TB;
-    const _Float16* pbase = static_cast<const _Float16*>(a.P16) + a.hq * a.pcum[b];
+    const _Float16* pbase =
+        static_cast<const _Float16*>(a.P16) + static_cast<int64_t>(a.ngroups) * MB * 16 * a.pcum[b];
     const float* mbase = a.msub + a.hq * (a.pcum[b] / 16);
-    // P operand: lane (row mb*16 + l16, tokens block + 32 kp + 8 g4 .. +7);
-    // rows past the group read its last row (never stored), blocks past the
-    // split read its last block (never used)
+    // P operand: lane (row mb*16 + l16, tokens block + 32 kp + 8 g4 .. +7),
+    // one contiguous KB per (16-row block, 32 tokens); rows past the group
+    // (never stored) are zeroed after the load, blocks past the split read its
+    // last block (never used)
     int64_t poff[MB], moff[MB];
+    bool row_ok[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int r = qi0 + min(mb * 16 + l16, rows - 1);
-      poff[mb] = static_cast<int64_t>(r) * mpad + tau_beg + 8 * g4;
+      poff[mb] = p16_index(rg * MB + mb, l16, tau_beg + 8 * g4, mpad);
       moff[mb] = static_cast<int64_t>(r) * (mpad / 16);
+      row_ok[mb] = mb * 16 + l16 < rows;
     }
     // References only grow inside a pass-1 split, so a row whose first tile
     // already has the split's final reference kept it throughout: when that
@@ -712,7 +728,7 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          pn[mb][kp] = *reinterpret_cast<const uint4*>(pbase + poff[mb] + tt + 32 * kp);
+          pn[mb][kp] = *reinterpret_cast<const uint4*>(pbase + poff[mb] + (tt / 32 + kp) * 512);
           if (moved_any) {
             const int tau = tau_beg + tt + 32 * kp + 8 * g4;
             mn[mb][kp] = mbase[moff[mb] + min(tau, m16 - 16) / 16];
@@ -730,6 +746,16 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
           P[mb][kp] = __builtin_bit_cast(half8, pc[mb][kp]);
           ms[mb][kp] = mc[mb][kp];
         }
+      // rows past the group hold no probabilities
+      if (rows < MR) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (!row_ok[mb]) P[mb][kp][e] = 0;
+      }
       // tokens past the last written 16-token tile hold no probabilities
       if (tau0 + TB > m16) {
 #pragma unroll

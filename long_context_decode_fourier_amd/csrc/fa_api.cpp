@@ -488,8 +488,10 @@ fa_status_t plan_decode(const Shape& sh, DecPlan* p) {
     }
     a.nitems2 = it;
     const size_t rows_all = static_cast<size_t>(sh.Hq);
+    // P16 in whole 16-row blocks of each row group
+    const size_t p16_rows = static_cast<size_t>(a.ngroups) * a.mb * 16;
     p->off_P16 = p->ws_bytes;
-    p->off_msub = p->off_P16 + align_up(rows_all * static_cast<size_t>(pc) * 2);
+    p->off_msub = p->off_P16 + align_up(p16_rows * static_cast<size_t>(pc) * 2);
     p->off_Wp = p->off_msub + align_up(rows_all * static_cast<size_t>(pc / 16) * sizeof(float));
     p->ws_bytes = p->off_Wp + align_up(static_cast<size_t>(sgc) * rows_all * a.kpad * sizeof(float));
   }
