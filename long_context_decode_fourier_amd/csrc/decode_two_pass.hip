@@ -27,14 +27,18 @@
 //   split 4 sg + w whole, with no barrier until the end, in blocks of 64
 //   tokens, in a frame that rotates with the block: with
 //   U_j[f] = sum_t P[tau_j + t] e^{i theta_f t} (t < 64) the moment of the
-//   split is W[f] = sum_j e^{i theta_f tau_j} U_j[f], accumulated as
-//   V <- V e^{-i theta_f 64} + U_j and turned back once at the end,
-//   W = e^{i theta_f tau_last} V (exact integer phase).  The table
-//   e^{i theta_f t} of the lane's 16 frequencies and 64 offsets is the same for
-//   every block, so it is generated once per item and held in registers as the
-//   B operand of v_mfma_f32_16x16x32_f16 (cosines and sines as two 16-column
-//   blocks; the MFMA accumulates U straight onto V); per block and 16
-//   frequencies only the frame rotation of V remains on the VALU.  The P
+//   split is W[f] = sum_j e^{i theta_f tau_j} U_j[f], that is
+//   W = e^{i theta_f tau_last} V with V_j = U_j + e^{-i theta_f 64} V_{j-1}
+//   (exact integer phase for tau_last).  V comes from the second-order
+//   recurrence s_j = U_j + 2 cos(theta_f 64) s_{j-1} - s_{j-2} on the cosine
+//   and sine parts, V_j = s_j - e^{i theta_f 64} s_{j-1}: one FMA per
+//   accumulator and block, where the frame rotation of V took four per pair;
+//   the recurrence restarts from its output every 16 blocks, which bounds the
+//   growth of its states.  The table e^{i theta_f t} of the lane's 16
+//   frequencies and 64 offsets is the same for every block, so it is
+//   generated once per item (negated) and held in registers as the B operand
+//   of v_mfma_f32_16x16x32_f16 (cosines and sines as two 16-column blocks; the
+//   MFMA subtracts U straight from the state s_{j-2}).  The P
 //   operand is loaded from P16 (the 4 waves of a split group and the slices
 //   of a split group read the same P, which stays in L2).  Each wave's W is
 //   relative to its split's reference; scaled by exp(m_split - m_row) (the
@@ -638,13 +642,15 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     }
   __syncthreads();
 
-  // the moments in the rotating frame, then (in place) the split's W; zero
-  // for a wave without a split
-  floatx4 Vc[NGW][MB], Vs[NGW][MB];
+  // the two states of the moments' recurrence in the rotating frame (sets V
+  // and S, whose roles alternate between blocks), then (in place in V) the
+  // split's W; zero for a wave without a split
+  floatx4 Vc[NGW][MB], Vs[NGW][MB], Sc[NGW][MB], Ss[NGW][MB];
 #pragma unroll
   for (int j = 0; j < NGW; ++j)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) Vc[j][mb] = Vs[j][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb)
+      Vc[j][mb] = Vs[j][mb] = Sc[j][mb] = Ss[j][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if (active) {
     // the split's final reference of the lane's P rows (A layout)
@@ -655,11 +661,12 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
       mfA[mb] = a.part[(prow + static_cast<int64_t>(r) * ns + sidx) * a.RS];
     }
     // Fixed basis table of the lane's frequencies f = 16 (gbeg + j) + l16 at
-    // the block offsets t = 32 kp + 8 g4 + e (the B operand layout), fp16, and
-    // the frame rotation e^{-i theta_f TB} between consecutive blocks
+    // the block offsets t = 32 kp + 8 g4 + e (the B operand layout), fp16 and
+    // negated (the MFMAs subtract U from a state), and e^{i theta_f TB}, the
+    // frame's turn from one block to the next
     const float inv_period = 1.0f / static_cast<float>(period);
     half8 Ec[NGW][2], Es[NGW][2];
-    float rc[NGW], rs[NGW];
+    float rc[NGW], rs[NGW], c2[NGW];
 #pragma unroll
     for (int j = 0; j < NGW; ++j) {
       if (j >= ng) break;  // uniform: groups past the item's are never used
@@ -677,8 +684,8 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
           ph = add_mod(ph, fm, period);
           const float x1 = static_cast<float>(ph) * inv_period;
           ph = add_mod(ph, fm, period);
-          pc[e2] = pack_f16(cos_rev(x0), cos_rev(x1));
-          ps[e2] = pack_f16(sin_rev(x0), sin_rev(x1));
+          pc[e2] = pack_f16(-cos_rev(x0), -cos_rev(x1));
+          ps[e2] = pack_f16(-sin_rev(x0), -sin_rev(x1));
         }
         Ec[j][kp] = __builtin_bit_cast(half8, make_uint4(pc[0], pc[1], pc[2], pc[3]));
         Es[j][kp] = __builtin_bit_cast(half8, make_uint4(ps[0], ps[1], ps[2], ps[3]));
@@ -686,6 +693,7 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
       const float xr = static_cast<float>((f * TB) % period) * inv_period;
       rc[j] = cos_rev(xr);
       rs[j] = sin_rev(xr);
+      c2[j] = 2.0f * rc[j];
     }
     const int tau_beg = sidx * chunk, tau_end = min(M, tau_beg + chunk);
     const int nblk = (tau_end - tau_beg + TB - 1) / TB;
@@ -735,7 +743,15 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
           }
         }
     };
-    auto block = [&](int t, const uint4 (&pc)[MB][2], const float (&mc)[MB][2]) {
+    // Block t of the split: U_t = sum_{i < TB} P[tau_t + i] e^{i theta_f i}
+    // (complex per row and frequency; cosine and sine parts), and the frame
+    // sum V_t = U_t + e^{-i theta_f TB} V_{t-1} through the second-order
+    // recurrence s_t = U_t + 2 cos(theta_f TB) s_{t-1} - s_{t-2} on each real
+    // part (s_{-1} = s_{-2} = 0), whose output is V_t = s_t - e^{i theta_f TB}
+    // s_{t-1}: one FMA per accumulator per block instead of a complex
+    // rotation.  D holds s_{t-2} and becomes s_t; O holds s_{t-1}.
+    auto block = [&](int t, const uint4 (&pc)[MB][2], const float (&mc)[MB][2], floatx4 (&Dc)[NGW][MB],
+                     floatx4 (&Ds)[NGW][MB], const floatx4 (&Oc)[NGW][MB], const floatx4 (&Os)[NGW][MB]) {
       const int tau0 = tau_beg + t * TB;
       half8 P[MB][2];
       float ms[MB][2];
@@ -793,36 +809,66 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
 #pragma unroll
       for (int j = 0; j < NGW; ++j) {
         if (j < ng) {
-          // V <- V e^{-i theta_f TB}: the frame moves to this block's start
-          if (t > 0) {
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float vc = Vc[j][mb][r], vs = Vs[j][mb][r];
-                Vc[j][mb][r] = fmaf(vc, rc[j], vs * rs[j]);
-                Vs[j][mb][r] = fmaf(vs, rc[j], -vc * rs[j]);
-              }
-          }
-          // V += P e^{i theta_f t}, t = 0 .. TB-1 (cosines, sines)
+          // D = s_{t-2} - U_t (the table is negated)
 #pragma unroll
           for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-              Vc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P[mb][kp], Ec[j][kp], Vc[j][mb], 0, 0, 0);
-              Vs[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P[mb][kp], Es[j][kp], Vs[j][mb], 0, 0, 0);
+              Dc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P[mb][kp], Ec[j][kp], Dc[j][mb], 0, 0, 0);
+              Ds[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P[mb][kp], Es[j][kp], Ds[j][mb], 0, 0, 0);
+            }
+          // s_t = 2 cos(theta_f TB) s_{t-1} - D
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              Dc[j][mb][r] = fmaf(c2[j], Oc[j][mb][r], -Dc[j][mb][r]);
+              Ds[j][mb][r] = fmaf(c2[j], Os[j][mb][r], -Ds[j][mb][r]);
             }
         }
       }
     };
+    // Out = L - e^{i theta_f TB} Q, the recurrence's output from its latest
+    // state L and the one before, Q (elementwise, so Out may be L or Q)
+    auto output = [&](const floatx4 (&Lc)[NGW][MB], const floatx4 (&Ls)[NGW][MB], const floatx4 (&Qc)[NGW][MB],
+                      const floatx4 (&Qs)[NGW][MB], floatx4 (&Oc)[NGW][MB], floatx4 (&Os)[NGW][MB]) {
+#pragma unroll
+      for (int j = 0; j < NGW; ++j) {
+        if (j >= ng) break;  // uniform
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float lc = Lc[j][mb][r], ls = Ls[j][mb][r], qc = Qc[j][mb][r], qs = Qs[j][mb][r];
+            Oc[j][mb][r] = fmaf(rs[j], qs, fmaf(-rc[j], qc, lc));
+            Os[j][mb][r] = fmaf(-rs[j], qc, fmaf(-rc[j], qs, ls));
+          }
+      }
+    };
+    // even blocks take s_t into V, odd blocks into S; every kMomentRun blocks
+    // (after an odd block) the recurrence restarts from its output (S <- V_t,
+    // V <- 0), which bounds the growth of its states (for theta_f TB near 0
+    // or pi they grow with the square of the blocks since the start)
     load_p(pa, ma, 0);
     for (int t = 0; t < nblk; t += 2) {
       load_p(pb, mbr, t + 1);
-      block(t, pa, ma);
+      block(t, pa, ma, Vc, Vs, Sc, Ss);
       if (t + 1 >= nblk) break;  // uniform
       load_p(pa, ma, t + 2);
-      block(t + 1, pb, mbr);
+      block(t + 1, pb, mbr, Sc, Ss, Vc, Vs);
+      if (t + 2 < nblk && (t + 2) % kMomentRun == 0) {  // uniform
+        output(Sc, Ss, Vc, Vs, Sc, Ss);
+#pragma unroll
+        for (int j = 0; j < NGW; ++j)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) Vc[j][mb] = Vs[j][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+    // V_last into V
+    if (nblk & 1)
+      output(Vc, Vs, Sc, Ss, Vc, Vs);
+    else
+      output(Sc, Ss, Vc, Vs, Vc, Vs);
     // back to absolute phases: W = e^{i theta_f tau_last} V (in place),
     // tau_last the start of the last block (exact integer phase)
     const int tau_last = tau_beg + (nblk - 1) * TB;
@@ -938,7 +984,7 @@ hipError_t launch_decode_score(const DecodeArgs& a, int nitems, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-int decode_moment_max_groups(int mb) { return mb > 1 ? 4 : 4; }
+int decode_moment_max_groups(int mb) { return mb > 1 ? 3 : 3; }
 
 size_t decode_moment_smem(int mb, int ngw) {
   return sizeof(float) * (static_cast<size_t>(kMomentWaves) * ngw * 2 * 16 * mb * 16 + 16 * mb);
@@ -946,8 +992,8 @@ size_t decode_moment_smem(int mb, int ngw) {
 
 hipError_t launch_decode_moment(const DecodeArgs& a, hipStream_t s) {
   if (a.nitems2 == 0) return hipSuccess;
-  if (a.mb > 1) return launch_moment_one<2, 4>(a, s);
-  return launch_moment_one<1, 4>(a, s);
+  if (a.mb > 1) return launch_moment_one<2, 3>(a, s);
+  return launch_moment_one<1, 3>(a, s);
 }
 
 }  // namespace fa
