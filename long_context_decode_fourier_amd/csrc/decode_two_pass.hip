@@ -609,28 +609,21 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
   const bool active = sidx < nsm;
   const int64_t prow = static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(qi0) * ns;
 
+  // The prologue's loads go out together and the basis table is generated
+  // while they are in flight: the row maxima, this wave's split references,
+  // the first tile references (whether any moved) and the first block's P.
+
   // maximum of every row over all its splits (the merge uses the same):
-  // 64 * NW / MR threads period row, each with its splits' loads all in flight
-  // before the first use, then a reduction over the row's lanes
-  {
-    constexpr int TPR = 64 * NW / MR;  // threads period row (a power of two <= 64)
-    constexpr int kLoads = 8;
-    const int row = tid / TPR, part = tid % TPR;
-    float m = -INFINITY;
-    if (row < rows) {
-      const float* pr = a.part + (prow + static_cast<int64_t>(row) * ns) * a.RS;
-      for (int j0 = part; j0 < ns; j0 += TPR * kLoads) {
-        float v[kLoads];
+  // 64 * NW / MR threads per row, each with its splits' loads all in flight
+  // before the first use (row and split indices clamped, so that every thread
+  // loads), then a reduction over the row's lanes
+  constexpr int TPR = 64 * NW / MR;  // threads per row (a power of two <= 64)
+  constexpr int kLoads = 8;
+  const int mrow = tid / TPR, mpart = tid % TPR;
+  const float* mpr = a.part + (prow + static_cast<int64_t>(min(mrow, rows - 1)) * ns) * a.RS;
+  float mv[kLoads];
 #pragma unroll
-        for (int u = 0; u < kLoads; ++u) v[u] = pr[static_cast<int64_t>(min(j0 + TPR * u, ns - 1)) * a.RS];
-#pragma unroll
-        for (int u = 0; u < kLoads; ++u) m = fmaxf(m, v[u]);
-      }
-    }
-#pragma unroll
-    for (int o = TPR / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    if (part == 0) mg[row] = m;
-  }
+  for (int u = 0; u < kLoads; ++u) mv[u] = mpr[static_cast<int64_t>(min(mpart + TPR * u, ns - 1)) * a.RS];
   // this wave's split: its final reference of the lane's output rows (C layout)
   float mfC[MB][4];
 #pragma unroll
@@ -640,7 +633,6 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
       const int row = min(mb * 16 + 4 * g4 + r, rows - 1);
       mfC[mb][r] = a.part[(prow + static_cast<int64_t>(row) * ns + min(sidx, nsm - 1)) * a.RS];
     }
-  __syncthreads();
 
   // the two states of the moments' recurrence in the rotating frame (sets V
   // and S, whose roles alternate between blocks), then (in place in V) the
@@ -652,21 +644,50 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     for (int mb = 0; mb < MB; ++mb)
       Vc[j][mb] = Vs[j][mb] = Sc[j][mb] = Ss[j][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // the split's tokens and P operand (set and used by active waves only):
+  // lane (row mb*16 + l16, tokens block + 32 kp + 8 g4 .. +7), one contiguous
+  // KB per (16-row block, 32 tokens); rows past the group (never stored) are
+  // zeroed after the load, blocks past the split read its last block (never
+  // used)
+  const int tau_beg = sidx * chunk, tau_end = min(M, tau_beg + chunk);
+  const int nblk = (tau_end - tau_beg + TB - 1) / TB;
+  const _Float16* pbase =
+      static_cast<const _Float16*>(a.P16) + static_cast<int64_t>(a.ngroups) * MB * 16 * a.pcum[b];
+  const float* mbase = a.msub + a.hq * (a.pcum[b] / 16);
+  int64_t poff[MB], moff[MB];
+  bool row_ok[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = qi0 + min(mb * 16 + l16, rows - 1);
+    poff[mb] = p16_index(rg * MB + mb, l16, tau_beg + 8 * g4, mpad);
+    moff[mb] = static_cast<int64_t>(r) * (mpad / 16);
+    row_ok[mb] = mb * 16 + l16 < rows;
+  }
+  // the split's final reference of the lane's P rows (A layout), the
+  // reference of the split's first tile, and block 0's P (two register sets
+  // of P alternate between blocks below; block 0 is in pa)
+  float mfA[MB], mfirst[MB];
+  uint4 pa[MB][2], pb[MB][2];
+  float ma[MB][2], mbr[MB][2];
   if (active) {
-    // the split's final reference of the lane's P rows (A layout)
-    float mfA[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int r = min(mb * 16 + l16, rows - 1);
       mfA[mb] = a.part[(prow + static_cast<int64_t>(r) * ns + sidx) * a.RS];
+      mfirst[mb] = mbase[moff[mb] + tau_beg / 16];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) pa[mb][kp] = *reinterpret_cast<const uint4*>(pbase + poff[mb] + kp * 512);
     }
-    // Fixed basis table of the lane's frequencies f = 16 (gbeg + j) + l16 at
-    // the block offsets t = 32 kp + 8 g4 + e (the B operand layout), fp16 and
-    // negated (the MFMAs subtract U from a state), and e^{i theta_f TB}, the
-    // frame's turn from one block to the next
-    const float inv_period = 1.0f / static_cast<float>(period);
-    half8 Ec[NGW][2], Es[NGW][2];
-    float rc[NGW], rs[NGW], c2[NGW];
+  }
+
+  // Fixed basis table of the lane's frequencies f = 16 (gbeg + j) + l16 at
+  // the block offsets t = 32 kp + 8 g4 + e (the B operand layout), fp16 and
+  // negated (the MFMAs subtract U from a state), and e^{i theta_f TB}, the
+  // frame's turn from one block to the next
+  const float inv_period = 1.0f / static_cast<float>(period);
+  half8 Ec[NGW][2], Es[NGW][2];
+  float rc[NGW], rs[NGW], c2[NGW];
+  if (active) {
 #pragma unroll
     for (int j = 0; j < NGW; ++j) {
       if (j >= ng) break;  // uniform: groups past the item's are never used
@@ -695,53 +716,64 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
       rs[j] = sin_rev(xr);
       c2[j] = 2.0f * rc[j];
     }
-    const int tau_beg = sidx * chunk, tau_end = min(M, tau_beg + chunk);
-    const int nblk = (tau_end - tau_beg + TB - 1) / TB;
-    const _Float16* pbase =
-        static_cast<const _Float16*>(a.P16) + static_cast<int64_t>(a.ngroups) * MB * 16 * a.pcum[b];
-    const float* mbase = a.msub + a.hq * (a.pcum[b] / 16);
-    // P operand: lane (row mb*16 + l16, tokens block + 32 kp + 8 g4 .. +7),
-    // one contiguous KB per (16-row block, 32 tokens); rows past the group
-    // (never stored) are zeroed after the load, blocks past the split read its
-    // last block (never used)
-    int64_t poff[MB], moff[MB];
-    bool row_ok[MB];
+  }
+
+  // the row maxima (splits past the first kLoads per thread in further rounds)
+  {
+    float m = -INFINITY;
+    if (mrow < rows) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int r = qi0 + min(mb * 16 + l16, rows - 1);
-      poff[mb] = p16_index(rg * MB + mb, l16, tau_beg + 8 * g4, mpad);
-      moff[mb] = static_cast<int64_t>(r) * (mpad / 16);
-      row_ok[mb] = mb * 16 + l16 < rows;
+      for (int u = 0; u < kLoads; ++u) m = fmaxf(m, mv[u]);
+      for (int j0 = mpart + TPR * kLoads; j0 < ns; j0 += TPR * kLoads) {
+        float v[kLoads];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) v[u] = mpr[static_cast<int64_t>(min(j0 + TPR * u, ns - 1)) * a.RS];
+#pragma unroll
+        for (int u = 0; u < kLoads; ++u) m = fmaxf(m, v[u]);
+      }
     }
+#pragma unroll
+    for (int o = TPR / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (mpart == 0) mg[mrow] = m;
+  }
+  __syncthreads();
+
+  if (active) {
     // References only grow inside a pass-1 split, so a row whose first tile
     // already has the split's final reference kept it throughout: when that
     // holds for every row of the wave, no tile needs rescaling and the
     // period-tile references are not read at all
     bool moved_any;
     {
-      bool mv = false;
+      bool mv_any = false;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) mv = mv || mbase[moff[mb] + tau_beg / 16] != mfA[mb];
-      moved_any = __any(mv);
+      for (int mb = 0; mb < MB; ++mb) mv_any = mv_any || mfirst[mb] != mfA[mb];
+      moved_any = __any(mv_any);
     }
     // loads of block t, one block ahead into the other of two register sets
     // (blocks alternate between them, so no set is copied): P (and, in a split
     // whose reference moved, the references of the lane's 16-token tiles)
     // together, so that the wait for them never covers the next block's loads
-    uint4 pa[MB][2], pb[MB][2];
-    float ma[MB][2], mbr[MB][2];
+    auto load_m = [&](float (&mn)[MB][2], int t) {
+      const int tt = min(t, nblk - 1) * TB;
+      if (moved_any) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            const int tau = tau_beg + tt + 32 * kp + 8 * g4;
+            mn[mb][kp] = mbase[moff[mb] + min(tau, m16 - 16) / 16];
+          }
+      }
+    };
     auto load_p = [&](uint4 (&pn)[MB][2], float (&mn)[MB][2], int t) {
       const int tt = min(t, nblk - 1) * TB;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
+        for (int kp = 0; kp < 2; ++kp)
           pn[mb][kp] = *reinterpret_cast<const uint4*>(pbase + poff[mb] + (tt / 32 + kp) * 512);
-          if (moved_any) {
-            const int tau = tau_beg + tt + 32 * kp + 8 * g4;
-            mn[mb][kp] = mbase[moff[mb] + min(tau, m16 - 16) / 16];
-          }
-        }
+      load_m(mn, t);
     };
     // Block t of the split: U_t = sum_{i < TB} P[tau_t + i] e^{i theta_f i}
     // (complex per row and frequency; cosine and sine parts), and the frame
@@ -849,7 +881,7 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     // (after an odd block) the recurrence restarts from its output (S <- V_t,
     // V <- 0), which bounds the growth of its states (for theta_f TB near 0
     // or pi they grow with the square of the blocks since the start)
-    load_p(pa, ma, 0);
+    load_m(ma, 0);  // block 0's P is in pa already
     for (int t = 0; t < nblk; t += 2) {
       load_p(pb, mbr, t + 1);
       block(t, pa, ma, Vc, Vs, Sc, Ss);
