@@ -572,6 +572,7 @@ constexpr ScoreVariant kScoreVariants[] = {
 };
 
 // ============================================================== pass 2 ====
+constexpr int kMomentRun = 16;  // 64-token blocks between restarts of the moment recurrence
 // MB: 16-row blocks; NGW: max frequency groups (of 16) per item.  Two
 // blocks per CU, as the planner's rounds assume: the bound keeps the kernel
 // within 256 registers (two waves per SIMD; unbounded it took 284, one wave).

@@ -172,7 +172,6 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s);
 // the (m, l, o_U) partials) and pass 2 (W = P phi into Wp).
 constexpr int kMomentTile = 128;   // tokens per pass-2 step of one wave
 constexpr int kMomentWaves = 4;    // pass-1 splits per split group (one wave each)
-constexpr int kMomentRun = 16;     // pass-2 blocks of 64 tokens between restarts of the moment recurrence
 struct ScoreVariant {
   int mb, maxu, pf, xp, xu, kcm, kpp_max;
 };
