@@ -1082,6 +1082,17 @@ constexpr int kMergeBatch = 32;  // split loads in flight per thread after the f
 constexpr int kMergeFirstDeep = 64;
 constexpr int kMergeFirstLean = 0;
 constexpr int kMergeDeepBlocks = 512;  // two 256-thread blocks per CU
+// Two-pass path: slices of 256 entries that hold any o_U / o_E entry (they
+// also sum the W entries among theirs), then blocks of kMergeWSlices slices of
+// W entries only.
+constexpr int kMergeWSlices = 4;
+__host__ __device__ inline int merge_vec_mixed_slices(const DecodeArgs& a) { return (a.du + a.dc + 255) / 256; }
+__host__ __device__ inline int merge_vec_slices(const DecodeArgs& a) {
+  const int nvec = a.du + a.dc + a.k;
+  if (!a.two_pass) return (nvec + 255) / 256;
+  const int y0 = merge_vec_mixed_slices(a);
+  return y0 + (nvec - 256 * y0 + 256 * kMergeWSlices - 1) / (256 * kMergeWSlices);
+}
 
 template <int FIRST>
 __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
@@ -1092,29 +1103,47 @@ __global__ __launch_bounds__(256) void decode_merge_vec_kernel(DecodeArgs a) {
   const int M = a.seq.mid[b], per = a.seq.per[b];
   const bool has_mid = a.dc > 0 && M > 0;
   const int nvec = a.du + a.dc + (has_mid ? a.k : 0);
-  const int idx = blockIdx.y * 256 + threadIdx.x;
-  if (blockIdx.y * 256 >= nvec) return;  // uniform per block
-  if (a.two_pass && blockIdx.y * 256 >= a.du + a.dc) {
-    // a block of W entries only: pass 2 has already scaled each split group's
-    // W to the row's maximum, so it needs no split weights: the groups'
-    // entries are summed in order, eight loads in flight (clamped indices,
-    // groups past the last add 0)
-    if (idx >= nvec) return;
-    const int n = idx - a.du - a.dc;
+  const int y0 = merge_vec_mixed_slices(a);
+  if (a.two_pass && static_cast<int>(blockIdx.y) >= y0) {
+    // kMergeWSlices slices of W entries only (entry 256 y0 + 256 (kMergeWSlices
+    // (blockIdx.y - y0) + q) + tid for slice q): pass 2 has already scaled each
+    // split group's W to the row's maximum, so it needs no split weights: the
+    // groups' entries are summed in order, eight loads per slice in flight
+    // (clamped indices, groups past the last add 0)
+    const int first = 256 * y0 + 256 * kMergeWSlices * (static_cast<int>(blockIdx.y) - y0);
+    if (first >= nvec) return;  // uniform per block (rows without middle have no W entries)
+    // from here nvec > 256 y0 >= du + dc, so every clamped entry below is a W entry
     const int nsg = (ns - a.edge_split + kMomentWaves - 1) / kMomentWaves;
-    const float* wp = a.Wp + (static_cast<int64_t>(a.sgcum[b]) * a.hq + i) * a.kpad + n;
     const int64_t sgs = static_cast<int64_t>(a.hq) * a.kpad;
-    float v = 0.0f;
+    const int e0 = first + threadIdx.x;
+    const float* wrow = a.Wp + (static_cast<int64_t>(a.sgcum[b]) * a.hq + i) * a.kpad;
+    float v[kMergeWSlices];
+#pragma unroll
+    for (int q = 0; q < kMergeWSlices; ++q) v[q] = 0.0f;
     for (int sg0 = 0; sg0 < nsg; sg0 += 8) {
-      float x[8];
+      float x[kMergeWSlices][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = wp[static_cast<int64_t>(min(sg0 + j, nsg - 1)) * sgs];
+      for (int q = 0; q < kMergeWSlices; ++q) {
+        const int n = min(e0 + 256 * q, nvec - 1) - a.du - a.dc;  // clamped: past nvec stores nothing
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v += (sg0 + j < nsg) ? x[j] : 0.0f;
+        for (int j = 0; j < 8; ++j) x[q][j] = wrow[static_cast<int64_t>(min(sg0 + j, nsg - 1)) * sgs + n];
+      }
+#pragma unroll
+      for (int q = 0; q < kMergeWSlices; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[q] += (sg0 + j < nsg) ? x[q][j] : 0.0f;
     }
-    a.mrg[static_cast<int64_t>(row) * a.MS + a.dc + n] = v * basis_alpha(n, per);
+#pragma unroll
+    for (int q = 0; q < kMergeWSlices; ++q) {
+      const int e = e0 + 256 * q;
+      if (e >= nvec) break;
+      const int n = e - a.du - a.dc;
+      a.mrg[static_cast<int64_t>(row) * a.MS + a.dc + n] = v[q] * basis_alpha(n, per);
+    }
     return;
   }
+  const int idx = blockIdx.y * 256 + threadIdx.x;
+  if (blockIdx.y * 256 >= nvec) return;  // uniform per block
   const float* P = a.part + (static_cast<int64_t>(a.prow0[b]) + static_cast<int64_t>(i) * ns) * a.RS;
   // The entry this thread sums (threads past nvec load the last one and
   // store nothing) and the splits that hold it: with edge splits (the last
@@ -1427,8 +1456,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, int nitems, hipStream_t s) {
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
   int max_splits = 1;
   for (int b = 0; b < a.nseq; ++b) max_splits = max(max_splits, a.seq.nsplit[b]);
-  const int nvec = a.du + a.dc + a.k;
-  const dim3 vgrid(a.nseq * a.hq, (nvec + 255) / 256);
+  const dim3 vgrid(a.nseq * a.hq, merge_vec_slices(a));
   const size_t vsm = sizeof(float) * max_splits;
   hipError_t e;
   if (static_cast<int64_t>(vgrid.x) * vgrid.y <= kMergeDeepBlocks) {
