@@ -287,6 +287,45 @@ def test_two_pass_shapes(fb, name):
     _full_check(fb, w)
 
 
+def _plant_tones(w, freqs):
+    """Add cos(2 pi f tau / M_b) for every f in freqs to each compressible value
+    dim of the middle rows, rounded to bf16 again (the oracle and the library
+    read the same cache)."""
+    c = w.cfg
+    vc = w.vc.copy()
+    for b in range(c.batch):
+        M = w.mid_len(b)
+        if M == 0:
+            continue
+        tau = np.arange(M, dtype=np.int64)
+        tone = sum(np.cos(2.0 * np.pi * ((f * tau) % M) / M) for f in freqs).astype(np.float32)
+        for h in range(c.n_kv_heads):
+            r = w.row0(b, h) + c.sink
+            vc[r:r + M] = wl.bf16_bits(wl.bf16_to_f32(vc[r:r + M]) + tone[:, None])
+    w.vc = vc
+
+
+# Pass 2 sums each split's value moments through the second-order recurrence
+# in 2 cos(64 theta_f) (64-token blocks), restarted every 16 blocks; its
+# states grow fastest where 64 theta_f is a multiple of pi.  With M = 16000
+# that holds at f = 125, 375 (pi) and f = 250, 500 (0); unit tones at those
+# frequencies in the values carry the moments there into the outputs.  Twenty
+# sequences give pass-1 splits of 1408 tokens (22 blocks: one restart and a
+# short last split per sequence), on the 8-row (one 16-row block) variant.
+def test_two_pass_degenerate_frequencies(fb):
+    name = "tp_degenerate_frequencies"
+    cfg = wl.custom(name=name, seed=251, dtype="bf16", batch=20, n_q_heads=8, n_kv_heads=2,
+                    head_dim=128, n_comp=64, n_coef=1025)
+    _say("case %s lens=20 x 16096 tones f = 125, 250, 375, 500" % name)
+    w = wl.make(cfg, lens=[16096] * 20)
+    _plant_tones(w, (125, 250, 375, 500))
+    plan = fb.attend_plan(fb.Desc.from_workload(w))
+    _say("  plan %s" % plan)
+    assert (plan["rows"], plan["path"]) == (8, "two_pass")
+    assert plan["items"] == 240  # 12 splits of 1408 middle tokens per sequence
+    _full_check(fb, w)
+
+
 # A fixed basis period P (the descriptor's period field, the basis of
 # streaming appends): P past every middle, for the fp32 kernels, the bf16
 # one-pass MFMA path (several tiles, ragged tails), the bf16 VALU path (exact
