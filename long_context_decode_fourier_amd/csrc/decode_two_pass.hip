@@ -575,7 +575,8 @@ constexpr ScoreVariant kScoreVariants[] = {
 constexpr int kMomentRun = 16;  // 64-token blocks between restarts of the moment recurrence
 // MB: 16-row blocks; NGW: max frequency groups (of 16) per item.  Two
 // blocks per CU, as the planner's rounds assume: the bound keeps the kernel
-// within 256 registers (two waves per SIMD; unbounded it took 284, one wave).
+// within 256 registers (two waves per SIMD); with NGW = 3 both state sets of
+// the moment recurrence, the table and two sets of P fit in them.
 template <int MB, int NGW>
 __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(DecodeArgs a) {
   constexpr int NW = kMomentWaves, MR = 16 * MB, TT = kMomentTile;
