@@ -666,11 +666,10 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     row_ok[mb] = mb * 16 + l16 < rows;
   }
   // the split's final reference of the lane's P rows (A layout), the
-  // reference of the split's first tile, and block 0's P (two register sets
-  // of P alternate between blocks below; block 0 is in pa)
+  // reference of the split's first tile, and block 0's P (three register sets
+  // of P rotate between blocks below; block 0 is in pa)
   float mfA[MB], mfirst[MB];
-  uint4 pa[MB][2], pb[MB][2];
-  float ma[MB][2], mbr[MB][2];
+  uint4 pa[MB][2], pb[MB][2], pq[MB][2];
   if (active) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -752,10 +751,8 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
       for (int mb = 0; mb < MB; ++mb) mv_any = mv_any || mfirst[mb] != mfA[mb];
       moved_any = __any(mv_any);
     }
-    // loads of block t, one block ahead into the other of two register sets
-    // (blocks alternate between them, so no set is copied): P (and, in a split
-    // whose reference moved, the references of the lane's 16-token tiles)
-    // together, so that the wait for them never covers the next block's loads
+    // the references of the lane's 16-token tiles of block t (a split whose
+    // reference moved) and block t's P operand
     auto load_m = [&](float (&mn)[MB][2], int t) {
       const int tt = min(t, nblk - 1) * TB;
       if (moved_any) {
@@ -768,14 +765,13 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
           }
       }
     };
-    auto load_p = [&](uint4 (&pn)[MB][2], float (&mn)[MB][2], int t) {
+    auto load_p = [&](uint4 (&pn)[MB][2], int t) {
       const int tt = min(t, nblk - 1) * TB;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
           pn[mb][kp] = *reinterpret_cast<const uint4*>(pbase + poff[mb] + (tt / 32 + kp) * 512);
-      load_m(mn, t);
     };
     // Block t of the split: U_t = sum_{i < TB} P[tau_t + i] e^{i theta_f i}
     // (complex per row and frequency; cosine and sine parts), and the frame
@@ -784,18 +780,14 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     // part (s_{-1} = s_{-2} = 0), whose output is V_t = s_t - e^{i theta_f TB}
     // s_{t-1}: one FMA per accumulator per block instead of a complex
     // rotation.  D holds s_{t-2} and becomes s_t; O holds s_{t-1}.
-    auto block = [&](int t, const uint4 (&pc)[MB][2], const float (&mc)[MB][2], floatx4 (&Dc)[NGW][MB],
-                     floatx4 (&Ds)[NGW][MB], const floatx4 (&Oc)[NGW][MB], const floatx4 (&Os)[NGW][MB]) {
+    auto block = [&](int t, const uint4 (&pc)[MB][2], floatx4 (&Dc)[NGW][MB], floatx4 (&Ds)[NGW][MB],
+                     const floatx4 (&Oc)[NGW][MB], const floatx4 (&Os)[NGW][MB]) {
       const int tau0 = tau_beg + t * TB;
       half8 P[MB][2];
-      float ms[MB][2];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-          P[mb][kp] = __builtin_bit_cast(half8, pc[mb][kp]);
-          ms[mb][kp] = mc[mb][kp];
-        }
+        for (int kp = 0; kp < 2; ++kp) P[mb][kp] = __builtin_bit_cast(half8, pc[mb][kp]);
       // rows past the group hold no probabilities
       if (rows < MR) {
 #pragma unroll
@@ -817,7 +809,10 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
               for (int e = 0; e < 8; ++e) P[mb][kp][e] = 0;
       }
       // 16-token tiles whose reference moved later in their split: rescale
+      // (their references read here, when needed: rare with the lazy reference)
       if (moved_any) {
+        float ms[MB][2];
+        load_m(ms, t);
         float fs[MB][2];
         bool moved = false;
 #pragma unroll
@@ -883,20 +878,41 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     // (after an odd block) the recurrence restarts from its output (S <- V_t,
     // V <- 0), which bounds the growth of its states (for theta_f TB near 0
     // or pi they grow with the square of the blocks since the start)
-    load_m(ma, 0);  // block 0's P is in pa already
-    for (int t = 0; t < nblk; t += 2) {
-      load_p(pb, mbr, t + 1);
-      block(t, pa, ma, Vc, Vs, Sc, Ss);
-      if (t + 1 >= nblk) break;  // uniform
-      load_p(pa, ma, t + 2);
-      block(t + 1, pb, mbr, Sc, Ss, Vc, Vs);
-      if (t + 2 < nblk && (t + 2) % kMomentRun == 0) {  // uniform
+    // after an odd block t (S holds s_t): restart every kMomentRun blocks
+    auto restart = [&](int t) {
+      if (t + 1 < nblk && (t + 1) % kMomentRun == 0) {  // uniform
         output(Sc, Ss, Vc, Vs, Sc, Ss);
 #pragma unroll
         for (int j = 0; j < NGW; ++j)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) Vc[j][mb] = Vs[j][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
+    };
+    // P two blocks ahead in three register sets (block t in set t % 3; block
+    // 0's is in pa already), six blocks per round so that the sets and the
+    // state roles come back to their places
+    load_p(pb, 1);
+    for (int t = 0; t < nblk; t += 6) {
+      load_p(pq, t + 2);
+      block(t, pa, Vc, Vs, Sc, Ss);
+      if (t + 1 >= nblk) break;  // uniform
+      load_p(pa, t + 3);
+      block(t + 1, pb, Sc, Ss, Vc, Vs);
+      restart(t + 1);
+      if (t + 2 >= nblk) break;
+      load_p(pb, t + 4);
+      block(t + 2, pq, Vc, Vs, Sc, Ss);
+      if (t + 3 >= nblk) break;
+      load_p(pq, t + 5);
+      block(t + 3, pa, Sc, Ss, Vc, Vs);
+      restart(t + 3);
+      if (t + 4 >= nblk) break;
+      load_p(pa, t + 6);
+      block(t + 4, pb, Vc, Vs, Sc, Ss);
+      if (t + 5 >= nblk) break;
+      load_p(pb, t + 7);
+      block(t + 5, pq, Sc, Ss, Vc, Vs);
+      restart(t + 5);
     }
     // V_last into V
     if (nblk & 1)
