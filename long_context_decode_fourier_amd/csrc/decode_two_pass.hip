@@ -743,7 +743,7 @@ __global__ __launch_bounds__(64 * kMomentWaves, 2) void decode_moment_kernel(Dec
     // References only grow inside a pass-1 split, so a row whose first tile
     // already has the split's final reference kept it throughout: when that
     // holds for every row of the wave, no tile needs rescaling and the
-    // period-tile references are not read at all
+    // per-tile references are not read at all
     bool moved_any;
     {
       bool mv_any = false;
